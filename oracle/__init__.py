@@ -1,0 +1,187 @@
+"""CPU oracle for the MXFP4 hot path -- TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct definition of MXFP4 block quantization
+(OCP Microscaling Formats v1.0, E2M1 elements with an E8M0 scale per 32
+elements) and of the block-scaled NT GEMM that consumes the blobs, written in
+plain C (``mx_oracle.c``) and wrapped here with ctypes and numpy.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``mxfp4_precision_amd``) never imports, links or calls it, and the two share
+no code: only the seeded input generators (``mxfp4_precision_amd.synth``, which
+hold none of the method's arithmetic) feed both.
+
+Pins (what checks this oracle against something other than itself) live in
+``tests/test_oracle_*.py``.  Every oracle function has at least one pin; the
+list is kept in the design notes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mx_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+BLOCK = 32
+PAD = 128
+
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_u32 = ctypes.c_uint32
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+
+
+def build(force: bool = False) -> str:
+    """Compile mx_oracle.c with gcc (plain C, OpenMP over independent rows)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_quantize.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _u64, _u32, _u64, _vp, _vp]
+        L.oracle_quantize.restype = _int
+        L.oracle_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp]
+        L.oracle_dequantize.restype = _int
+        L.oracle_gemm_entries.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp]
+        L.oracle_gemm_entries.restype = _int
+        L.oracle_gemm_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]
+        L.oracle_gemm_rows.restype = _int
+        L.oracle_bf16_from_double_array.argtypes = [_vp, _i64, _vp]
+        L.oracle_bf16_from_double_array.restype = None
+        L.oracle_philox4x32_10.argtypes = [_vp, _vp, _vp]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_sr_byte.argtypes = [_u64, _u32, _u32, _u64]
+        L.oracle_sr_byte.restype = ctypes.c_uint
+        L.oracle_to_tiled.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+        L.oracle_to_tiled.restype = _int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def padded(n: int) -> int:
+    """Length of a quantized axis after padding to a multiple of 128."""
+    return cdiv(n, PAD) * PAD
+
+
+def blob_shapes(rows: int, length: int) -> Tuple[Tuple[int, int], Tuple[int, int]]:
+    """Canonical (data, scale) byte shapes for `rows` blob rows quantized along `length`."""
+    lp = padded(length)
+    return (rows, lp // 2), (rows, lp // BLOCK)
+
+
+def quantize(x: np.ndarray, direction: int, use_2d: bool = False, use_sr: bool = False,
+             seed: int = 0, tensor_id: int = 0, index_base: int = 0):
+    """Quantize bf16 bits x (M x N uint16) row-wise (direction 0) or column-wise (1).
+
+    Returns canonical (q, s) uint8 arrays: direction 0 -> (M, N_pad/2), (M, N_pad/32);
+    direction 1 -> (N, M_pad/2), (N, M_pad/32).
+    """
+    assert x.dtype == np.uint16 and x.ndim == 2
+    x = np.ascontiguousarray(x)
+    M, N = x.shape
+    rows, length = (M, N) if direction == 0 else (N, M)
+    qs, ss = blob_shapes(rows, length)
+    q = np.zeros(qs, dtype=np.uint8)
+    s = np.zeros(ss, dtype=np.uint8)
+    rc = lib().oracle_quantize(_ptr(x), M, N, N, direction, int(use_2d), int(use_sr),
+                               seed, tensor_id, index_base, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize rejected its arguments")
+    return q, s
+
+
+def dequantize(q: np.ndarray, s: np.ndarray, rows: int, length: int) -> np.ndarray:
+    """Exact fp64 values of a canonical blob, shape (rows, L_pad)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    assert q.shape == blob_shapes(rows, length)[0] and s.shape == blob_shapes(rows, length)[1]
+    out = np.empty((rows, padded(length)), dtype=np.float64)
+    lib().oracle_dequantize(_ptr(q), _ptr(s), rows, length, _ptr(out))
+    return out
+
+
+def gemm_entries(qa, sa, qb, sb, M: int, N: int, K: int, ii, jj) -> np.ndarray:
+    """fp64 C[ii[t], jj[t]] of C = deq(A) . deq(B)^T over the padded K."""
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    out = np.empty(ii.shape[0], dtype=np.float64)
+    qa, sa, qb, sb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qa, sa, qb, sb))
+    lib().oracle_gemm_entries(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K,
+                              ii.shape[0], _ptr(ii), _ptr(jj), _ptr(out))
+    return out
+
+
+def gemm_rows(qa, sa, qb, sb, M: int, N: int, K: int, i0: int, i1: int) -> np.ndarray:
+    """fp64 rows [i0, i1) of C = deq(A) . deq(B)^T."""
+    out = np.empty((i1 - i0, N), dtype=np.float64)
+    qa, sa, qb, sb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qa, sa, qb, sb))
+    rc = lib().oracle_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, i0, i1, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_gemm_rows rejected its arguments")
+    return out
+
+
+def bf16_from_double(a) -> np.ndarray:
+    """Correctly rounded (RNE) fp64 -> bf16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    lib().oracle_bf16_from_double_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    assert c.shape == (4,) and k.shape == (2,)
+    out = np.empty(4, dtype=np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sr_byte(seed: int, tensor_id: int, direction: int, n: int) -> int:
+    return int(lib().oracle_sr_byte(seed, tensor_id, direction, n))
+
+
+def tiled_shapes(rows: int, length: int) -> Tuple[int, int]:
+    """Byte sizes (data, scale) of the tiled layout."""
+    lp = padded(length)
+    r16 = cdiv(rows, 16) * 16
+    return r16 * lp // 2, r16 * cdiv(lp, 512) * 16
+
+
+def to_tiled(q: np.ndarray, s: np.ndarray, rows: int, length: int):
+    """Canonical blob -> the library's tiled layout (flat uint8 arrays)."""
+    dq, ds = tiled_shapes(rows, length)
+    qt = np.empty(dq, dtype=np.uint8)
+    st = np.empty(ds, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    lib().oracle_to_tiled(_ptr(q), _ptr(s), rows, length, _ptr(qt), _ptr(st))
+    return qt, st
