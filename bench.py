@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark: one MXFP4 linear-layer training step on MI355X (gfx950).
+
+A step is the whole hot path once, on the Flux-12B MLP fc2 shape
+(tokens 18432, in 12288, out 3072):
+  dual-quantize X (1D, RNE)  dual-quantize W (32x32 2D blocks, RNE)
+  GEMM fwd    Y  = X_row  . W_row^T        (18432 x 3072,  K 12288)
+  dual-quantize dY (stochastic rounding, seed 7, tensor id 2)
+  GEMM dgrad  dX = dY_row . W_col^T        (18432 x 12288, K 3072)
+  GEMM wgrad  dW = dY_col . X_col^T        (3072 x 12288,  K 18432)
+All blobs in the tiled layout, bf16 outputs, fp32 accumulation.  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line: value = GEMM TFLOP/s of the whole step (3 GEMMs' flops
+over the step's wall time), per-kernel timings from HIP events on the launch
+stream, a roofline object for the dominant kernel (the GEMM, dense MXFP4 MFMA
+peak) and one for the dual quantizer (HBM), and the CPU oracle timed on a
+bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "a4w4 GEMM TFLOP/s + dual-quantize GB/s (% roofline), Flux-12B-shaped linears"
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--tokens", type=int, default=18432)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=32,
+                   help="token slice of the step the CPU oracle is timed on")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_precision_amd as mx
+    from mxfp4_precision_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mx.lib()   # raises if libmxfp4.so is missing: there is no fallback
+    dev = torch.device("cuda:0")
+    T = mx.MX_LAYOUT_TILED
+
+    tokens, din, dout = args.tokens, 12288, 3072
+    t0 = time.time()
+    data = synth.fc2(tokens=tokens)
+    gen_s = time.time() - t0
+    X = torch.from_numpy(data["X"].view(np.int16)).to(dev)
+    W = torch.from_numpy(data["W"].view(np.int16)).to(dev)
+    dY = torch.from_numpy(data["dY"].view(np.int16)).to(dev)
+
+    def blob(rows, length):
+        return mx.empty_blob(rows, length, T, dev)
+
+    Xr, Xrs = blob(tokens, din); Xc, Xcs = blob(din, tokens)
+    Wr, Wrs = blob(dout, din); Wc, Wcs = blob(din, dout)
+    Gr, Grs = blob(tokens, dout); Gc, Gcs = blob(dout, tokens)
+    Y = torch.empty((tokens, dout), dtype=torch.int16, device=dev)
+    dX = torch.empty((tokens, din), dtype=torch.int16, device=dev)
+    dW = torch.empty((dout, din), dtype=torch.int16, device=dev)
+
+    o_plain = mx.quant_opts()
+    o_w = mx.quant_opts(use_2d_block=True, tensor_id=1)
+    o_g = mx.quant_opts(use_sr=True, seed=7, tensor_id=2)
+    stream = torch.cuda.current_stream()
+
+    names = ["quant_X", "quant_W", "gemm_fwd", "quant_dY", "gemm_dgrad", "gemm_wgrad"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        mx.mx_quantize_dual(X, tokens, din, din, o_plain, o_plain, T, Xr, Xrs, Xc, Xcs, stream)
+        mark(1)
+        mx.mx_quantize_dual(W, dout, din, din, o_w, o_w, T, Wr, Wrs, Wc, Wcs, stream)
+        mark(2)
+        mx.mx_gemm_a4w4(0, 1, tokens, dout, din, Xr, Xrs, Wr, Wrs, T, mx.MX_BF16, Y, dout, stream)
+        mark(3)
+        mx.mx_quantize_dual(dY, tokens, dout, dout, o_g, o_g, T, Gr, Grs, Gc, Gcs, stream)
+        mark(4)
+        mx.mx_gemm_a4w4(0, 1, tokens, din, dout, Gr, Grs, Wc, Wcs, T, mx.MX_BF16, dX, din, stream)
+        mark(5)
+        mx.mx_gemm_a4w4(0, 1, dout, din, tokens, Gc, Gcs, Xc, Xcs, T, mx.MX_BF16, dW, din, stream)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps, wall clock between synchronizations.
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = 1e3 * wall / args.steps
+
+    # Per-kernel durations: events recorded between launches on the launch stream.
+    evsets = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evsets[k])
+    torch.cuda.synchronize()
+    per = {n: float(np.mean([evs[i].elapsed_time(evs[i + 1]) for evs in evsets])) for i, n in enumerate(names)}
+
+    gemm_shapes = {"gemm_fwd": (tokens, dout, din), "gemm_dgrad": (tokens, din, dout),
+                   "gemm_wgrad": (dout, din, tokens)}
+    flops = {n: 2.0 * m * n_ * k for n, (m, n_, k) in gemm_shapes.items()}
+    step_flops = sum(flops.values())
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    def qbytes(M, N):
+        d1, s1 = mx.mx_blob_bytes(M, N, T)
+        d2, s2 = mx.mx_blob_bytes(N, M, T)
+        return 2.0 * M * N + d1 + s1 + d2 + s2
+    qb = {"quant_X": qbytes(tokens, din), "quant_W": qbytes(dout, din), "quant_dY": qbytes(tokens, dout)}
+
+    kernels = {}
+    for n in names:
+        entry = {"ms": round(per[n], 5)}
+        if n in flops:
+            entry["TFLOP/s"] = round(flops[n] / (per[n] * 1e-3) / 1e12, 1)
+            entry["frac_fp4_peak"] = round(flops[n] / (per[n] * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)
+        else:
+            entry["GB/s"] = round(qb[n] / (per[n] * 1e-3) / 1e9, 1)
+            entry["frac_hbm_peak"] = round(qb[n] / (per[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        kernels[n] = entry
+
+    # Dominant kernel: the GEMM (one kernel, three launches of equal flops per launch).
+    gemm_ms = float(np.mean([per[n] for n in gemm_shapes]))
+    gemm_achieved = (step_flops / 3) / (gemm_ms * 1e-3) / 1e12
+    # Dual quantizer roofline on the largest launch (X: 18432 x 12288).
+    qx_gbs = qb["quant_X"] / (per["quant_X"] * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4 (e2m1 x e2m1, e8m0 scales, fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded numpy PCG64, Flux-12B MLP fc2 shapes; random values, no weights)",
+        "config": {"workload": "MLP fc2 train step: X %dx%d GELU(N(0,1)), W %dx%d N(0,0.02) 2D-block, "
+                               "dY %dx%d N(0,1e-3) SR; dual quantize x3 + fwd/dgrad/wgrad a4w4 GEMMs"
+                               % (tokens, din, dout, din, tokens, dout),
+                   "tokens": tokens, "in_features": din, "out_features": dout,
+                   "layout": "tiled", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "mx_gemm_a4w4", "bound": "mfma",
+                     "achieved": round(gemm_achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_achieved / PEAK_FP4_TFLOPS, 4), "traffic": None},
+        "roofline_quantize": {"kernel": "mx_quantize_dual (X %dx%d)" % (tokens, din), "bound": "hbm",
+                              "achieved": round(qx_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(qx_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernels": kernels,
+        "input_gen_s": round(gen_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(data, args.cpu_tokens, din, dout)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(data, ct, din, dout):
+    """The CPU oracle, as it stands, on the first `ct` tokens of the same step:
+    dual-quantize X[:ct], W (2D) and dY[:ct] (SR), then the three GEMMs of that
+    slice (fwd and dgrad rows of the slice, wgrad over the slice's tokens)."""
+    import oracle
+    oracle.build()
+    x = np.ascontiguousarray(data["X"][:ct])
+    w = data["W"]
+    g = np.ascontiguousarray(data["dY"][:ct])
+    t0 = time.perf_counter()
+    xr = oracle.quantize(x, 0)
+    xc = oracle.quantize(x, 1)
+    wr = oracle.quantize(w, 0, use_2d=True, tensor_id=1)
+    wc = oracle.quantize(w, 1, use_2d=True, tensor_id=1)
+    gr = oracle.quantize(g, 0, use_sr=True, seed=7, tensor_id=2)
+    gc = oracle.quantize(g, 1, use_sr=True, seed=7, tensor_id=2)
+    oracle.gemm_rows(xr[0], xr[1], wr[0], wr[1], ct, dout, din, 0, ct)
+    oracle.gemm_rows(gr[0], gr[1], wc[0], wc[1], ct, din, dout, 0, ct)
+    oracle.gemm_rows(gc[0], gc[1], xc[0], xc[1], dout, din, ct, 0, dout)
+    dt = time.perf_counter() - t0
+    fl = 2.0 * ct * din * dout * 3
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "fc2 step on a %d-token slice (X %dx%d, W %dx%d, dY %dx%d): oracle dual "
+                      "quantize of all three + the slice's fwd, dgrad and wgrad GEMMs in fp64"
+                      % (ct, ct, din, dout, din, ct, dout)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+/*
+ * mxfp4.h -- C ABI of libmxfp4: MXFP4 block quantization of bf16 tensors and
+ * the block-scaled FP4 x FP4 ("a4w4") GEMM that consumes the blobs, for
+ * MI355X (gfx950).
+ *
+ * Formats follow the OCP Microscaling Formats (MX) Specification v1.0:
+ * 32-element blocks, one E8M0 scale byte per block (2^(byte-127), 0xFF = NaN)
+ * and E2M1 elements (sign, 2 exponent bits, 1 mantissa bit: magnitudes
+ * 0, .5, 1, 1.5, 2, 3, 4, 6).  Blob shapes, the 128-padding of the quantized
+ * axis and the row/col option triplets follow the page
+ * "primus_turbo_mxfp4_local.py" (ROCm docs download of Primus): its fake
+ * (shape-only) dual-quantize op and the arguments of its dual-quantize and
+ * FP4 GEMM calls.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors live in device memory the caller owns; the library allocates
+ *    nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously.  Returned status reflects argument validation and
+ *    the launch only; kernels never report errors after launch.
+ *  - Validation happens before any launch.  Nothing is written on error, and
+ *    there is no fallback path: an unsupported request is an error.
+ *  - Sizes are element counts (int64_t); strides are in elements.
+ *  - bf16 input x is M x N row-major with row stride ldx >= N elements.
+ *  - Thread-safe: calls on different streams may overlap.  Calls that write
+ *    the same output buffers race, as with any kernel.
+ *
+ * Error behaviour: every function returns an mx_status.  mx_last_error()
+ * gives a human-readable detail string for the calling thread's last failed
+ * call.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+    MX_SUCCESS = 0,
+    MX_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, stride < row length */
+    MX_ERR_MISALIGNED = 2,         /* pointer not 16-byte aligned, ldx or ldc not a multiple of 8 */
+    MX_ERR_UNSUPPORTED = 3,        /* option combination not implemented (e.g. transposes) */
+    MX_ERR_DEVICE_UNSUPPORTED = 4, /* current device is not gfx950 */
+    MX_ERR_HIP = 5                 /* HIP runtime error; detail in mx_last_error() */
+} mx_status;
+
+/*
+ * Blob layouts.
+ *
+ * MX_LAYOUT_CANONICAL -- the interchange layout of the fake dual-quantize op
+ * on the page "primus_turbo_mxfp4_local.py".  For a blob of R rows quantized
+ * along an axis of length L, L_pad = cdiv(L,128)*128:
+ *   data:  R x L_pad/2 bytes, row-major; element k of a row in byte k/2,
+ *          low nibble for even k, high nibble for odd k.
+ *   scale: R x L_pad/32 bytes, row-major; byte b scales elements [32b, 32b+32).
+ *   Row-wise blob of x: R = M, L = N.  Column-wise blob: R = N, L = M (the
+ *   transpose of x, quantized along M).  Padding elements are +0 (nibble 0);
+ *   pad-only blocks have scale byte 0.
+ *
+ * MX_LAYOUT_TILED -- this library's MFMA-native layout, written directly by
+ * the quantizers and read by the GEMM with one 16-byte load per lane.
+ * Rows are padded to R16 = cdiv(R,16)*16 (pad rows are zero bytes).
+ *   data: 1024-byte atoms.  Atom (g, c) holds rows [16g, 16g+16) x k in
+ *         [128c, 128c+128) and sits at byte (g * (L_pad/128) + c) * 1024.
+ *         Inside an atom, lane = (r%16) + 16*((k%128)/32) owns bytes
+ *         [16*lane, 16*lane+16); element k is in byte (k%32)/2 of that slice,
+ *         low nibble for even k.  (Lane L holds the 32 elements of row L%16,
+ *         k-block L/16: exactly the A/B operand of one 16x16x128 scaled MFMA.)
+ *         Total R16 * L_pad/2 bytes.
+ *   scale: 256-byte atoms.  Atom (g, h) holds the scales of rows [16g, 16g+16)
+ *         and k-blocks [16h, 16h+16) and sits at byte
+ *         (g * cdiv(L_pad,512) + h) * 256.  The scale of k-block kb of row r
+ *         is byte 4*lane + (kb%16)/4 with lane = (r%16) + 16*(kb%4): each
+ *         lane's dword packs its scales for 4 consecutive 128-wide k steps.
+ *         Bytes beyond L_pad/32 blocks are 0.  Total R16 * cdiv(L_pad,512) * 16 bytes.
+ */
+typedef enum mx_layout {
+    MX_LAYOUT_CANONICAL = 0,
+    MX_LAYOUT_TILED = 1
+} mx_layout;
+
+typedef enum mx_dtype {
+    MX_BF16 = 0,   /* bfloat16, round to nearest even */
+    MX_F32 = 1     /* float32 (verification output of the GEMM) */
+} mx_dtype;
+
+/*
+ * Per-direction quantization options; the row/col pairs mirror the flag
+ * triplets of the dual-quantize op on the page "primus_turbo_mxfp4_local.py"
+ * (2D block, stochastic rounding; its Hadamard and shuffle flags have no
+ * counterpart here).
+ *
+ * use_2d_block: 0 = 32-element blocks along the quantized axis; 1 = aligned
+ *   32x32 tiles of x share one scale (tile amax), replicated into every
+ *   blob row the tile covers; blob shapes are unchanged.
+ * use_sr: 0 = round to nearest, ties to even; 1 = stochastic rounding.  The
+ *   element with row-major index n = index_base + i*N + j of the logical M x N
+ *   tensor draws byte n%16 (little-endian) of Philox-4x32-10 (Salmon et al.,
+ *   SC'11) with counter (lo32(n>>4), hi32(n>>4), tensor_id, dir) and key
+ *   (lo32(seed), hi32(seed)); dir = 0 for the row-wise blob, 1 for the
+ *   column-wise blob.  With neighbouring grid values lo <= v < hi of the scaled
+ *   magnitude v, it rounds up iff byte < floor(256*(v-lo)/(hi-lo)).
+ * The scale never depends on use_sr.  NULL options = all zero.
+ */
+typedef struct mx_quant_opts {
+    uint32_t use_2d_block;
+    uint32_t use_sr;
+    uint64_t seed;
+    uint32_t tensor_id;
+    uint32_t reserved;     /* must be 0 */
+    uint64_t index_base;
+} mx_quant_opts;
+
+/*
+ * Byte sizes of one blob (rows blob rows, quantized along `length`) in
+ * `layout`.  Either output pointer may be NULL.  Canonical sizes equal the
+ * fake dual-quantize op's shapes: rows * L_pad/2 and rows * L_pad/32.
+ * Errors: MX_ERR_INVALID_ARGUMENT (negative size), MX_ERR_UNSUPPORTED (layout).
+ */
+mx_status mx_blob_bytes(int64_t rows, int64_t length, mx_layout layout,
+                        size_t *data_bytes, size_t *scale_bytes);
+
+/*
+ * Row-wise MXFP4 quantization of x (M x N bf16, stride ldx): blocks of 32
+ * along N, the row-only packer a forward pass with no backward behind it needs
+ * (page "Primus PR 1107", the commit that packs rows only when no backward will
+ * read the columns; the caller decides, the library never infers grad mode).
+ * Outputs: q (data) and s (scales) of the row-wise blob (R = M, L = N) in
+ * `layout`, sized by mx_blob_bytes.  Every output byte is written, padding
+ * included.  M == 0 or N == 0 is a no-op.
+ * Requires x and the outputs 16-byte aligned and ldx % 8 == 0.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, UNSUPPORTED, DEVICE_UNSUPPORTED, HIP.
+ */
+mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx,
+                              const mx_quant_opts *opts, mx_layout layout,
+                              void *q, void *s, void *stream);
+
+/*
+ * Dual quantization: the row-wise blob (R = M, L = N) and the column-wise blob
+ * (R = N, L = M: x transposed, blocks of 32 along M) from one read of x, as the
+ * dual-quantize op on the page "primus_turbo_mxfp4_local.py" returns them
+ * (row data, row scale, col data, col scale).  Options are per direction.
+ * Same requirements and errors as mx_quantize_rowwise.
+ */
+mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx,
+                           const mx_quant_opts *row_opts, const mx_quant_opts *col_opts,
+                           mx_layout layout, void *q_row, void *s_row,
+                           void *q_col, void *s_col, void *stream);
+
+/*
+ * Block-scaled FP4 x FP4 GEMM with fp32 accumulation:
+ *   C[i][j] = sum_k A[i][k] * B[j][k]   (i < M, j < N, k over the padded K)
+ * where A (M rows) and B (N rows) are blobs quantized along K and each
+ * element is e2m1(code) * 2^(scale-127).  This is the NT call that the
+ * forward (X_row . W_row^T), dgrad (dY_row . W_col^T) and wgrad
+ * (dY_col . X_col^T) of the MXFP4 linear on the page
+ * "primus_turbo_mxfp4_local.py" all make.
+ * transA must be 0 and transB must be 1 (both operands K-contiguous); any
+ * other combination returns MX_ERR_UNSUPPORTED.  layout must be
+ * MX_LAYOUT_TILED.  K is the logical K; the blobs carry cdiv(K,128)*128.
+ * C is M x N row-major with stride ldc >= N, out_dtype MX_BF16 (round to
+ * nearest even; overflow to +-Inf) or MX_F32.  A NaN scale byte yields NaN in
+ * the affected outputs (hardware-defined propagation).  M == 0 or N == 0 is a
+ * no-op; K == 0 writes zeros.
+ * Requires 16-byte aligned pointers and ldc % 8 == 0.
+ */
+mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                       const void *A, const void *A_scale,
+                       const void *B, const void *B_scale,
+                       mx_layout layout, mx_dtype out_dtype,
+                       void *C, int64_t ldc, void *stream);
+
+/*
+ * Host-side layout conversion of one blob (rows, length) between the two
+ * layouts; plain host pointers, synchronous.  to_tiled = 1: canonical ->
+ * tiled; 0: tiled -> canonical.  Destination buffers are sized by
+ * mx_blob_bytes for their layout.
+ */
+mx_status mx_layout_convert_host(int to_tiled, int64_t rows, int64_t length,
+                                 const void *q_src, const void *s_src,
+                                 void *q_dst, void *s_dst);
+
+/*
+ * Device dequantization (a test aid): out[r][k] = element value as float32
+ * for r < rows, k < length (logical, unpadded), row stride ldo >= length.
+ * Values are exact in float32 for scale bytes <= 252 (the quantizers never
+ * emit more for finite input); byte 0xFF gives NaN.
+ */
+mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t length,
+                        mx_layout layout, void *out_f32, int64_t ldo, void *stream);
+
+/* 1 if device `device` is gfx950 (the only target), else 0. */
+int mx_device_supported(int device);
+
+/* Static name of a status code. */
+const char *mx_status_string(mx_status status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char *mx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,179 @@
+"""Python binding of libmxfp4 (MXFP4 quantize + block-scaled a4w4 GEMM for gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libmxfp4.so``.  Functions carry the C ABI's names (``include/mxfp4.h``) and
+take device pointers as ints or torch tensors (their ``data_ptr()``), sizes as
+ints, and a stream as a ``torch.cuda.Stream``, an int handle, or None (torch's
+current stream).  A non-zero status raises ``MXError``; if the shared library
+is missing, the first call raises: there is no fallback.
+
+Build the library with ``python -m mxfp4_precision_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
+
+MX_SUCCESS = 0
+MX_ERR_INVALID_ARGUMENT = 1
+MX_ERR_MISALIGNED = 2
+MX_ERR_UNSUPPORTED = 3
+MX_ERR_DEVICE_UNSUPPORTED = 4
+MX_ERR_HIP = 5
+
+MX_LAYOUT_CANONICAL = 0
+MX_LAYOUT_TILED = 1
+MX_BF16 = 0
+MX_F32 = 1
+
+EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4",
+            "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
+            "mx_status_string", "mx_last_error")
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (_status_name(status), detail))
+        self.status = status
+
+
+class mx_quant_opts(ctypes.Structure):
+    _fields_ = [("use_2d_block", ctypes.c_uint32), ("use_sr", ctypes.c_uint32),
+                ("seed", ctypes.c_uint64), ("tensor_id", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32), ("index_base", ctypes.c_uint64)]
+
+
+def quant_opts(use_2d_block: bool = False, use_sr: bool = False, seed: int = 0,
+               tensor_id: int = 0, index_base: int = 0) -> mx_quant_opts:
+    return mx_quant_opts(int(use_2d_block), int(use_sr), seed, tensor_id, 0, index_base)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmxfp4.so not found at %s: build it with "
+                           "`python -m mxfp4_precision_amd.build` (no fallback path exists)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    optp = ctypes.POINTER(mx_quant_opts)
+    L.mx_blob_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    L.mx_quantize_rowwise.argtypes = [vp, i64, i64, i64, optp, i32, vp, vp, vp]
+    L.mx_quantize_dual.argtypes = [vp, i64, i64, i64, optp, optp, i32, vp, vp, vp, vp, vp]
+    L.mx_gemm_a4w4.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, i64, vp]
+    L.mx_layout_convert_host.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+    L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
+    L.mx_device_supported.argtypes = [i32]
+    L.mx_device_supported.restype = i32
+    L.mx_status_string.argtypes = [i32]
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_last_error.argtypes = []
+    L.mx_last_error.restype = ctypes.c_char_p
+    for name in ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4",
+                 "mx_layout_convert_host", "mx_dequantize"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _status_name(st: int) -> str:
+    try:
+        return lib().mx_status_string(st).decode()
+    except Exception:
+        return "status %d" % st
+
+
+def _check(st: int):
+    if st != MX_SUCCESS:
+        raise MXError(st, lib().mx_last_error().decode())
+
+
+def _ptr(p) -> Optional[int]:
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p
+    if hasattr(p, "data_ptr"):
+        return p.data_ptr()
+    if hasattr(p, "ctypes"):          # numpy array (host pointer)
+        return p.ctypes.data
+    raise TypeError("expected a pointer, tensor or array, got %r" % type(p))
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _opts(o):
+    return ctypes.byref(o) if o is not None else None
+
+
+# ------------------------------------------------------------------ C ABI names
+
+def mx_blob_bytes(rows: int, length: int, layout: int) -> Tuple[int, int]:
+    d, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().mx_blob_bytes(rows, length, layout, ctypes.byref(d), ctypes.byref(s)))
+    return d.value, s.value
+
+
+def mx_quantize_rowwise(x, M: int, N: int, ldx: int, opts, layout: int, q, s, stream=None):
+    _check(lib().mx_quantize_rowwise(_ptr(x), M, N, ldx, _opts(opts), layout, _ptr(q), _ptr(s),
+                                     _stream(stream)))
+
+
+def mx_quantize_dual(x, M: int, N: int, ldx: int, row_opts, col_opts, layout: int,
+                     q_row, s_row, q_col, s_col, stream=None):
+    _check(lib().mx_quantize_dual(_ptr(x), M, N, ldx, _opts(row_opts), _opts(col_opts), layout,
+                                  _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+
+
+def mx_gemm_a4w4(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B, B_scale,
+                 layout: int, out_dtype: int, C, ldc: int, stream=None):
+    _check(lib().mx_gemm_a4w4(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
+                              layout, out_dtype, _ptr(C), ldc, _stream(stream)))
+
+
+def mx_layout_convert_host(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst):
+    _check(lib().mx_layout_convert_host(to_tiled, rows, length, _ptr(q_src), _ptr(s_src),
+                                        _ptr(q_dst), _ptr(s_dst)))
+
+
+def mx_dequantize(q, s, rows: int, length: int, layout: int, out_f32, ldo: int, stream=None):
+    _check(lib().mx_dequantize(_ptr(q), _ptr(s), rows, length, layout, _ptr(out_f32), ldo,
+                               _stream(stream)))
+
+
+def mx_device_supported(device: int) -> bool:
+    return bool(lib().mx_device_supported(device))
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(status).decode()
+
+
+def mx_last_error() -> str:
+    return lib().mx_last_error().decode()
+
+
+# ------------------------------------------------- allocation helpers (plumbing)
+
+def empty_blob(rows: int, length: int, layout: int, device="cuda"):
+    """Allocate (data, scale) uint8 tensors of the right byte sizes on `device`."""
+    import torch
+    db, sb = mx_blob_bytes(rows, length, layout)
+    return (torch.empty(max(db, 1), dtype=torch.uint8, device=device),
+            torch.empty(max(sb, 1), dtype=torch.uint8, device=device))

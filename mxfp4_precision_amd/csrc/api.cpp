@@ -1,0 +1,239 @@
+// libmxfp4 C ABI: argument validation, device check, dispatch to the kernels.
+// Every check runs before any launch and fails loudly with a status code and
+// a thread-local detail message; there is no fallback path (the page
+// "primus_turbo_mxfp4_local.py" turns mis-dispatch into a hard init-time error
+// for the same reason: silent fallbacks hid wrong layouts and lost speed).
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "mx_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+mx_status fail(mx_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device cache of the gfx950 check: 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+int query_supported(int dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+mx_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(MX_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MX_ERR_DEVICE_UNSUPPORTED, "device index %d out of range", dev);
+    int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = query_supported(dev) ? 1 : 2;
+        g_dev_ok[dev].store(v, std::memory_order_relaxed);
+    }
+    if (v != 1) return fail(MX_ERR_DEVICE_UNSUPPORTED, "device %d is not gfx950 (MI355X)", dev);
+    return MX_SUCCESS;
+}
+
+mx_status check_launch(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(MX_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return MX_SUCCESS;
+}
+
+mx_status check_opts(const mx_quant_opts *o, const char *which) {
+    if (!o) return MX_SUCCESS;
+    if (o->use_2d_block > 1 || o->use_sr > 1)
+        return fail(MX_ERR_INVALID_ARGUMENT, "%s options: use_2d_block and use_sr must be 0 or 1", which);
+    if (o->reserved != 0) return fail(MX_ERR_INVALID_ARGUMENT, "%s options: reserved must be 0", which);
+    return MX_SUCCESS;
+}
+
+mx::DirOpts to_dir(const mx_quant_opts *o) {
+    mx::DirOpts d{};
+    if (o) {
+        d.use_2d = o->use_2d_block;
+        d.use_sr = o->use_sr;
+        d.key0 = (uint32_t)o->seed;
+        d.key1 = (uint32_t)(o->seed >> 32);
+        d.tensor_id = o->tensor_id;
+        d.index_base = o->index_base;
+    }
+    return d;
+}
+
+mx_status check_layout(mx_layout layout) {
+    if (layout != MX_LAYOUT_CANONICAL && layout != MX_LAYOUT_TILED)
+        return fail(MX_ERR_UNSUPPORTED, "unknown layout %d (valid: MX_LAYOUT_CANONICAL=0, MX_LAYOUT_TILED=1)",
+                    (int)layout);
+    return MX_SUCCESS;
+}
+
+mx_status validate_x(const void *x, int64_t M, int64_t N, int64_t ldx) {
+    if (M < 0 || N < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative shape M=%lld N=%lld", (long long)M, (long long)N);
+    if (ldx < N || ldx < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldx=%lld must be >= max(N, 1)=%lld", (long long)ldx, (long long)N);
+    if (!x) return fail(MX_ERR_INVALID_ARGUMENT, "x is NULL");
+    if (!aligned16(x)) return fail(MX_ERR_MISALIGNED, "x must be 16-byte aligned");
+    if (ldx % 8) return fail(MX_ERR_MISALIGNED, "ldx=%lld must be a multiple of 8", (long long)ldx);
+    return MX_SUCCESS;
+}
+
+mx_status validate_out(const void *q, const void *s, const char *name) {
+    if (!q || !s) return fail(MX_ERR_INVALID_ARGUMENT, "%s output pointer is NULL", name);
+    if (!aligned16(q) || !aligned16(s)) return fail(MX_ERR_MISALIGNED, "%s outputs must be 16-byte aligned", name);
+    return MX_SUCCESS;
+}
+
+#define MX_TRY(expr)                     \
+    do {                                 \
+        mx_status _st = (expr);          \
+        if (_st != MX_SUCCESS) return _st; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *data_bytes,
+                        size_t *scale_bytes) {
+    if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
+    MX_TRY(check_layout(layout));
+    const int64_t Lp = mx::padded(length);
+    int64_t db, sb;
+    if (layout == MX_LAYOUT_CANONICAL) {
+        db = rows * (Lp / 2);
+        sb = rows * (Lp / 32);
+    } else {
+        const int64_t r16 = mx::cdiv(rows, 16) * 16;
+        db = r16 * (Lp / 2);
+        sb = r16 * mx::cdiv(Lp, 512) * 16;
+    }
+    if (data_bytes) *data_bytes = (size_t)db;
+    if (scale_bytes) *scale_bytes = (size_t)sb;
+    return MX_SUCCESS;
+}
+
+mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx, const mx_quant_opts *opts,
+                              mx_layout layout, void *q, void *s, void *stream) {
+    MX_TRY(validate_x(x, M, N, ldx));
+    MX_TRY(check_opts(opts, "row"));
+    MX_TRY(check_layout(layout));
+    MX_TRY(validate_out(q, s, "row-wise"));
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    mx::QuantArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M; a.N = N; a.ldx = ldx;
+    a.M_pad = mx::padded(M); a.N_pad = mx::padded(N);
+    a.row = to_dir(opts);
+    a.q_row = static_cast<uint8_t *>(q);
+    a.s_row = static_cast<uint8_t *>(s);
+    return check_launch(mx::launch_quantize(a, false, layout, static_cast<hipStream_t>(stream)),
+                        "mx_quantize_rowwise");
+}
+
+mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, const mx_quant_opts *row_opts,
+                           const mx_quant_opts *col_opts, mx_layout layout, void *q_row, void *s_row,
+                           void *q_col, void *s_col, void *stream) {
+    MX_TRY(validate_x(x, M, N, ldx));
+    MX_TRY(check_opts(row_opts, "row"));
+    MX_TRY(check_opts(col_opts, "col"));
+    MX_TRY(check_layout(layout));
+    MX_TRY(validate_out(q_row, s_row, "row-wise"));
+    MX_TRY(validate_out(q_col, s_col, "column-wise"));
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    mx::QuantArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M; a.N = N; a.ldx = ldx;
+    a.M_pad = mx::padded(M); a.N_pad = mx::padded(N);
+    a.row = to_dir(row_opts);
+    a.col = to_dir(col_opts);
+    a.q_row = static_cast<uint8_t *>(q_row);
+    a.s_row = static_cast<uint8_t *>(s_row);
+    a.q_col = static_cast<uint8_t *>(q_col);
+    a.s_col = static_cast<uint8_t *>(s_col);
+    return check_launch(mx::launch_quantize(a, true, layout, static_cast<hipStream_t>(stream)),
+                        "mx_quantize_dual");
+}
+
+mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                       const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
+                       mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+    if (transA != 0 || transB != 1)
+        return fail(MX_ERR_UNSUPPORTED,
+                    "transA=%d transB=%d: only transA=0, transB=1 (C = A . B^T, both operands K-contiguous) "
+                    "is supported; quantize the other direction instead of transposing",
+                    transA, transB);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(MX_ERR_INVALID_ARGUMENT, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                    (long long)K);
+    MX_TRY(check_layout(layout));
+    if (layout != MX_LAYOUT_TILED)
+        return fail(MX_ERR_UNSUPPORTED, "mx_gemm_a4w4 reads MX_LAYOUT_TILED blobs only");
+    if (out_dtype != MX_BF16 && out_dtype != MX_F32)
+        return fail(MX_ERR_UNSUPPORTED, "out_dtype %d (valid: MX_BF16=0, MX_F32=1)", (int)out_dtype);
+    if (ldc < N || ldc < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldc=%lld must be >= max(N, 1)", (long long)ldc);
+    if (!C) return fail(MX_ERR_INVALID_ARGUMENT, "C is NULL");
+    if (K > 0 && (!A || !A_scale || !B || !B_scale))
+        return fail(MX_ERR_INVALID_ARGUMENT, "operand pointer is NULL");
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(A_scale) || !aligned16(B) || !aligned16(B_scale))))
+        return fail(MX_ERR_MISALIGNED, "operands and C must be 16-byte aligned");
+    if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    return check_launch(mx::launch_gemm(M, N, K, static_cast<const uint8_t *>(A),
+                                        static_cast<const uint8_t *>(A_scale), static_cast<const uint8_t *>(B),
+                                        static_cast<const uint8_t *>(B_scale), out_dtype, C, ldc,
+                                        static_cast<hipStream_t>(stream)),
+                        "mx_gemm_a4w4");
+}
+
+mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t length, mx_layout layout,
+                        void *out_f32, int64_t ldo, void *stream) {
+    if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
+    MX_TRY(check_layout(layout));
+    if (ldo < length || ldo < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldo must be >= max(length, 1)");
+    if (!q || !s || !out_f32) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (rows == 0 || length == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    return check_launch(mx::launch_dequantize(static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(s),
+                                              rows, length, layout, static_cast<float *>(out_f32), ldo,
+                                              static_cast<hipStream_t>(stream)),
+                        "mx_dequantize");
+}
+
+int mx_device_supported(int device) {
+    if (device < 0 || device >= kMaxDevices) return 0;
+    return query_supported(device);
+}
+
+const char *mx_status_string(mx_status status) {
+    switch (status) {
+        case MX_SUCCESS: return "MX_SUCCESS";
+        case MX_ERR_INVALID_ARGUMENT: return "MX_ERR_INVALID_ARGUMENT";
+        case MX_ERR_MISALIGNED: return "MX_ERR_MISALIGNED";
+        case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+        case MX_ERR_DEVICE_UNSUPPORTED: return "MX_ERR_DEVICE_UNSUPPORTED";
+        case MX_ERR_HIP: return "MX_ERR_HIP";
+    }
+    return "MX_ERR_UNKNOWN";
+}
+
+const char *mx_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal declarations shared by the libmxfp4 translation units (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxfp4.h"
+
+namespace mx {
+
+constexpr int64_t kBlock = 32;   // elements per scale block
+constexpr int64_t kPad = 128;    // quantized-axis padding
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t padded(int64_t n) { return cdiv(n, kPad) * kPad; }
+
+// Per-direction options in the form the kernels take them.
+struct DirOpts {
+    uint32_t use_2d;
+    uint32_t use_sr;
+    uint32_t key0, key1;        // Philox key = seed
+    uint32_t tensor_id;
+    uint64_t index_base;
+};
+
+struct QuantArgs {
+    const uint16_t *x;
+    int64_t M, N, ldx;
+    int64_t M_pad, N_pad;       // padded quantized axes (col blob, row blob)
+    DirOpts row, col;
+    uint8_t *q_row, *s_row, *q_col, *s_col;
+};
+
+// Kernel launchers (quantize.hip, gemm.hip).  They assume validated arguments.
+hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
+                       const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C,
+                       int64_t ldc, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t length,
+                             mx_layout layout, float *out, int64_t ldo, hipStream_t stream);
+
+}  // namespace mx

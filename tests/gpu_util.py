@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: move seeded host inputs to the device, call
+the HIP library through its C ABI binding, and bring the blobs back."""
+import sys
+
+import numpy as np
+import torch
+
+import mxfp4_precision_amd as mx
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev_bf16(bits: np.ndarray, ldx: int = None):
+    """bf16 bits (M x N uint16) -> device int16 tensor with row stride ldx."""
+    M, N = bits.shape
+    ldx = ldx or max(8, (N + 7) // 8 * 8)   # the library wants ldx % 8 == 0
+    t = torch.zeros((M, ldx), dtype=torch.int16)
+    t[:, :N] = torch.from_numpy(bits.view(np.int16))
+    return t.cuda(), ldx
+
+
+def quantize_rowwise(x_dev, M, N, ldx, layout, opts=None):
+    q, s = mx.empty_blob(M, N, layout)
+    mx.mx_quantize_rowwise(x_dev, M, N, ldx, opts or mx.quant_opts(), layout, q, s)
+    return q, s
+
+
+def quantize_dual(x_dev, M, N, ldx, layout, row_opts=None, col_opts=None):
+    qr, sr = mx.empty_blob(M, N, layout)
+    qc, sc = mx.empty_blob(N, M, layout)
+    mx.mx_quantize_dual(x_dev, M, N, ldx, row_opts or mx.quant_opts(), col_opts or mx.quant_opts(),
+                        layout, qr, sr, qc, sc)
+    return qr, sr, qc, sc
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def canon_shape(oracle_mod, rows, length, q, s):
+    (a, b), (c, d) = oracle_mod.blob_shapes(rows, length)
+    return q[: a * b].reshape(a, b), s[: c * d].reshape(c, d)
+
+
+def gemm(A, As, B, Bs, M, N, K, out_dtype=mx.MX_BF16, ldc=None):
+    ldc = ldc or ((N + 7) // 8 * 8)
+    dt = torch.int16 if out_dtype == mx.MX_BF16 else torch.float32
+    C = torch.full((max(M, 1), ldc), -1, dtype=dt, device="cuda")
+    mx.mx_gemm_a4w4(0, 1, M, N, K, A, As, B, Bs, mx.MX_LAYOUT_TILED, out_dtype, C, ldc)
+    return C
+
+
+def bf16_bits_to_f64(b):
+    return (np.asarray(b).astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def ulp_bf16(v):
+    """Spacing of bf16 numbers at |v| (subnormal floor 2^-133)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_gemm_bf16(got_bits, ref64, tau, oracle_mod, what=""):
+    """Elementwise: |C - bf16(ref)| <= 2 ulp_bf16(max(|bf16(ref)|, tau)).  Returns (#exact, #tau-only)."""
+    refb = oracle_mod.bf16_from_double(ref64)
+    got = bf16_bits_to_f64(got_bits)
+    refv = bf16_bits_to_f64(refb)
+    bound = 2 * ulp_bf16(np.maximum(np.abs(refv), tau))
+    err = np.abs(got - refv)
+    bad = ~(err <= bound)
+    assert not bad.any(), "%s: %d elements off; first %s got %r ref %r" % (
+        what, int(bad.sum()), np.argwhere(bad)[:3].tolist(), got[bad][:3], refv[bad][:3])
+    exact = int((got_bits.astype(np.uint16) == refb).sum())
+    tau_only = int((err > 2 * ulp_bf16(np.abs(refv))).sum())
+    return exact, tau_only
+
+
+def tau_bound(oracle_mod, qa, sa, qb, sb, M, N, K, ii, jj):
+    """(K_pad/32) 2^-24 sum_k |a_ik b_jk|: worst-case fp32 summation error of exact block partials."""
+    ii = np.asarray(ii); jj = np.asarray(jj)
+    da = np.abs(oracle_mod.dequantize(qa[ii], sa[ii], len(ii), K))
+    db = np.abs(oracle_mod.dequantize(qb[jj], sb[jj], len(jj), K))
+    kp = da.shape[1]
+    s = np.einsum("ij,ij->i", da, db)
+    return (kp / 32) * 2.0 ** -24 * s

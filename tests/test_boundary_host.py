@@ -1,0 +1,152 @@
+"""Host-side checks of the libmxfp4 C ABI that need no GPU: the library loads
+and exports every function include/mxfp4.h declares, argument validation
+rejects bad calls before any launch, blob sizes match the canonical shapes of
+the fake dual-quantize op (page "primus_turbo_mxfp4_local.py") and the tiled
+layout's definition, and the host layout converter agrees with the oracle's
+independent permutation."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp4_precision_amd as mx
+from mxfp4_precision_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.LIB_PATH):
+        from mxfp4_precision_amd import build
+        build.build()
+    return mx.lib()
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(mx_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(mx.EXPORTED) <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for st, name in [(0, "MX_SUCCESS"), (1, "MX_ERR_INVALID_ARGUMENT"), (2, "MX_ERR_MISALIGNED"),
+                     (3, "MX_ERR_UNSUPPORTED"), (4, "MX_ERR_DEVICE_UNSUPPORTED"), (5, "MX_ERR_HIP")]:
+        assert mx.mx_status_string(st) == name
+
+
+@pytest.mark.parametrize("rows,length", [(1, 1), (4600, 3072), (3072, 4600), (127, 129), (256, 512),
+                                         (18432, 12288), (0, 5), (7, 0)])
+def test_blob_bytes(L, oracle_mod, rows, length):
+    d, s = mx.mx_blob_bytes(rows, length, mx.MX_LAYOUT_CANONICAL)
+    (qr, qc), (sr, sc) = oracle_mod.blob_shapes(rows, length)
+    assert d == qr * qc and s == sr * sc
+    dt, st = mx.mx_blob_bytes(rows, length, mx.MX_LAYOUT_TILED)
+    assert (dt, st) == oracle_mod.tiled_shapes(rows, length)
+
+
+def test_blob_bytes_errors(L):
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_blob_bytes(-1, 4, 0)
+    assert e.value.status == mx.MX_ERR_INVALID_ARGUMENT
+    with pytest.raises(mx.MXError) as e:
+        mx.mx_blob_bytes(1, 4, 7)
+    assert e.value.status == mx.MX_ERR_UNSUPPORTED
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+        return mx.MX_SUCCESS
+    except mx.MXError as e:
+        return e.status
+
+
+def test_quantize_validation_runs_before_any_launch(L):
+    """Every bad argument is rejected on the host (no device is touched here)."""
+    A16 = 1 << 20          # fake, 16-byte aligned addresses: never dereferenced
+    o = mx.quant_opts()
+    Q = mx.mx_quantize_rowwise
+    assert _status(Q, A16, -1, 8, 8, o, 0, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(Q, A16, 4, 16, 8, o, 0, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT   # ldx < N
+    assert _status(Q, 0, 4, 8, 8, o, 0, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT       # x NULL
+    assert _status(Q, A16 + 2, 4, 8, 8, o, 0, A16, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(Q, A16, 4, 8, 12, o, 0, A16, A16, 0) == mx.MX_ERR_MISALIGNED           # ldx % 8
+    assert _status(Q, A16, 4, 8, 8, o, 5, A16, A16, 0) == mx.MX_ERR_UNSUPPORTED           # layout
+    assert _status(Q, A16, 4, 8, 8, o, 0, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT        # q NULL
+    assert _status(Q, A16, 4, 8, 8, o, 0, A16, A16 + 4, 0) == mx.MX_ERR_MISALIGNED
+    bad = mx.quant_opts(); bad.use_sr = 2
+    assert _status(Q, A16, 4, 8, 8, bad, 0, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    bad = mx.quant_opts(); bad.reserved = 1
+    assert _status(Q, A16, 4, 8, 8, bad, 0, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    # empty tensors are a no-op success before any device query
+    assert _status(Q, A16, 0, 8, 8, o, 0, A16, A16, 0) == mx.MX_SUCCESS
+    assert _status(Q, A16, 4, 0, 8, o, 0, A16, A16, 0) == mx.MX_SUCCESS
+    D = mx.mx_quantize_dual
+    assert _status(D, A16, 4, 8, 8, o, o, 0, A16, A16, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(D, A16, 4, 8, 8, o, bad, 0, A16, A16, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(D, A16, 0, 8, 8, o, o, 0, A16, A16, A16, A16, 0) == mx.MX_SUCCESS
+    assert "reserved" in mx.mx_last_error() or mx.mx_last_error() != ""
+
+
+def test_gemm_validation(L):
+    A16 = 1 << 20
+    G = mx.mx_gemm_a4w4
+    T = mx.MX_LAYOUT_TILED
+    for ta, tb in [(0, 0), (1, 1), (1, 0)]:
+        assert _status(G, ta, tb, 4, 4, 4, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    assert "transA" in mx.mx_last_error()
+    assert _status(G, 0, 1, -1, 4, 4, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, 0, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED   # canonical
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, T, 9, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED   # dtype
+    assert _status(G, 0, 1, 4, 16, 4, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_INVALID_ARGUMENT  # ldc
+    assert _status(G, 0, 1, 4, 4, 4, 0, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, T, 0, 0, 8, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(G, 0, 1, 4, 4, 4, A16 + 8, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, T, 0, A16, 12, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(G, 0, 1, 0, 4, 4, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_SUCCESS
+
+
+def test_dequantize_validation(L):
+    A16 = 1 << 20
+    assert _status(mx.mx_dequantize, A16, A16, -1, 4, 0, A16, 4, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(mx.mx_dequantize, A16, A16, 2, 8, 0, A16, 4, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(mx.mx_dequantize, A16, A16, 0, 8, 0, A16, 8, 0) == mx.MX_SUCCESS
+
+
+@pytest.mark.parametrize("rows,length", [(1, 1), (37, 640), (40, 700), (16, 512), (100, 3000)])
+def test_host_layout_convert_matches_oracle(L, oracle_mod, rows, length):
+    x = synth.random_bf16(rows * 7 + length, (rows, length))
+    q, s = oracle_mod.quantize(x, 0)
+    qt_ref, st_ref = oracle_mod.to_tiled(q, s, rows, length)
+    dt, sz = mx.mx_blob_bytes(rows, length, mx.MX_LAYOUT_TILED)
+    qt = np.full(dt, 0xAB, np.uint8)
+    st = np.full(sz, 0xCD, np.uint8)
+    mx.mx_layout_convert_host(1, rows, length, q, s, qt, st)
+    assert (qt == qt_ref).all() and (st == st_ref).all()
+    q2 = np.zeros_like(q)
+    s2 = np.zeros_like(s)
+    mx.mx_layout_convert_host(0, rows, length, qt, st, q2, s2)
+    assert (q2 == q).all() and (s2 == s).all()
+
+
+def test_device_supported_without_gpu(L):
+    # no GPU in a CPU-only container: the query reports unsupported instead of crashing
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("GPU present")
+    assert mx.mx_device_supported(0) is False

@@ -1,0 +1,134 @@
+"""GPU parity of the block-scaled a4w4 GEMM against the oracle's fp64 NT product.
+
+Bar (elementwise, bf16 output): |C - bf16(C_ref)| <= 2 ulp_bf16(max(|bf16(C_ref)|, tau)),
+tau = (K_pad/32) 2^-24 sum_k |a_ik b_jk| (worst-case fp32 summation error of
+exact per-block partial sums).  Bar (fp32 output): relative Frobenius error
+<= 1e-5 against the fp64 reference.  Full-size shapes are checked on sampled
+entries the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import mxfp4_precision_amd as mx
+from mxfp4_precision_amd import synth
+
+from gpu_util import (check_gemm_bf16, gemm, host, log, quantize_dual, quantize_rowwise, tau_bound,
+                      to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+TILED = mx.MX_LAYOUT_TILED
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_case(oracle_mod, a_bits, b_bits, full=True, nsample=2048, seed=0, what=""):
+    M, K = a_bits.shape
+    N, K2 = b_bits.shape
+    assert K == K2
+    ad, lda = to_dev_bf16(a_bits)
+    bd, ldb = to_dev_bf16(b_bits)
+    qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
+    qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
+    Cb = gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16)
+    Cf = gemm(qa, sa, qb, sb, M, N, K, mx.MX_F32)
+    cb = host(Cb)[:M, :N].view(np.uint16)
+    cf = host(Cf)[:M, :N].astype(np.float64)
+    oqa, osa = oracle_mod.quantize(a_bits, 0)
+    oqb, osb = oracle_mod.quantize(b_bits, 0)
+    if full:
+        ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ii, jj = ii.ravel(), jj.ravel()
+    else:
+        rng = np.random.default_rng(seed)
+        ii = np.concatenate([rng.integers(0, M, nsample), [0, M - 1, M - 1, 0]])
+        jj = np.concatenate([rng.integers(0, N, nsample), [0, N - 1, 0, N - 1]])
+    ref = oracle_mod.gemm_entries(oqa, osa, oqb, osb, M, N, K, ii, jj)
+    tau = tau_bound(oracle_mod, oqa, osa, oqb, osb, M, N, K, ii, jj)
+    exact, tau_only = check_gemm_bf16(cb[ii, jj], ref, tau, oracle_mod, what)
+    gotf = cf[ii, jj]
+    rel = np.linalg.norm(gotf - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-5, (what, rel)
+    log("%s: %d/%d bf16 exact, %d tau-floor only, fp32 rel %.3g" % (what, exact, ii.size, tau_only, rel))
+    return cb, cf
+
+
+def test_tiny_workload(oracle_mod):
+    """256x512 . (384x512)^T, seed 0, every entry."""
+    _require_gpu()
+    d = synth.tiny()
+    run_case(oracle_mod, d["A"], d["W"], full=True, what="tiny")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (17, 33, 129), (100, 70, 300), (128, 128, 128),
+                                   (129, 257, 640), (64, 16, 2048), (250, 130, 900)])
+def test_ragged(oracle_mod, M, N, K):
+    _require_gpu()
+    a = synth.random_bf16(M * 3 + K, (M, K), std=1.0)
+    b = synth.random_bf16(N * 5 + K, (N, K), std=0.05)
+    run_case(oracle_mod, a, b, full=True, what="ragged %dx%dx%d" % (M, N, K))
+
+
+def test_k_zero_writes_zeros(oracle_mod):
+    _require_gpu()
+    C = torch.full((5, 8), 7, dtype=torch.int16, device="cuda")
+    dummy = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    mx.mx_gemm_a4w4(0, 1, 5, 6, 0, dummy, dummy, dummy, dummy, TILED, mx.MX_BF16, C, 8)
+    c = host(C)
+    assert (c[:, :6] == 0).all() and (c[:, 6:] == 7).all()
+
+
+def test_ldc_and_untouched_padding(oracle_mod):
+    """C rows are written at stride ldc; columns N..ldc-1 stay untouched."""
+    _require_gpu()
+    a = synth.random_bf16(41, (40, 256))
+    b = synth.random_bf16(42, (24, 256))
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, 40, 256, lda, TILED)
+    qb, sb = quantize_rowwise(bd, 24, 256, ldb, TILED)
+    C = gemm(qa, sa, qb, sb, 40, 24, 256, mx.MX_BF16, ldc=40)
+    c = host(C)
+    assert (c[:, 24:] == -1).all()
+    C2 = gemm(qa, sa, qb, sb, 40, 24, 256, mx.MX_BF16)
+    assert (host(C2)[:, :24] == c[:, :24]).all()
+
+
+def test_special_scales(oracle_mod):
+    """Outliers, zero blocks, scale-0 (tiny) blocks and saturated blocks in both operands."""
+    _require_gpu()
+    a = synth.random_bf16(43, (64, 512), std=1.0)
+    b = synth.random_bf16(44, (48, 512), std=1.0)
+    a[3, :32] = 0
+    a[5, 100] = synth.bf16_bits(np.array([3e4], np.float32))[0]
+    b[7, 200:232] = 0x0001
+    b[9, :] = 0x7F7F >> 1
+    run_case(oracle_mod, a, b, full=True, what="special scales")
+
+
+def test_nan_scale_propagates(oracle_mod):
+    """A NaN in an input block gives scale 0xFF; the affected outputs are NaN."""
+    _require_gpu()
+    a = synth.random_bf16(45, (32, 256))
+    b = synth.random_bf16(46, (32, 256))
+    a[4, 10] = 0x7FC0
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, 32, 256, lda, TILED)
+    qb, sb = quantize_rowwise(bd, 32, 256, ldb, TILED)
+    C = host(gemm(qa, sa, qb, sb, 32, 32, 256, mx.MX_F32))
+    assert np.isnan(C[4, :32]).all()
+    assert np.isfinite(np.delete(C[:, :32], 4, axis=0)).all()
+
+
+def test_qkv_full_size_sampled(oracle_mod):
+    """QKV forward 4608x3072 . (9216x3072)^T (seed 2), sampled entries."""
+    _require_gpu()
+    d = synth.qkv()
+    log("qkv full size")
+    run_case(oracle_mod, d["A"], d["W"], full=False, nsample=4096, what="qkv")
