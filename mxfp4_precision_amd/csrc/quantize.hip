@@ -18,12 +18,18 @@
 // A workgroup stacks 4 waves (128 x 128) so column-blob writes form 64-byte
 // runs in the canonical layout and whole 1 KB atoms in the tiled layout.
 //
-// Encoding.  With u = |x| * 2^(1-c) as an fp32 bit pattern, the E2M1 normal
-// numbers (1 <= v < 8) coincide with fp32 normal numbers and the E2M1
-// subnormal step (0.5) with the fp32 subnormal range, so the 3-bit code is
-// u >> 22 after rounding at bit 22: round-to-nearest-even adds
-// 0x1FFFFF + bit22; stochastic rounding adds 1 iff the random byte is below
-// the next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)).
+// Encoding, round to nearest even: V_CVT_SCALEF32_PK_FP4_BF16 converts a bf16
+// pair divided by the fp32 scale 2^(byte-127) to two E2M1 nibbles.  Its
+// rounding (ties to even, saturation at 6, sign kept, subnormal inputs and the
+// subnormal scale 2^-127 included) was checked exhaustively against the
+// definition for every finite bf16 value at every scale byte that can hold it;
+// the GPU parity tests repeat that sweep through this kernel.
+//
+// Encoding, stochastic: with u = |x| * 2^(1-c) as an fp32 bit pattern, the
+// E2M1 normal numbers (1 <= v < 8) coincide with fp32 normal numbers and the
+// E2M1 subnormal step (0.5) with the fp32 subnormal range, so the code is
+// the truncation u >> 22 plus 1 iff the element's random byte is below the
+// next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)).
 
 #include "mx_internal.h"
 
@@ -47,21 +53,35 @@ __device__ __forceinline__ uint32_t scaled_u(uint32_t x16, uint32_t c) {
     return __float_as_uint(__builtin_ldexpf(xf, 1 - (int)c));
 }
 
-__device__ __forceinline__ uint32_t code_rne(uint32_t u) {
-    uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
-    return r < 7u ? r : 7u;
-}
-
 __device__ __forceinline__ uint32_t code_sr(uint32_t u, uint32_t rbyte) {
     uint32_t r = (u >> 22) + (rbyte < ((u >> 14) & 0xFFu) ? 1u : 0u);
     return r < 7u ? r : 7u;
 }
 
-// Nibble of one element (x16 = bf16 bits in the low half) under scale c.
-__device__ __forceinline__ uint32_t nibble_rne(uint32_t x16, uint32_t c) {
-    if (c == 0xFFu) return 0u;
-    return code_rne(scaled_u(x16, c)) | ((x16 >> 12) & 8u);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 2^(c-127) as fp32 (c = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float scale_f32(uint32_t c) {
+    return __uint_as_float(c ? (c << 23) : 0x00400000u);
 }
+
+// Four bf16 pairs (element 2i in the low half of p_i) -> 8 nibbles, RNE, saturating.
+__device__ __forceinline__ uint32_t pack8_rne(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
+                                              uint32_t c) {
+    const float sf = scale_f32(c);
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p0), sf, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p1), sf, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p2), sf, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p3), sf, 3);
+    return c == 0xFFu ? 0u : r;      // Inf/NaN block: all nibbles 0
+}
+
+// bf16 pair (lo, hi) from the same half of two words: half 0 = low halves.
+__device__ __forceinline__ uint32_t pair_of(uint32_t lo_word, uint32_t hi_word, int half) {
+    return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
+}
+
 __device__ __forceinline__ uint32_t nibble_sr(uint32_t x16, uint32_t c, uint32_t rbyte) {
     if (c == 0xFFu) return 0u;
     return code_sr(scaled_u(x16, c), rbyte) | ((x16 >> 12) & 8u);
@@ -185,7 +205,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int64_t i = row0 + 8 * q + t;
-            const uint32_t sc = scale_code(a.row.use_2d ? tile_amax : ramax[t]);
+            // rows past M exist only as zero padding of the tiled layout: scale 0 there
+            const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
             uint32_t packed = 0;
             if (a.row.use_sr) {
                 uint32_t rlo = 0, rhi = 0;
@@ -198,11 +219,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
                     packed |= nibble_sr(x16, sc, rb) << (4 * e);
                 }
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    packed |= nibble_rne(x16, sc) << (4 * e);
-                }
+                packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
             }
             if (i < rows_out) {
                 if (LAYOUT == MX_LAYOUT_CANONICAL) {
@@ -272,19 +289,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t j = j0 + u;
-            const uint32_t sc = scale_code(a.col.use_2d ? tile_amax : camax[u]);
+            const uint32_t sc = j < N ? scale_code(a.col.use_2d ? tile_amax : camax[u]) : 0u;
             uint32_t packed = 0;
+            if (a.col.use_sr) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-                uint32_t nib;
-                if (a.col.use_sr) {
+                for (int t = 0; t < 8; ++t) {
+                    uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
                     uint32_t rb = ((u < 4 ? rl[t] : rh[t]) >> (8 * (u & 3))) & 0xFFu;
-                    nib = nibble_sr(x16, sc, rb);
-                } else {
-                    nib = nibble_rne(x16, sc);
+                    packed |= nibble_sr(x16, sc, rb) << (4 * t);
                 }
-                packed |= nib << (4 * t);
+            } else {
+                const int w = u >> 1, h = u & 1;
+                packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
+                                   pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h), sc);
             }
             if (j < rows_out) {
                 if (LAYOUT == MX_LAYOUT_CANONICAL) {
