@@ -31,6 +31,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kFmtFp4 = 4;              // MFMA f8f6f4 format code for E2M1
 constexpr int kBM = 256, kBN = 256;     // workgroup tile
@@ -39,6 +40,8 @@ constexpr int kGA = kBM / 16;           // A atoms (row groups) per k-step per w
 constexpr int kGB = kBN / 16;
 constexpr int kTA = kWM / 16;           // A atoms per wave
 constexpr int kTB = kWN / 16;
+constexpr int kMA = kWM / 32;           // 32x32 MFMA tiles per wave along M (A rows)
+constexpr int kMB = kWN / 32;           // ... along N (B rows)
 constexpr int kAtoms = kGA + kGB;       // atoms per stage
 constexpr int kLoadsPerThread = kAtoms / 4;   // 4 waves, one atom per wave instruction
 constexpr int kXcds = 8;
@@ -51,12 +54,72 @@ __device__ __forceinline__ uint32_t bf16_rne_pair(float lo, float hi) {
     return (ra & 0xFFFFu) | (rb << 16);
 }
 
-// Buffer resource over [p, p + bytes): loads take a wave-uniform SGPR offset
-// plus the lane's VGPR offset.  Every offset the kernel forms is clamped
-// inside the buffer, so no access relies on the range check.
+// Buffer resource over [p, p + bytes).  Loads address it with a per-lane
+// byte offset; an offset at or past `bytes` reads zeros (the hardware range
+// check of raw buffers), which is how k-steps past K_pad become zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
+
+// LDS: 4 k-step stages of 32 atoms (the stage of step k is k % 4, which is
+// also its OPSEL scale byte) and one k-group buffer of 32 scale atoms.  A
+// group's scales are read into registers at its first step; the next group's
+// scales are queued one step later, after every wave passed that read.
+// Separate arrays keep every LDS address a compile-time constant plus lane.
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kAtoms * 1024];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kAtoms * 1024];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kAtoms * 1024];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kAtoms * 1024];
+__shared__ __attribute__((aligned(1024))) uint8_t g_scale[kAtoms * 256];
+
+template <int S>
+__device__ __forceinline__ uint8_t *stage_buf() {
+    return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+}
+
+#define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Offset that lies past every operand buffer: a buffer load there returns 0.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct GemmCtx {
+    __amdgpu_buffer_rsrc_t rA, rB, rAs, rBs;
+    int ld_row[kLoadsPerThread];    // byte offset of this wave's r-th atom row (k-step 0)
+    int sc_row[kLoadsPerThread];    // byte offset of this wave's r-th scale-atom row (k-group 0)
+    int64_t ksteps, kgroups;
+    int wave, lane16, lane4;
+};
+
+// DMA k-step k into stage S (global -> LDS, no registers): wave w copies atoms
+// 4r + w.  Steps past K_pad read out of range and land as zeros.  When k
+// opens a k-group, that group's 32 scale atoms go to the scale buffer.
+template <int S>
+__device__ __forceinline__ void issue_step(const GemmCtx &c, int64_t k) {
+    const bool valid = k < c.ksteps;
+    const uint32_t koff = (uint32_t)(k * 1024);
+#pragma unroll
+    for (int r = 0; r < kLoadsPerThread; ++r) {
+        const int a = 4 * r + c.wave;
+        const uint32_t voff = valid ? (uint32_t)c.ld_row[r] + koff + c.lane16 : kOutOfRange + c.lane16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS(stage_buf<S>() + a * 1024), 16,
+                                                 voff, 0, 0, 0);
+    }
+    if (S == 0) {
+        const int64_t h = k / 4;
+        const bool hvalid = h < c.kgroups;
+        const uint32_t hoff = (uint32_t)(h * 256);
+#pragma unroll
+        for (int r = 0; r < kLoadsPerThread; ++r) {
+            const int a = 4 * r + c.wave;
+            const uint32_t voff = hvalid ? (uint32_t)c.sc_row[r] + hoff + c.lane4 : kOutOfRange + c.lane4;
+            uint8_t *dst = g_scale + a * 256;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(dst), 4, voff, 0, 0, 0);
+        }
+    }
+}
+
+// Vector-memory instructions a wave issues for k-step j (data, plus scales at a group start).
+__host__ __device__ constexpr int issued_for(int j_mod4) { return kLoadsPerThread * (j_mod4 == 0 ? 2 : 1); }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
@@ -65,8 +128,6 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
                                                         const uint8_t *__restrict__ B,
                                                         const uint8_t *__restrict__ Bs,
                                                         void *__restrict__ C, int64_t ldc) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kAtoms * 1024];
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wm = wave >> 1, wn = wave & 1;
@@ -83,21 +144,20 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
     const int tm = first_m + (id % band) % gsz;
     const int tn = (id % band) / gsz;
 
-    const int64_t ksteps = K_pad / 128;
-    const int64_t kgroups = cdiv(K_pad, 512);
+    GemmCtx c;
+    c.ksteps = K_pad / 128;
+    c.kgroups = cdiv(K_pad, 512);
+    c.wave = wave;
+    c.lane16 = lane * 16;
+    c.lane4 = lane * 4;
     const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);   // row groups present in memory
     const int64_t gA0 = (int64_t)tm * kGA, gB0 = (int64_t)tn * kGB;
-
-    // ---- global -> register staging of one k-step: wave w loads atoms 4r + w.
-    // Row groups past the operand are clamped to its last group (their results
-    // are never stored); k-steps past K_pad (the tail of the last k-group) are
-    // loaded clamped and zeroed, so every k-group runs 4 branch-free steps and
-    // the padding contributes exact zeros (the layout's pad scale bytes are 0).
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, nGA * ksteps * 1024);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(B, nGB * ksteps * 1024);
-    const __amdgpu_buffer_rsrc_t rAs = make_rsrc(As, nGA * kgroups * 256);
-    const __amdgpu_buffer_rsrc_t rBs = make_rsrc(Bs, nGB * kgroups * 256);
-    int ld_row[kLoadsPerThread];                 // wave-uniform atom-row offsets (bytes)
+    c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
+    c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
+    c.rAs = make_rsrc(As, nGA * c.kgroups * 256);
+    c.rBs = make_rsrc(Bs, nGB * c.kgroups * 256);
+    // Row groups past an operand are clamped to its last group: those rows of C
+    // are never stored, so their contents do not matter.
 #pragma unroll
     for (int r = 0; r < kLoadsPerThread; ++r) {
         const int a = 4 * r + wave;
@@ -105,140 +165,118 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
         int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
         const int64_t gmax = (isA ? nGA : nGB) - 1;
         g = g < gmax ? g : gmax;
-        ld_row[r] = (int)(g * ksteps * 1024);
+        c.ld_row[r] = (int)(g * c.ksteps * 1024);
+        c.sc_row[r] = (int)(g * c.kgroups * 256);
     }
-    int sa_row[kTA], sb_row[kTB];                // wave-uniform scale-row offsets (bytes)
-#pragma unroll
-    for (int j = 0; j < kTA; ++j) {
-        int64_t g = gA0 + wm * kTA + j;
-        g = g < nGA - 1 ? g : nGA - 1;
-        sa_row[j] = (int)(g * kgroups * 256);
-    }
-#pragma unroll
-    for (int i = 0; i < kTB; ++i) {
-        int64_t g = gB0 + wn * kTB + i;
-        g = g < nGB - 1 ? g : nGB - 1;
-        sb_row[i] = (int)(g * kgroups * 256);
-    }
-    const int lane16 = lane * 16, lane4 = lane * 4;
 
-    uint4 stage[kLoadsPerThread];
-    // Issue the 8 global loads of k-step k (clamped into the operand); the data
-    // is consumed only by store_step, after this step's MFMAs.
-    auto load_step = [&](int64_t k) {
-        const int kc = (int)(k < ksteps ? k : ksteps - 1);
+    v16f acc[kMB][kMA];
 #pragma unroll
-        for (int r = 0; r < kLoadsPerThread; ++r) {
-            const bool isA = 4 * r + wave < kGA;
-            stage[r] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(isA ? rA : rB, lane16, ld_row[r] + kc * 1024, 0));
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+
+    issue_step<0>(c, 0);
+    issue_step<1>(c, 1);
+    issue_step<2>(c, 2);
+
+    // Scale dwords for the current k-group: one per lane per 32-row tile and
+    // 64-wide k half (byte = k-step within the group, picked by OPSEL).
+    uint32_t sa[kMA][2], sb[kMB][2];
+    // One 128-wide k-step from stage S (= k % 4 = OPSEL), as two 64-wide halves
+    // of V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Lane L of a 32-row operand tile
+    // takes row L%32, k-block 2*half + L/32: in the tiled layout that is atom
+    // (L%32)/16, slice (L%16) + 16*(2*half + L/32) -- four contiguous 256-byte
+    // runs per ds_read_b128, so the reads stay conflict-free.
+    // Every step first waits for its own DMA (the two later steps stay in
+    // flight), meets the other waves at a barrier (their DMA for this step is
+    // done, and they are done reading the stage refilled next), then queues
+    // step k+3.
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;   // half 0; half 1 adds 512
+    const int sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;       // half 0; half 1 adds 128
+    auto one_step = [&](int64_t k, auto s_tag) {
+        constexpr int S = decltype(s_tag)::value;
+        constexpr int kPending = issued_for((S + 1) & 3) + issued_for((S + 2) & 3);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kPending) : "memory");
+        issue_step<(S + 3) & 3>(c, k + 3);
+        if (S == 0) {
+#pragma unroll
+            for (int t = 0; t < kMA; ++t)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    sa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (wm * kTA + 2 * t) * 256 + sc_off + hh * 128);
+#pragma unroll
+            for (int t = 0; t < kMB; ++t)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    sb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (kGA + wn * kTB + 2 * t) * 256 + sc_off + hh * 128);
         }
-    };
-    // Write the staged step into LDS buffer buf; steps past K_pad become zeros.
-    auto store_step = [&](int buf, bool keep) {
-        const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+        const uint8_t *a_lds = stage_buf<S>() + (wm * kTA) * 1024 + frag_off;
+        const uint8_t *b_lds = stage_buf<S>() + (kGA + wn * kTB) * 1024 + frag_off;
 #pragma unroll
-        for (int r = 0; r < kLoadsPerThread; ++r)
-            *reinterpret_cast<uint4 *>(&lds[buf][(4 * r + wave) * 1024 + lane16]) =
-                uint4{stage[r].x & m, stage[r].y & m, stage[r].z & m, stage[r].w & m};
-    };
-
-    uint32_t sa_cur[kTA], sb_cur[kTB], sa_nxt[kTA], sb_nxt[kTB];
-    auto load_scales = [&](int64_t h, uint32_t (&sa)[kTA], uint32_t (&sb)[kTB]) {
-        const int hc = (int)(h < kgroups ? h : kgroups - 1);
+        for (int hh = 0; hh < 2; ++hh) {
+            uint4 af[kMA], bf[kMB];
 #pragma unroll
-        for (int j = 0; j < kTA; ++j) sa[j] = __builtin_amdgcn_raw_buffer_load_b32(rAs, lane4, sa_row[j] + hc * 256, 0);
+            for (int t = 0; t < kMA; ++t) af[t] = *reinterpret_cast<const uint4 *>(a_lds + t * 2048 + hh * 512);
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) sb[i] = __builtin_amdgcn_raw_buffer_load_b32(rBs, lane4, sb_row[i] + hc * 256, 0);
-    };
-
-    v4f acc[kTB][kTA];
+            for (int t = 0; t < kMB; ++t) bf[t] = *reinterpret_cast<const uint4 *>(b_lds + t * 2048 + hh * 512);
 #pragma unroll
-    for (int i = 0; i < kTB; ++i)
+            for (int i = 0; i < kMB; ++i) {
+                const v8i bop = {(int)bf[i].x, (int)bf[i].y, (int)bf[i].z, (int)bf[i].w, 0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < kTA; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    load_scales(0, sa_cur, sb_cur);
-    load_step(0);
-    store_step(0, true);
-    __syncthreads();
-
-    // One 128-wide k-step from LDS buffer buf; OPSEL picks the step's scale byte.
-    // The next step's loads are in flight meanwhile; sched_barriers keep the
-    // compiler from sinking MFMAs past the buffer hand-over.
-    auto one_step = [&](int64_t k, auto opsel_tag) {
-        constexpr int OPSEL = decltype(opsel_tag)::value;
-        const int buf = (int)(k & 1);
-        load_step(k + 1);
-        const uint8_t *a_lds = &lds[buf][(wm * kTA) * 1024 + lane16];
-        const uint8_t *b_lds = &lds[buf][(kGA + wn * kTB) * 1024 + lane16];
-        uint4 af[kTA];
-#pragma unroll
-        for (int j = 0; j < kTA; ++j) af[j] = *reinterpret_cast<const uint4 *>(a_lds + j * 1024);
-        uint4 bnext = *reinterpret_cast<const uint4 *>(b_lds);
-#pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-            const uint4 bcur = bnext;
-            if (i + 1 < kTB) bnext = *reinterpret_cast<const uint4 *>(b_lds + (i + 1) * 1024);
-            const v8i bop = {(int)bcur.x, (int)bcur.y, (int)bcur.z, (int)bcur.w, 0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < kTA; ++j) {
-                const v8i aop = {(int)af[j].x, (int)af[j].y, (int)af[j].z, (int)af[j].w, 0, 0, 0, 0};
-                // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    bop, aop, acc[i][j], kFmtFp4, kFmtFp4, OPSEL, (int)sb_cur[i], OPSEL, (int)sa_cur[j]);
+                for (int j = 0; j < kMA; ++j) {
+                    const v8i aop = {(int)af[j].x, (int)af[j].y, (int)af[j].z, (int)af[j].w, 0, 0, 0, 0};
+                    // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bop, aop, acc[i][j], kFmtFp4, kFmtFp4, S, (int)sb[i][hh], S, (int)sa[j][hh]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();                // every wave is done reading the buffer about to be refilled
-        store_step(buf ^ 1, k + 1 < ksteps);
-        __syncthreads();                // the refilled buffer is visible
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    for (int64_t h = 0; h < kgroups; ++h) {
+    for (int64_t h = 0; h < c.kgroups; ++h) {
         const int64_t k0 = 4 * h;
-        load_scales(h + 1, sa_nxt, sb_nxt);
         one_step(k0, std::integral_constant<int, 0>{});
         one_step(k0 + 1, std::integral_constant<int, 1>{});
         one_step(k0 + 2, std::integral_constant<int, 2>{});
         one_step(k0 + 3, std::integral_constant<int, 3>{});
-#pragma unroll
-        for (int j = 0; j < kTA; ++j) sa_cur[j] = sa_nxt[j];
-#pragma unroll
-        for (int i = 0; i < kTB; ++i) sb_cur[i] = sb_nxt[i];
     }
+    // drain the trailing (out-of-range) DMAs before the workgroup exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- epilogue: acc[i][j][r] = C[m0 + 16j + lane%16][n0 + 16i + 4*(lane/16) + r]
+    // ---- epilogue: acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4]
     const int64_t m0 = (int64_t)tm * kBM + wm * kWM;
     const int64_t n0 = (int64_t)tn * kBN + wn * kWN;
 #pragma unroll
-    for (int j = 0; j < kTA; ++j) {
-        const int64_t row = m0 + 16 * j + (lane & 15);
+    for (int j = 0; j < kMA; ++j) {
+        const int64_t row = m0 + 32 * j + lrow;
         if (row >= M) continue;
 #pragma unroll
-        for (int i = 0; i < kTB; ++i) {
-            const int64_t col = n0 + 16 * i + 4 * (lane >> 4);
-            const v4f v = acc[i][j];
-            if (OUT_BF16) {
-                uint16_t *dst = reinterpret_cast<uint16_t *>(C) + row * ldc + col;
-                if (col + 3 < N) {
-                    uint2 p = {bf16_rne_pair(v[0], v[1]), bf16_rne_pair(v[2], v[3])};
-                    *reinterpret_cast<uint2 *>(dst) = p;
-                } else {
-                    const uint32_t p01 = bf16_rne_pair(v[0], v[1]), p23 = bf16_rne_pair(v[2], v[3]);
-                    if (col < N) dst[0] = (uint16_t)p01;
-                    if (col + 1 < N) dst[1] = (uint16_t)(p01 >> 16);
-                    if (col + 2 < N) dst[2] = (uint16_t)p23;
-                }
-            } else {
-                float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
-                if (col + 3 < N) {
-                    *reinterpret_cast<v4f *>(dst) = v;
-                } else {
+        for (int i = 0; i < kMB; ++i) {
 #pragma unroll
-                    for (int r = 0; r < 3; ++r)
-                        if (col + r < N) dst[r] = v[r];
+            for (int q = 0; q < 4; ++q) {
+                const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
+                const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (OUT_BF16) {
+                    uint16_t *dst = reinterpret_cast<uint16_t *>(C) + row * ldc + col;
+                    const uint32_t p01 = bf16_rne_pair(v[0], v[1]), p23 = bf16_rne_pair(v[2], v[3]);
+                    if (col + 3 < N) {
+                        *reinterpret_cast<uint2 *>(dst) = uint2{p01, p23};
+                    } else {
+                        if (col < N) dst[0] = (uint16_t)p01;
+                        if (col + 1 < N) dst[1] = (uint16_t)(p01 >> 16);
+                        if (col + 2 < N) dst[2] = (uint16_t)p23;
+                    }
+                } else {
+                    float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
+                    if (col + 3 < N) {
+                        *reinterpret_cast<v4f *>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 3; ++r)
+                            if (col + r < N) dst[r] = v[r];
+                    }
                 }
             }
         }
