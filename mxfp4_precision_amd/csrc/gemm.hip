@@ -26,6 +26,7 @@
 
 #include "mx_internal.h"
 
+
 namespace mx {
 namespace {
 
@@ -179,59 +180,105 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
     issue_step<1>(c, 1);
     issue_step<2>(c, 2);
 
-    // Scale dwords for the current k-group: one per lane per 32-row tile and
-    // 64-wide k half (byte = k-step within the group, picked by OPSEL).
-    uint32_t sa[kMA][2], sb[kMB][2];
-    // One 128-wide k-step from stage S (= k % 4 = OPSEL), as two 64-wide halves
-    // of V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Lane L of a 32-row operand tile
-    // takes row L%32, k-block 2*half + L/32: in the tiled layout that is atom
+    // Lane L of a 32-row operand tile takes row L%32, k-block 2*half + L/32 of
+    // V_MFMA_SCALE_F32_32X32X64_F8F6F4: in the tiled layout that is atom
     // (L%32)/16, slice (L%16) + 16*(2*half + L/32) -- four contiguous 256-byte
-    // runs per ds_read_b128, so the reads stay conflict-free.
-    // Every step first waits for its own DMA (the two later steps stay in
-    // flight), meets the other waves at a barrier (their DMA for this step is
-    // done, and they are done reading the stage refilled next), then queues
-    // step k+3.
+    // runs per ds_read_b128, so the reads stay conflict-free.  Its scale is
+    // byte (k-step % 4) of the dword at the same slice of the scale atom.
     const int lrow = lane & 31, lhi = lane >> 5;
     const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;   // half 0; half 1 adds 512
     const int sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;       // half 0; half 1 adds 128
+
+    uint32_t sa[kMA][2], sb[kMB][2], sa_n[kMA][2], sb_n[kMB][2];
+    uint4 fa0[kMA], fb0[kMB], fa1[kMA], fb1[kMB];
+    auto read_scales = [&](uint32_t (&xa)[kMA][2], uint32_t (&xb)[kMB][2]) {
+#pragma unroll
+        for (int t = 0; t < kMA; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                xa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (wm * kTA + 2 * t) * 256 + sc_off + hh * 128);
+#pragma unroll
+        for (int t = 0; t < kMB; ++t)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                xb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (kGA + wn * kTB + 2 * t) * 256 + sc_off + hh * 128);
+    };
+    auto read_frags = [&](const uint8_t *stage, int hh, uint4 (&xa)[kMA], uint4 (&xb)[kMB]) {
+        const uint8_t *a_lds = stage + (wm * kTA) * 1024 + frag_off + hh * 512;
+        const uint8_t *b_lds = stage + (kGA + wn * kTB) * 1024 + frag_off + hh * 512;
+#pragma unroll
+        for (int t = 0; t < kMA; ++t) xa[t] = *reinterpret_cast<const uint4 *>(a_lds + t * 2048);
+#pragma unroll
+        for (int t = 0; t < kMB; ++t) xb[t] = *reinterpret_cast<const uint4 *>(b_lds + t * 2048);
+    };
+    auto mfmas = [&](auto s_tag, int hh, const uint4 (&xa)[kMA], const uint4 (&xb)[kMB]) {
+        constexpr int S = decltype(s_tag)::value;
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) {
+            const v8i bop = {(int)xb[i].x, (int)xb[i].y, (int)xb[i].z, (int)xb[i].w, 0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < kMA; ++j) {
+                const v8i aop = {(int)xa[j].x, (int)xa[j].y, (int)xa[j].z, (int)xa[j].w, 0, 0, 0, 0};
+                // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    bop, aop, acc[i][j], kFmtFp4, kFmtFp4, S, (int)sb[i][hh], S, (int)sa[j][hh]);
+            }
+        }
+    };
+
+    // Prologue: step 0 landed, group 0 scales and step 0's first half in registers.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + issued_for(2)) : "memory");
+    read_scales(sa, sb);
+    read_frags(stage_buf<0>(), 0, fa0, fb0);
+
+    // One 128-wide k-step (stage S = k % 4 = OPSEL), software-pipelined so the
+    // MFMA pipe never drains: the first half's 16 MFMAs are interleaved with
+    // the reads of the second half's operands; then the workgroup meets at the
+    // barrier that publishes step k+1 (each wave waits for its own DMA of step
+    // k+1 first) and frees stage k-1; the second half's 16 MFMAs are
+    // interleaved with the DMA of step k+3 into stage k-1 and the reads of
+    // step k+1's first half.  Every memory instruction issues in the shadow of
+    // an MFMA (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read,
+    // 0x100 DS read).
     auto one_step = [&](int64_t k, auto s_tag) {
         constexpr int S = decltype(s_tag)::value;
-        constexpr int kPending = issued_for((S + 1) & 3) + issued_for((S + 2) & 3);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kPending) : "memory");
-        issue_step<(S + 3) & 3>(c, k + 3);
-        if (S == 0) {
+        mfmas(s_tag, 0, fa0, fb0);
+        read_frags(stage_buf<S>(), 1, fa1, fb1);
 #pragma unroll
-            for (int t = 0; t < kMA; ++t)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    sa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (wm * kTA + 2 * t) * 256 + sc_off + hh * 128);
-#pragma unroll
-            for (int t = 0; t < kMB; ++t)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    sb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (kGA + wn * kTB + 2 * t) * 256 + sc_off + hh * 128);
+        for (int t = 0; t < kMA + kMB; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        const uint8_t *a_lds = stage_buf<S>() + (wm * kTA) * 1024 + frag_off;
-        const uint8_t *b_lds = stage_buf<S>() + (kGA + wn * kTB) * 1024 + frag_off;
+        __builtin_amdgcn_sched_group_barrier(0x008, kMA * kMB - (kMA + kMB), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3)) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue_step<(S + 3) & 3>(c, k + 3);
+        mfmas(s_tag, 1, fa1, fb1);
+        if (S == 3) read_scales(sa_n, sb_n);
+        read_frags(stage_buf<(S + 1) & 3>(), 0, fa0, fb0);
+        constexpr int kDma = issued_for((S + 3) & 3);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            uint4 af[kMA], bf[kMB];
+        for (int t = 0; t < kDma; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+        }
+        constexpr int kDs = (kMA + kMB) + (S == 3 ? 2 * (kMA + kMB) : 0);
+        constexpr int kMfmaLeft = kMA * kMB - kDma;
+        constexpr int kPairs = kDs < kMfmaLeft ? kDs : kMfmaLeft;
 #pragma unroll
-            for (int t = 0; t < kMA; ++t) af[t] = *reinterpret_cast<const uint4 *>(a_lds + t * 2048 + hh * 512);
+        for (int t = 0; t < kPairs; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        }
+        if (kMfmaLeft > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfmaLeft - kPairs, 1);
+        if (kDs > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kDs - kPairs, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (S == 3) {
 #pragma unroll
-            for (int t = 0; t < kMB; ++t) bf[t] = *reinterpret_cast<const uint4 *>(b_lds + t * 2048 + hh * 512);
+            for (int t = 0; t < kMA; ++t) { sa[t][0] = sa_n[t][0]; sa[t][1] = sa_n[t][1]; }
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-                const v8i bop = {(int)bf[i].x, (int)bf[i].y, (int)bf[i].z, (int)bf[i].w, 0, 0, 0, 0};
-#pragma unroll
-                for (int j = 0; j < kMA; ++j) {
-                    const v8i aop = {(int)af[j].x, (int)af[j].y, (int)af[j].z, (int)af[j].w, 0, 0, 0, 0};
-                    // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bop, aop, acc[i][j], kFmtFp4, kFmtFp4, S, (int)sb[i][hh], S, (int)sa[j][hh]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < kMB; ++t) { sb[t][0] = sb_n[t][0]; sb[t][1] = sb_n[t][1]; }
         }
     };
 
@@ -321,3 +368,4 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
 }
 
 }  // namespace mx
+
