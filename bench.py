@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=32,
                    help="token slice of the step the CPU oracle is timed on")
+    p.add_argument("--profile-copy-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (a known-size kernel "
+                        "that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
 
 
@@ -82,6 +85,14 @@ def main():
     Y = torch.empty((tokens, dout), dtype=torch.int16, device=dev)
     dX = torch.empty((tokens, din), dtype=torch.int16, device=dev)
     dW = torch.empty((dout, din), dtype=torch.int16, device=dev)
+
+    if args.profile_copy_mib:
+        n = args.profile_copy_mib << 20
+        src = torch.ones(n // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     o_plain = mx.quant_opts()
     o_w = mx.quant_opts(use_2d_block=True, tensor_id=1)
@@ -150,6 +161,7 @@ def main():
             entry["frac_hbm_peak"] = round(qb[n] / (per[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         kernels[n] = entry
 
+    traffic = load_traffic()
     # Dominant kernel: the GEMM (one kernel, three launches of equal flops per launch).
     gemm_ms = float(np.mean([per[n] for n in gemm_shapes]))
     gemm_achieved = (step_flops / 3) / (gemm_ms * 1e-3) / 1e12
@@ -176,10 +188,12 @@ def main():
                    "layout": "tiled", "parallelism": "none (1 GPU)"},
         "roofline": {"kernel": "mx_gemm_a4w4", "bound": "mfma",
                      "achieved": round(gemm_achieved, 1), "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_achieved / PEAK_FP4_TFLOPS, 4), "traffic": None},
+                     "frac": round(gemm_achieved / PEAK_FP4_TFLOPS, 4),
+                     "traffic": traffic.get("gemm") if traffic else None},
         "roofline_quantize": {"kernel": "mx_quantize_dual (X %dx%d)" % (tokens, din), "bound": "hbm",
                               "achieved": round(qx_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": round(qx_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                              "frac": round(qx_gbs / PEAK_HBM_GBS, 4),
+                              "traffic": traffic.get("quant_X") if traffic else None},
         "kernels": kernels,
         "input_gen_s": round(gen_s, 1),
     }
@@ -187,6 +201,25 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(data, args.cpu_tokens, din, dout)
     print(json.dumps(out), flush=True)
+
+
+def load_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (profiles/hbm_traffic_fc2_step.json, calibrated against a plain 1 GiB copy), used only
+    while the kernel sources are the ones the counters were taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_fc2_step.json")
+    try:
+        rec = json.load(open(path))
+        for name, digest in rec["source_sha256"].items():
+            src = os.path.join(ROOT, "mxfp4_precision_amd", "csrc", name)
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != digest:
+                return None
+        L = rec["launches"]
+        gemm = sum(L[n]["hbm_bytes"] for n in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad")) / 3.0
+        return {"gemm": int(gemm), "quant_X": int(L["quant_X"]["hbm_bytes"])}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(data, ct, din, dout):
