@@ -40,6 +40,7 @@ constexpr int kWaveRows = 32;
 constexpr int kTileCols = 128;
 constexpr int kWaves = 4;
 constexpr int kTileRows = kWaveRows * kWaves;
+constexpr int kLinePitch = 80;          // LDS bytes per staged 64-byte blob-row line
 
 __device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
     if (amax16 >= 0x7F80u) return 0xFFu;            // Inf or NaN in the block
@@ -138,7 +139,7 @@ __device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
     return umax(v, (uint32_t)__shfl_xor((int)v, mask, 64));
 }
 
-template <int LAYOUT, bool DUAL>
+template <int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -197,93 +198,66 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         tile_amax = m;
     }
 
-    // ---- row-wise blob
-    {
-        const int64_t Lp = a.N_pad;
-        const int64_t rows_out = (LAYOUT == MX_LAYOUT_TILED) ? cdiv(M, 16) * 16 : M;
-        const int64_t kb = col0 / 32 + c / 4;        // k-block of this lane's columns
+    // ---- encode both directions into LDS, then write whole 16-byte slices.
+    // Staging: one 64-byte line per blob row of this workgroup's tile (128 blob
+    // rows per direction, 128 quantized elements each), padded to 80 bytes to
+    // spread LDS banks; scales as 4 bytes per blob row.
+    __shared__ __attribute__((aligned(16))) uint8_t s_data[2][kTileRows * kLinePitch];
+    __shared__ __attribute__((aligned(16))) uint8_t s_scale[2][kTileRows * 4];
+    const int r_loc0 = wave * kWaveRows + 8 * q;      // this lane's first tile row
+
+    // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int64_t i = row0 + 8 * q + t;
-            // rows past M exist only as zero padding of the tiled layout: scale 0 there
-            const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
-            uint32_t packed = 0;
-            if (a.row.use_sr) {
-                uint32_t rlo = 0, rhi = 0;
-                if (i < M && j0 < N) rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0,
-                                           a.row, 0u, rlo, rhi);
+    for (int t = 0; t < 8; ++t) {
+        const int64_t i = row0 + 8 * q + t;
+        // rows past M exist only as zero padding of the tiled layout: scale 0 there
+        const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
+        uint32_t packed = 0;
+        if (ROW_SR) {
+            uint32_t rlo = 0, rhi = 0;
+            if (i < M && j0 < N) rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0,
+                                       a.row, 0u, rlo, rhi);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    uint32_t rb = ((e < 4 ? rlo : rhi) >> (8 * (e & 3))) & 0xFFu;
-                    packed |= nibble_sr(x16, sc, rb) << (4 * e);
-                }
-            } else {
-                packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
+            for (int e = 0; e < 8; ++e) {
+                uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                uint32_t rb = ((e < 4 ? rlo : rhi) >> (8 * (e & 3))) & 0xFFu;
+                packed |= nibble_sr(x16, sc, rb) << (4 * e);
             }
-            if (i < rows_out) {
-                if (LAYOUT == MX_LAYOUT_CANONICAL) {
-                    *reinterpret_cast<uint32_t *>(a.q_row + i * (Lp / 2) + col0 / 2 + 4 * c) = packed;
-                    if ((c & 3) == 0) a.s_row[i * (Lp / 32) + kb] = (uint8_t)sc;
-                } else {
-                    const int64_t ksteps = Lp / 128, kgroups = cdiv(Lp, 512);
-                    const int64_t g = i / 16;
-                    const int64_t atom = (g * ksteps + col0 / 128) * 1024;
-                    const int lane_t = (int)(i % 16) + 16 * (c / 4);
-                    *reinterpret_cast<uint32_t *>(a.q_row + atom + lane_t * 16 + 4 * (c & 3)) = packed;
-                    if ((c & 3) == 0) {
-                        const int64_t satom = (g * kgroups + kb / 16) * 256;
-                        const int slane = (int)(i % 16) + 16 * (int)(kb % 4);
-                        a.s_row[satom + 4 * slane + (kb % 16) / 4] = (uint8_t)sc;
-                    }
-                    // zero the unused tail of the last scale atom (blocks past L_pad/32)
-                    const int64_t nblk = Lp / 32;
-                    const int64_t tail = (16 - nblk % 16) % 16;
-                    if (col0 + kTileCols == Lp && c < tail) {
-                        const int64_t zb = nblk + c;
-                        const int64_t zatom = (g * kgroups + zb / 16) * 256;
-                        const int zl = (int)(i % 16) + 16 * (int)(zb % 4);
-                        a.s_row[zatom + 4 * zl + (zb % 16) / 4] = 0;
-                    }
-                }
-            }
+        } else {
+            packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
         }
+        *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
+        if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
     }
 
-    if (!DUAL) return;
-
-    // ---- column-wise blob: per column u of the lane, 8 rows in-lane, then lanes q^1, q^2
-    uint32_t camax[8];
+    if (DUAL) {
+        // column-wise: per column u of the lane, 8 rows in-lane, then lanes q^1, q^2
+        uint32_t camax[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        uint32_t lo = 0, hi = 0;
+        for (int w = 0; w < 4; ++w) {
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            lo = umax(lo, d[t][w] & 0x7FFFu);
-            hi = umax(hi, (d[t][w] >> 16) & 0x7FFFu);
+            for (int t = 0; t < 8; ++t) {
+                lo = umax(lo, d[t][w] & 0x7FFFu);
+                hi = umax(hi, (d[t][w] >> 16) & 0x7FFFu);
+            }
+            uint32_t pk = lo | (hi << 16);
+            uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 16, 64);
+            lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu); hi = umax(pk >> 16, o1 >> 16);
+            pk = lo | (hi << 16);
+            uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 32, 64);
+            camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
+            camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
         }
-        uint32_t pk = lo | (hi << 16);
-        uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 16, 64);
-        lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu); hi = umax(pk >> 16, o1 >> 16);
-        pk = lo | (hi << 16);
-        uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 32, 64);
-        camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
-        camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
-    }
-    {
-        const int64_t Lp = a.M_pad;
-        const int64_t rows_out = (LAYOUT == MX_LAYOUT_TILED) ? cdiv(N, 16) * 16 : N;
-        const int64_t kb = (row0) / 32;              // k-block along M of this wave
         // SR bytes: element (i, j) with i = row0+8q+t, j = j0+u: n = base + i*N + j
         uint32_t rl[8], rh[8];
-        if (a.col.use_sr) {
+        if (COL_SR) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 const int64_t i = row0 + 8 * q + t;
                 rl[t] = rh[t] = 0;
                 if (i < M && j0 < N)
-                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u,
-                          rl[t], rh[t]);
+                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rl[t], rh[t]);
             }
         }
 #pragma unroll
@@ -291,7 +265,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             const int64_t j = j0 + u;
             const uint32_t sc = j < N ? scale_code(a.col.use_2d ? tile_amax : camax[u]) : 0u;
             uint32_t packed = 0;
-            if (a.col.use_sr) {
+            if (COL_SR) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
@@ -303,30 +277,70 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
                 packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
                                    pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h), sc);
             }
-            if (j < rows_out) {
+            // blob row = tile column 8c+u; this wave's 32 rows are bytes [16*wave, 16*wave+16)
+            *reinterpret_cast<uint32_t *>(&s_data[1][(8 * c + u) * kLinePitch + 16 * wave + 4 * q]) = packed;
+            if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+        }
+    }
+    __syncthreads();
+
+    // ---- write out: direction 0 = row-wise blob, 1 = column-wise blob
+#pragma unroll
+    for (int dir = 0; dir < (DUAL ? 2 : 1); ++dir) {
+        const int64_t R = dir == 0 ? M : N;                      // blob rows
+        const int64_t Lp = dir == 0 ? a.N_pad : a.M_pad;         // padded quantized axis
+        const int64_t rbase = dir == 0 ? row0 - wave * kWaveRows : col0;   // first blob row of the tile
+        const int64_t kbase = dir == 0 ? col0 : row0 - wave * kWaveRows;   // first element along the axis
+        uint8_t *qd = dir == 0 ? a.q_row : a.q_col;
+        uint8_t *sd = dir == 0 ? a.s_row : a.s_col;
+        const int64_t rows_out = (LAYOUT == MX_LAYOUT_TILED) ? cdiv(R, 16) * 16 : R;
+        // data: 512 slices of 16 bytes (one blob row, one 32-element block each)
+#pragma unroll
+        for (int rep = 0; rep < 2; ++rep) {
+            const int ch = (int)threadIdx.x + 256 * rep;
+            int r_loc, part;
+            if (LAYOUT == MX_LAYOUT_TILED) {       // consecutive threads fill one 1 KB atom
+                const int lt = ch & 63;
+                r_loc = 16 * (ch >> 6) + (lt & 15);
+                part = lt >> 4;
+            } else {                                // consecutive threads fill one 64-byte row run
+                r_loc = ch >> 2;
+                part = ch & 3;
+            }
+            const int64_t r = rbase + r_loc;
+            if (r < rows_out) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(&s_data[dir][r_loc * kLinePitch + 16 * part]);
+                int64_t off;
+                if (LAYOUT == MX_LAYOUT_TILED)
+                    off = ((r / 16) * (Lp / 128) + kbase / 128) * 1024 + ((r % 16) + 16 * part) * 16;
+                else
+                    off = r * (Lp / 2) + kbase / 2 + 16 * part;
+                *reinterpret_cast<uint4 *>(qd + off) = v;
+            }
+        }
+        // scales: 4 bytes per blob row
+        if (threadIdx.x < kTileRows) {
+            const int r_loc = (int)threadIdx.x;
+            const int64_t r = rbase + r_loc;
+            if (r < rows_out) {
+                const uint32_t s4 = *reinterpret_cast<const uint32_t *>(&s_scale[dir][r_loc * 4]);
+                const int64_t kb0 = kbase / 32;
                 if (LAYOUT == MX_LAYOUT_CANONICAL) {
-                    *reinterpret_cast<uint32_t *>(a.q_col + j * (Lp / 2) + row0 / 2 + 4 * q) = packed;
-                    if (q == 0) a.s_col[j * (Lp / 32) + kb] = (uint8_t)sc;
+                    *reinterpret_cast<uint32_t *>(sd + r * (Lp / 32) + kb0) = s4;
                 } else {
-                    const int64_t ksteps = Lp / 128, kgroups = cdiv(Lp, 512);
-                    const int64_t g = j / 16;
-                    const int64_t atom = (g * ksteps + row0 / 128) * 1024;
-                    const int lane_t = (int)(j % 16) + 16 * wave;   // (row%128)/32 == wave
-                    *reinterpret_cast<uint32_t *>(a.q_col + atom + lane_t * 16 + 4 * q) = packed;
-                    if (q == 0) {
-                        const int64_t satom = (g * kgroups + kb / 16) * 256;
-                        const int slane = (int)(j % 16) + 16 * (int)(kb % 4);
-                        a.s_col[satom + 4 * slane + (kb % 16) / 4] = (uint8_t)sc;
-                    }
+                    const int64_t kgroups = cdiv(Lp, 512);
+                    const int64_t satom = ((r / 16) * kgroups + kb0 / 16) * 256;
+                    const int m = (int)((kb0 % 16) / 4);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        sd[satom + 4 * ((r % 16) + 16 * b) + m] = (uint8_t)(s4 >> (8 * b));
+                    // the last tile along the axis zeroes the scale bytes past L_pad/32
+                    // blocks in its final scale atom
                     const int64_t nblk = Lp / 32;
-                    const int64_t tail = (16 - nblk % 16) % 16;
-                    if (wave == 0 && (int64_t)blockIdx.y * kTileRows + kTileRows == Lp) {
-                        for (int64_t z = q; z < tail; z += 4) {
-                            const int64_t zb = nblk + z;
-                            const int64_t zatom = (g * kgroups + zb / 16) * 256;
-                            const int zl = (int)(j % 16) + 16 * (int)(zb % 4);
-                            a.s_col[zatom + 4 * zl + (zb % 16) / 4] = 0;
-                        }
+                    if (kbase + kTileCols == Lp && nblk % 16 != 0) {
+                        const int64_t zatom = ((r / 16) * kgroups + nblk / 16) * 256;
+                        for (int64_t zb = nblk; zb < (nblk / 16 + 1) * 16; ++zb)
+                            sd[zatom + 4 * ((r % 16) + 16 * (zb % 4)) + (zb % 16) / 4] = 0;
                     }
                 }
             }
@@ -336,17 +350,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 
 }  // namespace
 
+template <int LAYOUT, bool DUAL>
+hipError_t launch_sr(const QuantArgs &a, dim3 grid, hipStream_t stream) {
+    const bool rs = a.row.use_sr != 0, cs = DUAL && a.col.use_sr != 0;
+    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, true>), grid, dim3(256), 0, stream, a);
+    else if (rs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, false>), grid, dim3(256), 0, stream, a);
+    else if (cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, false>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
     dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
-    dim3 block(256);
-    if (layout == MX_LAYOUT_CANONICAL) {
-        if (dual) hipLaunchKernelGGL((quantize_kernel<MX_LAYOUT_CANONICAL, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((quantize_kernel<MX_LAYOUT_CANONICAL, false>), grid, block, 0, stream, a);
-    } else {
-        if (dual) hipLaunchKernelGGL((quantize_kernel<MX_LAYOUT_TILED, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((quantize_kernel<MX_LAYOUT_TILED, false>), grid, block, 0, stream, a);
-    }
-    return hipGetLastError();
+    if (layout == MX_LAYOUT_CANONICAL)
+        return dual ? launch_sr<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
+                    : launch_sr<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
+    return dual ? launch_sr<MX_LAYOUT_TILED, true>(a, grid, stream) : launch_sr<MX_LAYOUT_TILED, false>(a, grid, stream);
 }
 
 }  // namespace mx
