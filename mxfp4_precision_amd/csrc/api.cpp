@@ -163,6 +163,7 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, con
     a.M_pad = mx::padded(M); a.N_pad = mx::padded(N);
     a.row = to_dir(row_opts);
     a.col = to_dir(col_opts);
+    a.sr_pairs = (N % 16 == 0 && a.row.index_base % 16 == 0 && a.col.index_base % 16 == 0) ? 1u : 0u;
     a.q_row = static_cast<uint8_t *>(q_row);
     a.s_row = static_cast<uint8_t *>(s_row);
     a.q_col = static_cast<uint8_t *>(q_col);

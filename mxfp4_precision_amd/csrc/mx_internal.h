@@ -28,6 +28,7 @@ struct QuantArgs {
     int64_t M, N, ldx;
     int64_t M_pad, N_pad;       // padded quantized axes (col blob, row blob)
     DirOpts row, col;
+    uint32_t sr_pairs;          // 1: N and both index bases are multiples of 16
     uint8_t *q_row, *s_row, *q_col, *s_col;
 };
 

@@ -94,10 +94,10 @@ __device__ __forceinline__ void philox10(uint32_t &c0, uint32_t &c1, uint32_t &c
                                          uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;    // one v_mad_u64_u32 each
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0; c1 = (uint32_t)p1; c2 = n2; c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
     }
 }
@@ -198,6 +198,43 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         tile_amax = m;
     }
 
+    // ---- stochastic-rounding bytes.  One Philox block covers 16 consecutive
+    // row-major elements: the columns of lanes c and c^1.  When both
+    // directions round stochastically and every group starts on a lane pair
+    // (N and both index bases multiples of 16), lane c&1 == d computes the
+    // blocks of direction d for its 8 rows and the pair swaps the halves it
+    // does not need, halving the Philox work; otherwise each lane computes
+    // its own 8-byte windows.
+    uint32_t rrow_lo[8], rrow_hi[8], rcol_lo[8], rcol_hi[8];
+    if (ROW_SR && COL_SR && a.sr_pairs) {
+        const uint32_t p = (uint32_t)(c & 1);
+        const DirOpts &o = p ? a.col : a.row;
+        const uint64_t jpair = (uint64_t)(col0 + 16 * (c >> 1));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t i = row0 + 8 * q + t;
+            const uint64_t g = (o.index_base + (uint64_t)i * (uint64_t)N + jpair) >> 4;
+            uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p;
+            philox10(w0, w1, w2, w3, o.key0, o.key1);
+            const uint32_t r0 = (uint32_t)__shfl_xor((int)(p ? w0 : w2), 1, 64);
+            const uint32_t r1 = (uint32_t)__shfl_xor((int)(p ? w1 : w3), 1, 64);
+            rrow_lo[t] = p ? r0 : w0;
+            rrow_hi[t] = p ? r1 : w1;
+            rcol_lo[t] = p ? w2 : r0;
+            rcol_hi[t] = p ? w3 : r1;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t i = row0 + 8 * q + t;
+            rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
+            if (ROW_SR && i < M && j0 < N)
+                rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
+            if (DUAL && COL_SR && i < M && j0 < N)
+                rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
+        }
+    }
+
     // ---- encode both directions into LDS, then write whole 16-byte slices.
     // Staging: one 64-byte line per blob row of this workgroup's tile (128 blob
     // rows per direction, 128 quantized elements each), padded to 80 bytes to
@@ -214,13 +251,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
         uint32_t packed = 0;
         if (ROW_SR) {
-            uint32_t rlo = 0, rhi = 0;
-            if (i < M && j0 < N) rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0,
-                                       a.row, 0u, rlo, rhi);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                uint32_t rb = ((e < 4 ? rlo : rhi) >> (8 * (e & 3))) & 0xFFu;
+                uint32_t rb = ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu;
                 packed |= nibble_sr(x16, sc, rb) << (4 * e);
             }
         } else {
@@ -249,17 +283,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
             camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
         }
-        // SR bytes: element (i, j) with i = row0+8q+t, j = j0+u: n = base + i*N + j
-        uint32_t rl[8], rh[8];
-        if (COL_SR) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int64_t i = row0 + 8 * q + t;
-                rl[t] = rh[t] = 0;
-                if (i < M && j0 < N)
-                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rl[t], rh[t]);
-            }
-        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t j = j0 + u;
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-                    uint32_t rb = ((u < 4 ? rl[t] : rh[t]) >> (8 * (u & 3))) & 0xFFu;
+                    uint32_t rb = ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu;
                     packed |= nibble_sr(x16, sc, rb) << (4 * t);
                 }
             } else {

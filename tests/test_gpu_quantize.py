@@ -227,3 +227,18 @@ def test_device_dequantize(oracle_mod):
         qw, sw = oracle_mod.quantize(x, 0)
         want = oracle_mod.dequantize(qw, sw, 50, 300)[:, :300]
         assert (got == want).all()
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_stochastic_rounding_distinct_direction_keys(oracle_mod, layout):
+    """Both directions stochastic with different seeds, tensor ids and index bases
+    (multiples of 16, so lane pairs share Philox blocks), plus a 2D row direction."""
+    _require_gpu()
+    x = synth.random_bf16(24, (160, 256), std=0.3)
+    ro = mx.quant_opts(use_sr=True, seed=11, tensor_id=4, index_base=32)
+    co = mx.quant_opts(use_sr=True, seed=(9 << 35) + 3, tensor_id=5, index_base=4096)
+    rkw = dict(use_sr=True, seed=11, tensor_id=4, index_base=32)
+    ckw = dict(use_sr=True, seed=(9 << 35) + 3, tensor_id=5, index_base=4096)
+    check_dual(oracle_mod, x, layout, ro, co, rkw, ckw)
+    ro2 = mx.quant_opts(use_sr=True, use_2d_block=True, seed=11, tensor_id=4)
+    check_dual(oracle_mod, x, layout, ro2, co, dict(use_sr=True, use_2d=True, seed=11, tensor_id=4), ckw)
