@@ -5,27 +5,39 @@
 // forward, dgrad and wgrad of the MXFP4 linear on the page
 // "primus_turbo_mxfp4_local.py" compute.
 //
-// Each 16x16x128 step is one V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both
-// formats FP4: lane L supplies 16 bytes (32 elements) of row L%16, k-block
-// L/16 of each operand, and that block's E8M0 scale as one byte of a VGPR
-// chosen by OPSEL.  The tiled layout stores exactly those 16 bytes at
-// lane*16 of a 1 KB atom and packs a lane's scales for 4 consecutive k-steps
-// into one dword, so operands move with 16-byte loads and ds_read_b128 that
-// never conflict, and a k-group of 4 steps needs one scale dword per lane.
+// MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both formats FP4.  Lane L of a
+// 32-row operand tile supplies 16 bytes (32 elements) of row L%32, k-block
+// 2*half + L/32 of a 128-wide k-step, and that block's E8M0 scale as the byte
+// of a VGPR that OPSEL picks.  The tiled layout puts exactly those 16 bytes at
+// a fixed slice of a 1 KB atom (16 rows x 128 k) and a lane's scales for 4
+// consecutive k-steps in one dword of a 256-byte scale atom, so operands move
+// as whole atoms and are read from LDS with conflict-free ds_read_b128.
 //
-// Tiling: a 256-thread workgroup computes a 256x256 tile of C; its 4 waves
-// each own 128x128 (8x8 MFMA tiles, 256 fp32 accumulators per lane).  Per
-// 128-wide k-step the workgroup stages 16 A atoms and 16 B atoms (32 KB) in
-// LDS, double-buffered: the next step's global loads are in flight while the
-// current step's 64 MFMAs per wave run.  The MFMA is issued with B as the
-// "A" operand, so each lane's 4 accumulators are 4 consecutive columns of one
-// row of C and the epilogue stores 8 contiguous bytes per lane.
-// Workgroups are ordered so that each XCD (8 on MI355X, dispatched
-// round-robin) works on a compact band of output tiles, keeping the A rows
-// and B columns it shares within its own L2.
+// Workgroup: 8 waves (two per SIMD), 256x256 tile of C; wave w owns the
+// 128x64 block at rows 128*(w%2), columns 64*(w/2): 4x2 MFMA tiles, 128 fp32
+// accumulators per lane, under 256 registers so two waves share each SIMD.
+// Every LDS read or DMA instruction a wave issues stalls that wave's MFMA
+// stream for tens of cycles; with two waves per SIMD the other wave's MFMAs
+// fill that gap.
+//
+// Pipeline: LDS holds 4 k-step stages of 32 atoms (16 A + 16 B, 32 KB) and one
+// k-group (4 steps) of scale atoms.  Atoms travel global -> LDS by DMA
+// (buffer_load ... lds, no registers); step k+3 is in flight while step k
+// computes.  Each k-step is two halves of 8 MFMAs per wave; one slot = one
+// MFMA plus, in fixed order, the LDS read of an operand of the next half and
+// the DMA instructions assigned to that slot, so memory instructions are
+// spread evenly between MFMAs.  Half 0 of step k issues the second part of
+// step k+2's DMA, half 1 the first part of step k+3's; the barrier between
+// the halves publishes step k+1 and frees the stage of step k-1.
+//
+// The MFMA is issued with B as the "A" operand, so each lane's accumulators
+// are 4 consecutive columns of one row of C.  Workgroups are ordered so that
+// each XCD (8 on MI355X, dispatched round-robin) works on a compact band of
+// output tiles, keeping the A rows and B columns it shares within its own L2.
+
+#include <type_traits>
 
 #include "mx_internal.h"
-
 
 namespace mx {
 namespace {
@@ -33,27 +45,30 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kFmtFp4 = 4;              // MFMA f8f6f4 format code for E2M1
-constexpr int kBM = 256, kBN = 256;     // workgroup tile
-constexpr int kWM = 128, kWN = 128;     // wave tile
-constexpr int kGA = kBM / 16;           // A atoms (row groups) per k-step per workgroup
+constexpr int kFmtFp4 = 4;                 // MFMA f8f6f4 format code for E2M1
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBM = 256, kBN = 256;        // workgroup tile
+constexpr int kWM = 128, kWN = 64;         // wave tile
+constexpr int kWavesM = kBM / kWM;         // wave grid 2 x 4
+constexpr int kGA = kBM / 16;              // A atoms (16-row groups) per k-step per workgroup
 constexpr int kGB = kBN / 16;
-constexpr int kTA = kWM / 16;           // A atoms per wave
+constexpr int kTA = kWM / 16;              // A atoms per wave
 constexpr int kTB = kWN / 16;
-constexpr int kMA = kWM / 32;           // 32x32 MFMA tiles per wave along M (A rows)
-constexpr int kMB = kWN / 32;           // ... along N (B rows)
-constexpr int kAtoms = kGA + kGB;       // atoms per stage
-constexpr int kLoadsPerThread = kAtoms / 4;   // 4 waves, one atom per wave instruction
+constexpr int kMA = kWM / 32;              // 32x32 MFMA tiles per wave along M (A rows)
+constexpr int kMB = kWN / 32;              // ... along N (B rows)
+constexpr int kAtoms = kGA + kGB;          // atoms per stage
+constexpr int kLoads = kAtoms / kWaves;    // data DMAs per wave per k-step
+constexpr int kHalfLoads = kLoads / 2;
+constexpr int kSlots = kMA * kMB;          // MFMAs per wave per half-step
 constexpr int kXcds = 8;
-constexpr int kGroupM = 8;              // tile rows per band in the tile order
+constexpr int kGroupM = 8;                 // tile rows per band in the tile order
 
-__device__ __forceinline__ uint32_t bf16_rne_pair(float lo, float hi) {
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    uint32_t ra = (a & 0x7FFFFFFFu) > 0x7F800000u ? ((a >> 16) | 0x40u) : ((a + 0x7FFFu + ((a >> 16) & 1u)) >> 16);
-    uint32_t rb = (b & 0x7FFFFFFFu) > 0x7F800000u ? ((b >> 16) | 0x40u) : ((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
-    return (ra & 0xFFFFu) | (rb << 16);
-}
+static_assert(kAtoms % kWaves == 0 && kLoads % 2 == 0, "DMA split");
+static_assert(kMA + kMB <= kSlots, "one operand read per slot");
 
 // Buffer resource over [p, p + bytes).  Loads address it with a per-lane
 // byte offset; an offset at or past `bytes` reads zeros (the hardware range
@@ -62,10 +77,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// LDS: 4 k-step stages of 32 atoms (the stage of step k is k % 4, which is
-// also its OPSEL scale byte) and one k-group buffer of 32 scale atoms.  A
-// group's scales are read into registers at its first step; the next group's
-// scales are queued one step later, after every wave passed that read.
 // Separate arrays keep every LDS address a compile-time constant plus lane.
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kAtoms * 1024];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kAtoms * 1024];
@@ -85,53 +96,170 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 struct GemmCtx {
     __amdgpu_buffer_rsrc_t rA, rB, rAs, rBs;
-    int ld_row[kLoadsPerThread];    // byte offset of this wave's r-th atom row (k-step 0)
-    int sc_row[kLoadsPerThread];    // byte offset of this wave's r-th scale-atom row (k-group 0)
+    int ld_row[kLoads];    // byte offset of this wave's r-th atom row (k-step 0)
+    int sc_row[kLoads];    // byte offset of this wave's r-th scale-atom row (k-group 0)
     int64_t ksteps, kgroups;
     int wave, lane16, lane4;
 };
 
-// DMA k-step k into stage S (global -> LDS, no registers): wave w copies atoms
-// 4r + w.  Steps past K_pad read out of range and land as zeros.  When k
-// opens a k-group, that group's 32 scale atoms go to the scale buffer.
-template <int S>
-__device__ __forceinline__ void issue_step(const GemmCtx &c, int64_t k) {
-    const bool valid = k < c.ksteps;
-    const uint32_t koff = (uint32_t)(k * 1024);
-#pragma unroll
-    for (int r = 0; r < kLoadsPerThread; ++r) {
-        const int a = 4 * r + c.wave;
-        const uint32_t voff = valid ? (uint32_t)c.ld_row[r] + koff + c.lane16 : kOutOfRange + c.lane16;
+struct Regs {
+    uint4 a0[kMA], b0[kMB], a1[kMA], b1[kMB];       // operands of half 0 / half 1
+    uint32_t sa[kMA][2], sb[kMB][2];                // scales of the current k-group
+    uint32_t sa_n[kMA][2], sb_n[kMB][2];            // ... of the next one
+};
+
+// DMA instruction V of k-step k into stage S = k % 4: V < kLoads copies data
+// atom kWaves*V + wave; V >= kLoads (only when k opens a k-group) copies scale
+// atom kWaves*(V - kLoads) + wave.  Past K_pad the offset is out of range and
+// the atom lands as zeros.
+template <int S, int V>
+__device__ __forceinline__ void dma_op(const GemmCtx &c, int64_t k) {
+    if constexpr (V < kLoads) {
+        const int a = kWaves * V + c.wave;
+        const uint32_t base = k < c.ksteps ? (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS(stage_buf<S>() + a * 1024), 16,
-                                                 voff, 0, 0, 0);
-    }
-    if (S == 0) {
+                                                 base + c.lane16, 0, 0, 0);
+    } else {
+        constexpr int R = V - kLoads;
+        const int a = kWaves * R + c.wave;
         const int64_t h = k / 4;
-        const bool hvalid = h < c.kgroups;
-        const uint32_t hoff = (uint32_t)(h * 256);
-#pragma unroll
-        for (int r = 0; r < kLoadsPerThread; ++r) {
-            const int a = 4 * r + c.wave;
-            const uint32_t voff = hvalid ? (uint32_t)c.sc_row[r] + hoff + c.lane4 : kOutOfRange + c.lane4;
-            uint8_t *dst = g_scale + a * 256;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(dst), 4, voff, 0, 0, 0);
-        }
+        const uint32_t base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(g_scale + a * 256), 4,
+                                                 base + c.lane4, 0, 0, 0);
     }
 }
 
-// Vector-memory instructions a wave issues for k-step j (data, plus scales at a group start).
-__host__ __device__ constexpr int issued_for(int j_mod4) { return kLoadsPerThread * (j_mod4 == 0 ? 2 : 1); }
+// A k-step's DMA is issued in two parts: part P holds data atoms
+// [P*kHalfLoads, (P+1)*kHalfLoads) and, when the step opens a k-group, the
+// scale atoms with the same indices.
+__host__ __device__ constexpr int part_ops(int S) { return S == 0 ? 2 * kHalfLoads : kHalfLoads; }
+__host__ __device__ constexpr int part_op(int S, int P, int n) {
+    return n < kHalfLoads ? kHalfLoads * P + n : kLoads + kHalfLoads * P + (n - kHalfLoads);
+}
+// vector-memory instructions a wave issues for a k-step with stage S
+__host__ __device__ constexpr int issued_for(int S) { return 2 * part_ops(S); }
+// slot of the n-th of nv DMA instructions in a half-step
+__host__ __device__ constexpr int dma_slot(int n, int nv) {
+    const int s = 1 + (n * kSlots) / nv;
+    return s > kSlots - 1 ? kSlots - 1 : s;
+}
+
+template <int S, int P, int n = 0>
+__device__ __forceinline__ void dma_part(const GemmCtx &c, int64_t k) {
+    if constexpr (n < part_ops(S)) {
+        dma_op<S, part_op(S, P, n)>(c, k);
+        dma_part<S, P, n + 1>(c, k);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void mfma_tile(v16f &acc, const uint4 &xb, const uint4 &xa, uint32_t sbv, uint32_t sav) {
+    const v8i bop = {(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+    const v8i aop = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+    // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc, kFmtFp4, kFmtFp4, S, (int)sbv, S,
+                                                          (int)sav);
+}
+
+struct Lds {
+    int frag_off;   // this lane's slice within a 32-row pair of atoms (half 0)
+    int sc_off;     // ... within a pair of scale atoms
+    int a_atom0;    // first A atom of this wave's rows
+    int b_atom0;    // first B atom of this wave's columns
+};
+
+// Slot T of half H of the k-step with stage S.
+//  - MFMA T: tile (i, j) = (T / kMA, T % kMA) with the operands of half H.
+//  - LDS read T (T < kMA + kMB) of the other operand set: half 0 reads the
+//    second half of stage S, half 1 the first half of stage S+1, in order of
+//    first use (b[0], a[0..kMA), b[1..kMB)).
+//  - at S == 3, half 1 also reads the next k-group's scales, two per slot.
+//  - the DMA instructions this slot carries (half 0: part 1 of step k+2,
+//    half 1: part 0 of step k+3).
+template <int S, int H, int T>
+__device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
+    constexpr int i = T / kMA, j = T % kMA;
+    if constexpr (H == 0) mfma_tile<S>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
+    else mfma_tile<S>(acc[i][j], r.b1[i], r.a1[j], r.sb[i][1], r.sa[j][1]);
+
+    if constexpr (T < kMA + kMB) {
+        constexpr int RS = H == 0 ? S : ((S + 1) & 3);
+        constexpr int RH = H == 0 ? 1 : 0;
+        const uint8_t *st = stage_buf<RS>() + l.frag_off + RH * 512;
+        if constexpr (T == 0 || T > kMA) {
+            constexpr int bi = T == 0 ? 0 : T - kMA;
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + (l.b_atom0 + 2 * bi) * 1024);
+            if constexpr (H == 0) r.b1[bi] = v; else r.b0[bi] = v;
+        } else {
+            constexpr int ai = T - 1;
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + (l.a_atom0 + 2 * ai) * 1024);
+            if constexpr (H == 0) r.a1[ai] = v; else r.a0[ai] = v;
+        }
+    }
+    constexpr int kScStart = kSlots - (kMA + kMB);
+    if constexpr (H == 1 && S == 3 && T >= kScStart) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int q = 2 * (T - kScStart) + e;
+            const int hh = q & 1, t = q >> 1;
+            if (t < kMA)
+                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            else
+                r.sb_n[t - kMA][hh] =
+                    *reinterpret_cast<const uint32_t *>(g_scale + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
+        }
+    }
+
+    constexpr int DS = H == 0 ? ((S + 2) & 3) : ((S + 3) & 3);
+    constexpr int P = H == 0 ? 1 : 0;
+    constexpr int nv = part_ops(DS);
+    const int64_t dk = H == 0 ? k + 2 : k + 3;
+    if constexpr (dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0)>(c, dk);
+    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1)>(c, dk);
+    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2)>(c, dk);
+    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3)>(c, dk);
+    static_assert(part_ops(0) <= 4, "dma slots");
+    // keep this slot's instructions in this slot
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int S, int H, int T = 0>
+__device__ __forceinline__ void half_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
+    if constexpr (T < kSlots) {
+        slot<S, H, T>(c, k, acc, r, l);
+        half_step<S, H, T + 1>(c, k, acc, r, l);
+    }
+}
+
+// One 128-wide k-step.  The barrier waits for this wave's DMA of step k+1
+// (only step k+2's instructions may still be outstanding) and then for every
+// wave, which publishes step k+1 and certifies that all reads of step k-1's
+// stage are done before half 1 starts overwriting it.
+template <int S>
+__device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
+    __builtin_amdgcn_sched_barrier(0);
+    half_step<S, 0>(c, k, acc, r, l);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3)) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    half_step<S, 1>(c, k, acc, r, l);
+    if constexpr (S == 3) {
+#pragma unroll
+        for (int t = 0; t < kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
+#pragma unroll
+        for (int t = 0; t < kMB; ++t) { r.sb[t][0] = r.sb_n[t][0]; r.sb[t][1] = r.sb_n[t][1]; }
+    }
+}
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
-                                                        int tiles_n, const uint8_t *__restrict__ A,
-                                                        const uint8_t *__restrict__ As,
-                                                        const uint8_t *__restrict__ B,
-                                                        const uint8_t *__restrict__ Bs,
-                                                        void *__restrict__ C, int64_t ldc) {
+__global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
+                                                             int tiles_n, const uint8_t *__restrict__ A,
+                                                             const uint8_t *__restrict__ As,
+                                                             const uint8_t *__restrict__ B,
+                                                             const uint8_t *__restrict__ Bs,
+                                                             void *__restrict__ C, int64_t ldc) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
 
     // ---- tile order: XCD-contiguous ranges, bands of kGroupM tile rows
     const int nb = gridDim.x;
@@ -160,8 +288,8 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
     // Row groups past an operand are clamped to its last group: those rows of C
     // are never stored, so their contents do not matter.
 #pragma unroll
-    for (int r = 0; r < kLoadsPerThread; ++r) {
-        const int a = 4 * r + wave;
+    for (int r = 0; r < kLoads; ++r) {
+        const int a = kWaves * r + wave;
         const bool isA = a < kGA;
         int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
         const int64_t gmax = (isA ? nGA : nGB) - 1;
@@ -176,118 +304,49 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
 #pragma unroll
         for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
 
-    issue_step<0>(c, 0);
-    issue_step<1>(c, 1);
-    issue_step<2>(c, 2);
+    // Prologue: steps 0 and 1 whole, the first part of step 2 (its second
+    // part goes out in step 0's first half).
+    dma_part<0, 0>(c, 0);
+    dma_part<0, 1>(c, 0);
+    dma_part<1, 0>(c, 1);
+    dma_part<1, 1>(c, 1);
+    dma_part<2, 0>(c, 2);
 
-    // Lane L of a 32-row operand tile takes row L%32, k-block 2*half + L/32 of
-    // V_MFMA_SCALE_F32_32X32X64_F8F6F4: in the tiled layout that is atom
-    // (L%32)/16, slice (L%16) + 16*(2*half + L/32) -- four contiguous 256-byte
-    // runs per ds_read_b128, so the reads stay conflict-free.  Its scale is
-    // byte (k-step % 4) of the dword at the same slice of the scale atom.
+    // Lane L of a 32-row operand tile takes row L%32, k-block 2*half + L/32:
+    // atom (L%32)/16, slice (L%16) + 16*(2*half + L/32).  Its scale is byte
+    // (k-step % 4) of the dword at the same slice of the scale atom.
     const int lrow = lane & 31, lhi = lane >> 5;
-    const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;   // half 0; half 1 adds 512
-    const int sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;       // half 0; half 1 adds 128
+    Lds l;
+    l.frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;
+    l.sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;
+    l.a_atom0 = wm * kTA;
+    l.b_atom0 = kGA + wn * kTB;
 
-    uint32_t sa[kMA][2], sb[kMB][2], sa_n[kMA][2], sb_n[kMB][2];
-    uint4 fa0[kMA], fb0[kMB], fa1[kMA], fb1[kMB];
-    auto read_scales = [&](uint32_t (&xa)[kMA][2], uint32_t (&xb)[kMB][2]) {
+    Regs r;
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + part_ops(2)) : "memory");
 #pragma unroll
-        for (int t = 0; t < kMA; ++t)
+    for (int t = 0; t < kMA; ++t)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                xa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (wm * kTA + 2 * t) * 256 + sc_off + hh * 128);
+        for (int hh = 0; hh < 2; ++hh)
+            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
 #pragma unroll
-        for (int t = 0; t < kMB; ++t)
+    for (int t = 0; t < kMB; ++t)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                xb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (kGA + wn * kTB + 2 * t) * 256 + sc_off + hh * 128);
-    };
-    auto read_frags = [&](const uint8_t *stage, int hh, uint4 (&xa)[kMA], uint4 (&xb)[kMB]) {
-        const uint8_t *a_lds = stage + (wm * kTA) * 1024 + frag_off + hh * 512;
-        const uint8_t *b_lds = stage + (kGA + wn * kTB) * 1024 + frag_off + hh * 512;
+        for (int hh = 0; hh < 2; ++hh)
+            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
 #pragma unroll
-        for (int t = 0; t < kMA; ++t) xa[t] = *reinterpret_cast<const uint4 *>(a_lds + t * 2048);
+    for (int t = 0; t < kMA; ++t)
+        r.a0[t] = *reinterpret_cast<const uint4 *>(g_stage0 + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
 #pragma unroll
-        for (int t = 0; t < kMB; ++t) xb[t] = *reinterpret_cast<const uint4 *>(b_lds + t * 2048);
-    };
-    auto mfmas = [&](auto s_tag, int hh, const uint4 (&xa)[kMA], const uint4 (&xb)[kMB]) {
-        constexpr int S = decltype(s_tag)::value;
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            const v8i bop = {(int)xb[i].x, (int)xb[i].y, (int)xb[i].z, (int)xb[i].w, 0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < kMA; ++j) {
-                const v8i aop = {(int)xa[j].x, (int)xa[j].y, (int)xa[j].z, (int)xa[j].w, 0, 0, 0, 0};
-                // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    bop, aop, acc[i][j], kFmtFp4, kFmtFp4, S, (int)sb[i][hh], S, (int)sa[j][hh]);
-            }
-        }
-    };
-
-    // Prologue: step 0 landed, group 0 scales and step 0's first half in registers.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + issued_for(2)) : "memory");
-    read_scales(sa, sb);
-    read_frags(stage_buf<0>(), 0, fa0, fb0);
-
-    // One 128-wide k-step (stage S = k % 4 = OPSEL), software-pipelined so the
-    // MFMA pipe never drains: the first half's 16 MFMAs are interleaved with
-    // the reads of the second half's operands; then the workgroup meets at the
-    // barrier that publishes step k+1 (each wave waits for its own DMA of step
-    // k+1 first) and frees stage k-1; the second half's 16 MFMAs are
-    // interleaved with the DMA of step k+3 into stage k-1 and the reads of
-    // step k+1's first half.  Every memory instruction issues in the shadow of
-    // an MFMA (sched_group_barrier masks: 0x008 MFMA, 0x020 VMEM read,
-    // 0x100 DS read).
-    auto one_step = [&](int64_t k, auto s_tag) {
-        constexpr int S = decltype(s_tag)::value;
-        mfmas(s_tag, 0, fa0, fb0);
-        read_frags(stage_buf<S>(), 1, fa1, fb1);
-#pragma unroll
-        for (int t = 0; t < kMA + kMB; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kMA * kMB - (kMA + kMB), 0);
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3)) : "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        issue_step<(S + 3) & 3>(c, k + 3);
-        mfmas(s_tag, 1, fa1, fb1);
-        if (S == 3) read_scales(sa_n, sb_n);
-        read_frags(stage_buf<(S + 1) & 3>(), 0, fa0, fb0);
-        constexpr int kDma = issued_for((S + 3) & 3);
-#pragma unroll
-        for (int t = 0; t < kDma; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-        }
-        constexpr int kDs = (kMA + kMB) + (S == 3 ? 2 * (kMA + kMB) : 0);
-        constexpr int kMfmaLeft = kMA * kMB - kDma;
-        constexpr int kPairs = kDs < kMfmaLeft ? kDs : kMfmaLeft;
-#pragma unroll
-        for (int t = 0; t < kPairs; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-        }
-        if (kMfmaLeft > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfmaLeft - kPairs, 1);
-        if (kDs > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kDs - kPairs, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (S == 3) {
-#pragma unroll
-            for (int t = 0; t < kMA; ++t) { sa[t][0] = sa_n[t][0]; sa[t][1] = sa_n[t][1]; }
-#pragma unroll
-            for (int t = 0; t < kMB; ++t) { sb[t][0] = sb_n[t][0]; sb[t][1] = sb_n[t][1]; }
-        }
-    };
+    for (int t = 0; t < kMB; ++t)
+        r.b0[t] = *reinterpret_cast<const uint4 *>(g_stage0 + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
 
     for (int64_t h = 0; h < c.kgroups; ++h) {
         const int64_t k0 = 4 * h;
-        one_step(k0, std::integral_constant<int, 0>{});
-        one_step(k0 + 1, std::integral_constant<int, 1>{});
-        one_step(k0 + 2, std::integral_constant<int, 2>{});
-        one_step(k0 + 3, std::integral_constant<int, 3>{});
+        k_step<0>(c, k0, acc, r, l);
+        k_step<1>(c, k0 + 1, acc, r, l);
+        k_step<2>(c, k0 + 2, acc, r, l);
+        k_step<3>(c, k0 + 3, acc, r, l);
     }
     // drain the trailing (out-of-range) DMAs before the workgroup exits
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -306,8 +365,10 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
                 const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
                 const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 if (OUT_BF16) {
+                    // V_CVT_PK_BF16_F32: round to nearest even
                     uint16_t *dst = reinterpret_cast<uint16_t *>(C) + row * ldc + col;
-                    const uint32_t p01 = bf16_rne_pair(v[0], v[1]), p23 = bf16_rne_pair(v[2], v[3]);
+                    const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v[0], v[1]}), bf16x2_t));
+                    const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v[2], v[3]}), bf16x2_t));
                     if (col + 3 < N) {
                         *reinterpret_cast<uint2 *>(dst) = uint2{p01, p23};
                     } else {
@@ -321,8 +382,8 @@ __global__ __launch_bounds__(256) void gemm_a4w4_kernel(int64_t M, int64_t N, in
                         *reinterpret_cast<v4f *>(dst) = v;
                     } else {
 #pragma unroll
-                        for (int r = 0; r < 3; ++r)
-                            if (col + r < N) dst[r] = v[r];
+                        for (int e = 0; e < 3; ++e)
+                            if (col + e < N) dst[e] = v[e];
                     }
                 }
             }
@@ -359,13 +420,12 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
     const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
     if (out_dtype == MX_BF16)
-        hipLaunchKernelGGL(gemm_a4w4_kernel<true>, grid, dim3(256), 0, stream, M, N, K_pad, tiles_m, tiles_n,
+        hipLaunchKernelGGL(gemm_a4w4_kernel<true>, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n,
                            A, As, B, Bs, C, ldc);
     else
-        hipLaunchKernelGGL(gemm_a4w4_kernel<false>, grid, dim3(256), 0, stream, M, N, K_pad, tiles_m,
+        hipLaunchKernelGGL(gemm_a4w4_kernel<false>, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m,
                            tiles_n, A, As, B, Bs, C, ldc);
     return hipGetLastError();
 }
 
 }  // namespace mx
-
