@@ -77,16 +77,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Separate arrays keep every LDS address a compile-time constant plus lane.
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kAtoms * 1024];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kAtoms * 1024];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kAtoms * 1024];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kAtoms * 1024];
+// LDS: 4 k-step stages of 32 atoms and one k-group of scale atoms, as
+// separate arrays so that the compiler can tell a DMA into one stage from a
+// read of another.  After the k-loop the stages hold the bf16 C tile: rows
+// [64s, 64s + 64) in stage s, 512 bytes per row, 16-byte chunk c of row r at
+// chunk c ^ (r % 32) so that reads and writes of a column of rows spread
+// over all banks.
+constexpr int kStageBytes = kAtoms * 1024;
+static_assert(kBN * 2 * (kBM / 4) == kStageBytes, "a quarter of the bf16 C tile fills one stage");
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_scale[kAtoms * 256];
 
 template <int S>
 __device__ __forceinline__ uint8_t *stage_buf() {
     return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+}
+__device__ __forceinline__ uint8_t *scale_buf() { return g_scale; }
+__device__ __forceinline__ uint8_t *stage_dyn(int s) {
+    return s == 0 ? g_stage0 : s == 1 ? g_stage1 : s == 2 ? g_stage2 : g_stage3;
+}
+// byte address of bf16 C element (r, col) of the staged tile, col % 4 == 0
+__device__ __forceinline__ uint8_t *c_stage(int r, int col) {
+    const int chunk = (col >> 3) ^ (r & 31);
+    return stage_dyn(r >> 6) + (r & 63) * (kBN * 2) + chunk * 16 + (col & 7) * 2;
 }
 
 #define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
@@ -124,7 +140,7 @@ __device__ __forceinline__ void dma_op(const GemmCtx &c, int64_t k) {
         const int a = kWaves * R + c.wave;
         const int64_t h = k / 4;
         const uint32_t base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(g_scale + a * 256), 4,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(scale_buf() + a * 256), 4,
                                                  base + c.lane4, 0, 0, 0);
     }
 }
@@ -203,10 +219,10 @@ __device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kM
             const int q = 2 * (T - kScStart) + e;
             const int hh = q & 1, t = q >> 1;
             if (t < kMA)
-                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
             else
                 r.sb_n[t - kMA][hh] =
-                    *reinterpret_cast<const uint32_t *>(g_scale + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
+                    *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
         }
     }
 
@@ -328,18 +344,18 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
     for (int t = 0; t < kMA; ++t)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
 #pragma unroll
     for (int t = 0; t < kMB; ++t)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(g_scale + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
 #pragma unroll
     for (int t = 0; t < kMA; ++t)
-        r.a0[t] = *reinterpret_cast<const uint4 *>(g_stage0 + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
+        r.a0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
 #pragma unroll
     for (int t = 0; t < kMB; ++t)
-        r.b0[t] = *reinterpret_cast<const uint4 *>(g_stage0 + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
+        r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
 
     for (int64_t h = 0; h < c.kgroups; ++h) {
         const int64_t k0 = 4 * h;
@@ -348,35 +364,72 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
         k_step<2>(c, k0 + 2, acc, r, l);
         k_step<3>(c, k0 + 3, acc, r, l);
     }
-    // drain the trailing (out-of-range) DMAs before the workgroup exits
+    // drain the trailing (out-of-range) DMAs before LDS is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4]
-    const int64_t m0 = (int64_t)tm * kBM + wm * kWM;
-    const int64_t n0 = (int64_t)tn * kBN + wn * kWN;
+    const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
+    if (OUT_BF16) {
+        // Round to bf16 (V_CVT_PK_BF16_F32, nearest even), stage the tile in
+        // LDS, then write whole 512-byte row segments: each store instruction
+        // covers 2 rows with 16 bytes per lane.  Every wave waited for its
+        // own DMAs above; the barrier makes sure all of them have landed and
+        // every stage read is done before the tile overwrites the stages.
+        __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kMA; ++j) {
-        const int64_t row = m0 + 32 * j + lrow;
-        if (row >= M) continue;
+        for (int j = 0; j < kMA; ++j)
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) {
+            for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
-                const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if (OUT_BF16) {
-                    // V_CVT_PK_BF16_F32: round to nearest even
-                    uint16_t *dst = reinterpret_cast<uint16_t *>(C) + row * ldc + col;
-                    const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v[0], v[1]}), bf16x2_t));
-                    const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{v[2], v[3]}), bf16x2_t));
-                    if (col + 3 < N) {
-                        *reinterpret_cast<uint2 *>(dst) = uint2{p01, p23};
-                    } else {
-                        if (col < N) dst[0] = (uint16_t)p01;
-                        if (col + 1 < N) dst[1] = (uint16_t)(p01 >> 16);
-                        if (col + 2 < N) dst[2] = (uint16_t)p23;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
+                    const uint32_t p01 = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
+                    const uint32_t p23 = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
+                    *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
+                }
+        __syncthreads();
+        constexpr int kRowsPerWave = kBM / kWaves;        // 32: 16 instructions of 2 rows
+        const int cl = (lane & 31) * 8;
+        const int64_t col = tn0 + cl;
+        uint4 v[kRowsPerWave / 2];
+#pragma unroll
+        for (int it = 0; it < kRowsPerWave / 2; ++it)
+            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave + 2 * it + (lane >> 5), cl));
+        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave + (lane >> 5)) * ldc + col;
+        if (tm0 + kBM <= M && tn0 + kBN <= N) {
+#pragma unroll
+            for (int it = 0; it < kRowsPerWave / 2; ++it)
+                *reinterpret_cast<uint4 *>(dst0 + 2 * it * ldc) = v[it];
+        } else {
+#pragma unroll
+            for (int it = 0; it < kRowsPerWave / 2; ++it) {
+                const int64_t row = tm0 + kRowsPerWave * wave + 2 * it + (lane >> 5);
+                if (row >= M || col >= N) continue;
+                uint16_t *dst = dst0 + 2 * it * ldc;
+                if (col + 7 < N) {
+                    *reinterpret_cast<uint4 *>(dst) = v[it];
                 } else {
+                    const uint32_t w4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (col + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+    } else {
+        const int64_t m0 = tm0 + wm * kWM, n0 = tn0 + wn * kWN;
+#pragma unroll
+        for (int j = 0; j < kMA; ++j) {
+            const int64_t row = m0 + 32 * j + lrow;
+            if (row >= M) continue;
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
+                    const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                     float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
                     if (col + 3 < N) {
                         *reinterpret_cast<v4f *>(dst) = v;
