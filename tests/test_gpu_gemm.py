@@ -132,3 +132,48 @@ def test_qkv_full_size_sampled(oracle_mod):
     d = synth.qkv()
     log("qkv full size")
     run_case(oracle_mod, d["A"], d["W"], full=False, nsample=4096, what="qkv")
+
+
+def test_many_tiles_ragged_and_repeatable(oracle_mod):
+    """4500x4100 output = 306 tiles of 256x256 (more than one round on 256
+    CUs, ragged last row and column of tiles) with K 700 -> 768 (a k-group
+    whose second half is padding).  Sampled entries against the oracle, then
+    two more calls must give bit-identical output."""
+    _require_gpu()
+    M, N, K = 4500, 4100, 700
+    a = synth.random_bf16(71, (M, K), std=1.0)
+    b = synth.random_bf16(72, (N, K), std=0.05)
+    log("many tiles %dx%dx%d" % (M, N, K))
+    cb, _ = run_case(oracle_mod, a, b, full=False, nsample=16384, what="many-tiles")
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
+    qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
+    for _ in range(2):
+        again = host(gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16))[:M, :N].view(np.uint16)
+        assert np.array_equal(again, cb)
+
+
+_FC2 = {}
+
+
+def _fc2_operands(which):
+    if not _FC2:
+        _FC2.update(synth.fc2())
+    X, W, dY = _FC2["X"], _FC2["W"], _FC2["dY"]
+    if which == "fwd":      # Y = X W^T: 18432 x 3072, K 12288
+        return X, W
+    if which == "dgrad":    # dX = dY W: 18432 x 12288, K 3072
+        return dY, np.ascontiguousarray(W.T)
+    return np.ascontiguousarray(dY.T), np.ascontiguousarray(X.T)   # dW = dY^T X: 3072 x 12288, K 18432
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_fc2_full_size_sampled(oracle_mod, which):
+    """The three GEMMs of the fc2 training step at full size (18432 tokens,
+    12288 -> 3072), sampled entries, in the launch configuration the benchmark
+    times (864, 3456 and 576 output tiles)."""
+    _require_gpu()
+    a, b = _fc2_operands(which)
+    log("fc2 %s %dx%dx%d" % (which, a.shape[0], b.shape[0], a.shape[1]))
+    run_case(oracle_mod, a, b, full=False, nsample=4096, seed=5, what="fc2-" + which)
