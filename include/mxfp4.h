@@ -175,6 +175,40 @@ mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K,
                        void *C, int64_t ldc, void *stream);
 
 /*
+ * mx_gemm_a4w4 with the linear layer's bias added in the epilogue:
+ *   C[i][j] = round(sum_k A[i][k] * B[j][k] + bias[j])
+ * bias: N bf16 values (device pointer, 16-byte aligned, caller-owned), added
+ * to the fp32 accumulator before the one rounding to out_dtype.  This fuses
+ * the separate `output + bias` that the parallel linear layers on the page
+ * "primus_turbo_mxfp4_local.py" apply after the FP4 GEMM (there the sum is
+ * rounded to bf16 twice; here once).  K == 0 writes bias broadcast over the
+ * rows.  Arguments and errors otherwise as mx_gemm_a4w4 (NULL bias:
+ * MX_ERR_INVALID_ARGUMENT; misaligned bias: MX_ERR_MISALIGNED).
+ */
+mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                            const void *A, const void *A_scale,
+                            const void *B, const void *B_scale,
+                            mx_layout layout, mx_dtype out_dtype, const void *bias,
+                            void *C, int64_t ldc, void *stream);
+
+/*
+ * Device-side layout conversion of one blob (rows, length) between the two
+ * layouts, asynchronous on `stream`: the tiled layout is the one this
+ * library's GEMM reads, the canonical one the interchange shapes of the page
+ * "primus_turbo_mxfp4_local.py" (its fake dual-quantize op), so blobs made
+ * elsewhere can be fed in and blobs made here handed out.  to_tiled = 1:
+ * canonical -> tiled (padding rows and unused scale slots are written as 0);
+ * 0: tiled -> canonical.  Device pointers, caller-owned, sized by
+ * mx_blob_bytes for their layout; source and destination must not overlap.
+ * Errors: MX_ERR_INVALID_ARGUMENT (negative shape, NULL pointer),
+ * MX_ERR_MISALIGNED (data pointers not 16-byte aligned),
+ * MX_ERR_DEVICE_UNSUPPORTED, MX_ERR_HIP (launch failure).  rows == 0 or
+ * length == 0 is a no-op.
+ */
+mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const void *q_src,
+                            const void *s_src, void *q_dst, void *s_dst, void *stream);
+
+/*
  * Host-side layout conversion of one blob (rows, length) between the two
  * layouts; plain host pointers, synchronous.  to_tiled = 1: canonical ->
  * tiled; 0: tiled -> canonical.  Destination buffers are sized by

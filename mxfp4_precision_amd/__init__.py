@@ -30,8 +30,8 @@ MX_LAYOUT_TILED = 1
 MX_BF16 = 0
 MX_F32 = 1
 
-EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4",
-            "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
+EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
+            "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
             "mx_status_string", "mx_last_error")
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.mx_quantize_rowwise.argtypes = [vp, i64, i64, i64, optp, i32, vp, vp, vp]
     L.mx_quantize_dual.argtypes = [vp, i64, i64, i64, optp, optp, i32, vp, vp, vp, vp, vp]
     L.mx_gemm_a4w4.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, i64, vp]
+    L.mx_gemm_a4w4_bias.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, vp, i64, vp]
+    L.mx_layout_convert.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
     L.mx_layout_convert_host.argtypes = [i32, i64, i64, vp, vp, vp, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     L.mx_device_supported.argtypes = [i32]
@@ -78,8 +80,8 @@ def lib() -> ctypes.CDLL:
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_last_error.argtypes = []
     L.mx_last_error.restype = ctypes.c_char_p
-    for name in ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4",
-                 "mx_layout_convert_host", "mx_dequantize"):
+    for name in ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
+                 "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -145,6 +147,17 @@ def mx_gemm_a4w4(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B
                  layout: int, out_dtype: int, C, ldc: int, stream=None):
     _check(lib().mx_gemm_a4w4(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
                               layout, out_dtype, _ptr(C), ldc, _stream(stream)))
+
+
+def mx_gemm_a4w4_bias(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B, B_scale,
+                      layout: int, out_dtype: int, bias, C, ldc: int, stream=None):
+    _check(lib().mx_gemm_a4w4_bias(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
+                                   layout, out_dtype, _ptr(bias), _ptr(C), ldc, _stream(stream)))
+
+
+def mx_layout_convert(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst, stream=None):
+    _check(lib().mx_layout_convert(to_tiled, rows, length, _ptr(q_src), _ptr(s_src), _ptr(q_dst), _ptr(s_dst),
+                                   _stream(stream)))
 
 
 def mx_layout_convert_host(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst):

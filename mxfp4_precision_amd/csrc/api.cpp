@@ -172,9 +172,11 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, con
                         "mx_quantize_dual");
 }
 
-mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
-                       const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
-                       mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+namespace {
+
+mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                      const void *A_scale, const void *B, const void *B_scale, mx_layout layout, mx_dtype out_dtype,
+                      const void *bias, bool want_bias, void *C, int64_t ldc, void *stream) {
     if (transA != 0 || transB != 1)
         return fail(MX_ERR_UNSUPPORTED,
                     "transA=%d transB=%d: only transA=0, transB=1 (C = A . B^T, both operands K-contiguous) "
@@ -185,23 +187,55 @@ mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K, 
                     (long long)K);
     MX_TRY(check_layout(layout));
     if (layout != MX_LAYOUT_TILED)
-        return fail(MX_ERR_UNSUPPORTED, "mx_gemm_a4w4 reads MX_LAYOUT_TILED blobs only");
+        return fail(MX_ERR_UNSUPPORTED, "%s reads MX_LAYOUT_TILED blobs only", name);
     if (out_dtype != MX_BF16 && out_dtype != MX_F32)
         return fail(MX_ERR_UNSUPPORTED, "out_dtype %d (valid: MX_BF16=0, MX_F32=1)", (int)out_dtype);
     if (ldc < N || ldc < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldc=%lld must be >= max(N, 1)", (long long)ldc);
     if (!C) return fail(MX_ERR_INVALID_ARGUMENT, "C is NULL");
     if (K > 0 && (!A || !A_scale || !B || !B_scale))
         return fail(MX_ERR_INVALID_ARGUMENT, "operand pointer is NULL");
-    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(A_scale) || !aligned16(B) || !aligned16(B_scale))))
-        return fail(MX_ERR_MISALIGNED, "operands and C must be 16-byte aligned");
+    if (want_bias && !bias) return fail(MX_ERR_INVALID_ARGUMENT, "bias is NULL");
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(A_scale) || !aligned16(B) || !aligned16(B_scale))) ||
+        (want_bias && !aligned16(bias)))
+        return fail(MX_ERR_MISALIGNED, "operands, bias and C must be 16-byte aligned");
     if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
     if (M == 0 || N == 0) return MX_SUCCESS;
     MX_TRY(check_device());
     return check_launch(mx::launch_gemm(M, N, K, static_cast<const uint8_t *>(A),
                                         static_cast<const uint8_t *>(A_scale), static_cast<const uint8_t *>(B),
-                                        static_cast<const uint8_t *>(B_scale), out_dtype, C, ldc,
-                                        static_cast<hipStream_t>(stream)),
-                        "mx_gemm_a4w4");
+                                        static_cast<const uint8_t *>(B_scale),
+                                        want_bias ? static_cast<const uint16_t *>(bias) : nullptr, out_dtype, C,
+                                        ldc, static_cast<hipStream_t>(stream)),
+                        name);
+}
+
+}  // namespace
+
+mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                       const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
+                       mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+    return gemm_common("mx_gemm_a4w4", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype, nullptr,
+                       false, C, ldc, stream);
+}
+
+mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                            const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
+                            mx_dtype out_dtype, const void *bias, void *C, int64_t ldc, void *stream) {
+    return gemm_common("mx_gemm_a4w4_bias", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype,
+                       bias, true, C, ldc, stream);
+}
+
+mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const void *q_src, const void *s_src,
+                            void *q_dst, void *s_dst, void *stream) {
+    if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
+    if (!q_src || !s_src || !q_dst || !s_dst) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (!aligned16(q_src) || !aligned16(q_dst)) return fail(MX_ERR_MISALIGNED, "data pointers must be 16-byte aligned");
+    if (rows == 0 || length == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    return check_launch(mx::launch_layout_convert(to_tiled != 0, rows, length, static_cast<const uint8_t *>(q_src),
+                                                  static_cast<const uint8_t *>(s_src), static_cast<uint8_t *>(q_dst),
+                                                  static_cast<uint8_t *>(s_dst), static_cast<hipStream_t>(stream)),
+                        "mx_layout_convert");
 }
 
 mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t length, mx_layout layout,

@@ -266,12 +266,15 @@ __device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[
     }
 }
 
-template <bool OUT_BF16>
+// BIAS: C[i][j] = (sum) + bias[j], bias a bf16 vector of N, added in fp32
+// before the output rounding.
+template <bool OUT_BF16, bool BIAS>
 __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
                                                              int tiles_n, const uint8_t *__restrict__ A,
                                                              const uint8_t *__restrict__ As,
                                                              const uint8_t *__restrict__ B,
                                                              const uint8_t *__restrict__ Bs,
+                                                             const uint16_t *__restrict__ bias,
                                                              void *__restrict__ C, int64_t ldc) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -301,6 +304,25 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
     c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
     c.rAs = make_rsrc(As, nGA * c.kgroups * 256);
     c.rBs = make_rsrc(Bs, nGB * c.kgroups * 256);
+
+    // This lane's bias values (columns n0 + 32i + 8q + 4(lane/32) + 0..3 of its
+    // tile, 4 bf16 per (i, q)), loaded before the k-loop so they have long
+    // arrived by the epilogue.  The range check of a buffer load zeroes whole
+    // dwords, so the range ends at the 16-byte boundary after the last entry
+    // (the bias is 16-byte aligned, so that block is inside the caller's
+    // allocation's last page); columns past it read 0, columns past N are
+    // never stored.
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    v2u bias_bits[BIAS ? kMB * 4 : 1];
+    if constexpr (BIAS) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, cdiv(N * 2, 16) * 16);
+        const int col0 = tn * kBN + wn * kWN + 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < kMB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
+    }
     // Row groups past an operand are clamped to its last group: those rows of C
     // are never stored, so their contents do not matter.
 #pragma unroll
@@ -369,6 +391,23 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
 
     // ---- epilogue: acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4]
     const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int i = 0; i < kMB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v2u bb = bias_bits[i * 4 + q];
+                const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
+                const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
+#pragma unroll
+                for (int j = 0; j < kMA; ++j) {
+                    acc[i][j][4 * q] += b0;
+                    acc[i][j][4 * q + 1] += b1;
+                    acc[i][j][4 * q + 2] += b2;
+                    acc[i][j][4 * q + 3] += b3;
+                }
+            }
+    }
     if (OUT_BF16) {
         // Round to bf16 (V_CVT_PK_BF16_F32, nearest even), stage the tile in
         // LDS, then write whole 512-byte row segments: each store instruction
@@ -444,27 +483,32 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
     }
 }
 
+// K == 0: C[i][j] = 0, or bias[j] (bf16 bits; exact in either output type).
 template <typename T>
-__global__ void fill_zero_kernel(T *C, int64_t M, int64_t N, int64_t ldc) {
+__global__ void fill_kernel(T *C, int64_t M, int64_t N, int64_t ldc, const uint16_t *bias) {
     int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx < M * N) C[(idx / N) * ldc + idx % N] = T(0);
+    if (idx >= M * N) return;
+    const int64_t j = idx % N;
+    const uint16_t b = bias ? bias[j] : (uint16_t)0;
+    if constexpr (sizeof(T) == 2) C[(idx / N) * ldc + j] = b;
+    else C[(idx / N) * ldc + j] = __uint_as_float((uint32_t)b << 16);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
-                       const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C,
+                       const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream) {
     const int64_t K_pad = padded(K);
     if (K_pad == 0) {
         const int64_t n = M * N;
         dim3 grid((unsigned)cdiv(n, 256));
         if (out_dtype == MX_BF16)
-            hipLaunchKernelGGL(fill_zero_kernel<uint16_t>, grid, dim3(256), 0, stream,
-                               reinterpret_cast<uint16_t *>(C), M, N, ldc);
+            hipLaunchKernelGGL(fill_kernel<uint16_t>, grid, dim3(256), 0, stream, reinterpret_cast<uint16_t *>(C),
+                               M, N, ldc, bias);
         else
-            hipLaunchKernelGGL(fill_zero_kernel<float>, grid, dim3(256), 0, stream,
-                               reinterpret_cast<float *>(C), M, N, ldc);
+            hipLaunchKernelGGL(fill_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<float *>(C), M, N,
+                               ldc, bias);
         return hipGetLastError();
     }
     // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
@@ -472,12 +516,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
         return hipErrorInvalidValue;
     const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
     dim3 grid((unsigned)(tiles_m * tiles_n));
-    if (out_dtype == MX_BF16)
-        hipLaunchKernelGGL(gemm_a4w4_kernel<true>, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n,
-                           A, As, B, Bs, C, ldc);
-    else
-        hipLaunchKernelGGL(gemm_a4w4_kernel<false>, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m,
-                           tiles_n, A, As, B, Bs, C, ldc);
+    auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_kernel<true, true> : gemm_a4w4_kernel<true, false>)
+                                       : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, As, B, Bs, bias,
+                       C, ldc);
     return hipGetLastError();
 }
 

@@ -32,11 +32,13 @@ struct QuantArgs {
     uint8_t *q_row, *s_row, *q_col, *s_col;
 };
 
-// Kernel launchers (quantize.hip, gemm.hip).  They assume validated arguments.
+// Kernel launchers (quantize.hip, gemm.hip, convert.hip, dequantize.hip).  They assume validated arguments.
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
-                       const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C,
+                       const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream);
+hipError_t launch_layout_convert(bool to_tiled, int64_t rows, int64_t length, const uint8_t *q_src,
+                                 const uint8_t *s_src, uint8_t *q_dst, uint8_t *s_dst, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t length,
                              mx_layout layout, float *out, int64_t ldo, hipStream_t stream);
 

@@ -148,6 +148,22 @@ def gemm_rows(qa, sa, qb, sb, M: int, N: int, K: int, i0: int, i1: int) -> np.nd
     return out
 
 
+def bf16_to_double(bits) -> np.ndarray:
+    """bf16 bit patterns -> their exact fp64 values (a bf16 is the top half of an fp32)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def gemm_bias_entries(qa, sa, qb, sb, M: int, N: int, K: int, bias_bits, ii, jj) -> np.ndarray:
+    """fp64 C[ii[t], jj[t]] + bias[jj[t]]: the NT product plus the linear
+    layer's bf16 bias vector (one entry per output column), the sum that the
+    parallel linear layers of the page "primus_turbo_mxfp4_local.py" form
+    after the FP4 GEMM (``output + bias``).  Taken exactly here; rounding to
+    the output type is a separate step (bf16_from_double)."""
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    return gemm_entries(qa, sa, qb, sb, M, N, K, ii, jj) + bf16_to_double(bias_bits)[jj]
+
+
 def bf16_from_double(a) -> np.ndarray:
     """Correctly rounded (RNE) fp64 -> bf16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float64)

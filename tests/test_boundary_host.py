@@ -144,6 +144,17 @@ def test_host_layout_convert_matches_oracle(L, oracle_mod, rows, length):
     assert (q2 == q).all() and (s2 == s).all()
 
 
+def test_device_layout_convert_validation(L):
+    A16 = 1 << 20
+    C = mx.mx_layout_convert
+    assert _status(C, 1, -1, 8, A16, A16, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(C, 1, 4, 8, 0, A16, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(C, 0, 4, 8, A16, A16, A16, 0, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(C, 1, 4, 8, A16 + 4, A16, A16, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(C, 1, 4, 8, A16, A16, A16 + 8, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(C, 1, 0, 8, A16, A16, A16, A16, 0) == mx.MX_SUCCESS
+
+
 def test_device_supported_without_gpu(L):
     # no GPU in a CPU-only container: the query reports unsupported instead of crashing
     import torch

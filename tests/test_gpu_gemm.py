@@ -177,3 +177,57 @@ def test_fc2_full_size_sampled(oracle_mod, which):
     a, b = _fc2_operands(which)
     log("fc2 %s %dx%dx%d" % (which, a.shape[0], b.shape[0], a.shape[1]))
     run_case(oracle_mod, a, b, full=False, nsample=4096, seed=5, what="fc2-" + which)
+
+
+def gemm_bias(A, As, B, Bs, M, N, K, bias, out_dtype=mx.MX_BF16):
+    ldc = (N + 7) // 8 * 8
+    dt = torch.int16 if out_dtype == mx.MX_BF16 else torch.float32
+    C = torch.full((max(M, 1), ldc), -1, dtype=dt, device="cuda")
+    mx.mx_gemm_a4w4_bias(0, 1, M, N, K, A, As, B, Bs, TILED, out_dtype, bias, C, ldc)
+    return C
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (100, 70, 300), (300, 257, 1000), (512, 513, 640)])
+def test_bias_epilogue(oracle_mod, M, N, K):
+    """C = A.B^T + bias (bias added to the fp32 accumulator, one rounding):
+    every entry against the oracle's exact sum, bf16 within 2 ulp of the
+    correctly rounded value (tau floor as above), fp32 rel. Frobenius <= 1e-5.
+    N not a multiple of 8 exercises the bias reads past the last column."""
+    _require_gpu()
+    a = synth.random_bf16(M * 13 + K, (M, K), std=1.0)
+    b = synth.random_bf16(N * 17 + K, (N, K), std=0.05)
+    bias = synth.random_bf16(N + 5, (N,), std=2.0)
+    log("bias epilogue %dx%dx%d" % (M, N, K))
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
+    qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
+    bias_d = torch.zeros(((N + 7) // 8 * 8,), dtype=torch.int16)
+    bias_d[:N] = torch.from_numpy(bias.view(np.int16))
+    bias_d = bias_d.cuda()
+    cb = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_BF16))[:M, :N].view(np.uint16)
+    cf = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_F32))[:M, :N].astype(np.float64)
+    oqa, osa = oracle_mod.quantize(a, 0)
+    oqb, osb = oracle_mod.quantize(b, 0)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ii, jj = ii.ravel(), jj.ravel()
+    ref = oracle_mod.gemm_bias_entries(oqa, osa, oqb, osb, M, N, K, bias, ii, jj)
+    tau = tau_bound(oracle_mod, oqa, osa, oqb, osb, M, N, K, ii, jj)
+    check_gemm_bf16(cb[ii, jj], ref, tau, oracle_mod, "bias")
+    rel = np.linalg.norm(cf[ii, jj] - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-5, rel
+
+
+def test_bias_k_zero_writes_bias(oracle_mod):
+    """K == 0: every row of C is the bias, exactly, in both output types."""
+    _require_gpu()
+    M, N = 33, 20
+    bias = synth.random_bf16(64, (N,), std=2.0)
+    bias_d = torch.zeros((24,), dtype=torch.int16)
+    bias_d[:N] = torch.from_numpy(bias.view(np.int16))
+    bias_d = bias_d.cuda()
+    dummy = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    cb = host(gemm_bias(dummy, dummy, dummy, dummy, M, N, 0, bias_d, mx.MX_BF16))[:M, :N].view(np.uint16)
+    cf = host(gemm_bias(dummy, dummy, dummy, dummy, M, N, 0, bias_d, mx.MX_F32))[:M, :N]
+    assert (cb == bias[None, :]).all()
+    assert (cf.astype(np.float64) == oracle_mod.bf16_to_double(bias)[None, :]).all()

@@ -242,3 +242,26 @@ def test_stochastic_rounding_distinct_direction_keys(oracle_mod, layout):
     check_dual(oracle_mod, x, layout, ro, co, rkw, ckw)
     ro2 = mx.quant_opts(use_sr=True, use_2d_block=True, seed=11, tensor_id=4)
     check_dual(oracle_mod, x, layout, ro2, co, dict(use_sr=True, use_2d=True, seed=11, tensor_id=4), ckw)
+
+
+@pytest.mark.parametrize("rows,length", [(1, 1), (37, 640), (40, 700), (16, 512), (333, 3000)])
+def test_device_layout_convert(oracle_mod, rows, length):
+    """Canonical -> tiled on the device equals the oracle's own permutation of
+    the oracle's canonical blob (padding rows and scale slots written as 0 over
+    a poisoned destination); tiled -> canonical gives the canonical blob back."""
+    _require_gpu()
+    x = synth.random_bf16(rows * 11 + length, (rows, length))
+    q, s = oracle_mod.quantize(x, 0)
+    qt_ref, st_ref = oracle_mod.to_tiled(q, s, rows, length)
+    log("device layout convert %dx%d" % (rows, length))
+    qd = torch.from_numpy(q.reshape(-1).copy()).cuda()
+    sd = torch.from_numpy(s.reshape(-1).copy()).cuda()
+    dt, sz = mx.mx_blob_bytes(rows, length, TILED)
+    qt = torch.full((dt,), 0xAB, dtype=torch.uint8, device="cuda")
+    st = torch.full((sz,), 0xCD, dtype=torch.uint8, device="cuda")
+    mx.mx_layout_convert(1, rows, length, qd, sd, qt, st)
+    assert (host(qt) == qt_ref).all() and (host(st) == st_ref).all()
+    q2 = torch.full_like(qd, 0x5A)
+    s2 = torch.full_like(sd, 0x5A)
+    mx.mx_layout_convert(0, rows, length, qt, st, q2, s2)
+    assert (host(q2) == q.reshape(-1)).all() and (host(s2) == s.reshape(-1)).all()

@@ -164,3 +164,37 @@ def test_bf16_cast_specials(oracle_mod):
     assert got[0] == 0x7F80 and got[1] == 0xFF80
     assert (got[2] & 0x7F80) == 0x7F80 and (got[2] & 0x7F)
     assert got[3] == 0x7F80 and got[4] == 0xFF80
+
+
+def test_gemm_bias_hand_value(oracle_mod):
+    """The hand dot product above (16 in every entry) plus a bias of -3.5, 0.25
+    and 2^-9 per column: 12.5, 16.25 and 16 + 2^-9 exactly."""
+    a = synth.bf16_bits(np.ones((2, 32), np.float32) * 4.0)
+    b = synth.bf16_bits(np.ones((3, 32), np.float32) * 4.0)
+    qa, sa = oracle_mod.quantize(a, 0)
+    qb, sb = oracle_mod.quantize(b, 0)
+    qa[:, :16] = 0x22
+    qb[:, :16] = 0x11
+    bias = synth.bf16_bits(np.array([-3.5, 0.25, 2.0 ** -9], np.float32))
+    ii, jj = np.meshgrid(np.arange(2), np.arange(3), indexing="ij")
+    C = oracle_mod.gemm_bias_entries(qa, sa, qb, sb, 2, 3, 32, bias, ii.ravel(), jj.ravel()).reshape(2, 3)
+    assert (C == np.array([[12.5, 16.25, 16 + 2.0 ** -9]] * 2)).all()
+    # rounded to bf16 (spacing 1/8 at 16), 16 + 2^-9 becomes 16
+    assert (oracle_mod.bf16_from_double(C[0]) == synth.bf16_bits(np.array([12.5, 16.25, 16.0], np.float32))).all()
+
+
+def test_gemm_bias_special_cases(oracle_mod):
+    """K = 0: the output is the bias itself; a zero bias: the plain product."""
+    M, N, K = 5, 7, 96
+    a = synth.random_bf16(61, (M, K))
+    b = synth.random_bf16(62, (N, K))
+    bias = synth.random_bf16(63, (N,), std=3.0)
+    qa, sa = oracle_mod.quantize(a, 0)
+    qb, sb = oracle_mod.quantize(b, 0)
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    ii, jj = ii.ravel(), jj.ravel()
+    z = oracle_mod.gemm_bias_entries(qa, sa, qb, sb, M, N, 0, bias, ii, jj)
+    assert (oracle_mod.bf16_from_double(z) == bias[jj]).all()
+    plain = oracle_mod.gemm_entries(qa, sa, qb, sb, M, N, K, ii, jj)
+    zero = np.zeros(N, np.uint16)
+    assert (oracle_mod.gemm_bias_entries(qa, sa, qb, sb, M, N, K, zero, ii, jj) == plain).all()
