@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         build()
         L = ctypes.CDLL(_LIB_PATH)
-        L.oracle_quantize.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _u64, _u32, _u64, _vp, _vp]
+        L.oracle_quantize.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _u64, _u32, _u64, _u32, _vp, _vp]
         L.oracle_quantize.restype = _int
         L.oracle_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp]
         L.oracle_dequantize.restype = _int
@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_sr_byte.restype = ctypes.c_uint
         L.oracle_to_tiled.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
         L.oracle_to_tiled.restype = _int
+        L.oracle_rht_signs.argtypes = [_u32]
+        L.oracle_rht_signs.restype = _u32
+        L.oracle_rht32.argtypes = [_vp, _u32, _vp]
+        L.oracle_rht32.restype = None
         _lib = L
     return _lib
 
@@ -97,8 +101,11 @@ def blob_shapes(rows: int, length: int) -> Tuple[Tuple[int, int], Tuple[int, int
 
 
 def quantize(x: np.ndarray, direction: int, use_2d: bool = False, use_sr: bool = False,
-             seed: int = 0, tensor_id: int = 0, index_base: int = 0):
+             seed: int = 0, tensor_id: int = 0, index_base: int = 0, rht: int = 0):
     """Quantize bf16 bits x (M x N uint16) row-wise (direction 0) or column-wise (1).
+
+    rht != 0: random Hadamard transform of every 32-element block first, with
+    the sign pattern of seed `rht` (see rht32).
 
     Returns canonical (q, s) uint8 arrays: direction 0 -> (M, N_pad/2), (M, N_pad/32);
     direction 1 -> (N, M_pad/2), (N, M_pad/32).
@@ -111,10 +118,24 @@ def quantize(x: np.ndarray, direction: int, use_2d: bool = False, use_sr: bool =
     q = np.zeros(qs, dtype=np.uint8)
     s = np.zeros(ss, dtype=np.uint8)
     rc = lib().oracle_quantize(_ptr(x), M, N, N, direction, int(use_2d), int(use_sr),
-                               seed, tensor_id, index_base, _ptr(q), _ptr(s))
+                               seed, tensor_id, index_base, rht, _ptr(q), _ptr(s))
     if rc != 0:
         raise ValueError("oracle_quantize rejected its arguments")
     return q, s
+
+
+def rht_signs(rht: int) -> int:
+    """The 32-bit sign pattern D of seed `rht` (bit p set: negate block position p)."""
+    return int(lib().oracle_rht_signs(rht))
+
+
+def rht32(x: np.ndarray, signs: int) -> np.ndarray:
+    """The random Hadamard transform of one 32-element fp32 block (see mx_oracle.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape == (32,)
+    out = np.empty(32, dtype=np.float32)
+    lib().oracle_rht32(_ptr(x), signs, _ptr(out))
+    return out
 
 
 def dequantize(q: np.ndarray, s: np.ndarray, rows: int, length: int) -> np.ndarray:

@@ -19,6 +19,16 @@
  *             dataflow of the autograd Function (fwd, dgrad, wgrad: all NT).
  *   [PHILOX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
  *             as 1, 2, 3", SC'11, sec. 4.2 (Philox-4x32, 10 rounds).
+ *   [RHT]     the same page's dual-quantize calls, which switch on a random
+ *             Hadamard transform ("rht") for the column-wise blobs of the
+ *             activation and of the gradient -- the two operands of wgrad --
+ *             and say nothing more about it.  The reading taken here: within
+ *             each 32-element block along the quantized axis, y = c * H32 * D * x,
+ *             H32 the 32x32 Sylvester Hadamard matrix, D = diag(+-1) a fixed
+ *             sign pattern drawn from a seed, c = 1/sqrt(32) rounded to fp32,
+ *             evaluated in fp32 as a fast Walsh-Hadamard transform (stages
+ *             over index bits 0..4); both wgrad operands use the same D, so
+ *             (H D)^T (H D) = 32 I and c^2 * 32 ~ 1 leave the product unchanged.
  *
  * Readings where the pages are silent are listed in the design notes; the
  * ones that shape this file: sign of zero is copied from x; an all-zero or
@@ -28,7 +38,8 @@
  * row's block slot; stochastic rounding uses one Philox byte per element.
  *
  * Every value here is computed in fp64 (exact for all the quantizer's
- * arithmetic: bf16 inputs times powers of two).
+ * arithmetic: bf16 inputs times powers of two), except the random Hadamard
+ * transform, which is defined in fp32 (the precision the reading fixes).
  */
 #include <math.h>
 #include <stdint.h>
@@ -151,6 +162,48 @@ unsigned oracle_sr_byte(uint64_t seed, uint32_t tensor_id, uint32_t dir, uint64_
     return (w[idx / 4] >> (8 * (idx % 4))) & 0xFFu;
 }
 
+/* ------------------------------------------------------------------- RHT */
+
+/* [RHT] the sign pattern D of seed `rht`: bit p of the first output word of
+ * Philox-4x32-10 at counter (0, 0, 0, 2), key (rht, 0); bit set = negate the
+ * element at block position p. */
+uint32_t oracle_rht_signs(uint32_t rht)
+{
+    uint32_t ctr[4] = {0, 0, 0, 2};
+    uint32_t key[2] = {rht, 0};
+    uint32_t w[4];
+    oracle_philox4x32_10(ctr, key, w);
+    return w[0];
+}
+
+/* [RHT] c = the fp32 number nearest to 1/sqrt(32). */
+#define RHT_SCALE_BITS 0x3E3504F3u
+
+/*
+ * [RHT] one 32-element block: u = D x; then for stage k = 0..4, every pair
+ * (i, i + 2^k) with bit k of i clear becomes (u_i + u_(i+2^k), u_i - u_(i+2^k)),
+ * each sum rounded to fp32; finally each entry times c in fp32.  The stages
+ * build H32 u with H32[j][i] = (-1)^popcount(i & j).
+ */
+void oracle_rht32(const float in[32], uint32_t signs, float out[32])
+{
+    float u[32];
+    float c;
+    uint32_t cb = RHT_SCALE_BITS;
+    memcpy(&c, &cb, sizeof c);
+    for (int p = 0; p < 32; ++p) u[p] = ((signs >> p) & 1u) ? -in[p] : in[p];
+    for (int k = 0; k < 5; ++k) {
+        int h = 1 << k;
+        for (int i = 0; i < 32; ++i) {
+            if (i & h) continue;
+            float a = u[i], b = u[i + h];
+            u[i] = a + b;
+            u[i + h] = a - b;
+        }
+    }
+    for (int p = 0; p < 32; ++p) out[p] = u[p] * c;
+}
+
 /* -------------------------------------------------------------- quantize */
 
 /*
@@ -163,13 +216,21 @@ unsigned oracle_sr_byte(uint64_t seed, uint32_t tensor_id, uint32_t dir, uint64_
  * use_2d: the block is the aligned 32x32 tile of x; its scale is written into
  * every blob row slot the tile covers.
  * use_sr: stochastic rounding with the byte oracle_sr_byte(seed, tensor_id, dir, n).
+ * rht != 0: each 32-element block along the quantized axis (pads included, as
+ * +0) is replaced by its random Hadamard transform with signs
+ * oracle_rht_signs(rht) before the scale and the codes are taken; the pad
+ * positions of a block that holds real elements then carry codes too, and
+ * their stochastic-rounding byte uses the same index formula (n = index_base
+ * + i N + j with the padded coordinates).  Not combined with use_2d.
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_quantize(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, int dir,
                     int use_2d, int use_sr, uint64_t seed, uint32_t tensor_id,
-                    uint64_t index_base, uint8_t *q, uint8_t *s)
+                    uint64_t index_base, uint32_t rht, uint8_t *q, uint8_t *s)
 {
     if (M < 0 || N < 0 || ldx < N || (dir != 0 && dir != 1)) return -1;
+    if (rht && use_2d) return -1;
+    const uint32_t rht_signs = rht ? oracle_rht_signs(rht) : 0u;
     const int64_t R = dir == 0 ? M : N;        /* blob rows */
     const int64_t L = dir == 0 ? N : M;        /* quantized axis */
     const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
@@ -194,6 +255,48 @@ int oracle_quantize(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, int di
             }
             if (i1 > M) i1 = M;
             if (j1 > N) j1 = N;
+            if (rht) {
+                /* the block's 32 positions along the axis, pads as +0, transformed */
+                float xin[32], y[32];
+                for (int64_t t = 0; t < MX_BLOCK; ++t) {
+                    int64_t k = b * MX_BLOCK + t;
+                    xin[t] = 0.0f;
+                    if (k < L) {
+                        uint16_t bits = dir == 0 ? x[r * ldx + k] : x[k * ldx + r];
+                        xin[t] = (float)bf16_value(bits);
+                    }
+                }
+                oracle_rht32(xin, rht_signs, y);
+                double amax = 0.0;
+                int nonfinite = 0;
+                for (int t = 0; t < MX_BLOCK; ++t) {
+                    if (!isfinite(y[t])) nonfinite = 1;
+                    else if (fabs((double)y[t]) > amax) amax = fabs((double)y[t]);
+                }
+                int e = shared_exponent(amax);
+                s[r * nblk + b] = nonfinite ? 0xFF : (uint8_t)(e + 127);
+                for (int64_t t = 0; t < MX_BLOCK; ++t) {
+                    int64_t k = b * MX_BLOCK + t;
+                    unsigned nibble = 0;
+                    if (!nonfinite) {
+                        double v = ldexp(fabs((double)y[t]), -e);   /* exact */
+                        int code;
+                        if (use_sr) {
+                            int64_t i = dir == 0 ? r : k;
+                            int64_t j = dir == 0 ? k : r;
+                            uint64_t n = index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j;
+                            code = sr_code(v, oracle_sr_byte(seed, tensor_id, (uint32_t)dir, n));
+                        } else {
+                            code = rne_code(v);
+                        }
+                        nibble = (signbit(y[t]) ? 8u : 0u) | (unsigned)code;
+                    }
+                    uint8_t *byte = &q[r * (L_pad / 2) + k / 2];
+                    if (k % 2 == 0) *byte = (uint8_t)nibble;
+                    else *byte = (uint8_t)(*byte | (nibble << 4));
+                }
+                continue;
+            }
             double amax = 0.0;
             int nonfinite = 0;
             for (int64_t i = i0; i < i1; ++i)

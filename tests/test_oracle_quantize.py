@@ -331,7 +331,7 @@ def test_strided_input_equals_contiguous(oracle_mod):
     L = oracle_mod.lib()
     q = np.zeros((10, 64), dtype=np.uint8)
     s = np.zeros((10, 4), dtype=np.uint8)
-    L.oracle_quantize(big.ctypes.data, 10, 100, 136, 0, 0, 0, 0, 0, 0, q.ctypes.data, s.ctypes.data)
+    L.oracle_quantize(big.ctypes.data, 10, 100, 136, 0, 0, 0, 0, 0, 0, 0, q.ctypes.data, s.ctypes.data)
     q0, s0 = oracle_mod.quantize(x, 0)
     assert (q == q0).all() and (s == s0).all()
 
