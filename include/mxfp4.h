@@ -104,6 +104,21 @@ typedef enum mx_dtype {
  *   (lo32(seed), hi32(seed)); dir = 0 for the row-wise blob, 1 for the
  *   column-wise blob.  With neighbouring grid values lo <= v < hi of the scaled
  *   magnitude v, it rounds up iff byte < floor(256*(v-lo)/(hi-lo)).
+ * rht: 0 = off; otherwise each 32-element block along the quantized axis is
+ *   replaced, before its scale and codes are taken, by the random Hadamard
+ *   transform y = c * H32 * D * x evaluated in fp32 (the page
+ *   "primus_turbo_mxfp4_local.py" switches "rht" on for the column-wise blobs
+ *   of the activation and the gradient, the two wgrad operands, and defines
+ *   nothing more; this definition is the library's): D negates position p
+ *   when bit p of the first word of Philox-4x32-10 at counter (0, 0, 0, 2),
+ *   key (rht, 0) is set; H32 = Sylvester Hadamard matrix, applied as a fast
+ *   Walsh-Hadamard transform over position bits 0..4, each (a, b) -> (a + b,
+ *   a - b) rounded to fp32; c = fp32(1/sqrt(32)).  Pads count as +0 before
+ *   the transform, so pad positions of a block that holds real elements get
+ *   codes too (their SR byte uses the same index formula on padded
+ *   coordinates).  Both operands of a GEMM must be transformed with the same
+ *   rht value along the shared K axis: (H D)^T (H D) c^2 ~= I leaves the
+ *   product unchanged.  Not combined with use_2d_block (MX_ERR_UNSUPPORTED).
  * The scale never depends on use_sr.  NULL options = all zero.
  */
 typedef struct mx_quant_opts {
@@ -111,7 +126,7 @@ typedef struct mx_quant_opts {
     uint32_t use_sr;
     uint64_t seed;
     uint32_t tensor_id;
-    uint32_t reserved;     /* must be 0 */
+    uint32_t rht;          /* random Hadamard transform seed, 0 = off */
     uint64_t index_base;
 } mx_quant_opts;
 

@@ -44,12 +44,12 @@ class MXError(RuntimeError):
 class mx_quant_opts(ctypes.Structure):
     _fields_ = [("use_2d_block", ctypes.c_uint32), ("use_sr", ctypes.c_uint32),
                 ("seed", ctypes.c_uint64), ("tensor_id", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32), ("index_base", ctypes.c_uint64)]
+                ("rht", ctypes.c_uint32), ("index_base", ctypes.c_uint64)]
 
 
 def quant_opts(use_2d_block: bool = False, use_sr: bool = False, seed: int = 0,
-               tensor_id: int = 0, index_base: int = 0) -> mx_quant_opts:
-    return mx_quant_opts(int(use_2d_block), int(use_sr), seed, tensor_id, 0, index_base)
+               tensor_id: int = 0, index_base: int = 0, rht: int = 0) -> mx_quant_opts:
+    return mx_quant_opts(int(use_2d_block), int(use_sr), seed, tensor_id, rht, index_base)
 
 
 _lib = None

@@ -59,7 +59,8 @@ mx_status check_opts(const mx_quant_opts *o, const char *which) {
     if (!o) return MX_SUCCESS;
     if (o->use_2d_block > 1 || o->use_sr > 1)
         return fail(MX_ERR_INVALID_ARGUMENT, "%s options: use_2d_block and use_sr must be 0 or 1", which);
-    if (o->reserved != 0) return fail(MX_ERR_INVALID_ARGUMENT, "%s options: reserved must be 0", which);
+    if (o->rht != 0 && o->use_2d_block)
+        return fail(MX_ERR_UNSUPPORTED, "%s options: rht is not combined with use_2d_block", which);
     return MX_SUCCESS;
 }
 
@@ -72,6 +73,7 @@ mx::DirOpts to_dir(const mx_quant_opts *o) {
         d.key1 = (uint32_t)(o->seed >> 32);
         d.tensor_id = o->tensor_id;
         d.index_base = o->index_base;
+        d.rht = o->rht;
     }
     return d;
 }

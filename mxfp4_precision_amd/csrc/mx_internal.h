@@ -21,6 +21,7 @@ struct DirOpts {
     uint32_t key0, key1;        // Philox key = seed
     uint32_t tensor_id;
     uint64_t index_base;
+    uint32_t rht;               // random Hadamard transform seed, 0 = off
 };
 
 struct QuantArgs {

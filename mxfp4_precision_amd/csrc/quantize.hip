@@ -31,6 +31,20 @@
 // the truncation u >> 22 plus 1 iff the element's random byte is below the
 // next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)).
 
+// Random Hadamard transform (when a direction's rht seed is non-zero): the
+// page's dual-quantize op has an "rht" switch for the column-wise blobs of
+// the activation and the gradient (the wgrad operands) and defines nothing
+// more.  Here each 32-element block along the quantized axis becomes
+// c * H32 * D * x in fp32: D negates the positions whose bit is set in a
+// sign word drawn from the seed (Philox-4x32-10, counter (0,0,0,2), key
+// (seed, 0), first word), H32 is the Sylvester Hadamard matrix applied as a
+// fast Walsh-Hadamard transform (pairs differing in position bit k = 0..4,
+// (a, b) -> (a + b, a - b)), c = fp32(1/sqrt(32)).  A lane holds 8 positions
+// of a block, so bits 0..2 are in-lane butterflies and bits 3, 4 exchange
+// with the lanes that hold the other 8-position slices.  Pads are +0 before
+// the transform.  Scale and codes then come from the fp32 values, encoded
+// with exact comparisons (RNE) or exact fraction bits (SR) of |y| 2^(127-c).
+
 #include "mx_internal.h"
 
 namespace mx {
@@ -139,7 +153,106 @@ __device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
     return umax(v, (uint32_t)__shfl_xor((int)v, mask, 64));
 }
 
-template <int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR>
+// ------------------------------------------------------------------ RHT
+constexpr uint32_t kRhtScaleBits = 0x3E3504F3u;   // fp32 nearest to 1/sqrt(32)
+
+__device__ __forceinline__ uint32_t rht_sign_word(uint32_t seed) {
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 2;
+    philox10(c0, c1, c2, c3, seed, 0u);
+    return c0;
+}
+
+// z[a][b]: a = position within this lane's 8-position slice of a block (the
+// transform axis), b = independent blocks.  `slice` = which slice (0..3) of
+// the 32 positions this lane holds; the slices differing in position bit 3
+// and bit 4 sit in lanes lane^MASK3 and lane^MASK4.
+template <int MASK3, int MASK4>
+__device__ __forceinline__ void rht_blocks(float (&z)[8][8], uint32_t signs, int slice) {
+#pragma clang fp contract(off)
+    const uint32_t sl = signs >> (8 * slice);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+        if ((sl >> a) & 1u)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) z[a][b] = -z[a][b];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int h = 1 << k;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            if (a & h) continue;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const float x = z[a][b], y = z[a + h][b];
+                z[a][b] = x + y;
+                z[a + h][b] = x - y;
+            }
+        }
+    }
+    const bool hi3 = (slice & 1) != 0, hi4 = (slice & 2) != 0;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const float p = __shfl_xor(z[a][b], MASK3, 64);
+            z[a][b] = hi3 ? p - z[a][b] : z[a][b] + p;
+        }
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const float p = __shfl_xor(z[a][b], MASK4, 64);
+            z[a][b] = hi4 ? p - z[a][b] : z[a][b] + p;
+        }
+    const float cs = __uint_as_float(kRhtScaleBits);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) z[a][b] = z[a][b] * cs;
+}
+
+// Scale byte from the block's max |y| as fp32 bits (NaN sorts above Inf).
+__device__ __forceinline__ uint32_t scale_code_f32(uint32_t amax_bits) {
+    if (amax_bits >= 0x7F800000u) return 0xFFu;
+    const uint32_t e = amax_bits >> 23;
+    return e > 2u ? e - 2u : 0u;
+}
+
+// E2M1 code of v (an exact fp32 value in [0, 8)), round to nearest even:
+// each boundary is a midpoint; at a tie the even code wins.
+__device__ __forceinline__ uint32_t code_rne_f32(float v) {
+    return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) + (uint32_t)(v >= 1.75f) +
+           (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) + (uint32_t)(v > 5.0f);
+}
+
+// Stochastic code of v: the lower grid index and floor(256 (v-lo)/(hi-lo)),
+// both read off v's bits (exact), round up iff the random byte is below it.
+__device__ __forceinline__ uint32_t code_sr_f32(float v, uint32_t rbyte) {
+    const uint32_t b = __float_as_uint(v);
+    uint32_t lo, t;
+    if (v >= 1.0f) {
+        lo = 2u + 2u * ((b >> 23) - 127u) + ((b >> 22) & 1u);
+        t = (b >> 14) & 0xFFu;
+    } else if (v >= 0.5f) {
+        lo = 1u;
+        t = (b >> 15) & 0xFFu;
+    } else {
+        lo = 0u;
+        t = (uint32_t)__builtin_ldexpf(v, 9);
+    }
+    const uint32_t r = lo + (rbyte < t ? 1u : 0u);
+    return r < 7u ? r : 7u;
+}
+
+template <bool SR>
+__device__ __forceinline__ uint32_t nibble_f32(float y, uint32_t c, uint32_t rbyte) {
+    if (c == 0xFFu) return 0u;
+    const float v = __builtin_ldexpf(__builtin_fabsf(y), 127 - (int)c);
+    const uint32_t code = SR ? code_sr_f32(v, rbyte) : code_rne_f32(v);
+    return code | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+template <int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -228,9 +341,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         for (int t = 0; t < 8; ++t) {
             const int64_t i = row0 + 8 * q + t;
             rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
-            if (ROW_SR && i < M && j0 < N)
+            // pads too: after a Hadamard transform they carry values (otherwise they are 0 and
+            // round to 0 with any byte)
+            if (ROW_SR)
                 rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
-            if (DUAL && COL_SR && i < M && j0 < N)
+            if (DUAL && COL_SR)
                 rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
         }
     }
@@ -244,6 +359,36 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     const int r_loc0 = wave * kWaveRows + 8 * q;      // this lane's first tile row
 
     // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
+    if (RHT && a.row.rht) {
+        // z[u][t]: transform axis = the lane's 8 columns (slice c%4 of the row block)
+        float z[8][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) z[u][t] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
+        rht_blocks<1, 2>(z, rht_sign_word(a.row.rht), c & 3);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) m = umax(m, __float_as_uint(z[u][t]) & 0x7FFFFFFFu);
+            m = xor_max(m, 1);
+            m = xor_max(m, 2);
+            const int64_t i = row0 + 8 * q + t;
+            const uint32_t sc = i < M ? scale_code_f32(m) : 0u;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t rb = ROW_SR ? ((u < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
+                packed |= nibble_f32<ROW_SR>(z[u][t], sc, rb) << (4 * u);
+            }
+            // rows past M are the tiled layout's zero padding (the transform of an
+            // all-zero row can hold -0, whose sign bit must not leak into it)
+            if (i >= M) packed = 0;
+            *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
+            if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+        }
+    } else
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int64_t i = row0 + 8 * q + t;
@@ -264,7 +409,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
     }
 
-    if (DUAL) {
+    if (DUAL && RHT && a.col.rht) {
+        // z[t][u]: transform axis = the lane's 8 rows (slice q of the column block)
+        float z[8][8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) z[t][u] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
+        rht_blocks<16, 32>(z, rht_sign_word(a.col.rht), q);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m = umax(m, __float_as_uint(z[t][u]) & 0x7FFFFFFFu);
+            m = xor_max(m, 16);
+            m = xor_max(m, 32);
+            const int64_t j = j0 + u;
+            const uint32_t sc = j < N ? scale_code_f32(m) : 0u;
+            uint32_t packed = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
+                packed |= nibble_f32<COL_SR>(z[t][u], sc, rb) << (4 * t);
+            }
+            if (j >= N) packed = 0;    // tiled zero-padding rows of the column blob
+            *reinterpret_cast<uint32_t *>(&s_data[1][(8 * c + u) * kLinePitch + 16 * wave + 4 * q]) = packed;
+            if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+        }
+    } else if (DUAL) {
         // column-wise: per column u of the lane, 8 rows in-lane, then lanes q^1, q^2
         uint32_t camax[8];
 #pragma unroll
@@ -373,22 +545,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 
 }  // namespace
 
-template <int LAYOUT, bool DUAL>
+template <int LAYOUT, bool DUAL, bool RHT>
 hipError_t launch_sr(const QuantArgs &a, dim3 grid, hipStream_t stream) {
     const bool rs = a.row.use_sr != 0, cs = DUAL && a.col.use_sr != 0;
-    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, true>), grid, dim3(256), 0, stream, a);
-    else if (rs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, false>), grid, dim3(256), 0, stream, a);
-    else if (cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, true>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, false>), grid, dim3(256), 0, stream, a);
+    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, true, RHT>), grid, dim3(256), 0, stream, a);
+    else if (rs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, false, RHT>), grid, dim3(256), 0, stream, a);
+    else if (cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, true, RHT>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, false, RHT>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int LAYOUT, bool DUAL>
+hipError_t launch_rht(const QuantArgs &a, dim3 grid, hipStream_t stream) {
+    return (a.row.rht || (DUAL && a.col.rht)) ? launch_sr<LAYOUT, DUAL, true>(a, grid, stream)
+                                              : launch_sr<LAYOUT, DUAL, false>(a, grid, stream);
 }
 
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
     dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
     if (layout == MX_LAYOUT_CANONICAL)
-        return dual ? launch_sr<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
-                    : launch_sr<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
-    return dual ? launch_sr<MX_LAYOUT_TILED, true>(a, grid, stream) : launch_sr<MX_LAYOUT_TILED, false>(a, grid, stream);
+        return dual ? launch_rht<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
+                    : launch_rht<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
+    return dual ? launch_rht<MX_LAYOUT_TILED, true>(a, grid, stream)
+                : launch_rht<MX_LAYOUT_TILED, false>(a, grid, stream);
 }
 
 }  // namespace mx

@@ -265,3 +265,76 @@ def test_device_layout_convert(oracle_mod, rows, length):
     s2 = torch.full_like(sd, 0x5A)
     mx.mx_layout_convert(0, rows, length, qt, st, q2, s2)
     assert (host(q2) == q.reshape(-1)).all() and (host(s2) == s.reshape(-1)).all()
+
+
+RHT_SHAPES = [(1, 1), (33, 70), (127, 129), (200, 1000), (300, 136)]
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", RHT_SHAPES)
+def test_rht_column_wise(oracle_mod, layout, shape):
+    """Random Hadamard transform on the column-wise blob (the recipe's wgrad
+    operands), RNE, every byte against the oracle; ragged shapes put real
+    elements and pads in one transformed block."""
+    _require_gpu()
+    x = synth.random_bf16(300 + shape[0] + shape[1], shape, std=1.0)
+    col = mx.quant_opts(rht=0x1234)
+    check_dual(oracle_mod, x, layout, None, col, None, dict(rht=0x1234))
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", RHT_SHAPES)
+def test_rht_both_directions_stochastic(oracle_mod, layout, shape):
+    """RHT on both blobs with stochastic rounding, different seeds per direction;
+    an index base that is not a multiple of 16 (Philox windows straddle counters)."""
+    _require_gpu()
+    x = synth.random_bf16(400 + shape[0] + shape[1], shape, std=0.3)
+    row = mx.quant_opts(use_sr=True, seed=5, tensor_id=2, index_base=7, rht=77)
+    col = mx.quant_opts(use_sr=True, seed=6, tensor_id=2, index_base=7, rht=78)
+    check_dual(oracle_mod, x, layout, row, col, dict(use_sr=True, seed=5, tensor_id=2, index_base=7, rht=77),
+               dict(use_sr=True, seed=6, tensor_id=2, index_base=7, rht=78))
+
+
+def test_rht_rowwise_and_specials(oracle_mod):
+    """Row-wise RHT through mx_quantize_rowwise, with Inf/NaN blocks (scale 0xFF,
+    zero codes), signed zeros and large/small magnitudes in other blocks."""
+    _require_gpu()
+    x = synth.random_bf16(41, (96, 256), std=1.0)
+    x[3, 5] = 0x7F80                   # +Inf
+    x[40, 200] = 0xFFC0                # NaN
+    x[70, 32:64] = 0x8000              # a block of -0
+    x[80, 64:96] = synth.bf16_bits(np.full(32, 3e38, np.float32))
+    x[90, 96:128] = synth.bf16_bits(np.full(32, 1e-38, np.float32))
+    check_rowwise(oracle_mod, x, TILED, mx.quant_opts(rht=3), dict(rht=3))
+    check_rowwise(oracle_mod, x, CANON, mx.quant_opts(use_sr=True, seed=9, rht=3), dict(use_sr=True, seed=9, rht=3))
+
+
+def test_fc2_full_size_rht_recipe(oracle_mod):
+    """The recipe's backward operands at full size: dY 18432x3072 dual with SR on
+    both blobs and RHT on the column-wise one, every byte; then the wgrad GEMM of
+    the RHT'd dY and X column-wise blobs (same sign seed) on sampled entries."""
+    _require_gpu()
+    d = synth.fc2()
+    row = mx.quant_opts(use_sr=True, seed=7, tensor_id=2)
+    col = mx.quant_opts(use_sr=True, seed=7, tensor_id=2, rht=0xABCD)
+    log("fc2 dY 18432x3072 SR + column RHT")
+    check_dual(oracle_mod, d["dY"], TILED, row, col, dict(use_sr=True, seed=7, tensor_id=2),
+               dict(use_sr=True, seed=7, tensor_id=2, rht=0xABCD))
+    # wgrad on a 2048-token slice: dW = dY^T X with both column blobs transformed
+    T, din, dout = 2048, 12288, 3072
+    g = np.ascontiguousarray(d["dY"][:T])
+    xx = np.ascontiguousarray(d["X"][:T])
+    gd, ldg = to_dev_bf16(g)
+    xd, ldxx = to_dev_bf16(xx)
+    _, _, gq, gs = quantize_dual(gd, T, dout, ldg, TILED, None, col)
+    _, _, xq, xs = quantize_dual(xd, T, din, ldxx, TILED, None, mx.quant_opts(rht=0xABCD))
+    C = torch.empty((dout, din), dtype=torch.float32, device="cuda")
+    mx.mx_gemm_a4w4(0, 1, dout, din, T, gq, gs, xq, xs, TILED, mx.MX_F32, C, din)
+    got = host(C)
+    oqg, osg = oracle_mod.quantize(g, 1, use_sr=True, seed=7, tensor_id=2, rht=0xABCD)
+    oqx, osx = oracle_mod.quantize(xx, 1, rht=0xABCD)
+    rng = np.random.default_rng(3)
+    ii, jj = rng.integers(0, dout, 2048), rng.integers(0, din, 2048)
+    ref = oracle_mod.gemm_entries(oqg, osg, oqx, osx, dout, din, T, ii, jj)
+    rel = np.linalg.norm(got[ii, jj] - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-5, rel
