@@ -15,7 +15,10 @@ Prints one JSON line: value = GEMM TFLOP/s of the whole step (3 GEMMs' flops
 over the step's wall time), per-kernel timings from HIP events on the launch
 stream, a roofline object for the dominant kernel (the GEMM, dense MXFP4 MFMA
 peak) and one for the dual quantizer (HBM), and the CPU oracle timed on a
-bounded sample of the same step.
+bounded sample of the same step.  "extras" times, on the same tensors, the
+library's options the step does not use: the random Hadamard transform on
+the column-wise blobs (the recipe's wgrad operands), the bias epilogue of the
+forward GEMM, and the device layout conversion.
 """
 from __future__ import annotations
 
@@ -42,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--tokens", type=int, default=18432)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the timings of the options outside the step (RHT, bias epilogue, layout conversion)")
     p.add_argument("--cpu-tokens", type=int, default=32,
                    help="token slice of the step the CPU oracle is timed on")
     p.add_argument("--profile-copy-mib", type=int, default=0,
@@ -168,6 +173,9 @@ def main():
     # Dual quantizer roofline on the largest launch (X: 18432 x 12288).
     qx_gbs = qb["quant_X"] / (per["quant_X"] * 1e-3) / 1e9
 
+    extras = None if args.no_extras else time_extras(mx, torch, dev, stream, X, dY, tokens, din, dout,
+                                                      Xr, Xrs, Wr, Wrs, qb, flops["gemm_fwd"])
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -197,10 +205,56 @@ def main():
         "kernels": kernels,
         "input_gen_s": round(gen_s, 1),
     }
+    if extras is not None:
+        out["extras"] = extras
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(data, args.cpu_tokens, din, dout)
     print(json.dumps(out), flush=True)
+
+
+def time_extras(mx, torch, dev, stream, X, dY, tokens, din, dout, Xr, Xrs, Wr, Wrs, qb, fwd_flops, reps=10):
+    """Event-timed launches (mean of `reps` after 2 warmups) of the options outside the step."""
+    T = mx.MX_LAYOUT_TILED
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    plain = mx.quant_opts()
+    rht = mx.quant_opts(rht=0x5248)
+    sr = mx.quant_opts(use_sr=True, seed=7, tensor_id=2)
+    sr_rht = mx.quant_opts(use_sr=True, seed=7, tensor_id=2, rht=0x5248)
+    qr, qrs = mx.empty_blob(tokens, din, T, dev); qc, qcs = mx.empty_blob(din, tokens, T, dev)
+    gr, grs = mx.empty_blob(tokens, dout, T, dev); gc, gcs = mx.empty_blob(dout, tokens, T, dev)
+    out = {}
+    ms = timed(lambda: mx.mx_quantize_dual(X, tokens, din, din, plain, rht, T, qr, qrs, qc, qcs, stream))
+    out["quant_X_col_rht"] = {"ms": round(ms, 5), "GB/s": round(qb["quant_X"] / (ms * 1e-3) / 1e9, 1),
+                              "what": "X dual, column-wise blob with the random Hadamard transform"}
+    ms = timed(lambda: mx.mx_quantize_dual(dY, tokens, dout, dout, sr, sr_rht, T, gr, grs, gc, gcs, stream))
+    out["quant_dY_sr_col_rht"] = {"ms": round(ms, 5), "GB/s": round(qb["quant_dY"] / (ms * 1e-3) / 1e9, 1),
+                                  "what": "dY dual, stochastic rounding, column-wise blob transformed"}
+    bias = torch.zeros((dout,), dtype=torch.int16, device=dev)
+    Yb = torch.empty((tokens, dout), dtype=torch.int16, device=dev)
+    ms = timed(lambda: mx.mx_gemm_a4w4_bias(0, 1, tokens, dout, din, Xr, Xrs, Wr, Wrs, T, mx.MX_BF16, bias, Yb,
+                                            dout, stream))
+    out["gemm_fwd_bias"] = {"ms": round(ms, 5), "TFLOP/s": round(fwd_flops / (ms * 1e-3) / 1e12, 1),
+                            "what": "fwd GEMM with the bias added in the epilogue"}
+    d_bytes, s_bytes = mx.mx_blob_bytes(tokens, din, mx.MX_LAYOUT_CANONICAL)
+    cq = torch.empty((d_bytes,), dtype=torch.uint8, device=dev)
+    cs = torch.empty((s_bytes,), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: mx.mx_layout_convert(0, tokens, din, Xr, Xrs, cq, cs, stream))
+    out["layout_convert_to_canonical"] = {"ms": round(ms, 5),
+                                          "GB/s": round(2.0 * (d_bytes + s_bytes) / (ms * 1e-3) / 1e9, 1),
+                                          "what": "X row-wise blob %dx%d, tiled -> canonical" % (tokens, din)}
+    return out
 
 
 def load_traffic():

@@ -42,8 +42,11 @@
 // (a, b) -> (a + b, a - b)), c = fp32(1/sqrt(32)).  A lane holds 8 positions
 // of a block, so bits 0..2 are in-lane butterflies and bits 3, 4 exchange
 // with the lanes that hold the other 8-position slices.  Pads are +0 before
-// the transform.  Scale and codes then come from the fp32 values, encoded
-// with exact comparisons (RNE) or exact fraction bits (SR) of |y| 2^(127-c).
+// the transform.  Scale and codes then come from the fp32 values: RNE with
+// V_CVT_SCALEF32_PK_FP4_F32 (a probe compared it with the comparison rule
+// below on every non-negative finite fp32 pattern at scale bytes 0, 1, 127,
+// 130, 200 and 254: no difference), SR from exact fraction bits of
+// |y| 2^(127-c).
 
 #include "mx_internal.h"
 
@@ -162,53 +165,69 @@ __device__ __forceinline__ uint32_t rht_sign_word(uint32_t seed) {
     return c0;
 }
 
-// z[a][b]: a = position within this lane's 8-position slice of a block (the
-// transform axis), b = independent blocks.  `slice` = which slice (0..3) of
-// the 32 positions this lane holds; the slices differing in position bit 3
-// and bit 4 sit in lanes lane^MASK3 and lane^MASK4.
+// One butterfly stage between lane pairs (lane, lane ^ MASK) on 8 values:
+// the lane with the bit clear (holding a) keeps a + b, its partner (holding
+// b) keeps a - b.
+//  MASK 16 / 32: V_PERMLANE16_SWAP / V_PERMLANE32_SWAP of a value with itself
+//    returns (a, b) in both lanes of a pair (checked on MI355X: the first
+//    result is the lower row / half's value, the second the upper one's), so
+//    both lanes compute fma(+-1, b, a), which rounds exactly like a +- b.
+//  MASK 1 / 2: DPP quad permutations [1,0,3,2] / [2,3,0,1] fetch the partner.
+template <int MASK>
+__device__ __forceinline__ void rht_cross_stage(float (&v)[8], bool hi) {
+#pragma clang fp contract(off)
+    if constexpr (MASK == 16 || MASK == 32) {
+        const float sgn = hi ? -1.0f : 1.0f;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            const uint32_t x = __float_as_uint(v[a]);
+            uint32_t lo, up;
+            if constexpr (MASK == 16) {
+                const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+                lo = r[0]; up = r[1];
+            } else {
+                const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                lo = r[0]; up = r[1];
+            }
+            v[a] = __builtin_fmaf(sgn, __uint_as_float(up), __uint_as_float(lo));
+        }
+    } else {
+        static_assert(MASK == 1 || MASK == 2, "lane exchange");
+        constexpr int kCtl = MASK == 1 ? 0xB1 : 0x4E;
+#pragma unroll
+        for (int a = 0; a < 8; ++a) {
+            const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[a]), kCtl, 0xF, 0xF, false));
+            v[a] = hi ? p - v[a] : v[a] + p;
+        }
+    }
+}
+
+// The transform of one block, of which this lane holds positions
+// 8*slice .. 8*slice+7 in v[0..7]; the slices differing in position bit 3 /
+// bit 4 sit in lanes lane^MASK3 / lane^MASK4.
 template <int MASK3, int MASK4>
-__device__ __forceinline__ void rht_blocks(float (&z)[8][8], uint32_t signs, int slice) {
+__device__ __forceinline__ void rht8(float (&v)[8], uint32_t signs, int slice) {
 #pragma clang fp contract(off)
     const uint32_t sl = signs >> (8 * slice);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
-        if ((sl >> a) & 1u)
-#pragma unroll
-            for (int b = 0; b < 8; ++b) z[a][b] = -z[a][b];
+        if ((sl >> a) & 1u) v[a] = -v[a];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const int h = 1 << k;
 #pragma unroll
         for (int a = 0; a < 8; ++a) {
             if (a & h) continue;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const float x = z[a][b], y = z[a + h][b];
-                z[a][b] = x + y;
-                z[a + h][b] = x - y;
-            }
+            const float x = v[a], y = v[a + h];
+            v[a] = x + y;
+            v[a + h] = x - y;
         }
     }
-    const bool hi3 = (slice & 1) != 0, hi4 = (slice & 2) != 0;
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const float p = __shfl_xor(z[a][b], MASK3, 64);
-            z[a][b] = hi3 ? p - z[a][b] : z[a][b] + p;
-        }
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const float p = __shfl_xor(z[a][b], MASK4, 64);
-            z[a][b] = hi4 ? p - z[a][b] : z[a][b] + p;
-        }
+    rht_cross_stage<MASK3>(v, (slice & 1) != 0);
+    rht_cross_stage<MASK4>(v, (slice & 2) != 0);
     const float cs = __uint_as_float(kRhtScaleBits);
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) z[a][b] = z[a][b] * cs;
+    for (int a = 0; a < 8; ++a) v[a] = v[a] * cs;
 }
 
 // Scale byte from the block's max |y| as fp32 bits (NaN sorts above Inf).
@@ -216,13 +235,6 @@ __device__ __forceinline__ uint32_t scale_code_f32(uint32_t amax_bits) {
     if (amax_bits >= 0x7F800000u) return 0xFFu;
     const uint32_t e = amax_bits >> 23;
     return e > 2u ? e - 2u : 0u;
-}
-
-// E2M1 code of v (an exact fp32 value in [0, 8)), round to nearest even:
-// each boundary is a midpoint; at a tie the even code wins.
-__device__ __forceinline__ uint32_t code_rne_f32(float v) {
-    return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) + (uint32_t)(v >= 1.75f) +
-           (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) + (uint32_t)(v > 5.0f);
 }
 
 // Stochastic code of v: the lower grid index and floor(256 (v-lo)/(hi-lo)),
@@ -244,12 +256,22 @@ __device__ __forceinline__ uint32_t code_sr_f32(float v, uint32_t rbyte) {
     return r < 7u ? r : 7u;
 }
 
-template <bool SR>
-__device__ __forceinline__ uint32_t nibble_f32(float y, uint32_t c, uint32_t rbyte) {
+__device__ __forceinline__ uint32_t nibble_f32_sr(float y, uint32_t c, uint32_t rbyte) {
     if (c == 0xFFu) return 0u;
     const float v = __builtin_ldexpf(__builtin_fabsf(y), 127 - (int)c);
-    const uint32_t code = SR ? code_sr_f32(v, rbyte) : code_rne_f32(v);
-    return code | ((__float_as_uint(y) >> 28) & 8u);
+    return code_sr_f32(v, rbyte) | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// Eight fp32 values (element e in nibble e) -> E2M1 codes of y / 2^(c-127), RNE, saturating, sign kept.
+__device__ __forceinline__ uint32_t pack8_rne_f32(float y0, float y1, float y2, float y3, float y4, float y5,
+                                                  float y6, float y7, uint32_t c) {
+    const float sf = scale_f32(c);
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y0, y1, sf, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y2, y3, sf, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y4, y5, sf, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, y6, y7, sf, 3);
+    return c == 0xFFu ? 0u : r;
 }
 
 template <int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
@@ -360,27 +382,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 
     // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
     if (RHT && a.row.rht) {
-        // z[u][t]: transform axis = the lane's 8 columns (slice c%4 of the row block)
-        float z[8][8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int u = 0; u < 8; ++u) z[u][t] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
-        rht_blocks<1, 2>(z, rht_sign_word(a.row.rht), c & 3);
+        // per row t: the lane's 8 columns are slice c%4 of their 32-column block
+        const uint32_t signs = rht_sign_word(a.row.rht);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
+            rht8<1, 2>(v, signs, c & 3);
             uint32_t m = 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) m = umax(m, __float_as_uint(z[u][t]) & 0x7FFFFFFFu);
+            for (int u = 0; u < 8; ++u) m = umax(m, __float_as_uint(v[u]) & 0x7FFFFFFFu);
             m = xor_max(m, 1);
             m = xor_max(m, 2);
             const int64_t i = row0 + 8 * q + t;
             const uint32_t sc = i < M ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
+            if (ROW_SR) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint32_t rb = ROW_SR ? ((u < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
-                packed |= nibble_f32<ROW_SR>(z[u][t], sc, rb) << (4 * u);
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t rb = ((u < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (u & 3))) & 0xFFu;
+                    packed |= nibble_f32_sr(v[u], sc, rb) << (4 * u);
+                }
+            } else {
+                packed = pack8_rne_f32(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
             }
             // rows past M are the tiled layout's zero padding (the transform of an
             // all-zero row can hold -0, whose sign bit must not leak into it)
@@ -410,27 +435,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     }
 
     if (DUAL && RHT && a.col.rht) {
-        // z[t][u]: transform axis = the lane's 8 rows (slice q of the column block)
-        float z[8][8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int u = 0; u < 8; ++u) z[t][u] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
-        rht_blocks<16, 32>(z, rht_sign_word(a.col.rht), q);
+        // per column u: the lane's 8 rows are slice q of their 32-row block
+        const uint32_t signs = rht_sign_word(a.col.rht);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = __uint_as_float(((d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu) << 16);
+            rht8<16, 32>(v, signs, q);
             uint32_t m = 0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) m = umax(m, __float_as_uint(z[t][u]) & 0x7FFFFFFFu);
+            for (int t = 0; t < 8; ++t) m = umax(m, __float_as_uint(v[t]) & 0x7FFFFFFFu);
             m = xor_max(m, 16);
             m = xor_max(m, 32);
             const int64_t j = j0 + u;
             const uint32_t sc = j < N ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
+            if (COL_SR) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
-                packed |= nibble_f32<COL_SR>(z[t][u], sc, rb) << (4 * t);
+                for (int t = 0; t < 8; ++t) {
+                    const uint32_t rb = ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu;
+                    packed |= nibble_f32_sr(v[t], sc, rb) << (4 * t);
+                }
+            } else {
+                packed = pack8_rne_f32(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
             }
             if (j >= N) packed = 0;    // tiled zero-padding rows of the column blob
             *reinterpret_cast<uint32_t *>(&s_data[1][(8 * c + u) * kLinePitch + 16 * wave + 4 * q]) = packed;
