@@ -77,6 +77,17 @@ def lib() -> ctypes.CDLL:
         L.oracle_rht_signs.restype = _u32
         L.oracle_rht32.argtypes = [_vp, _u32, _vp]
         L.oracle_rht32.restype = None
+        L.oracle_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e5m2_value.restype = ctypes.c_double
+        L.oracle_e5m2_from_double.argtypes = [ctypes.c_double]
+        L.oracle_e5m2_from_double.restype = ctypes.c_uint8
+        L.oracle_quantize_fp8_tw.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]
+        L.oracle_quantize_fp8_tw.restype = _int
+        L.oracle_gemm_fp8_entries.argtypes = [_vp, ctypes.c_float, _vp, ctypes.c_float, _i64, _i64, _i64, _i64,
+                                              _vp, _vp, _vp]
+        L.oracle_gemm_fp8_entries.restype = _int
+        L.oracle_fp8_to_tiled.argtypes = [_vp, _i64, _i64, _vp]
+        L.oracle_fp8_to_tiled.restype = _int
         _lib = L
     return _lib
 
@@ -166,6 +177,51 @@ def gemm_rows(qa, sa, qb, sb, M: int, N: int, K: int, i0: int, i1: int) -> np.nd
     rc = lib().oracle_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K, i0, i1, _ptr(out))
     if rc != 0:
         raise ValueError("oracle_gemm_rows rejected its arguments")
+    return out
+
+
+def e5m2_value(code: int) -> float:
+    """Exact value of an FP8 E5M2 code (OFP8)."""
+    return float(lib().oracle_e5m2_value(code))
+
+
+def e5m2_from_double(v: float) -> int:
+    """E5M2 code of v: RNE, finite overflow saturates to 57344, Inf kept, NaN -> 0x7F."""
+    return int(lib().oracle_e5m2_from_double(float(v)))
+
+
+def quantize_fp8_tw(x: np.ndarray, direction: int):
+    """Tensorwise E5M2 of bf16 bits x (M x N): returns (q, scale_inv, amax); q is
+    (M, N_pad) for direction 0, (N, M_pad) for direction 1 (the transpose)."""
+    assert x.dtype == np.uint16 and x.ndim == 2
+    x = np.ascontiguousarray(x)
+    M, N = x.shape
+    rows, length = (M, N) if direction == 0 else (N, M)
+    q = np.zeros((rows, padded(length)), dtype=np.uint8)
+    si = np.zeros(1, np.float32)
+    am = np.zeros(1, np.float32)
+    if lib().oracle_quantize_fp8_tw(_ptr(x), M, N, N, direction, _ptr(q), _ptr(si), _ptr(am)) != 0:
+        raise ValueError("oracle_quantize_fp8_tw rejected its arguments")
+    return q, float(si[0]), float(am[0])
+
+
+def gemm_fp8_entries(qa, sa_inv: float, qb, sb_inv: float, M: int, N: int, K: int, ii, jj) -> np.ndarray:
+    """fp64 C[ii, jj] of the tensorwise FP8 NT product (times both inverse scales)."""
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    out = np.empty(ii.shape[0], dtype=np.float64)
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    qb = np.ascontiguousarray(qb, dtype=np.uint8)
+    lib().oracle_gemm_fp8_entries(_ptr(qa), sa_inv, _ptr(qb), sb_inv, M, N, K, ii.shape[0], _ptr(ii), _ptr(jj),
+                                  _ptr(out))
+    return out
+
+
+def fp8_to_tiled(q: np.ndarray, rows: int, length: int) -> np.ndarray:
+    """Canonical FP8 blob (rows x L_pad) -> the library's FP8 tiled layout (flat uint8)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(cdiv(rows, 16) * 16 * padded(length), dtype=np.uint8)
+    lib().oracle_fp8_to_tiled(_ptr(q), rows, length, _ptr(out))
     return out
 
 

@@ -19,6 +19,13 @@
  *             dataflow of the autograd Function (fwd, dgrad, wgrad: all NT).
  *   [PHILOX]  Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
  *             as 1, 2, 3", SC'11, sec. 4.2 (Philox-4x32, 10 rounds).
+ *   [FP8]     OCP 8-bit Floating Point Specification (OFP8) v1.0, E5M2:
+ *             bias 15, 2 mantissa bits, subnormals, Inf and NaN encodings,
+ *             largest finite value 57344.  The same page's hybrid backward
+ *             re-quantizes the saved bf16 tensors "tensorwise" to E5M2
+ *             (one scale per tensor, returned as its inverse) and calls an
+ *             FP8 GEMM that multiplies by both inverse scales; the scale
+ *             rule itself is not on the pages (reading below).
  *   [RHT]     the same page's dual-quantize calls, which switch on a random
  *             Hadamard transform ("rht") for the column-wise blobs of the
  *             activation and of the gradient -- the two operands of wgrad --
@@ -406,6 +413,138 @@ int oracle_gemm_rows(const uint8_t *qa, const uint8_t *sa, const uint8_t *qb, co
             for (int64_t k = 0; k < K_pad; ++k)
                 acc += element_value(qa, sa, K_pad, i, k) * element_value(qb, sb, K_pad, j, k);
             out[(i - i0) * N + j] = acc;
+        }
+    return 0;
+}
+
+/* ------------------------------------------------- FP8 E5M2, tensorwise */
+
+#define E5M2_MAX 57344.0
+
+/* [FP8] value of an E5M2 code. */
+double oracle_e5m2_value(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -16);            /* subnormal: m/4 * 2^-14 */
+    else v = ldexp(1.0 + m / 4.0, e - 15);
+    return sign ? -v : v;
+}
+
+/*
+ * [FP8] E5M2 code of v: round to nearest, ties to the even code; finite
+ * values beyond 57344 saturate to 57344 (the reading of a saturating cast);
+ * +-Inf stays +-Inf; NaN becomes 0x7F with v's sign.
+ */
+uint8_t oracle_e5m2_from_double(double v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs(v);
+    if (isinf(a)) return (uint8_t)(sign | 0x7C);
+    if (a == 0.0) return sign;
+    int ex;
+    (void)frexp(a, &ex);                 /* a in [2^(ex-1), 2^ex) */
+    int unit_exp = (ex - 1) - 2;         /* spacing of 3-significant-bit numbers in this binade */
+    if (unit_exp < -16) unit_exp = -16;  /* subnormal spacing 2^-16 */
+    double units = ldexp(a, -unit_exp);
+    double fl = floor(units), rem = units - fl;
+    double n = fl;
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) n = fl + 1.0;
+    double r = ldexp(n, unit_exp);
+    if (r > E5M2_MAX) r = E5M2_MAX;
+    /* encode the (now representable) magnitude r */
+    if (r == 0.0) return sign;
+    int rex;
+    (void)frexp(r, &rex);
+    int e = rex - 1 + 15;                /* biased exponent */
+    uint8_t code;
+    if (e <= 0) code = (uint8_t)ldexp(r, 16);                      /* subnormal: m = r / 2^-16 */
+    else code = (uint8_t)((e << 2) | (int)(ldexp(r, -(rex - 1)) * 4.0 - 4.0));
+    return (uint8_t)(sign | code);
+}
+
+/*
+ * Tensorwise E5M2 quantization of an M x N bf16 tensor (reading of [P3]'s
+ * `_quantize_fp8_tw`, whose body is not on the pages):
+ *   amax  = max |x| over the tensor (any NaN or Inf: amax is that, not finite)
+ *   scale = fp32(57344 / amax) when amax is finite and > 0, else 1
+ *   code  = E5M2 of fp32(x * scale)  (the fp32 product is rounded first)
+ *   scale_inv = fp32(1 / scale)
+ * dir 0 writes the M x N_pad row blob, dir 1 the N x M_pad column blob (the
+ * transpose), padding +0 (code 0), row-major bytes.  Returns 0 or -1.
+ */
+int oracle_quantize_fp8_tw(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, int dir,
+                           uint8_t *q, float *scale_inv_out, float *amax_out)
+{
+    if (M < 0 || N < 0 || ldx < N || (dir != 0 && dir != 1)) return -1;
+    double amax = 0.0;
+    int nonfinite = 0;
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            uint16_t b = x[i * ldx + j];
+            if (!bf16_is_finite(b)) nonfinite = 1;
+            else if (fabs(bf16_value(b)) > amax) amax = fabs(bf16_value(b));
+        }
+    float scale = 1.0f;
+    if (!nonfinite && amax > 0.0) scale = (float)(E5M2_MAX / amax);   /* one rounding to fp32 */
+    if (scale_inv_out) *scale_inv_out = 1.0f / scale;
+    if (amax_out) *amax_out = nonfinite ? INFINITY : (float)amax;
+    const int64_t R = dir == 0 ? M : N, L = dir == 0 ? N : M;
+    const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < L_pad; ++k) {
+            uint8_t code = 0;
+            if (k < L) {
+                uint16_t b = dir == 0 ? x[r * ldx + k] : x[k * ldx + r];
+                float v = (float)bf16_value(b) * scale;             /* fp32 product */
+                code = oracle_e5m2_from_double((double)v);
+            }
+            q[r * L_pad + k] = code;
+        }
+    return 0;
+}
+
+/*
+ * The FP8 GEMM of the hybrid backward (NT form, both operands K-contiguous):
+ *   C[i][j] = (sum_{k < K_pad} e5m2(A[i][k]) * e5m2(B[j][k])) * sa_inv * sb_inv   in fp64.
+ */
+int oracle_gemm_fp8_entries(const uint8_t *qa, float sa_inv, const uint8_t *qb, float sb_inv,
+                            int64_t M, int64_t N, int64_t K, int64_t count,
+                            const int64_t *ii, const int64_t *jj, double *out)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
+    const int64_t K_pad = cdiv64(K, MX_PAD) * MX_PAD;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        double acc = 0.0;
+        if (i >= 0 && i < M && j >= 0 && j < N)
+            for (int64_t k = 0; k < K_pad; ++k)
+                acc += oracle_e5m2_value(qa[i * K_pad + k]) * oracle_e5m2_value(qb[j * K_pad + k]);
+        else
+            acc = NAN;
+        out[t] = acc * (double)sa_inv * (double)sb_inv;
+    }
+    return 0;
+}
+
+/*
+ * FP8 tiled layout: row groups of 16, k-steps of 64; atom (g, s) is 1 KB at
+ * (g * L_pad/64 + s) * 1024; lane = (r%16) + 16*((k%64)/16) owns bytes
+ * [16 lane, 16 lane + 16), element k at byte k%16.  Pad rows are zero.
+ */
+int oracle_fp8_to_tiled(const uint8_t *q, int64_t R, int64_t L, uint8_t *qt)
+{
+    if (R < 0 || L < 0) return -1;
+    const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
+    const int64_t R16 = cdiv64(R, 16) * 16;
+    memset(qt, 0, (size_t)(R16 * L_pad));
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < L_pad; ++k) {
+            int64_t lane = (r % 16) + 16 * ((k % 64) / 16);
+            qt[((r / 16) * (L_pad / 64) + k / 64) * 1024 + 16 * lane + k % 16] = q[r * L_pad + k];
         }
     return 0;
 }

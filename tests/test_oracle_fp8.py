@@ -1,0 +1,130 @@
+"""Pins of the oracle's tensorwise FP8 E5M2 path (the hybrid backward of the page
+"primus_turbo_mxfp4_local.py": saved bf16 tensors re-quantized to E5M2 with one
+scale per tensor, FP8 GEMM times both inverse scales).
+
+E5M2 per the OCP 8-bit floating point spec: bias 15, 2 mantissa bits, largest
+finite 57344.  Reading for the scale (its code is not on the pages):
+scale = fp32(57344 / amax), codes of fp32(x * scale) rounded to nearest even,
+finite overflow saturating, scale_inv = fp32(1 / scale).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from mxfp4_precision_amd import synth
+
+
+def finite_table():
+    """(code, exact value) of the 124 non-negative finite E5M2 codes, built from the
+    spec's fields by exact rational arithmetic."""
+    out = []
+    for c in range(0x7C):
+        e, m = c >> 2, c & 3
+        v = Fraction(m, 4) * Fraction(1, 2 ** 14) if e == 0 else (1 + Fraction(m, 4)) * Fraction(2) ** (e - 15)
+        out.append((c, v))
+    return out
+
+
+def brute_round(v: Fraction):
+    """Nearest table value, ties to the even code; beyond the largest: saturate."""
+    tab = finite_table()
+    if v >= tab[-1][1]:
+        return tab[-1][0]
+    best = min(tab, key=lambda cv: (abs(cv[1] - v), cv[0] & 1))
+    return best[0]
+
+
+def test_e5m2_decode_anchors(oracle_mod):
+    assert oracle_mod.e5m2_value(0x3C) == 1.0
+    assert oracle_mod.e5m2_value(0xC0) == -2.0
+    assert oracle_mod.e5m2_value(0x7B) == 57344.0
+    assert oracle_mod.e5m2_value(0x01) == 2.0 ** -16
+    assert oracle_mod.e5m2_value(0x03) == 0.75 * 2.0 ** -14
+    assert oracle_mod.e5m2_value(0x04) == 2.0 ** -14
+    assert oracle_mod.e5m2_value(0x7C) == np.inf and oracle_mod.e5m2_value(0xFC) == -np.inf
+    assert all(np.isnan(oracle_mod.e5m2_value(c)) for c in (0x7D, 0x7E, 0x7F, 0xFF))
+    for c, v in finite_table():
+        assert Fraction(oracle_mod.e5m2_value(c)) == v
+
+
+def test_e5m2_encode_against_brute_force(oracle_mod):
+    rng = np.random.default_rng(8)
+    tab = [v for _, v in finite_table()]
+    vals = []
+    for a, b in zip(tab, tab[1:]):
+        mid = (a + b) / 2
+        vals += [a, mid, mid + (b - a) / 1024, mid - (b - a) / 1024]
+    vals += [Fraction(float(x)) for x in rng.uniform(0, 60000, 300)]
+    vals += [Fraction(float(x)) for x in 2.0 ** rng.uniform(-20, 17, 300)]
+    vals += [Fraction(57344 + 4095), Fraction(57344 + 4096), Fraction(10 ** 6)]
+    for v in vals:
+        want = brute_round(v)
+        assert oracle_mod.e5m2_from_double(float(v)) == want, float(v)
+        assert oracle_mod.e5m2_from_double(-float(v)) == want | 0x80
+    assert oracle_mod.e5m2_from_double(np.inf) == 0x7C
+    assert oracle_mod.e5m2_from_double(-np.inf) == 0xFC
+    assert oracle_mod.e5m2_from_double(np.nan) == 0x7F
+    assert oracle_mod.e5m2_from_double(-0.0) == 0x80
+
+
+def test_tensorwise_scale_and_codes(oracle_mod):
+    x = synth.random_bf16(91, (37, 50), std=3.0)
+    q, sinv, amax = oracle_mod.quantize_fp8_tw(x, 0)
+    xf = synth.bf16_to_f32(x).astype(np.float64)
+    assert amax == np.abs(xf).max()
+    scale = np.float32(57344.0 / amax)
+    assert sinv == np.float32(np.float32(1.0) / scale)
+    # the largest element lands on the largest code
+    i, j = np.unravel_index(np.argmax(np.abs(xf)), xf.shape)
+    assert q[i, j] & 0x7F == 0x7B
+    # every code is the rounding of the fp32 product
+    prod = (synth.bf16_to_f32(x) * scale).astype(np.float32)
+    for (r, c), v in np.ndenumerate(prod):
+        assert q[r, c] == oracle_mod.e5m2_from_double(float(v))
+    assert (q[:, 50:] == 0).all() and q.shape == (37, 128)
+    # column blob = transpose, same scale
+    qc, sinv_c, _ = oracle_mod.quantize_fp8_tw(x, 1)
+    assert sinv_c == sinv and (qc[:, :37] == q[:, :50].T).all() and (qc[:, 37:] == 0).all()
+
+
+def test_tensorwise_special_tensors(oracle_mod):
+    z = np.zeros((5, 9), np.uint16)
+    q, sinv, amax = oracle_mod.quantize_fp8_tw(z, 0)
+    assert (q == 0).all() and sinv == 1.0 and amax == 0.0
+    x = synth.random_bf16(92, (4, 40), std=1e4)
+    x[2, 3] = 0x7F80          # +Inf: scale 1, values encoded as they are (saturating)
+    q, sinv, amax = oracle_mod.quantize_fp8_tw(x, 0)
+    assert sinv == 1.0 and amax == np.inf and q[2, 3] == 0x7C
+    xf = synth.bf16_to_f32(x)
+    for (r, c), v in np.ndenumerate(xf):
+        if np.isfinite(v):
+            assert q[r, c] == oracle_mod.e5m2_from_double(float(v))
+
+
+def test_fp8_gemm_against_numpy(oracle_mod):
+    M, N, K = 9, 7, 200
+    a = synth.random_bf16(93, (M, K), std=2.0)
+    b = synth.random_bf16(94, (N, K), std=1e-3)
+    qa, sa, _ = oracle_mod.quantize_fp8_tw(a, 0)
+    qb, sb, _ = oracle_mod.quantize_fp8_tw(b, 0)
+    da = np.vectorize(oracle_mod.e5m2_value)(qa)
+    db = np.vectorize(oracle_mod.e5m2_value)(qb)
+    ref = (da @ db.T) * sa * sb
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    got = oracle_mod.gemm_fp8_entries(qa, sa, qb, sb, M, N, K, ii.ravel(), jj.ravel()).reshape(M, N)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0)
+    # and the dequantized product approximates the bf16 one (E5M2: 2 mantissa bits)
+    exact = synth.bf16_to_f32(a).astype(np.float64) @ synth.bf16_to_f32(b).astype(np.float64).T
+    assert np.linalg.norm(got - exact) / np.linalg.norm(exact) < 0.1
+
+
+def test_fp8_tiled_positions(oracle_mod):
+    """Element (17, 70) of a 20 x 200 blob (L_pad 256, 4 k-steps of 64): row group 1,
+    k-step 1, lane 1 + 16*0 -> byte (1*4 + 1)*1024 + 16 + 6 = 5142; pad rows zero."""
+    q = np.zeros((20, 256), np.uint8)
+    q[17, 70] = 0xAB
+    q[0, 255] = 0xCD        # row 0, k-step 3, lane 0 + 16*3 = 48 -> 3*1024 + 768 + 15 = 3855
+    t = oracle_mod.fp8_to_tiled(q, 20, 200)
+    assert t.size == 32 * 256
+    assert t[5142] == 0xAB and t[3855] == 0xCD and np.count_nonzero(t) == 2
