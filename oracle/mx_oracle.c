@@ -469,7 +469,7 @@ uint8_t oracle_e5m2_from_double(double v)
  * Tensorwise E5M2 quantization of an M x N bf16 tensor (reading of [P3]'s
  * `_quantize_fp8_tw`, whose body is not on the pages):
  *   amax  = max |x| over the tensor (any NaN or Inf: amax is that, not finite)
- *   scale = fp32(57344 / amax) when amax is finite and > 0, else 1
+ *   scale = 57344 / amax as an fp32 division when amax is finite and > 0, else 1
  *   code  = E5M2 of fp32(x * scale)  (the fp32 product is rounded first)
  *   scale_inv = fp32(1 / scale)
  * dir 0 writes the M x N_pad row blob, dir 1 the N x M_pad column blob (the
@@ -487,8 +487,10 @@ int oracle_quantize_fp8_tw(const uint16_t *x, int64_t M, int64_t N, int64_t ldx,
             if (!bf16_is_finite(b)) nonfinite = 1;
             else if (fabs(bf16_value(b)) > amax) amax = fabs(bf16_value(b));
         }
+    /* fp32 arithmetic (correctly rounded float division; amax is a bf16 value, exact in fp32) */
+    volatile float famax = (float)amax;
     float scale = 1.0f;
-    if (!nonfinite && amax > 0.0) scale = (float)(E5M2_MAX / amax);   /* one rounding to fp32 */
+    if (!nonfinite && amax > 0.0) scale = 57344.0f / famax;
     if (scale_inv_out) *scale_inv_out = 1.0f / scale;
     if (amax_out) *amax_out = nonfinite ? INFINITY : (float)amax;
     const int64_t R = dir == 0 ? M : N, L = dir == 0 ? N : M;

@@ -73,8 +73,8 @@ def test_tensorwise_scale_and_codes(oracle_mod):
     q, sinv, amax = oracle_mod.quantize_fp8_tw(x, 0)
     xf = synth.bf16_to_f32(x).astype(np.float64)
     assert amax == np.abs(xf).max()
-    scale = np.float32(57344.0 / amax)
-    assert sinv == np.float32(np.float32(1.0) / scale)
+    scale = np.float32(57344.0) / np.float32(amax)          # fp32 division
+    assert sinv == np.float32(1.0) / scale
     # the largest element lands on the largest code
     i, j = np.unravel_index(np.argmax(np.abs(xf)), xf.shape)
     assert q[i, j] & 0x7F == 0x7B
