@@ -18,7 +18,8 @@ peak) and one for the dual quantizer (HBM), and the CPU oracle timed on a
 bounded sample of the same step.  "extras" times, on the same tensors, the
 library's options the step does not use: the random Hadamard transform on
 the column-wise blobs (the recipe's wgrad operands), the bias epilogue of the
-forward GEMM, and the device layout conversion.
+forward GEMM, the device layout conversion, and the hybrid backward's
+tensorwise FP8 quantize and FP8 dgrad/wgrad GEMMs.
 """
 from __future__ import annotations
 
@@ -173,7 +174,7 @@ def main():
     # Dual quantizer roofline on the largest launch (X: 18432 x 12288).
     qx_gbs = qb["quant_X"] / (per["quant_X"] * 1e-3) / 1e9
 
-    extras = None if args.no_extras else time_extras(mx, torch, dev, stream, X, dY, tokens, din, dout,
+    extras = None if args.no_extras else time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout,
                                                       Xr, Xrs, Wr, Wrs, qb, flops["gemm_fwd"])
 
     out = {
@@ -213,7 +214,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_extras(mx, torch, dev, stream, X, dY, tokens, din, dout, Xr, Xrs, Wr, Wrs, qb, fwd_flops, reps=10):
+def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr, Wrs, qb, fwd_flops, reps=10):
     """Event-timed launches (mean of `reps` after 2 warmups) of the options outside the step."""
     T = mx.MX_LAYOUT_TILED
 
@@ -247,6 +248,29 @@ def time_extras(mx, torch, dev, stream, X, dY, tokens, din, dout, Xr, Xrs, Wr, W
                                             dout, stream))
     out["gemm_fwd_bias"] = {"ms": round(ms, 5), "TFLOP/s": round(fwd_flops / (ms * 1e-3) / 1e12, 1),
                             "what": "fwd GEMM with the bias added in the epilogue"}
+    # hybrid backward: tensorwise E5M2 of dY (both blobs), W and X (column blobs), FP8 dgrad and wgrad
+    f8 = lambda r, l: torch.empty((mx.mx_fp8_blob_bytes(r, l, T),), dtype=torch.uint8, device=dev)
+    gr8, gc8, wc8, xc8 = f8(tokens, dout), f8(dout, tokens), f8(din, dout), f8(din, tokens)
+    info = torch.empty((3, 4), dtype=torch.float32, device=dev)
+    ms_q = timed(lambda: mx.mx_quantize_fp8_tw(dY, tokens, dout, dout, T, gr8, gc8, info[0], stream))
+    out["fp8_quant_dY_tw"] = {"ms": round(ms_q, 5),
+                              "GB/s": round((2.0 * tokens * dout + 2.0 * tokens * dout) / (ms_q * 1e-3) / 1e9, 1),
+                              "what": "dY tensorwise E5M2, row and column blobs (amax + quantize launches)"}
+    mx.mx_quantize_fp8_tw(X, tokens, din, din, T, None, xc8, info[1], stream)
+    mx.mx_quantize_fp8_tw(W, dout, din, din, T, None, wc8, info[2], stream)
+    dXf = torch.empty((tokens, din), dtype=torch.int16, device=dev)
+    dWf = torch.empty((dout, din), dtype=torch.int16, device=dev)
+    fl = 2.0 * tokens * din * dout
+    ms = timed(lambda: mx.mx_gemm_f8_tw(0, 1, tokens, din, dout, gr8, info[0, 1:], wc8, info[2, 1:], T, mx.MX_BF16,
+                                        dXf, din, stream))
+    out["fp8_gemm_dgrad"] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                             "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / 5000.0, 4),
+                             "what": "hybrid backward dgrad dY . W, tensorwise E5M2 (dense FP8 peak 5.0 PF/s)"}
+    ms = timed(lambda: mx.mx_gemm_f8_tw(0, 1, dout, din, tokens, gc8, info[0, 1:], xc8, info[1, 1:], T, mx.MX_BF16,
+                                        dWf, din, stream))
+    out["fp8_gemm_wgrad"] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                             "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / 5000.0, 4),
+                             "what": "hybrid backward wgrad dY^T . X, tensorwise E5M2"}
     d_bytes, s_bytes = mx.mx_blob_bytes(tokens, din, mx.MX_LAYOUT_CANONICAL)
     cq = torch.empty((d_bytes,), dtype=torch.uint8, device=dev)
     cs = torch.empty((s_bytes,), dtype=torch.uint8, device=dev)

@@ -207,6 +207,57 @@ mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_
                             void *C, int64_t ldc, void *stream);
 
 /*
+ * ---- Hybrid backward: tensorwise FP8 (E5M2) ----
+ * The page "primus_turbo_mxfp4_local.py" offers a backward that re-quantizes
+ * the saved bf16 activation, weight and gradient to FP8 E5M2 with one scale
+ * per tensor and runs FP8 GEMMs that multiply by both inverse scales.  E5M2
+ * per the OCP 8-bit floating point spec (bias 15, 2 mantissa bits, largest
+ * finite 57344).  The scale rule is the library's reading (the quantizer's
+ * code is not on the pages):
+ *   amax = max |x|;  scale = 57344 / amax as an fp32 division (1 if amax is 0
+ *   or not finite);  code = E5M2 of the fp32 product x * scale, round to
+ *   nearest even, finite overflow saturating to 57344, Inf kept, NaN -> 0x7F
+ *   with its sign;  scale_inv = 1 / scale (fp32).
+ * FP8 blobs: rows x L_pad bytes (L_pad = cdiv(length,128)*128, pads code 0).
+ *   MX_LAYOUT_CANONICAL: row-major.  MX_LAYOUT_TILED: rows padded to 16;
+ *   atom (row group g, k-step s of 64) = 1 KB at (g * L_pad/64 + s) * 1024;
+ *   lane = (r%16) + 16*((k%64)/16) owns bytes [16 lane, 16 lane + 16),
+ *   element k at byte k%16.
+ */
+
+/* Bytes of one FP8 blob.  Errors: MX_ERR_INVALID_ARGUMENT, MX_ERR_UNSUPPORTED. */
+mx_status mx_fp8_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *bytes);
+
+/*
+ * Tensorwise E5M2 quantization of x (M x N bf16, row stride ldx).  q_row
+ * (M rows along N) and q_col (N rows along M, the transpose) may each be NULL
+ * (not both).  info: device float[2], caller-owned: receives amax in [0] and
+ * scale_inv in [1]; [0] is also the reduction's working word, so calls that
+ * share an info buffer must not overlap.  Three launches on `stream`.
+ * Errors: MX_ERR_INVALID_ARGUMENT (NULL x/info, both outputs NULL, negative
+ * sizes, ldx < N), MX_ERR_MISALIGNED (x, outputs or info not 16-byte
+ * aligned, ldx % 8), MX_ERR_UNSUPPORTED (layout), MX_ERR_DEVICE_UNSUPPORTED,
+ * MX_ERR_HIP.  M == 0 or N == 0 is a no-op.
+ */
+mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, mx_layout layout,
+                             void *q_row, void *q_col, float *info, void *stream);
+
+/*
+ * C = (A . B^T) * a_scale_inv[0] * b_scale_inv[0] on tensorwise E5M2 blobs
+ * (MX_LAYOUT_TILED, both K-contiguous: the NT form of the hybrid backward's
+ * dgrad dY_row . W_col^T and wgrad dY_col . X_col^T), fp32 accumulation,
+ * bf16 (RNE) or fp32 output.  a_scale_inv / b_scale_inv: device pointers to
+ * the inverse scales (the [1] entries of the quantizer's info), read by the
+ * kernel, so no host synchronization.  Arguments and errors otherwise as
+ * mx_gemm_a4w4.
+ */
+mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                        const void *A, const float *a_scale_inv,
+                        const void *B, const float *b_scale_inv,
+                        mx_layout layout, mx_dtype out_dtype,
+                        void *C, int64_t ldc, void *stream);
+
+/*
  * Device-side layout conversion of one blob (rows, length) between the two
  * layouts, asynchronous on `stream`: the tiled layout is the one this
  * library's GEMM reads, the canonical one the interchange shapes of the page

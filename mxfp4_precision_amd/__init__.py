@@ -32,6 +32,7 @@ MX_F32 = 1
 
 EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
             "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
+            "mx_fp8_blob_bytes", "mx_quantize_fp8_tw", "mx_gemm_f8_tw",
             "mx_status_string", "mx_last_error")
 
 
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm_a4w4.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, i64, vp]
     L.mx_gemm_a4w4_bias.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, vp, i64, vp]
     L.mx_layout_convert.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp]
+    L.mx_fp8_blob_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t)]
+    L.mx_quantize_fp8_tw.argtypes = [vp, i64, i64, i64, i32, vp, vp, vp, vp]
+    L.mx_gemm_f8_tw.argtypes = [i32, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp, i64, vp]
     L.mx_layout_convert_host.argtypes = [i32, i64, i64, vp, vp, vp, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     L.mx_device_supported.argtypes = [i32]
@@ -81,7 +85,8 @@ def lib() -> ctypes.CDLL:
     L.mx_last_error.argtypes = []
     L.mx_last_error.restype = ctypes.c_char_p
     for name in ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
-                 "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize"):
+                 "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_fp8_blob_bytes",
+                 "mx_quantize_fp8_tw", "mx_gemm_f8_tw"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -153,6 +158,23 @@ def mx_gemm_a4w4_bias(transA: int, transB: int, M: int, N: int, K: int, A, A_sca
                       layout: int, out_dtype: int, bias, C, ldc: int, stream=None):
     _check(lib().mx_gemm_a4w4_bias(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
                                    layout, out_dtype, _ptr(bias), _ptr(C), ldc, _stream(stream)))
+
+
+def mx_fp8_blob_bytes(rows: int, length: int, layout: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().mx_fp8_blob_bytes(rows, length, layout, ctypes.byref(n)))
+    return n.value
+
+
+def mx_quantize_fp8_tw(x, M: int, N: int, ldx: int, layout: int, q_row, q_col, info, stream=None):
+    _check(lib().mx_quantize_fp8_tw(_ptr(x), M, N, ldx, layout, _ptr(q_row), _ptr(q_col), _ptr(info),
+                                    _stream(stream)))
+
+
+def mx_gemm_f8_tw(transA: int, transB: int, M: int, N: int, K: int, A, a_scale_inv, B, b_scale_inv,
+                  layout: int, out_dtype: int, C, ldc: int, stream=None):
+    _check(lib().mx_gemm_f8_tw(transA, transB, M, N, K, _ptr(A), _ptr(a_scale_inv), _ptr(B), _ptr(b_scale_inv),
+                               layout, out_dtype, _ptr(C), ldc, _stream(stream)))
 
 
 def mx_layout_convert(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst, stream=None):

@@ -227,6 +227,58 @@ mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_
                        bias, true, C, ldc, stream);
 }
 
+mx_status mx_fp8_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *bytes) {
+    if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
+    MX_TRY(check_layout(layout));
+    const int64_t r = layout == MX_LAYOUT_TILED ? mx::cdiv(rows, 16) * 16 : rows;
+    if (bytes) *bytes = (size_t)(r * mx::padded(length));
+    return MX_SUCCESS;
+}
+
+mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, mx_layout layout, void *q_row,
+                             void *q_col, float *info, void *stream) {
+    MX_TRY(validate_x(x, M, N, ldx));
+    MX_TRY(check_layout(layout));
+    if (!q_row && !q_col) return fail(MX_ERR_INVALID_ARGUMENT, "q_row and q_col are both NULL");
+    if (!info) return fail(MX_ERR_INVALID_ARGUMENT, "info is NULL");
+    if ((q_row && !aligned16(q_row)) || (q_col && !aligned16(q_col)) || !aligned16(info))
+        return fail(MX_ERR_MISALIGNED, "outputs and info must be 16-byte aligned");
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    return check_launch(mx::launch_quantize_fp8(static_cast<const uint16_t *>(x), M, N, ldx, layout,
+                                                static_cast<uint8_t *>(q_row), static_cast<uint8_t *>(q_col), info,
+                                                static_cast<hipStream_t>(stream)),
+                        "mx_quantize_fp8_tw");
+}
+
+mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
+                        const float *a_scale_inv, const void *B, const float *b_scale_inv, mx_layout layout,
+                        mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+    if (transA != 0 || transB != 1)
+        return fail(MX_ERR_UNSUPPORTED, "transA=%d transB=%d: only transA=0, transB=1 (C = A . B^T) is supported",
+                    transA, transB);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(MX_ERR_INVALID_ARGUMENT, "negative shape M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                    (long long)K);
+    MX_TRY(check_layout(layout));
+    if (layout != MX_LAYOUT_TILED) return fail(MX_ERR_UNSUPPORTED, "mx_gemm_f8_tw reads MX_LAYOUT_TILED blobs only");
+    if (out_dtype != MX_BF16 && out_dtype != MX_F32)
+        return fail(MX_ERR_UNSUPPORTED, "out_dtype %d (valid: MX_BF16=0, MX_F32=1)", (int)out_dtype);
+    if (ldc < N || ldc < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldc=%lld must be >= max(N, 1)", (long long)ldc);
+    if (!C) return fail(MX_ERR_INVALID_ARGUMENT, "C is NULL");
+    if (K > 0 && (!A || !B || !a_scale_inv || !b_scale_inv))
+        return fail(MX_ERR_INVALID_ARGUMENT, "operand or scale pointer is NULL");
+    if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
+        return fail(MX_ERR_MISALIGNED, "operands and C must be 16-byte aligned");
+    if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    return check_launch(mx::launch_gemm_fp8(M, N, K, static_cast<const uint8_t *>(A), a_scale_inv,
+                                            static_cast<const uint8_t *>(B), b_scale_inv, out_dtype, C, ldc,
+                                            static_cast<hipStream_t>(stream)),
+                        "mx_gemm_f8_tw");
+}
+
 mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const void *q_src, const void *s_src,
                             void *q_dst, void *s_dst, void *stream) {
     if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");

@@ -266,6 +266,91 @@ __device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[
     }
 }
 
+// Epilogue: write the 256x256 tile (tm, tn) of C from the accumulators;
+// acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4].
+// bf16: rounded (V_CVT_PK_BF16_F32, nearest even), staged in LDS, then
+// written as whole 512-byte row segments (each store instruction covers 2
+// rows with 16 bytes per lane); fp32: 16 bytes per lane straight from
+// registers.  Masked at the M/N edges.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn, int64_t M, int64_t N, void *C,
+                                           int64_t ldc, int wave, int lane) {
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
+    if (OUT_BF16) {
+        // Every wave waited for its own DMAs; the barrier makes sure all of
+        // them have landed and every stage read is done before the tile
+        // overwrites the stages.
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMA; ++j)
+#pragma unroll
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
+                    const uint32_t p01 = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
+                    const uint32_t p23 = __builtin_bit_cast(
+                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
+                    *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
+                }
+        __syncthreads();
+        constexpr int kRowsPerWave = kBM / kWaves;        // 32: 16 instructions of 2 rows
+        const int cl = (lane & 31) * 8;
+        const int64_t col = tn0 + cl;
+        uint4 v[kRowsPerWave / 2];
+#pragma unroll
+        for (int it = 0; it < kRowsPerWave / 2; ++it)
+            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave + 2 * it + (lane >> 5), cl));
+        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave + (lane >> 5)) * ldc + col;
+        if (tm0 + kBM <= M && tn0 + kBN <= N) {
+#pragma unroll
+            for (int it = 0; it < kRowsPerWave / 2; ++it)
+                *reinterpret_cast<uint4 *>(dst0 + 2 * it * ldc) = v[it];
+        } else {
+#pragma unroll
+            for (int it = 0; it < kRowsPerWave / 2; ++it) {
+                const int64_t row = tm0 + kRowsPerWave * wave + 2 * it + (lane >> 5);
+                if (row >= M || col >= N) continue;
+                uint16_t *dst = dst0 + 2 * it * ldc;
+                if (col + 7 < N) {
+                    *reinterpret_cast<uint4 *>(dst) = v[it];
+                } else {
+                    const uint32_t w4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+                    for (int e = 0; e < 7; ++e)
+                        if (col + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                }
+            }
+        }
+    } else {
+        const int64_t m0 = tm0 + wm * kWM, n0 = tn0 + wn * kWN;
+#pragma unroll
+        for (int j = 0; j < kMA; ++j) {
+            const int64_t row = m0 + 32 * j + lrow;
+            if (row >= M) continue;
+#pragma unroll
+            for (int i = 0; i < kMB; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
+                    const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
+                    if (col + 3 < N) {
+                        *reinterpret_cast<v4f *>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 3; ++e)
+                            if (col + e < N) dst[e] = v[e];
+                    }
+                }
+            }
+        }
+    }
+}
+
 // BIAS: C[i][j] = (sum) + bias[j], bias a bf16 vector of N, added in fp32
 // before the output rounding.
 template <bool OUT_BF16, bool BIAS>
@@ -389,8 +474,7 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
     // drain the trailing (out-of-range) DMAs before LDS is reused
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- epilogue: acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4]
-    const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
+    // ---- epilogue
     if constexpr (BIAS) {
 #pragma unroll
         for (int i = 0; i < kMB; ++i)
@@ -408,79 +492,140 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
                 }
             }
     }
-    if (OUT_BF16) {
-        // Round to bf16 (V_CVT_PK_BF16_F32, nearest even), stage the tile in
-        // LDS, then write whole 512-byte row segments: each store instruction
-        // covers 2 rows with 16 bytes per lane.  Every wave waited for its
-        // own DMAs above; the barrier makes sure all of them have landed and
-        // every stage read is done before the tile overwrites the stages.
-        __syncthreads();
+    store_tile<OUT_BF16>(acc, tm, tn, M, N, C, ldc, wave, lane);
+}
+
+// ------------------------------------------------------------ FP8 (E5M2)
+// The hybrid backward's GEMM: tensorwise E5M2 operands in the FP8 tiled
+// layout (16-row groups, 64-element k-steps, 1 KB atoms; lane
+// (r%16) + 16*((k%64)/16) owns 16 bytes), C = (A . B^T) * sa_inv * sb_inv.
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both formats E5M2 and unit block
+// scales (127): lane L of a 32-row operand tile supplies 32 bytes, row L%32,
+// elements [32*(L/32), 32*(L/32) + 32) of the 64-wide step = two 16-byte
+// slices of the atom, 256 bytes apart.  Same workgroup, wave tiles, XCD
+// order and LDS stages as the FP4 kernel; a k-step is 64 elements, its 32
+// atoms fill one 32 KB stage, step k+3 is in flight while step k computes.
+constexpr int kFmtBf8 = 1;          // MFMA f8f6f4 format code for E5M2
+constexpr int kUnitScale = 127;     // E8M0 2^0
+
+template <int S>
+__device__ __forceinline__ void fp8_dma_step(const GemmCtx &c, int64_t k) {
 #pragma unroll
-        for (int j = 0; j < kMA; ++j)
+    for (int r = 0; r < kLoads; ++r) {
+        const int a = kWaves * r + c.wave;
+        const uint32_t base = k < c.ksteps ? (uint32_t)c.ld_row[r] + (uint32_t)(k * 1024) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS(stage_buf<S>() + a * 1024), 16,
+                                                 base + c.lane16, 0, 0, 0);
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void fp8_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], int frag_off,
+                                         int a_atom0, int b_atom0) {
+    // step k landed for every wave (only steps k+1, k+2 may still be in flight),
+    // and every wave is done reading step k-1's stage
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kLoads) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t *st = stage_buf<S>() + frag_off;
+    uint4 b[kMB][2], a[kMA][2];
 #pragma unroll
-            for (int i = 0; i < kMB; ++i)
+    for (int i = 0; i < kMB; ++i) {
+        b[i][0] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024);
+        b[i][1] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024 + 256);
+    }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
-                    const uint32_t p01 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
-                    const uint32_t p23 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
-                    *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
-                }
-        __syncthreads();
-        constexpr int kRowsPerWave = kBM / kWaves;        // 32: 16 instructions of 2 rows
-        const int cl = (lane & 31) * 8;
-        const int64_t col = tn0 + cl;
-        uint4 v[kRowsPerWave / 2];
+    for (int j = 0; j < kMA; ++j) {
+        a[j][0] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024);
+        a[j][1] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024 + 256);
+    }
+    fp8_dma_step<(S + 3) & 3>(c, k + 3);
 #pragma unroll
-        for (int it = 0; it < kRowsPerWave / 2; ++it)
-            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave + 2 * it + (lane >> 5), cl));
-        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave + (lane >> 5)) * ldc + col;
-        if (tm0 + kBM <= M && tn0 + kBN <= N) {
-#pragma unroll
-            for (int it = 0; it < kRowsPerWave / 2; ++it)
-                *reinterpret_cast<uint4 *>(dst0 + 2 * it * ldc) = v[it];
-        } else {
-#pragma unroll
-            for (int it = 0; it < kRowsPerWave / 2; ++it) {
-                const int64_t row = tm0 + kRowsPerWave * wave + 2 * it + (lane >> 5);
-                if (row >= M || col >= N) continue;
-                uint16_t *dst = dst0 + 2 * it * ldc;
-                if (col + 7 < N) {
-                    *reinterpret_cast<uint4 *>(dst) = v[it];
-                } else {
-                    const uint32_t w4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-#pragma unroll
-                    for (int e = 0; e < 7; ++e)
-                        if (col + e < N) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-                }
-            }
-        }
-    } else {
-        const int64_t m0 = tm0 + wm * kWM, n0 = tn0 + wn * kWN;
+    for (int i = 0; i < kMB; ++i) {
+        const v8i bop = {(int)b[i][0].x, (int)b[i][0].y, (int)b[i][0].z, (int)b[i][0].w,
+                         (int)b[i][1].x, (int)b[i][1].y, (int)b[i][1].z, (int)b[i][1].w};
 #pragma unroll
         for (int j = 0; j < kMA; ++j) {
-            const int64_t row = m0 + 32 * j + lrow;
-            if (row >= M) continue;
-#pragma unroll
-            for (int i = 0; i < kMB; ++i) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
-                    const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
-                    if (col + 3 < N) {
-                        *reinterpret_cast<v4f *>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 3; ++e)
-                            if (col + e < N) dst[e] = v[e];
-                    }
-                }
-            }
+            const v8i aop = {(int)a[j][0].x, (int)a[j][0].y, (int)a[j][0].z, (int)a[j][0].w,
+                             (int)a[j][1].x, (int)a[j][1].y, (int)a[j][1].z, (int)a[j][1].w};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc[i][j], kFmtBf8, kFmtBf8, 0,
+                                                                        kUnitScale, 0, kUnitScale);
         }
     }
+    // reads first (the MFMAs need them), each DMA after an MFMA
+#pragma unroll
+    for (int t = 0; t < kLoads; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMA * kMB - kLoads, 0);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
+                                                            int tiles_n, const uint8_t *__restrict__ A,
+                                                            const float *__restrict__ a_scale_inv,
+                                                            const uint8_t *__restrict__ B,
+                                                            const float *__restrict__ b_scale_inv,
+                                                            void *__restrict__ C, int64_t ldc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int xcd = b % kXcds, local = b / kXcds;
+    const int per = nb / kXcds, rem = nb % kXcds;
+    const int id = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int band = kGroupM * tiles_n;
+    const int first_m = (id / band) * kGroupM;
+    const int gsz = min(tiles_m - first_m, kGroupM);
+    const int tm = first_m + (id % band) % gsz;
+    const int tn = (id % band) / gsz;
+
+    GemmCtx c;
+    c.ksteps = K_pad / 64;
+    c.kgroups = 0;
+    c.wave = wave;
+    c.lane16 = lane * 16;
+    c.lane4 = 0;
+    const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);
+    c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
+    c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
+    const int64_t gA0 = (int64_t)tm * kGA, gB0 = (int64_t)tn * kGB;
+#pragma unroll
+    for (int r = 0; r < kLoads; ++r) {
+        const int a = kWaves * r + wave;
+        const bool isA = a < kGA;
+        int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
+        const int64_t gmax = (isA ? nGA : nGB) - 1;
+        g = g < gmax ? g : gmax;
+        c.ld_row[r] = (int)(g * c.ksteps * 1024);
+    }
+    const float scale = a_scale_inv[0] * b_scale_inv[0];
+
+    v16f acc[kMB][kMA];
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+
+    fp8_dma_step<0>(c, 0);
+    fp8_dma_step<1>(c, 1);
+    fp8_dma_step<2>(c, 2);
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 32 * lhi) * 16;
+    const int a_atom0 = wm * kTA, b_atom0 = kGA + wn * kTB;
+    for (int64_t k = 0; k < c.ksteps; k += 4) {
+        fp8_step<0>(c, k, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<1>(c, k + 1, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<2>(c, k + 2, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<3>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int j = 0; j < kMA; ++j) acc[i][j] *= scale;
+    store_tile<OUT_BF16>(acc, tm, tn, M, N, C, ldc, wave, lane);
 }
 
 // K == 0: C[i][j] = 0, or bias[j] (bf16 bits; exact in either output type).
@@ -520,6 +665,32 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
                                        : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);
     hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, As, B, Bs, bias,
                        C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const float *a_scale_inv,
+                           const uint8_t *B, const float *b_scale_inv, mx_dtype out_dtype, void *C, int64_t ldc,
+                           hipStream_t stream) {
+    const int64_t K_pad = padded(K);
+    if (K_pad == 0) {
+        const int64_t n = M * N;
+        dim3 grid((unsigned)cdiv(n, 256));
+        if (out_dtype == MX_BF16)
+            hipLaunchKernelGGL(fill_kernel<uint16_t>, grid, dim3(256), 0, stream, reinterpret_cast<uint16_t *>(C),
+                               M, N, ldc, nullptr);
+        else
+            hipLaunchKernelGGL(fill_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<float *>(C), M, N,
+                               ldc, nullptr);
+        return hipGetLastError();
+    }
+    // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
+    if (cdiv(M, 16) * 16 * K_pad >= (int64_t(1) << 31) || cdiv(N, 16) * 16 * K_pad >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
+    dim3 grid((unsigned)(tiles_m * tiles_n));
+    auto kernel = out_dtype == MX_BF16 ? gemm_fp8_kernel<true> : gemm_fp8_kernel<false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, a_scale_inv, B,
+                       b_scale_inv, C, ldc);
     return hipGetLastError();
 }
 

@@ -38,6 +38,11 @@ hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipS
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream);
+hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const float *a_scale_inv,
+                           const uint8_t *B, const float *b_scale_inv, mx_dtype out_dtype, void *C, int64_t ldc,
+                           hipStream_t stream);
+hipError_t launch_quantize_fp8(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, mx_layout layout,
+                               uint8_t *q_row, uint8_t *q_col, float *info, hipStream_t stream);
 hipError_t launch_layout_convert(bool to_tiled, int64_t rows, int64_t length, const uint8_t *q_src,
                                  const uint8_t *s_src, uint8_t *q_dst, uint8_t *s_dst, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t length,

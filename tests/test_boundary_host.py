@@ -161,3 +161,21 @@ def test_device_supported_without_gpu(L):
     if torch.cuda.is_available():
         pytest.skip("GPU present")
     assert mx.mx_device_supported(0) is False
+
+
+def test_fp8_validation_and_sizes(L):
+    A16 = 1 << 20
+    assert mx.mx_fp8_blob_bytes(37, 200, mx.MX_LAYOUT_CANONICAL) == 37 * 256
+    assert mx.mx_fp8_blob_bytes(37, 200, mx.MX_LAYOUT_TILED) == 48 * 256
+    Q = mx.mx_quantize_fp8_tw
+    assert _status(Q, A16, 4, 8, 8, 1, 0, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT      # no output
+    assert _status(Q, A16, 4, 8, 8, 1, A16, 0, 0, 0) == mx.MX_ERR_INVALID_ARGUMENT      # info NULL
+    assert _status(Q, A16, 4, 8, 8, 1, A16 + 4, 0, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(Q, A16, 4, 8, 8, 7, A16, 0, A16, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, 0, 8, 8, 1, A16, 0, A16, 0) == mx.MX_SUCCESS
+    G = mx.mx_gemm_f8_tw
+    assert _status(G, 0, 0, 4, 4, 4, A16, A16, A16, A16, 1, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(G, 0, 1, 4, 4, 4, A16, 0, A16, A16, 1, 0, A16, 8, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, 0, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, 1, 0, A16, 12, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(G, 0, 1, 0, 4, 4, A16, A16, A16, A16, 1, 0, A16, 8, 0) == mx.MX_SUCCESS

@@ -1,0 +1,157 @@
+"""GPU parity of the hybrid backward's tensorwise FP8 (E5M2) path against the oracle:
+quantize bit-exact (both blobs, both layouts, amax and inverse scale); the FP8
+GEMM elementwise within tau = 2^-14 sum_k |a_ik b_jk| sa sb (+ 2^-22 |C| for the
+scale roundings) in fp32 output, and in bf16 within tau + 1 ulp_bf16(|C| + tau)
+of bf16(C) (rounding of a value within tau of C).  Why 2^-14:
+V_MFMA_SCALE_F32_32X32X64_F8F6F4 with E5M2 operands sums each instruction's 64
+products with about 22 bits relative to the largest of them (measured on MI355X:
+a single K = 64 instruction was off by up to ~400 * 2^-24 sum |a b|); the bar
+takes 1024 * 2^-24 = 2^-14 per instruction, summed over the instructions of K."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import mxfp4_precision_amd as mx
+from mxfp4_precision_amd import synth
+
+from gpu_util import host, log, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+TILED, CANON = mx.MX_LAYOUT_TILED, mx.MX_LAYOUT_CANONICAL
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def quant(x_bits, layout, want_row=True, want_col=True):
+    M, N = x_bits.shape
+    xd, ldx = to_dev_bf16(x_bits)
+    qr = torch.full((max(mx.mx_fp8_blob_bytes(M, N, layout), 16),), 0x5A, dtype=torch.uint8, device="cuda") \
+        if want_row else None
+    qc = torch.full((max(mx.mx_fp8_blob_bytes(N, M, layout), 16),), 0x5A, dtype=torch.uint8, device="cuda") \
+        if want_col else None
+    info = torch.full((4,), -1.0, dtype=torch.float32, device="cuda")
+    mx.mx_quantize_fp8_tw(xd, M, N, ldx, layout, qr, qc, info)
+    return qr, qc, info
+
+
+def check_quant(oracle_mod, x, layout):
+    M, N = x.shape
+    qr, qc, info = quant(x, layout)
+    want_r, sinv, amax = oracle_mod.quantize_fp8_tw(x, 0)
+    want_c, _, _ = oracle_mod.quantize_fp8_tw(x, 1)
+    inf = host(info)
+    assert inf[1] == np.float32(sinv), (inf[1], sinv)
+    assert inf[0] == np.float32(amax) or (np.isinf(amax) and inf[0] >= np.inf) or (np.isnan(inf[0]) and np.isinf(amax))
+    if layout == TILED:
+        want_r, want_c = oracle_mod.fp8_to_tiled(want_r, M, N), oracle_mod.fp8_to_tiled(want_c, N, M)
+    for got, want, what in ((qr, want_r, "row"), (qc, want_c, "col")):
+        g = host(got)[: want.size].reshape(-1)
+        bad = np.nonzero(g != want.reshape(-1))[0]
+        assert bad.size == 0, "%s %s: %d bytes differ, first %s got %s want %s" % (
+            what, (M, N), bad.size, bad[:5].tolist(), g[bad[:5]].tolist(), want.reshape(-1)[bad[:5]].tolist())
+    return qr, qc, info
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", [(1, 1), (33, 70), (127, 129), (200, 1000), (300, 136)])
+def test_fp8_quantize(oracle_mod, layout, shape):
+    _require_gpu()
+    x = synth.random_bf16(500 + shape[0] + shape[1], shape, std=2.5)
+    log("fp8 quantize %s layout %d" % (shape, layout))
+    check_quant(oracle_mod, x, layout)
+
+
+def test_fp8_quantize_special_tensors(oracle_mod):
+    """All-zero tensor (scale 1), a tensor with +Inf (scale 1, Inf kept, large
+    values saturate), one with NaN, and tiny values in the E5M2 subnormal range."""
+    _require_gpu()
+    check_quant(oracle_mod, np.zeros((40, 50), np.uint16), TILED)
+    x = synth.random_bf16(7, (64, 96), std=3e4)
+    x[5, 7] = 0x7F80
+    check_quant(oracle_mod, x, TILED)
+    y = synth.random_bf16(8, (64, 96), std=1.0)
+    y[9, 9] = 0xFFC1
+    check_quant(oracle_mod, y, CANON)
+    z = synth.random_bf16(9, (50, 70), std=1.0)
+    z[0, 0] = synth.bf16_bits(np.array([3e3], np.float32))[0]      # pushes most values into E5M2 subnormals
+    check_quant(oracle_mod, z, CANON)
+
+
+def fp8_tau(oracle_mod, qa, sa, qb, sb, ii, jj):
+    """2^-14 sum_k |a_ik b_jk| sa sb (see the module doc)."""
+    table = np.array([oracle_mod.e5m2_value(c) for c in range(256)])
+    table[~np.isfinite(table)] = 0.0
+    s = np.einsum("ij,ij->i", np.abs(table[qa[ii]]), np.abs(table[qb[jj]]))
+    return 2.0 ** -14 * s * sa * sb
+
+
+def ulp_bf16(v):
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+
+
+def check_bf16_within(got_bits, ref, tau, oracle_mod, what):
+    refb = oracle_mod.bf16_from_double(ref)
+    got = oracle_mod.bf16_to_double(got_bits)
+    bound = tau + ulp_bf16(np.abs(ref) + tau)
+    err = np.abs(got - oracle_mod.bf16_to_double(refb))
+    bad = ~(err <= bound)
+    assert not bad.any(), "%s: %d bf16 entries off; first got %r ref %r bound %r" % (
+        what, int(bad.sum()), got[bad][:3], ref[bad][:3], bound[bad][:3])
+    return int((got_bits == refb).sum())
+
+
+def run_gemm(oracle_mod, a, b, nsample=None, seed=0, what=""):
+    M, K = a.shape
+    N = b.shape[0]
+    qa, _, ia = quant(a, TILED, True, False)
+    qb, _, ib = quant(b, TILED, True, False)
+    ldc = (N + 7) // 8 * 8
+    outs = {}
+    for dt in (mx.MX_BF16, mx.MX_F32):
+        C = torch.full((max(M, 1), ldc), -1, dtype=torch.int16 if dt == mx.MX_BF16 else torch.float32, device="cuda")
+        mx.mx_gemm_f8_tw(0, 1, M, N, K, qa, ia[1:], qb, ib[1:], TILED, dt, C, ldc)
+        outs[dt] = host(C)[:M, :N]
+    oqa, sa, _ = oracle_mod.quantize_fp8_tw(a, 0)
+    oqb, sb, _ = oracle_mod.quantize_fp8_tw(b, 0)
+    if nsample is None:
+        ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ii, jj = ii.ravel(), jj.ravel()
+    else:
+        rng = np.random.default_rng(seed)
+        ii, jj = rng.integers(0, M, nsample), rng.integers(0, N, nsample)
+    ref = oracle_mod.gemm_fp8_entries(oqa, sa, oqb, sb, M, N, K, ii, jj)
+    tau = fp8_tau(oracle_mod, oqa, sa, oqb, sb, ii, jj) + 2.0 ** -22 * np.abs(ref)
+    exact = check_bf16_within(outs[mx.MX_BF16].view(np.uint16)[ii, jj], ref, tau, oracle_mod, what)
+    got = outs[mx.MX_F32].astype(np.float64)[ii, jj]
+    err = np.abs(got - ref)
+    bad = ~(err <= tau)
+    assert not bad.any(), "%s: %d fp32 entries beyond tau, first got %r ref %r tau %r" % (
+        what, int(bad.sum()), got[bad][:3], ref[bad][:3], tau[bad][:3])
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    log("%s: %d/%d bf16 exact, fp32 max err/tau %.3g, rel %.3g" % (what, exact, ii.size, float((err / tau).max()), rel))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (100, 70, 300), (300, 257, 1000), (512, 513, 640)])
+def test_fp8_gemm(oracle_mod, M, N, K):
+    _require_gpu()
+    a = synth.random_bf16(M * 7 + K, (M, K), std=1.0)
+    b = synth.random_bf16(N * 11 + K, (N, K), std=0.02)
+    run_gemm(oracle_mod, a, b, what="fp8 %dx%dx%d" % (M, N, K))
+
+
+def test_fp8_hybrid_backward_fc2_sampled(oracle_mod):
+    """The hybrid backward at the fc2 shape (18432 tokens, 12288 -> 3072): dgrad
+    dY . W and wgrad dY^T . X from tensorwise E5M2 operands, sampled entries."""
+    _require_gpu()
+    d = synth.fc2()
+    X, W, dY = d["X"], d["W"], d["dY"]
+    log("fp8 hybrid dgrad")
+    run_gemm(oracle_mod, dY, np.ascontiguousarray(W.T), nsample=4096, seed=1, what="fp8 dgrad")
+    log("fp8 hybrid wgrad")
+    run_gemm(oracle_mod, np.ascontiguousarray(dY.T), np.ascontiguousarray(X.T), nsample=4096, seed=2,
+             what="fp8 wgrad")
