@@ -267,7 +267,7 @@ mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
  * 0: tiled -> canonical.  Device pointers, caller-owned, sized by
  * mx_blob_bytes for their layout; source and destination must not overlap.
  * Errors: MX_ERR_INVALID_ARGUMENT (negative shape, NULL pointer),
- * MX_ERR_MISALIGNED (data pointers not 16-byte aligned),
+ * MX_ERR_MISALIGNED (data or scale pointers not 16-byte aligned),
  * MX_ERR_DEVICE_UNSUPPORTED, MX_ERR_HIP (launch failure).  rows == 0 or
  * length == 0 is a no-op.
  */

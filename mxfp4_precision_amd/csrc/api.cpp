@@ -283,7 +283,8 @@ mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const vo
                             void *q_dst, void *s_dst, void *stream) {
     if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
     if (!q_src || !s_src || !q_dst || !s_dst) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
-    if (!aligned16(q_src) || !aligned16(q_dst)) return fail(MX_ERR_MISALIGNED, "data pointers must be 16-byte aligned");
+    if (!aligned16(q_src) || !aligned16(q_dst) || !aligned16(s_src) || !aligned16(s_dst))
+        return fail(MX_ERR_MISALIGNED, "data and scale pointers must be 16-byte aligned");
     if (rows == 0 || length == 0) return MX_SUCCESS;
     MX_TRY(check_device());
     return check_launch(mx::launch_layout_convert(to_tiled != 0, rows, length, static_cast<const uint8_t *>(q_src),

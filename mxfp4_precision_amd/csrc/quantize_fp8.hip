@@ -30,15 +30,23 @@ __global__ void fp8_clear_kernel(float *info) {
     if (threadIdx.x == 0 && blockIdx.x == 0) reinterpret_cast<uint32_t *>(info)[0] = 0u;
 }
 
-// amax of |x| into info[0] (fp32 bits of a bf16 value, atomic max).
+// amax of |x| into info[0] (fp32 bits of a bf16 magnitude, atomic max).  Each
+// thread walks 16-byte chunks (row i, columns jc*8..) with a grid stride; the
+// (row, chunk) position advances by adding the stride's quotient and
+// remainder instead of dividing per chunk.  The block reduces in LDS and
+// issues one atomic, skipped when the stored maximum is already as large.
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t N,
                                                        int64_t ldx, float *info) {
-    const int64_t chunks_per_row = cdiv(N, 8);
-    const int64_t total = M * chunks_per_row;
+    __shared__ uint32_t s_max[4];
+    const int64_t cpr = cdiv(N, 8);
+    const int64_t total = M * cpr;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t sq = stride / cpr, sr = stride % cpr;
+    int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t i = c / cpr, jc = c % cpr;
     uint32_t m = 0;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = c / chunks_per_row, j0 = (c % chunks_per_row) * 8;
+    for (; c < total; c += stride) {
+        const int64_t j0 = jc * 8;
         const uint16_t *p = x + i * ldx + j0;
         if (j0 + 8 <= N) {
             const uint4 v = *reinterpret_cast<const uint4 *>(p);
@@ -55,14 +63,28 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const uint16_t *__restric
                 m = m > b ? m : b;
             }
         }
+        jc += sr;
+        i += sq;
+        if (jc >= cpr) {
+            jc -= cpr;
+            ++i;
+        }
     }
-    // wave max, then one atomic per wave (bf16 magnitude bits -> fp32 bits)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const uint32_t o = (uint32_t)__shfl_xor((int)m, off, 64);
         m = m > o ? m : o;
     }
-    if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(reinterpret_cast<uint32_t *>(info), m << 16);
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = s_max[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) m = m > s_max[w] ? m : s_max[w];
+        uint32_t *word = reinterpret_cast<uint32_t *>(info);
+        const uint32_t bits = m << 16;
+        if (bits > __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(word, bits);
+    }
 }
 
 // E5M2 code of an fp32 value (see the file comment).
@@ -155,7 +177,7 @@ hipError_t launch_quantize_fp8(const uint16_t *x, int64_t M, int64_t N, int64_t 
                                uint8_t *q_row, uint8_t *q_col, float *info, hipStream_t stream) {
     hipLaunchKernelGGL(fp8_clear_kernel, dim3(1), dim3(64), 0, stream, info);
     const int64_t chunks = M * cdiv(N, 8);
-    const unsigned ablocks = (unsigned)(cdiv(chunks, 256) < 4096 ? cdiv(chunks, 256) : 4096);
+    const unsigned ablocks = (unsigned)(cdiv(chunks, 256) < 1024 ? cdiv(chunks, 256) : 1024);
     hipLaunchKernelGGL(fp8_amax_kernel, dim3(ablocks), dim3(256), 0, stream, x, M, N, ldx, info);
     // the grid covers both padded axes: pad columns of the row blob, pad rows of the column blob
     dim3 grid((unsigned)(padded(N) / kTile), (unsigned)(padded(M) / kTile));

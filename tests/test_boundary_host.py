@@ -152,6 +152,8 @@ def test_device_layout_convert_validation(L):
     assert _status(C, 0, 4, 8, A16, A16, A16, 0, 0) == mx.MX_ERR_INVALID_ARGUMENT
     assert _status(C, 1, 4, 8, A16 + 4, A16, A16, A16, 0) == mx.MX_ERR_MISALIGNED
     assert _status(C, 1, 4, 8, A16, A16, A16 + 8, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(C, 1, 4, 8, A16, A16 + 4, A16, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(C, 0, 4, 8, A16, A16, A16, A16 + 1, 0) == mx.MX_ERR_MISALIGNED
     assert _status(C, 1, 0, 8, A16, A16, A16, A16, 0) == mx.MX_SUCCESS
 
 
