@@ -88,6 +88,17 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_fp8_entries.restype = _int
         L.oracle_fp8_to_tiled.argtypes = [_vp, _i64, _i64, _vp]
         L.oracle_fp8_to_tiled.restype = _int
+        L.oracle_fp6_value.argtypes = [ctypes.c_uint, _int]
+        L.oracle_fp6_value.restype = ctypes.c_double
+        L.oracle_quantize_fp6.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _int, _u64, _u32, _u64, _vp, _vp]
+        L.oracle_quantize_fp6.restype = _int
+        L.oracle_dequantize_fp6.argtypes = [_vp, _vp, _i64, _i64, _int, _vp]
+        L.oracle_dequantize_fp6.restype = _int
+        L.oracle_gemm_fp6_entries.argtypes = [_vp, _vp, _int, _vp, _vp, _int, _i64, _i64, _i64, _i64,
+                                              _vp, _vp, _vp, _vp]
+        L.oracle_gemm_fp6_entries.restype = _int
+        L.oracle_fp6_to_tiled.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+        L.oracle_fp6_to_tiled.restype = _int
         _lib = L
     return _lib
 
@@ -277,4 +288,79 @@ def to_tiled(q: np.ndarray, s: np.ndarray, rows: int, length: int):
     q = np.ascontiguousarray(q, dtype=np.uint8)
     s = np.ascontiguousarray(s, dtype=np.uint8)
     lib().oracle_to_tiled(_ptr(q), _ptr(s), rows, length, _ptr(qt), _ptr(st))
+    return qt, st
+
+
+# ------------------------------------------------------------------ MXFP6
+FP6_E2M3 = 2
+FP6_E3M2 = 3
+
+
+def fp6_value(code: int, fmt: int) -> float:
+    """Value of a 6-bit code (fmt 2 = E2M3, 3 = E3M2; OCP MX v1.0 sec. 5.3.2)."""
+    return float(lib().oracle_fp6_value(code, fmt))
+
+
+def fp6_blob_shapes(rows: int, length: int) -> Tuple[Tuple[int, int], Tuple[int, int]]:
+    """Canonical FP6 (data, scale) byte shapes: 6 bits per element, scales as MXFP4."""
+    lp = padded(length)
+    return (rows, lp * 3 // 4), (rows, lp // BLOCK)
+
+
+def quantize_fp6(x: np.ndarray, direction: int, fmt: int, use_2d: bool = False, use_sr: bool = False,
+                 seed: int = 0, tensor_id: int = 0, index_base: int = 0):
+    """MXFP6 quantization of bf16 bits x (M x N) along rows (0) or columns (1); canonical (q, s)."""
+    assert x.dtype == np.uint16 and x.ndim == 2
+    x = np.ascontiguousarray(x)
+    M, N = x.shape
+    rows, length = (M, N) if direction == 0 else (N, M)
+    qs, ss = fp6_blob_shapes(rows, length)
+    q = np.zeros(qs, dtype=np.uint8)
+    s = np.zeros(ss, dtype=np.uint8)
+    rc = lib().oracle_quantize_fp6(_ptr(x), M, N, N, direction, fmt, int(use_2d), int(use_sr),
+                                   seed, tensor_id, index_base, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_quantize_fp6 rejected its arguments")
+    return q, s
+
+
+def dequantize_fp6(q: np.ndarray, s: np.ndarray, rows: int, length: int, fmt: int) -> np.ndarray:
+    """Exact fp64 values of a canonical FP6 blob, shape (rows, L_pad)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    assert q.shape == fp6_blob_shapes(rows, length)[0] and s.shape == fp6_blob_shapes(rows, length)[1]
+    out = np.empty((rows, padded(length)), dtype=np.float64)
+    if lib().oracle_dequantize_fp6(_ptr(q), _ptr(s), rows, length, fmt, _ptr(out)) != 0:
+        raise ValueError("oracle_dequantize_fp6 rejected its arguments")
+    return out
+
+
+def gemm_fp6_entries(qa, sa, fmt_a: int, qb, sb, fmt_b: int, M: int, N: int, K: int, ii, jj):
+    """fp64 C[ii[t], jj[t]] of deq(A) . deq(B)^T on FP6 blobs, and sum |a b| per entry."""
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    out = np.empty(ii.shape[0], dtype=np.float64)
+    aout = np.empty(ii.shape[0], dtype=np.float64)
+    qa, sa, qb, sb = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qa, sa, qb, sb))
+    if lib().oracle_gemm_fp6_entries(_ptr(qa), _ptr(sa), fmt_a, _ptr(qb), _ptr(sb), fmt_b, M, N, K,
+                                     ii.shape[0], _ptr(ii), _ptr(jj), _ptr(out), _ptr(aout)) != 0:
+        raise ValueError("oracle_gemm_fp6_entries rejected its arguments")
+    return out, aout
+
+
+def fp6_tiled_shapes(rows: int, length: int) -> Tuple[int, int]:
+    """Byte sizes (data, scale) of the tiled FP6 layout."""
+    lp = padded(length)
+    r16 = cdiv(rows, 16) * 16
+    return r16 * lp * 3 // 4, r16 * cdiv(lp, 512) * 16
+
+
+def fp6_to_tiled(q: np.ndarray, s: np.ndarray, rows: int, length: int):
+    """Canonical FP6 blob -> the library's tiled FP6 layout (flat uint8 arrays)."""
+    dq, ds = fp6_tiled_shapes(rows, length)
+    qt = np.empty(dq, dtype=np.uint8)
+    st = np.empty(ds, dtype=np.uint8)
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    lib().oracle_fp6_to_tiled(_ptr(q), _ptr(s), rows, length, _ptr(qt), _ptr(st))
     return qt, st

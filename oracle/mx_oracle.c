@@ -26,6 +26,9 @@
  *             (one scale per tensor, returned as its inverse) and calls an
  *             FP8 GEMM that multiplies by both inverse scales; the scale
  *             rule itself is not on the pages (reading below).
+ *   [OCP-MX] sec. 5.3.2 also defines the FP6 element formats (E2M3, E3M2)
+ *             used by the MXFP6 section at the end of this file; the pages
+ *             only name an MXFP6 training campaign (Primus PR 1107).
  *   [RHT]     the same page's dual-quantize calls, which switch on a random
  *             Hadamard transform ("rht") for the column-wise blobs of the
  *             activation and of the gradient -- the two operands of wgrad --
@@ -625,6 +628,262 @@ int oracle_to_tiled(const uint8_t *q, const uint8_t *s, int64_t R, int64_t L,
             int64_t lane = (r % 16) + 16 * (kb % 4);
             int64_t off = ((r / 16) * kgroups + kb / 16) * 256 + 4 * lane + (kb % 16) / 4;
             st[off] = s[r * (L_pad / 32) + kb];
+        }
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------------- MXFP6 */
+/*
+ * [OCP-MX] sec. 5.3.2: the two 6-bit element formats, numbered like the
+ * format codes of the f8f6f4 matrix instructions: fmt 2 = FP6 E2M3 (2
+ * exponent bits, bias 1, 3 mantissa bits), fmt 3 = FP6 E3M2 (3 exponent
+ * bits, bias 3, 2 mantissa bits).  Sign in bit 5; no Inf or NaN codes;
+ * exponent field 0 holds the subnormals m * 2^(1-bias-mbits).  The pages
+ * name an MXFP6 training campaign and define none of it; the element
+ * formats, the scale rule (sec. 6.3 with emax_elem = 2 for E2M3, whose
+ * largest normal is 1.875 * 2^2, and 4 for E3M2, 1.75 * 2^4), and the
+ * rounding rules (as for MXFP4) are this reading's.
+ *
+ * Canonical FP6 blob: data R x L_pad*3/4 bytes; element k of a row occupies
+ * bits [6k, 6k+6) of the row read as a little-endian bit string (byte
+ * 6k/8, from bit 6k%8 up, spilling into the next byte); scales exactly as
+ * for MXFP4 (R x L_pad/32, byte b scales elements [32b, 32b+32)).
+ */
+static int fp6_params(int fmt, int *ebits, int *mbits, int *bias, int *emax)
+{
+    if (fmt == 2) { *ebits = 2; *mbits = 3; *bias = 1; *emax = 2; return 0; }
+    if (fmt == 3) { *ebits = 3; *mbits = 2; *bias = 3; *emax = 4; return 0; }
+    return -1;
+}
+
+/* [OCP-MX] sec. 5.3.2: value of a 6-bit code (NaN for an unknown format). */
+double oracle_fp6_value(unsigned code, int fmt)
+{
+    int ebits, mbits, bias, emax;
+    if (fp6_params(fmt, &ebits, &mbits, &bias, &emax) != 0) return NAN;
+    unsigned m = code & ((1u << mbits) - 1u);
+    unsigned e = (code >> mbits) & ((1u << ebits) - 1u);
+    double mag = e == 0 ? ldexp((double)m, 1 - bias - mbits)
+                        : ldexp(1.0 + ldexp((double)m, -mbits), (int)e - bias);
+    return ((code >> 5) & 1u) ? -mag : mag;
+}
+
+/* The 32 non-negative magnitudes of a format, in code order (increasing). */
+static void fp6_grid(int fmt, double mag[32])
+{
+    for (unsigned c = 0; c < 32; ++c) mag[c] = oracle_fp6_value(c, fmt);
+}
+
+/* Round to nearest on the grid, ties to the even code; above the largest
+ * magnitude saturate to it (code 31). */
+static int fp6_rne(double v, const double mag[32])
+{
+    if (v >= mag[31]) return 31;
+    int lo = 0;
+    while (mag[lo + 1] <= v) lo++;
+    double dlo = v - mag[lo], dhi = mag[lo + 1] - v;
+    if (dlo < dhi) return lo;
+    if (dhi < dlo) return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;
+}
+
+/* Stochastic rounding with one random byte r, the MXFP4 rule on this grid:
+ * t = floor(256 (v-lo)/(hi-lo)), round up iff r < t; v >= max gives max. */
+static int fp6_sr(double v, unsigned r, const double mag[32])
+{
+    if (v >= mag[31]) return 31;
+    int lo = 0;
+    while (mag[lo + 1] <= v) lo++;
+    double frac = (v - mag[lo]) / (mag[lo + 1] - mag[lo]);
+    unsigned t = (unsigned)floor(256.0 * frac);
+    return (r < t) ? lo + 1 : lo;
+}
+
+static void fp6_put(uint8_t *row, int64_t k, unsigned code)
+{
+    int64_t bit = 6 * k;
+    for (int b = 0; b < 6; ++b, ++bit) {
+        uint8_t m = (uint8_t)(1u << (bit % 8));
+        if ((code >> b) & 1u) row[bit / 8] |= m;
+        else row[bit / 8] &= (uint8_t)~m;
+    }
+}
+
+static unsigned fp6_get(const uint8_t *row, int64_t k)
+{
+    unsigned code = 0;
+    int64_t bit = 6 * k;
+    for (int b = 0; b < 6; ++b, ++bit)
+        code |= (unsigned)((row[bit / 8] >> (bit % 8)) & 1u) << b;
+    return code;
+}
+
+/*
+ * MXFP6 quantization of one direction of x (as oracle_quantize, same block,
+ * 2D-tile, stochastic-rounding and padding rules; no Hadamard transform):
+ * shared exponent e = floor(log2 amax) - emax_elem clamped to [-127, 127]
+ * (amax == 0: -127), scale byte e + 127, or 0xFF with all-zero codes when
+ * the block holds Inf/NaN; element code = sign | round(|x| * 2^-e) on the
+ * format's grid.  q is canonical (R x L_pad*3/4), s is R x L_pad/32.
+ */
+int oracle_quantize_fp6(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, int dir, int fmt,
+                        int use_2d, int use_sr, uint64_t seed, uint32_t tensor_id,
+                        uint64_t index_base, uint8_t *q, uint8_t *s)
+{
+    int ebits, mbits, bias, emax;
+    if (M < 0 || N < 0 || ldx < N || (dir != 0 && dir != 1)) return -1;
+    if (fp6_params(fmt, &ebits, &mbits, &bias, &emax) != 0) return -1;
+    double mag[32];
+    fp6_grid(fmt, mag);
+    const int64_t R = dir == 0 ? M : N;
+    const int64_t L = dir == 0 ? N : M;
+    const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
+    const int64_t nblk = L_pad / MX_BLOCK;
+    const int64_t row_bytes = L_pad * 3 / 4;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < nblk; ++b) {
+            int64_t i0, i1, j0, j1;
+            if (dir == 0) {
+                i0 = use_2d ? (r / 32) * 32 : r;
+                i1 = use_2d ? i0 + 32 : r + 1;
+                j0 = b * MX_BLOCK;
+                j1 = j0 + MX_BLOCK;
+            } else {
+                i0 = b * MX_BLOCK;
+                i1 = i0 + MX_BLOCK;
+                j0 = use_2d ? (r / 32) * 32 : r;
+                j1 = use_2d ? j0 + 32 : r + 1;
+            }
+            if (i1 > M) i1 = M;
+            if (j1 > N) j1 = N;
+            double amax = 0.0;
+            int nonfinite = 0;
+            for (int64_t i = i0; i < i1; ++i)
+                for (int64_t j = j0; j < j1; ++j) {
+                    uint16_t bits = x[i * ldx + j];
+                    if (!bf16_is_finite(bits)) nonfinite = 1;
+                    else if (fabs(bf16_value(bits)) > amax) amax = fabs(bf16_value(bits));
+                }
+            int e = -127;
+            if (amax > 0.0) {
+                int ex;
+                (void)frexp(amax, &ex);
+                e = (ex - 1) - emax;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            s[r * nblk + b] = nonfinite ? 0xFF : (uint8_t)(e + 127);
+            for (int64_t t = 0; t < MX_BLOCK; ++t) {
+                int64_t k = b * MX_BLOCK + t;
+                unsigned code = 0;
+                if (k < L && !nonfinite) {
+                    int64_t i = dir == 0 ? r : k;
+                    int64_t j = dir == 0 ? k : r;
+                    uint16_t bits = x[i * ldx + j];
+                    double v = ldexp(fabs(bf16_value(bits)), -e);   /* exact */
+                    int c;
+                    if (use_sr) {
+                        uint64_t n = index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j;
+                        c = fp6_sr(v, oracle_sr_byte(seed, tensor_id, (uint32_t)dir, n), mag);
+                    } else {
+                        c = fp6_rne(v, mag);
+                    }
+                    code = ((bits >> 15) ? 32u : 0u) | (unsigned)c;
+                }
+                fp6_put(q + r * row_bytes, k, code);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Exact fp64 values of a canonical FP6 blob (R x L_pad; NaN under scale 0xFF). */
+int oracle_dequantize_fp6(const uint8_t *q, const uint8_t *s, int64_t R, int64_t L, int fmt, double *out)
+{
+    int ebits, mbits, bias, emax;
+    if (R < 0 || L < 0 || fp6_params(fmt, &ebits, &mbits, &bias, &emax) != 0) return -1;
+    const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < L_pad; ++k) {
+            uint8_t sb = s[r * (L_pad / MX_BLOCK) + k / MX_BLOCK];
+            out[r * L_pad + k] = sb == 0xFF ? NAN
+                                 : ldexp(oracle_fp6_value(fp6_get(q + r * (L_pad * 3 / 4), k), fmt), (int)sb - 127);
+        }
+    return 0;
+}
+
+/*
+ * The block-scaled NT product on FP6 blobs, the same definition as
+ * oracle_gemm_entries: C[i][j] = sum over the padded K of deqA[i][k] deqB[j][k]
+ * in fp64, k order.  Also returns sum |deqA[i][k] deqB[j][k]| in abs_out (may
+ * be NULL), the scale of the hardware's accumulation error.
+ */
+int oracle_gemm_fp6_entries(const uint8_t *qa, const uint8_t *sa, int fmt_a,
+                            const uint8_t *qb, const uint8_t *sb, int fmt_b,
+                            int64_t M, int64_t N, int64_t K, int64_t count,
+                            const int64_t *ii, const int64_t *jj, double *out, double *abs_out)
+{
+    int ebits, mbits, bias, emax;
+    if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
+    if (fp6_params(fmt_a, &ebits, &mbits, &bias, &emax) != 0 || fp6_params(fmt_b, &ebits, &mbits, &bias, &emax) != 0)
+        return -1;
+    const int64_t K_pad = cdiv64(K, MX_PAD) * MX_PAD;
+    const int64_t rb = K_pad * 3 / 4, nblk = K_pad / MX_BLOCK;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < count; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        double acc = 0.0, aacc = 0.0;
+        if (i >= 0 && i < M && j >= 0 && j < N) {
+            for (int64_t k = 0; k < K_pad; ++k) {
+                uint8_t ea = sa[i * nblk + k / MX_BLOCK], eb = sb[j * nblk + k / MX_BLOCK];
+                double a = ea == 0xFF ? NAN : ldexp(oracle_fp6_value(fp6_get(qa + i * rb, k), fmt_a), (int)ea - 127);
+                double b = eb == 0xFF ? NAN : ldexp(oracle_fp6_value(fp6_get(qb + j * rb, k), fmt_b), (int)eb - 127);
+                acc += a * b;
+                aacc += fabs(a * b);
+            }
+        } else {
+            acc = NAN;
+            aacc = NAN;
+        }
+        out[t] = acc;
+        if (abs_out) abs_out[t] = aacc;
+    }
+    return 0;
+}
+
+/*
+ * Canonical FP6 blob -> the library's tiled FP6 layout.
+ *   data atom (row group g, k-step c = k/128) is 1536 bytes at
+ *     (g * (L_pad/128) + c) * 1536; lane = (r%16) + 16*((k%128)/32) owns the
+ *     24 bytes of row r's k-block (the canonical bytes of those 32 elements,
+ *     in order): bytes 0..15 at 16*lane, bytes 16..23 at 1024 + 8*lane.
+ *   scales: the MXFP4 tiled scale atoms (oracle_to_tiled).
+ * Pad rows (r >= R) and unused scale bytes are 0.
+ */
+int oracle_fp6_to_tiled(const uint8_t *q, const uint8_t *s, int64_t R, int64_t L, uint8_t *qt, uint8_t *st)
+{
+    if (R < 0 || L < 0) return -1;
+    const int64_t L_pad = cdiv64(L, MX_PAD) * MX_PAD;
+    const int64_t R16 = cdiv64(R, 16) * 16;
+    const int64_t ksteps = L_pad / 128;
+    const int64_t kgroups = cdiv64(L_pad, 512);
+    const int64_t rb = L_pad * 3 / 4;
+    memset(qt, 0, (size_t)(R16 * rb));
+    memset(st, 0, (size_t)(R16 * kgroups * 16));
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t kb = 0; kb < L_pad / 32; ++kb) {
+            int64_t lane = (r % 16) + 16 * (kb % 4);
+            int64_t atom = ((r / 16) * ksteps + kb / 4) * 1536;
+            const uint8_t *src = q + r * rb + kb * 24;
+            for (int b = 0; b < 24; ++b) {
+                int64_t off = b < 16 ? atom + 16 * lane + b : atom + 1024 + 8 * lane + (b - 16);
+                qt[off] = src[b];
+            }
+            int64_t soff = ((r / 16) * kgroups + kb / 16) * 256 + 4 * lane + (kb % 16) / 4;
+            st[soff] = s[r * (L_pad / 32) + kb];
         }
     }
     return 0;
