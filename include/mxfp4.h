@@ -257,6 +257,60 @@ mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
                         mx_layout layout, mx_dtype out_dtype,
                         void *C, int64_t ldc, void *stream);
 
+/* ------------------------------------------------------------------ MXFP6
+ *
+ * MXFP6: the same 32-element blocks and E8M0 scales with 6-bit elements.
+ * The pages name an MXFP6 Flux training campaign (Primus PR 1107) and define
+ * none of it; the formats are the OCP MX v1.0 FP6 elements (sec. 5.3.2):
+ *   MX_FP6_E2M3: sign, 2 exponent bits (bias 1), 3 mantissa bits; magnitudes
+ *     k/8 for k < 8 (subnormal), up to 7.5; emax_elem = 2.
+ *   MX_FP6_E3M2: sign, 3 exponent bits (bias 3), 2 mantissa bits; magnitudes
+ *     k/16 for k < 4 (subnormal), up to 28; emax_elem = 4.
+ * Code = sign << 5 | exponent << mbits | mantissa; no Inf/NaN codes.  Scale
+ * byte = max(E(amax) - emax_elem, 0) (0xFF and all-zero codes for a block
+ * holding Inf/NaN); elements round to nearest even, or stochastically by the
+ * rule of mx_quant_opts, saturating at the largest magnitude.
+ *
+ * Blob layouts (R rows, quantized axis L, L_pad = cdiv(L,128)*128):
+ *   canonical data: R x L_pad*3/4 bytes; element k of a row occupies bits
+ *     [6k, 6k+6) of the row read as a little-endian bit string (a 32-element
+ *     block is 24 bytes); scales as MX_LAYOUT_CANONICAL.
+ *   tiled data: 1536-byte atoms; atom (g, c) = rows [16g, 16g+16) x k in
+ *     [128c, 128c+128) at byte (g * (L_pad/128) + c) * 1536.  Lane
+ *     (r%16) + 16*((k%128)/32) owns the 24 canonical bytes of its row's
+ *     k-block: bytes 0..15 at 16*lane, bytes 16..23 at 1024 + 8*lane (the
+ *     six-register operand of the f8f6f4 matrix instruction, split so that
+ *     both parts load aligned).  Rows padded to cdiv(R,16)*16 with zeros;
+ *     scales exactly as MX_LAYOUT_TILED.
+ */
+typedef enum mx_fp6_format {
+    MX_FP6_E2M3 = 2,
+    MX_FP6_E3M2 = 3
+} mx_fp6_format;
+
+/* Byte sizes of one MXFP6 blob in `layout` (either output may be NULL).
+ * Errors: MX_ERR_INVALID_ARGUMENT (negative size), MX_ERR_UNSUPPORTED (layout). */
+mx_status mx_fp6_blob_bytes(int64_t rows, int64_t length, mx_layout layout,
+                            size_t *data_bytes, size_t *scale_bytes);
+
+/*
+ * MXFP6 quantization of x (M x N bf16, stride ldx): the row-wise blob (R = M,
+ * L = N) in row_fmt, and, when q_col / s_col are given, the column-wise blob
+ * (R = N, L = M) in col_fmt from the same read of x (q_col = s_col = NULL:
+ * row-wise only, as a forward pass with no backward behind it needs).  Options
+ * per direction as for mx_quantize_dual, except rht (MX_ERR_UNSUPPORTED).
+ * Outputs sized by mx_fp6_blob_bytes; every output byte is written.
+ * Requires x and the outputs 16-byte aligned and ldx % 8 == 0.  M == 0 or
+ * N == 0 is a no-op.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, UNSUPPORTED (format, layout, rht),
+ * DEVICE_UNSUPPORTED, HIP.
+ */
+mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx,
+                          int row_fmt, const mx_quant_opts *row_opts,
+                          int col_fmt, const mx_quant_opts *col_opts,
+                          mx_layout layout, void *q_row, void *s_row,
+                          void *q_col, void *s_col, void *stream);
+
 /*
  * Device-side layout conversion of one blob (rows, length) between the two
  * layouts, asynchronous on `stream`: the tiled layout is the one this

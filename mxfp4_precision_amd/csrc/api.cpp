@@ -174,6 +174,65 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, con
                         "mx_quantize_dual");
 }
 
+mx_status mx_fp6_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *data_bytes,
+                            size_t *scale_bytes) {
+    if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
+    MX_TRY(check_layout(layout));
+    const int64_t Lp = mx::padded(length);
+    const int64_t r = layout == MX_LAYOUT_CANONICAL ? rows : mx::cdiv(rows, 16) * 16;
+    if (data_bytes) *data_bytes = (size_t)(r * (Lp * 3 / 4));
+    if (scale_bytes) *scale_bytes = (size_t)(layout == MX_LAYOUT_CANONICAL ? r * (Lp / 32) : r * mx::cdiv(Lp, 512) * 16);
+    return MX_SUCCESS;
+}
+
+namespace {
+mx_status check_fp6_fmt(int fmt, const char *which) {
+    if (fmt != MX_FP6_E2M3 && fmt != MX_FP6_E3M2)
+        return fail(MX_ERR_UNSUPPORTED, "%s element format %d (valid: MX_FP6_E2M3=2, MX_FP6_E3M2=3)", which, fmt);
+    return MX_SUCCESS;
+}
+mx_status check_fp6_opts(const mx_quant_opts *o, const char *which) {
+    MX_TRY(check_opts(o, which));
+    if (o && o->rht) return fail(MX_ERR_UNSUPPORTED, "%s options: rht is not available for MXFP6", which);
+    return MX_SUCCESS;
+}
+}  // namespace
+
+mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx, int row_fmt,
+                          const mx_quant_opts *row_opts, int col_fmt, const mx_quant_opts *col_opts,
+                          mx_layout layout, void *q_row, void *s_row, void *q_col, void *s_col, void *stream) {
+    const bool dual = q_col || s_col;
+    MX_TRY(validate_x(x, M, N, ldx));
+    MX_TRY(check_fp6_fmt(row_fmt, "row"));
+    MX_TRY(check_fp6_opts(row_opts, "row"));
+    if (dual) {
+        MX_TRY(check_fp6_fmt(col_fmt, "col"));
+        MX_TRY(check_fp6_opts(col_opts, "col"));
+    }
+    MX_TRY(check_layout(layout));
+    MX_TRY(validate_out(q_row, s_row, "row-wise"));
+    if (dual) MX_TRY(validate_out(q_col, s_col, "column-wise"));
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    mx::QuantArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.M = M; a.N = N; a.ldx = ldx;
+    a.M_pad = mx::padded(M); a.N_pad = mx::padded(N);
+    a.row = to_dir(row_opts);
+    a.row.fmt = (uint32_t)row_fmt;
+    if (dual) {
+        a.col = to_dir(col_opts);
+        a.col.fmt = (uint32_t)col_fmt;
+    }
+    a.sr_pairs = (dual && N % 16 == 0 && a.row.index_base % 16 == 0 && a.col.index_base % 16 == 0) ? 1u : 0u;
+    a.q_row = static_cast<uint8_t *>(q_row);
+    a.s_row = static_cast<uint8_t *>(s_row);
+    a.q_col = static_cast<uint8_t *>(q_col);
+    a.s_col = static_cast<uint8_t *>(s_col);
+    return check_launch(mx::launch_quantize_fp6(a, dual, layout, static_cast<hipStream_t>(stream)),
+                        "mx_quantize_fp6");
+}
+
 namespace {
 
 mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,

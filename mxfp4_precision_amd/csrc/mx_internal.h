@@ -22,6 +22,7 @@ struct DirOpts {
     uint32_t tensor_id;
     uint64_t index_base;
     uint32_t rht;               // random Hadamard transform seed, 0 = off
+    uint32_t fmt;               // MXFP6 element format (2 = E2M3, 3 = E3M2); unused for MXFP4
 };
 
 struct QuantArgs {
@@ -35,6 +36,7 @@ struct QuantArgs {
 
 // Kernel launchers (quantize.hip, gemm.hip, convert.hip, dequantize.hip).  They assume validated arguments.
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
+hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream);

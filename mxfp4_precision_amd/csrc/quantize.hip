@@ -57,7 +57,6 @@ constexpr int kWaveRows = 32;
 constexpr int kTileCols = 128;
 constexpr int kWaves = 4;
 constexpr int kTileRows = kWaveRows * kWaves;
-constexpr int kLinePitch = 80;          // LDS bytes per staged 64-byte blob-row line
 
 __device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
     if (amax16 >= 0x7F80u) return 0xFFu;            // Inf or NaN in the block
@@ -274,8 +273,68 @@ __device__ __forceinline__ uint32_t pack8_rne_f32(float y0, float y1, float y2, 
     return c == 0xFFu ? 0u : r;
 }
 
-template <int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
+// ------------------------------------------------------------------ FP6
+// MXFP6 elements (OCP MX v1.0 sec. 5.3.2): fmt 2 = E2M3 (3 mantissa bits,
+// emax_elem 2), fmt 3 = E3M2 (2 mantissa bits, emax_elem 4).  As for E2M1,
+// u = |x| * 2^(adj-c) as fp32 bits maps the format's smallest normal to the
+// smallest fp32 normal (adj = 1 for E2M3, 3 for E3M2), so the code is the
+// field u >> sh (sh = 23 - mantissa bits: exponent and mantissa bits in
+// place, the subnormal step on the fp32 subnormal grid), exact for bf16
+// inputs.  RNE adds half an ulp minus one plus the code's low bit before the
+// shift and saturates at code 31; SR clamps u at code 31 and adds
+// (255 - byte) << (sh - 8): the carry into bit sh happens iff the byte is
+// below the next 8 bits, which equal floor(256 (v-lo)/(hi-lo)).
+struct Fp6Dir {
+    int sh, adj;
+    uint32_t emax;
+};
+__device__ __forceinline__ Fp6Dir fp6_dir(uint32_t fmt) {
+    return fmt == 2u ? Fp6Dir{20, 1, 2u} : Fp6Dir{21, 3, 4u};
+}
+__device__ __forceinline__ uint32_t scale_code_emax(uint32_t amax16, uint32_t emax) {
+    if (amax16 >= 0x7F80u) return 0xFFu;
+    const uint32_t e = amax16 >> 7;
+    return e > emax ? e - emax : 0u;
+}
+// 6-bit code (sign in bit 5) of bf16 x16 under scale byte c.
+template <bool SR>
+__device__ __forceinline__ uint32_t code6(uint32_t x16, uint32_t c, const Fp6Dir &f, uint32_t rbyte) {
+    const float xf = __uint_as_float((x16 & 0x7FFFu) << 16);
+    uint32_t u = __float_as_uint(__builtin_ldexpf(xf, f.adj - (int)c));
+    uint32_t code;
+    if constexpr (SR) {
+        const uint32_t top = 31u << f.sh;
+        u = u < top ? u : top;
+        code = (u + ((255u - rbyte) << (f.sh - 8))) >> f.sh;
+    } else {
+        code = (u + (1u << (f.sh - 1)) - 1u + ((u >> f.sh) & 1u)) >> f.sh;
+        code = code < 31u ? code : 31u;
+    }
+    return c == 0xFFu ? 0u : (code | ((x16 >> 10) & 0x20u));
+}
+// Eight 6-bit codes -> 48 bits, element e at bits [6e, 6e+6): lo = bits 0..31, hi = 32..47.
+__device__ __forceinline__ void pack6(const uint32_t (&k)[8], uint32_t &lo, uint32_t &hi) {
+    lo = k[0] | (k[1] << 6) | (k[2] << 12) | (k[3] << 18) | (k[4] << 24) | (k[5] << 30);
+    hi = (k[5] >> 2) | (k[6] << 4) | (k[7] << 10);
+}
+// 6 bytes at an even LDS byte offset o.
+__device__ __forceinline__ void lds_put6(uint8_t *base, int o, uint32_t lo, uint32_t hi) {
+    if ((o & 3) == 0) {
+        *reinterpret_cast<uint32_t *>(base + o) = lo;
+        *reinterpret_cast<uint16_t *>(base + o + 4) = (uint16_t)hi;
+    } else {
+        *reinterpret_cast<uint16_t *>(base + o) = (uint16_t)lo;
+        *reinterpret_cast<uint32_t *>(base + o + 2) = (lo >> 16) | (hi << 16);
+    }
+}
+
+// ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
+// options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
+// 64 bytes (FP4) or 96 bytes (FP6), padded by 16 bytes against bank conflicts.
+template <int ELEM, int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
+    static_assert(ELEM == 4 || (ELEM == 6 && !RHT), "element size");
+    constexpr int kLinePitch = ELEM == 4 ? 80 : 112;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15;
@@ -413,6 +472,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
             if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
         }
+    } else if constexpr (ELEM == 6) {
+        const Fp6Dir f = fp6_dir(a.row.fmt);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t i = row0 + 8 * q + t;
+            const uint32_t sc = i < M ? scale_code_emax(a.row.use_2d ? tile_amax : ramax[t], f.emax) : 0u;
+            uint32_t k6[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t rb = ROW_SR ? ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu : 0u;
+                k6[e] = code6<ROW_SR>(x16, sc, f, rb);
+            }
+            uint32_t lo, hi;
+            pack6(k6, lo, hi);
+            lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
+            if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+        }
     } else
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -483,6 +560,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
             camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
         }
+        if constexpr (ELEM == 6) {
+            const Fp6Dir f = fp6_dir(a.col.fmt);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t j = j0 + u;
+                const uint32_t sc = j < N ? scale_code_emax(a.col.use_2d ? tile_amax : camax[u], f.emax) : 0u;
+                uint32_t k6[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+                    const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
+                    k6[t] = code6<COL_SR>(x16, sc, f, rb);
+                }
+                uint32_t lo, hi;
+                pack6(k6, lo, hi);
+                // blob row = tile column 8c+u; this wave's 32 rows are bytes [24*wave, 24*wave+24)
+                lds_put6(s_data[1], (8 * c + u) * kLinePitch + 24 * wave + 6 * q, lo, hi);
+                if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+            }
+        } else
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t j = j0 + u;
@@ -517,6 +614,40 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
         uint8_t *qd = dir == 0 ? a.q_row : a.q_col;
         uint8_t *sd = dir == 0 ? a.s_row : a.s_col;
         const int64_t rows_out = (LAYOUT == MX_LAYOUT_TILED) ? cdiv(R, 16) * 16 : R;
+        if constexpr (ELEM == 6) {
+            if (LAYOUT == MX_LAYOUT_TILED) {
+                // 8 atoms of 16 blob rows: lane slot (r%16) + 16*b takes the block's bytes
+                // 0..15 at 16*lane and 16..23 at 1024 + 8*lane of a 1536-byte atom
+#pragma unroll
+                for (int rep = 0; rep < 2; ++rep) {
+                    const int slot = (int)threadIdx.x + 256 * rep;
+                    const int lane = slot & 63;
+                    const int r_loc = 16 * (slot >> 6) + (lane & 15);
+                    const int64_t r = rbase + r_loc;
+                    if (r < rows_out) {
+                        const uint8_t *src = &s_data[dir][r_loc * kLinePitch + 24 * (lane >> 4)];
+                        const uint2 v0 = *reinterpret_cast<const uint2 *>(src);
+                        const uint2 v1 = *reinterpret_cast<const uint2 *>(src + 8);
+                        const uint2 v2 = *reinterpret_cast<const uint2 *>(src + 16);
+                        const int64_t atom = ((r / 16) * (Lp / 128) + kbase / 128) * 1536;
+                        *reinterpret_cast<uint4 *>(qd + atom + 16 * lane) = uint4{v0.x, v0.y, v1.x, v1.y};
+                        *reinterpret_cast<uint2 *>(qd + atom + 1024 + 8 * lane) = v2;
+                    }
+                }
+            } else {
+                // 128 blob rows x 96 bytes: six 16-byte chunks per row, consecutive threads along a row
+#pragma unroll
+                for (int rep = 0; rep < 3; ++rep) {
+                    const int ch = (int)threadIdx.x + 256 * rep;
+                    const int r_loc = ch / 6, part = ch % 6;
+                    const int64_t r = rbase + r_loc;
+                    if (r < rows_out) {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(&s_data[dir][r_loc * kLinePitch + 16 * part]);
+                        *reinterpret_cast<uint4 *>(qd + r * (Lp * 3 / 4) + kbase * 3 / 4 + 16 * part) = v;
+                    }
+                }
+            }
+        } else
         // data: 512 slices of 16 bytes (one blob row, one 32-element block each)
 #pragma unroll
         for (int rep = 0; rep < 2; ++rep) {
@@ -573,20 +704,20 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
 
 }  // namespace
 
-template <int LAYOUT, bool DUAL, bool RHT>
+template <int ELEM, int LAYOUT, bool DUAL, bool RHT>
 hipError_t launch_sr(const QuantArgs &a, dim3 grid, hipStream_t stream) {
     const bool rs = a.row.use_sr != 0, cs = DUAL && a.col.use_sr != 0;
-    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, true, RHT>), grid, dim3(256), 0, stream, a);
-    else if (rs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, true, false, RHT>), grid, dim3(256), 0, stream, a);
-    else if (cs) hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, true, RHT>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((quantize_kernel<LAYOUT, DUAL, false, false, RHT>), grid, dim3(256), 0, stream, a);
+    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<ELEM, LAYOUT, DUAL, true, true, RHT>), grid, dim3(256), 0, stream, a);
+    else if (rs) hipLaunchKernelGGL((quantize_kernel<ELEM, LAYOUT, DUAL, true, false, RHT>), grid, dim3(256), 0, stream, a);
+    else if (cs) hipLaunchKernelGGL((quantize_kernel<ELEM, LAYOUT, DUAL, false, true, RHT>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((quantize_kernel<ELEM, LAYOUT, DUAL, false, false, RHT>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int LAYOUT, bool DUAL>
 hipError_t launch_rht(const QuantArgs &a, dim3 grid, hipStream_t stream) {
-    return (a.row.rht || (DUAL && a.col.rht)) ? launch_sr<LAYOUT, DUAL, true>(a, grid, stream)
-                                              : launch_sr<LAYOUT, DUAL, false>(a, grid, stream);
+    return (a.row.rht || (DUAL && a.col.rht)) ? launch_sr<4, LAYOUT, DUAL, true>(a, grid, stream)
+                                              : launch_sr<4, LAYOUT, DUAL, false>(a, grid, stream);
 }
 
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
@@ -596,6 +727,15 @@ hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipS
                     : launch_rht<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
     return dual ? launch_rht<MX_LAYOUT_TILED, true>(a, grid, stream)
                 : launch_rht<MX_LAYOUT_TILED, false>(a, grid, stream);
+}
+
+hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
+    dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
+    if (layout == MX_LAYOUT_CANONICAL)
+        return dual ? launch_sr<6, MX_LAYOUT_CANONICAL, true, false>(a, grid, stream)
+                    : launch_sr<6, MX_LAYOUT_CANONICAL, false, false>(a, grid, stream);
+    return dual ? launch_sr<6, MX_LAYOUT_TILED, true, false>(a, grid, stream)
+                : launch_sr<6, MX_LAYOUT_TILED, false, false>(a, grid, stream);
 }
 
 }  // namespace mx

@@ -181,3 +181,23 @@ def test_fp8_validation_and_sizes(L):
     assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, 0, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
     assert _status(G, 0, 1, 4, 4, 4, A16, A16, A16, A16, 1, 0, A16, 12, 0) == mx.MX_ERR_MISALIGNED
     assert _status(G, 0, 1, 0, 4, 4, A16, A16, A16, A16, 1, 0, A16, 8, 0) == mx.MX_SUCCESS
+
+
+def test_fp6_validation_and_sizes(L):
+    A16 = 1 << 20
+    C, T = mx.MX_LAYOUT_CANONICAL, mx.MX_LAYOUT_TILED
+    assert mx.mx_fp6_blob_bytes(37, 200, C) == (37 * 192, 37 * 8)
+    assert mx.mx_fp6_blob_bytes(37, 200, T) == (48 * 192, 48 * 16)
+    Q = mx.mx_quantize_fp6
+    o = mx.quant_opts()
+    no_device = (mx.MX_ERR_DEVICE_UNSUPPORTED, mx.MX_ERR_HIP)     # valid arguments reach the device check
+    assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, T, A16, A16, A16, A16, 0) in no_device
+    assert _status(Q, A16, 4, 8, 8, 4, o, 3, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, 4, 8, 8, 2, o, 1, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, 4, 8, 8, 2, o, 1, o, T, A16, A16, None, None, 0) in no_device   # col fmt unused
+    assert _status(Q, A16, 4, 8, 8, 2, mx.quant_opts(rht=5), 3, o, T, A16, A16, None, None, 0) == \
+        mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, T, A16 + 8, A16, None, None, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, T, A16, A16, A16, None, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, 5, A16, A16, None, None, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, 0, 8, 8, 2, o, 3, o, T, A16, A16, None, None, 0) == mx.MX_SUCCESS
