@@ -312,6 +312,22 @@ mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx,
                           void *q_col, void *s_col, void *stream);
 
 /*
+ * Block-scaled FP6 x FP6 GEMM with fp32 accumulation on tiled MXFP6 blobs:
+ *   C[i][j] = sum_k A[i][k] * B[j][k],  element = fp6(code) * 2^(scale-127)
+ * with A in fmt_a and B in fmt_b (MX_FP6_E2M3 or MX_FP6_E3M2, mixed allowed).
+ * Arguments, layout (MX_LAYOUT_TILED of the MXFP6 blobs), output and errors
+ * as mx_gemm_a4w4; MX_ERR_UNSUPPORTED also for an unknown format, MX_ERR_HIP
+ * when an operand blob reaches 2 GiB.  The matrix instruction's sum of 64
+ * E3M2 x E3M2 products keeps fewer bits than fp32 (measured on MI355X: error
+ * up to about 2^-14 of the sum of |products|); E2M3 operands sum exactly.
+ */
+mx_status mx_gemm_fp6(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                      int fmt_a, const void *A, const void *A_scale,
+                      int fmt_b, const void *B, const void *B_scale,
+                      mx_layout layout, mx_dtype out_dtype,
+                      void *C, int64_t ldc, void *stream);
+
+/*
  * Device-side layout conversion of one blob (rows, length) between the two
  * layouts, asynchronous on `stream`: the tiled layout is the one this
  * library's GEMM reads, the canonical one the interchange shapes of the page

@@ -35,7 +35,7 @@ MX_FP6_E3M2 = 3
 EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
             "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
             "mx_fp8_blob_bytes", "mx_quantize_fp8_tw", "mx_gemm_f8_tw",
-            "mx_fp6_blob_bytes", "mx_quantize_fp6",
+            "mx_fp6_blob_bytes", "mx_quantize_fp6", "mx_gemm_fp6",
             "mx_status_string", "mx_last_error")
 
 
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.mx_layout_convert_host.argtypes = [i32, i64, i64, vp, vp, vp, vp]
     L.mx_fp6_blob_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     L.mx_quantize_fp6.argtypes = [vp, i64, i64, i64, i32, optp, i32, optp, i32, vp, vp, vp, vp, vp]
+    L.mx_gemm_fp6.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     L.mx_device_supported.argtypes = [i32]
     L.mx_device_supported.restype = i32
@@ -163,6 +164,12 @@ def mx_quantize_fp6(x, M: int, N: int, ldx: int, row_fmt: int, row_opts, col_fmt
                     layout: int, q_row, s_row, q_col=None, s_col=None, stream=None):
     _check(lib().mx_quantize_fp6(_ptr(x), M, N, ldx, row_fmt, _opts(row_opts), col_fmt, _opts(col_opts), layout,
                                  _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+
+
+def mx_gemm_fp6(transA: int, transB: int, M: int, N: int, K: int, fmt_a: int, A, A_scale, fmt_b: int, B, B_scale,
+                layout: int, out_dtype: int, C, ldc: int, stream=None):
+    _check(lib().mx_gemm_fp6(transA, transB, M, N, K, fmt_a, _ptr(A), _ptr(A_scale), fmt_b, _ptr(B), _ptr(B_scale),
+                             layout, out_dtype, _ptr(C), ldc, _stream(stream)))
 
 
 def mx_gemm_a4w4(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B, B_scale,

@@ -237,7 +237,8 @@ namespace {
 
 mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
                       const void *A_scale, const void *B, const void *B_scale, mx_layout layout, mx_dtype out_dtype,
-                      const void *bias, bool want_bias, void *C, int64_t ldc, void *stream) {
+                      const void *bias, bool want_bias, void *C, int64_t ldc, void *stream, int fp6_a = 0,
+                      int fp6_b = 0) {
     if (transA != 0 || transB != 1)
         return fail(MX_ERR_UNSUPPORTED,
                     "transA=%d transB=%d: only transA=0, transB=1 (C = A . B^T, both operands K-contiguous) "
@@ -262,6 +263,12 @@ mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64
     if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
     if (M == 0 || N == 0) return MX_SUCCESS;
     MX_TRY(check_device());
+    if (fp6_a)
+        return check_launch(mx::launch_gemm_fp6(M, N, K, fp6_a, static_cast<const uint8_t *>(A),
+                                                static_cast<const uint8_t *>(A_scale), fp6_b,
+                                                static_cast<const uint8_t *>(B), static_cast<const uint8_t *>(B_scale),
+                                                out_dtype, C, ldc, static_cast<hipStream_t>(stream)),
+                            name);
     return check_launch(mx::launch_gemm(M, N, K, static_cast<const uint8_t *>(A),
                                         static_cast<const uint8_t *>(A_scale), static_cast<const uint8_t *>(B),
                                         static_cast<const uint8_t *>(B_scale),
@@ -284,6 +291,15 @@ mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_
                             mx_dtype out_dtype, const void *bias, void *C, int64_t ldc, void *stream) {
     return gemm_common("mx_gemm_a4w4_bias", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype,
                        bias, true, C, ldc, stream);
+}
+
+mx_status mx_gemm_fp6(int transA, int transB, int64_t M, int64_t N, int64_t K, int fmt_a, const void *A,
+                      const void *A_scale, int fmt_b, const void *B, const void *B_scale, mx_layout layout,
+                      mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+    MX_TRY(check_fp6_fmt(fmt_a, "A"));
+    MX_TRY(check_fp6_fmt(fmt_b, "B"));
+    return gemm_common("mx_gemm_fp6", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype, nullptr,
+                       false, C, ldc, stream, fmt_a, fmt_b);
 }
 
 mx_status mx_fp8_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *bytes) {

@@ -37,6 +37,9 @@ struct QuantArgs {
 // Kernel launchers (quantize.hip, gemm.hip, convert.hip, dequantize.hip).  They assume validated arguments.
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
 hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
+hipError_t launch_gemm_fp6(int64_t M, int64_t N, int64_t K, int fmt_a, const uint8_t *A, const uint8_t *As,
+                           int fmt_b, const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C, int64_t ldc,
+                           hipStream_t stream);
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream);

@@ -1,5 +1,12 @@
 """GPU parity of the MXFP6 path (OCP FP6 E2M3 / E3M2 elements, E8M0 block
-scales): quantizer bytes bit-exact against the oracle in both layouts."""
+scales): quantizer bytes bit-exact against the oracle in both layouts; the
+GEMM elementwise within tau = 2^-12 sum_k |a_ik b_jk| (+ 2^-22 |C|) in fp32
+output and within tau + 1 ulp_bf16(|C| + tau) of bf16(C) in bf16 output.
+Why 2^-12: V_MFMA_SCALE_F32_32X32X64_F8F6F4 sums the 64 products of an
+E3M2 x E3M2 instruction with fewer bits than fp32 (measured on MI355X over
+every code pair and random operands: error up to 2^-14.0 of the sum of
+|products|; E2M3 and mixed operands summed exactly); the bar allows 4x that
+per instruction, summed over the instructions of K."""
 import numpy as np
 import pytest
 
@@ -124,3 +131,90 @@ def test_fp6_specials_and_every_bf16(oracle_mod, fmt):
     log("fp6 specials fmt %d" % fmt)
     check_fp6(oracle_mod, sp, CANON, fmt, fmt)
     check_fp6(oracle_mod, sp, TILED, fmt, fmt, dict(use_sr=True, seed=3), dict(use_sr=True, seed=4, tensor_id=1))
+
+
+def quant_tiled(x, fmt):
+    M, N = x.shape
+    xd, ldx = to_dev_bf16(x)
+    q, sc = fp6_blob(M, N, TILED)
+    mx.mx_quantize_fp6(xd, M, N, ldx, fmt, mx.quant_opts(), 0, None, TILED, q, sc)
+    return q, sc
+
+
+def ulp_bf16(v):
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    return 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+
+
+def run_gemm(oracle_mod, a, fa, b, fb, nsample=None, seed=0, what=""):
+    """C = A . B^T through mx_gemm_fp6 (bf16 and fp32 outputs) against the oracle."""
+    M, K = a.shape
+    N = b.shape[0]
+    qa, sa = quant_tiled(a, fa)
+    qb, sb = quant_tiled(b, fb)
+    ldc = (N + 7) // 8 * 8
+    outs = {}
+    for dt in (mx.MX_BF16, mx.MX_F32):
+        C = torch.full((max(M, 1), ldc), -1, dtype=torch.int16 if dt == mx.MX_BF16 else torch.float32, device="cuda")
+        mx.mx_gemm_fp6(0, 1, M, N, K, fa, qa, sa, fb, qb, sb, TILED, dt, C, ldc)
+        outs[dt] = host(C)[:M, :N]
+    oqa, osa = oracle_mod.quantize_fp6(a, 0, fa)
+    oqb, osb = oracle_mod.quantize_fp6(b, 0, fb)
+    if nsample is None:
+        ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+        ii, jj = ii.ravel(), jj.ravel()
+    else:
+        rng = np.random.default_rng(seed)
+        ii, jj = rng.integers(0, M, nsample), rng.integers(0, N, nsample)
+    ref, sabs = oracle_mod.gemm_fp6_entries(oqa, osa, fa, oqb, osb, fb, M, N, K, ii, jj)
+    tau = 2.0 ** -12 * sabs + 2.0 ** -22 * np.abs(ref)
+    got_b = outs[mx.MX_BF16].view(np.uint16)[ii, jj]
+    refb = oracle_mod.bf16_from_double(ref)
+    gotv = oracle_mod.bf16_to_double(got_b)
+    bound = tau + ulp_bf16(np.abs(ref) + tau)
+    bad = ~(np.abs(gotv - oracle_mod.bf16_to_double(refb)) <= bound)
+    assert not bad.any(), "%s: %d bf16 entries off; first got %r ref %r bound %r" % (
+        what, int(bad.sum()), gotv[bad][:3], ref[bad][:3], bound[bad][:3])
+    got = outs[mx.MX_F32].astype(np.float64)[ii, jj]
+    err = np.abs(got - ref)
+    bad = ~(err <= tau)
+    assert not bad.any(), "%s: %d fp32 entries beyond tau, first got %r ref %r tau %r" % (
+        what, int(bad.sum()), got[bad][:3], ref[bad][:3], tau[bad][:3])
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    log("%s: %d/%d bf16 exact, fp32 max err/tau %.3g, rel %.3g" % (
+        what, int((got_b == refb).sum()), ii.size, float((err / np.maximum(tau, 1e-300)).max()), rel))
+
+
+@pytest.mark.parametrize("fa,fb", [(E2M3, E2M3), (E3M2, E2M3), (E2M3, E3M2), (E3M2, E3M2)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (100, 70, 300), (300, 257, 1000), (512, 513, 1664)])
+def test_fp6_gemm(oracle_mod, M, N, K, fa, fb):
+    """Several tiles with ragged edges; K from 1 step to a 12-step body plus a tail."""
+    _require_gpu()
+    log("fp6 gemm %dx%dx%d fmt %d x %d" % (M, N, K, fa, fb))
+    a = synth.random_bf16(M * 7 + K, (M, K), std=1.0)
+    b = synth.random_bf16(N * 11 + K, (N, K), std=0.02)
+    run_gemm(oracle_mod, a, fa, b, fb, what="fp6 %dx%dx%d %d/%d" % (M, N, K, fa, fb))
+
+
+def test_fp6_gemm_k_zero():
+    _require_gpu()
+    C = torch.full((5, 16), 7.0, dtype=torch.float32, device="cuda")
+    mx.mx_gemm_fp6(0, 1, 5, 9, 0, E2M3, None, None, E3M2, None, None, TILED, mx.MX_F32, C, 16)
+    c = host(C)
+    assert (c[:, :9] == 0).all() and (c[:, 9:] == 7.0).all()
+
+
+def test_fp6_fc2_step_sampled(oracle_mod):
+    """The fc2 training step's three products on MXFP6 operands at full size
+    (18432 tokens, 12288 -> 3072): forward X . W^T in E2M3, dgrad dY . W and
+    wgrad dY^T . X with the gradient in E3M2; sampled entries."""
+    _require_gpu()
+    d = synth.fc2()
+    X, W, dY = d["X"], d["W"], d["dY"]
+    log("fp6 fc2 fwd")
+    run_gemm(oracle_mod, X, E2M3, W, E2M3, nsample=2048, seed=1, what="fp6 fwd")
+    log("fp6 fc2 dgrad")
+    run_gemm(oracle_mod, dY, E3M2, np.ascontiguousarray(W.T), E2M3, nsample=2048, seed=2, what="fp6 dgrad")
+    log("fp6 fc2 wgrad")
+    run_gemm(oracle_mod, np.ascontiguousarray(dY.T), E3M2, np.ascontiguousarray(X.T), E2M3, nsample=2048, seed=3,
+             what="fp6 wgrad")
