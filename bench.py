@@ -271,6 +271,34 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
     out["fp8_gemm_wgrad"] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
                              "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / 5000.0, 4),
                              "what": "hybrid backward wgrad dY^T . X, tensorwise E5M2"}
+    # MXFP6: X and W in E2M3 (both blobs), dY in E3M2 with stochastic rounding; the step's three GEMMs
+    E2M3, E3M2 = mx.MX_FP6_E2M3, mx.MX_FP6_E3M2
+
+    def f6(r, l):
+        d, s_ = mx.mx_fp6_blob_bytes(r, l, T)
+        return (torch.empty((d,), dtype=torch.uint8, device=dev), torch.empty((s_,), dtype=torch.uint8, device=dev))
+    x6r, x6c, w6r, w6c, g6r, g6c = f6(tokens, din), f6(din, tokens), f6(dout, din), f6(din, dout), \
+        f6(tokens, dout), f6(dout, tokens)
+    x_bytes = 2.0 * tokens * din + sum(t.numel() for t in x6r + x6c)
+    ms = timed(lambda: mx.mx_quantize_fp6(X, tokens, din, din, E2M3, plain, E2M3, plain, T, *x6r, *x6c, stream))
+    out["fp6_quant_X"] = {"ms": round(ms, 5), "GB/s": round(x_bytes / (ms * 1e-3) / 1e9, 1),
+                          "what": "X dual MXFP6 E2M3 (row and column blobs)"}
+    g_bytes = 2.0 * tokens * dout + sum(t.numel() for t in g6r + g6c)
+    ms = timed(lambda: mx.mx_quantize_fp6(dY, tokens, dout, dout, E3M2, sr, E3M2, sr, T, *g6r, *g6c, stream))
+    out["fp6_quant_dY_sr"] = {"ms": round(ms, 5), "GB/s": round(g_bytes / (ms * 1e-3) / 1e9, 1),
+                              "what": "dY dual MXFP6 E3M2, stochastic rounding"}
+    mx.mx_quantize_fp6(W, dout, din, din, E2M3, mx.quant_opts(use_2d_block=True), E2M3,
+                       mx.quant_opts(use_2d_block=True), T, *w6r, *w6c, stream)
+    Y6 = torch.empty((tokens, dout), dtype=torch.int16, device=dev)
+    for name, args6, what in [
+            ("fp6_gemm_fwd", (tokens, dout, din, E2M3, *x6r, E2M3, *w6r, Y6, dout), "fwd X . W^T, E2M3 x E2M3"),
+            ("fp6_gemm_dgrad", (tokens, din, dout, E3M2, *g6r, E2M3, *w6c, dXf, din), "dgrad dY . W, E3M2 x E2M3"),
+            ("fp6_gemm_wgrad", (dout, din, tokens, E3M2, *g6c, E2M3, *x6c, dWf, din), "wgrad dY^T . X, E3M2 x E2M3")]:
+        M6, N6, K6, fa6, qa6, sa6, fb6, qb6, sb6, C6, ldc6 = args6
+        ms = timed(lambda: mx.mx_gemm_fp6(0, 1, M6, N6, K6, fa6, qa6, sa6, fb6, qb6, sb6, T, mx.MX_BF16, C6, ldc6,
+                                          stream))
+        out[name] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "frac_fp6_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4), "what": what}
     d_bytes, s_bytes = mx.mx_blob_bytes(tokens, din, mx.MX_LAYOUT_CANONICAL)
     cq = torch.empty((d_bytes,), dtype=torch.uint8, device=dev)
     cs = torch.empty((s_bytes,), dtype=torch.uint8, device=dev)

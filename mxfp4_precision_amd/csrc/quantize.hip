@@ -29,7 +29,8 @@
 // E2M1 normal numbers (1 <= v < 8) coincide with fp32 normal numbers and the
 // E2M1 subnormal step (0.5) with the fp32 subnormal range, so the code is
 // the truncation u >> 22 plus 1 iff the element's random byte is below the
-// next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)).
+// next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)); the
+// kernel gets that sum as one carry (see code_sr).
 
 // Random Hadamard transform (when a direction's rht seed is non-zero): the
 // page's dual-quantize op has an "rht" switch for the column-wise blobs of
@@ -70,9 +71,12 @@ __device__ __forceinline__ uint32_t scaled_u(uint32_t x16, uint32_t c) {
     return __float_as_uint(__builtin_ldexpf(xf, 1 - (int)c));
 }
 
+// u clamped at code 7 (6.0), plus (255 - byte) << 14: the carry into bit 22
+// happens iff the byte is below the 8 bits u >> 14 & 0xFF.
 __device__ __forceinline__ uint32_t code_sr(uint32_t u, uint32_t rbyte) {
-    uint32_t r = (u >> 22) + (rbyte < ((u >> 14) & 0xFFu) ? 1u : 0u);
-    return r < 7u ? r : 7u;
+    const uint32_t top = 7u << 22;
+    u = u < top ? u : top;
+    return (u + ((255u - rbyte) << 14)) >> 22;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
