@@ -22,8 +22,10 @@
 // stage is the one step k finished reading at the barrier between the
 // halves).  The stage index runs mod 3 and the position in the 4-step scale
 // group mod 4, so the k-loop body is 12 steps.  DMA per wave and step: four
-// 1 KB low parts and two 1 KB units each holding the high parts of two
-// atoms (lanes 0..31 and 32..63 read from different atoms).
+// 1 KB low parts and two 1 KB units each holding the high parts of the two
+// atoms of one 32-row operand tile, interleaved in 16-byte chunks (chunk c of
+// atom 2h+a at position 2c+a), so that the 8-byte reads of a half-wave (16
+// rows of each atom) fall on 64 different banks.
 
 #include "mx_internal.h"
 
@@ -119,8 +121,9 @@ __device__ __forceinline__ v6u read_op(const uint8_t *lo, const uint8_t *hi) {
 
 // DMA instruction V of k-step k into stage S: V < kLoLoads copies the low
 // kilobyte of atom kWaves*V + wave; V < kLoads copies the high parts of atoms
-// 2h, 2h+1 (h = kWaves*(V - kLoLoads) + wave); otherwise (only when k opens
-// a k-group) scale atom kWaves*(V - kLoads) + wave.
+// 2h, 2h+1 (h = kWaves*(V - kLoLoads) + wave; lane p fetches chunk p/2 of
+// atom 2h + p%2); otherwise (only when k opens a k-group) scale atom
+// kWaves*(V - kLoads) + wave.
 template <int S, int V>
 __device__ __forceinline__ void dma_op(const Ctx &c, int64_t k) {
     if constexpr (V < kLoLoads) {
@@ -173,11 +176,14 @@ __device__ __forceinline__ void mfma_tile(v16f &acc, const v6u &xb, const v6u &x
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc, FB, FA, G, (int)sbv, G, (int)sav);
 }
 
+// Per-lane LDS byte offsets of this wave's first A and B operand tiles
+// (half 0): the wave-dependent part is folded in once, so that every read
+// adds only a compile-time constant (tile, half) that fits the instruction's
+// offset field, and the stages need one base register per part and operand.
 struct Lds {
-    int frag_off;   // this lane's low 16 bytes within a 32-row pair of atoms (half 0)
-    int frag_hi;    // ... its high 8 bytes within the pair's high parts
-    int sc_off;
-    int a_atom0, b_atom0;
+    int lo_a, lo_b;   // low 16 bytes in a stage's low region
+    int hi_a, hi_b;   // high 8 bytes in a stage's interleaved high-part units
+    int sc_a, sc_b;   // scale dword in the scale atoms
 };
 
 // Slot T of half H of the k-step with stage S and k-group position G: MFMA
@@ -194,17 +200,14 @@ __device__ __forceinline__ void slot(const Ctx &c, int64_t k, v16f (&acc)[kMB][k
     if constexpr (T < kMA + kMB) {
         constexpr int RS = H == 0 ? S : (S + 1) % kStages;
         constexpr int RH = H == 0 ? 1 : 0;
-        const uint8_t *lo = stage_buf<RS>() + l.frag_off + RH * 512;
-        const uint8_t *hi = stage_buf<RS>() + kHiBase + l.frag_hi + RH * 256;
+        const uint8_t *st = stage_buf<RS>();
         if constexpr (T == 0 || T > kMA) {
             constexpr int bi = T == 0 ? 0 : T - kMA;
-            const int at = l.b_atom0 + 2 * bi;
-            const v6u v = read_op(lo + at * 1024, hi + at * 512);
+            const v6u v = read_op(st + l.lo_b + (2 * bi * 1024 + RH * 512), st + kHiBase + l.hi_b + (bi * 1024 + RH * 512));
             if constexpr (H == 0) r.b1[bi] = v; else r.b0[bi] = v;
         } else {
             constexpr int ai = T - 1;
-            const int at = l.a_atom0 + 2 * ai;
-            const v6u v = read_op(lo + at * 1024, hi + at * 512);
+            const v6u v = read_op(st + l.lo_a + (2 * ai * 1024 + RH * 512), st + kHiBase + l.hi_a + (ai * 1024 + RH * 512));
             if constexpr (H == 0) r.a1[ai] = v; else r.a0[ai] = v;
         }
     }
@@ -216,11 +219,10 @@ __device__ __forceinline__ void slot(const Ctx &c, int64_t k, v16f (&acc)[kMB][k
     if constexpr ((H == 1 && G == 3) || (H == 0 && G == 0)) {
         if constexpr (T >= kScStart) {
             constexpr int t = T - kScStart, hh = 1 - H;   // the half whose MFMAs are not running
-            if (t < kMA)
-                r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            if constexpr (t < kMA)
+                r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + l.sc_a + (2 * t * 256 + hh * 128));
             else
-                r.sb[t - kMA][hh] =
-                    *reinterpret_cast<const uint32_t *>(f6_scale + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
+                r.sb[t - kMA][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + l.sc_b + (2 * (t - kMA) * 256 + hh * 128));
         }
     }
 
@@ -387,8 +389,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_kernel(int64_t M, int64_t N
 #pragma unroll
     for (int r = 0; r < kHiLoads; ++r) {
         const int h = kWaves * r + wave;
-        const int a = 2 * h + (lane >> 5);
-        c.hi_off[r] = (uint32_t)(group_of(a) * c.ksteps * kAtomBytes) + 1024u + (uint32_t)((lane & 31) * 16);
+        const int a = 2 * h + (lane & 1);
+        c.hi_off[r] = (uint32_t)(group_of(a) * c.ksteps * kAtomBytes) + 1024u + (uint32_t)((lane >> 1) * 16);
     }
 #pragma unroll
     for (int r = 0; r < kScaleLoads; ++r) c.sc_row[r] = (int)(group_of(kWaves * r + wave) * c.kgroups * 256);
@@ -408,11 +410,21 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_kernel(int64_t M, int64_t N
 
     const int lrow = lane & 31, lhi = lane >> 5;
     Lds l;
-    l.frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;
-    l.frag_hi = ((lrow >> 4) * 512) + ((lrow & 15) + 16 * lhi) * 8;
-    l.sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;
-    l.a_atom0 = wm * kTA;
-    l.b_atom0 = kGA + wn * kTB;
+    {
+        // lane L of a 32-row tile: row L%32 = atom (L%32)/16, slice s = L%16 + 16*(L/32) (half 0)
+        const int sl = (lrow & 15) + 16 * lhi;
+        const int frag_off = ((lrow >> 4) * 1024) + sl * 16;
+        // high parts: slice s of atom 2t + a at chunk position 2(s/2) + a, 8 bytes in per s%2
+        const int frag_hi = 32 * (sl >> 1) + 16 * (lrow >> 4) + 8 * (sl & 1);
+        const int sc_off = ((lrow >> 4) * 256) + sl * 4;
+        const int a0 = wm * kTA, b0 = kGA + wn * kTB;     // first atoms of the wave's A and B tiles
+        l.lo_a = frag_off + a0 * 1024;
+        l.lo_b = frag_off + b0 * 1024;
+        l.hi_a = frag_hi + (a0 / 2) * 1024;
+        l.hi_b = frag_hi + (b0 / 2) * 1024;
+        l.sc_a = sc_off + a0 * 256;
+        l.sc_b = sc_off + b0 * 256;
+    }
 
     Regs r;
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + part_ops(2)) : "memory");
@@ -420,20 +432,18 @@ __global__ __launch_bounds__(kThreads) void gemm_fp6_kernel(int64_t M, int64_t N
     for (int t = 0; t < kMA; ++t)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + l.sc_a + t * 512 + hh * 128);
 #pragma unroll
     for (int t = 0; t < kMB; ++t)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(f6_scale + l.sc_b + t * 512 + hh * 128);
 #pragma unroll
     for (int t = 0; t < kMA; ++t)
-        r.a0[t] = read_op(f6_stage0 + (l.a_atom0 + 2 * t) * 1024 + l.frag_off,
-                          f6_stage0 + kHiBase + (l.a_atom0 + 2 * t) * 512 + l.frag_hi);
+        r.a0[t] = read_op(f6_stage0 + l.lo_a + t * 2048, f6_stage0 + kHiBase + l.hi_a + t * 1024);
 #pragma unroll
     for (int t = 0; t < kMB; ++t)
-        r.b0[t] = read_op(f6_stage0 + (l.b_atom0 + 2 * t) * 1024 + l.frag_off,
-                          f6_stage0 + kHiBase + (l.b_atom0 + 2 * t) * 512 + l.frag_hi);
+        r.b0[t] = read_op(f6_stage0 + l.lo_b + t * 2048, f6_stage0 + kHiBase + l.hi_b + t * 1024);
 
     // 12 steps per iteration: stage k % 3, k-group position k % 4.  Steps past
     // K_pad load zeros (out-of-range DMA) and add nothing.
