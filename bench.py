@@ -42,8 +42,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks settle over the first ~20 ms of back-to-back steps (the first
+    # timed steps after 3 warmups ran ~7% slower than the steady state)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--tokens", type=int, default=18432)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true",
