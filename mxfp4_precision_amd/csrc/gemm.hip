@@ -35,6 +35,7 @@
 // each XCD (8 on MI355X, dispatched round-robin) works on a compact band of
 // output tiles, keeping the A rows and B columns it shares within its own L2.
 
+#include <atomic>
 #include <type_traits>
 
 #include "mx_internal.h"
@@ -639,6 +640,19 @@ __global__ void fill_kernel(T *C, int64_t M, int64_t N, int64_t ldc, const uint1
     else C[(idx / N) * ldc + j] = __uint_as_float((uint32_t)b << 16);
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) n = 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
@@ -660,11 +674,21 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
     if (cdiv(M, 16) * K_pad / 2 >= (int64_t(1) << 31) || cdiv(N, 16) * K_pad / 2 >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
     const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-    dim3 grid((unsigned)(tiles_m * tiles_n));
+    const int tiles = tiles_m * tiles_n;
+    // Whole rounds of 256x256 tiles here; a last round that would fill at most
+    // half of the CUs goes to the tail kernel as 128x128 tiles instead.
+    const int cus = cu_count();
+    const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
     auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_kernel<true, true> : gemm_a4w4_kernel<true, false>)
                                        : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, As, B, Bs, bias,
-                       C, ldc);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles - tail)), dim3(kThreads), 0, stream, M, N, K_pad, tiles_m,
+                       tiles_n, A, As, B, Bs, bias, C, ldc);
+    if (tail) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_gemm_tail(M, N, K_pad, tiles_m, tiles_n, tiles - tail, tail, A, As, B, Bs, bias, out_dtype, C,
+                                ldc, stream);
+    }
     return hipGetLastError();
 }
 

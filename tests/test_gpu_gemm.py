@@ -231,3 +231,38 @@ def test_bias_k_zero_writes_bias(oracle_mod):
     cf = host(gemm_bias(dummy, dummy, dummy, dummy, M, N, 0, bias_d, mx.MX_F32))[:M, :N]
     assert (cb == bias[None, :]).all()
     assert (cf.astype(np.float64) == oracle_mod.bf16_to_double(bias)[None, :]).all()
+
+
+def test_tail_tiles_bias_every_entry_of_tail_rows(oracle_mod):
+    """Tile count past one round on 256 CUs with a small last round: the last
+    round runs as 128x128 tiles (4597x4349 -> 18x17 = 306 tiles of 256x256; the
+    last 50 of the tile order, which hold the ragged last row and column of
+    tiles, become 200 tiles of 128x128).  With a bias, in bf16 and fp32: every
+    entry of rows in the main and the tail region, against the oracle."""
+    _require_gpu()
+    M, N, K = 4597, 4349, 384
+    a = synth.random_bf16(91, (M, K), std=1.0)
+    b = synth.random_bf16(92, (N, K), std=0.05)
+    bias = synth.random_bf16(93, (N,), std=2.0)
+    log("tail tiles with bias %dx%dx%d" % (M, N, K))
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
+    qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
+    bias_d = torch.zeros(((N + 7) // 8 * 8,), dtype=torch.int16)
+    bias_d[:N] = torch.from_numpy(bias.view(np.int16))
+    bias_d = bias_d.cuda()
+    cb = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_BF16))[:M, :N].view(np.uint16)
+    cf = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_F32))[:M, :N].astype(np.float64)
+    oqa, osa = oracle_mod.quantize(a, 0)
+    oqb, osb = oracle_mod.quantize(b, 0)
+    rows = np.array([0, 127, 128, 2047, 2048 + 77, 4095, 4096, 4096 + 128, M - 2, M - 1])
+    ii = np.repeat(rows, N)
+    jj = np.tile(np.arange(N), rows.size)
+    ref = oracle_mod.gemm_bias_entries(oqa, osa, oqb, osb, M, N, K, bias, ii, jj)
+    tau = tau_bound(oracle_mod, oqa, osa, oqb, osb, M, N, K, ii, jj)
+    exact, _ = check_gemm_bf16(cb[ii, jj], ref, tau, oracle_mod, "tail-bias")
+    rel = np.linalg.norm(cf[ii, jj] - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-5, rel
+    assert (cb[:, N:] if cb.shape[1] > N else cb[:0]).size == 0
+    log("tail-bias: %d/%d bf16 exact, fp32 rel %.3g" % (exact, ii.size, rel))
