@@ -273,6 +273,22 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
     out["fp8_gemm_wgrad"] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
                              "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / 5000.0, 4),
                              "what": "hybrid backward wgrad dY^T . X, tensorwise E5M2"}
+    # quantizer prologue: dual quantize of bf16(dY * g) with the product formed in the staging read,
+    # against the unfused pair (torch's bf16 multiply writing the product, then the quantizer)
+    gfac = torch.empty_like(dY)
+    gfac.copy_((torch.rand(dY.shape, device=dev) + 0.5).to(torch.bfloat16).view(torch.int16))
+    prod = torch.empty_like(dY)
+    ms_f = timed(lambda: mx.mx_quantize_dual_mul(dY, gfac, tokens, dout, dout, dout, sr, sr, T, gr, grs, gc, gcs,
+                                                 stream))
+
+    def unfused():
+        torch.mul(dY.view(torch.bfloat16), gfac.view(torch.bfloat16), out=prod.view(torch.bfloat16))
+        mx.mx_quantize_dual(prod, tokens, dout, dout, sr, sr, T, gr, grs, gc, gcs, stream)
+    ms_u = timed(unfused)
+    out["quant_dY_mul_prologue"] = {"ms": round(ms_f, 5), "unfused_ms": round(ms_u, 5),
+                                    "GB/s": round((qb["quant_dY"] + 2.0 * tokens * dout) / (ms_f * 1e-3) / 1e9, 1),
+                                    "what": "dY dual SR of bf16(dY * g), product in the staging read, vs torch "
+                                            "multiply + quantize"}
     # MXFP6: X and W in E2M3 (both blobs), dY in E3M2 with stochastic rounding; the step's three GEMMs
     E2M3, E3M2 = mx.MX_FP6_E2M3, mx.MX_FP6_E3M2
 

@@ -167,6 +167,26 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx,
                            void *q_col, void *s_col, void *stream);
 
 /*
+ * Quantizer with a multiply prologue: quantizes y = bf16(x * g) (elementwise,
+ * each product formed in fp32 and rounded to bf16 nearest-even) exactly as
+ * mx_quantize_dual / mx_quantize_rowwise would quantize a stored y, but y is
+ * formed in the staging read and never written to memory.  It fuses the
+ * last elementwise step of a producer's backward into the packer, the
+ * pattern of the page "Primus PR 1107" (its QKV packer computes the
+ * gradient during its staging read instead of reading it back from HBM);
+ * that page's norm+RoPE backward itself is not part of this library, g
+ * carries any elementwise factor (an activation derivative, a mask, a gate).
+ * x: M x N bf16, stride ldx; g: M x N bf16, stride ldg.  q_col = s_col =
+ * NULL: row-wise blob only.  Options as mx_quantize_dual except rht
+ * (MX_ERR_UNSUPPORTED).  Same alignment rules for g as for x.
+ * Errors: INVALID_ARGUMENT, MISALIGNED, UNSUPPORTED, DEVICE_UNSUPPORTED, HIP.
+ */
+mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t N, int64_t ldx, int64_t ldg,
+                               const mx_quant_opts *row_opts, const mx_quant_opts *col_opts,
+                               mx_layout layout, void *q_row, void *s_row,
+                               void *q_col, void *s_col, void *stream);
+
+/*
  * Block-scaled FP4 x FP4 GEMM with fp32 accumulation:
  *   C[i][j] = sum_k A[i][k] * B[j][k]   (i < M, j < N, k over the padded K)
  * where A (M rows) and B (N rows) are blobs quantized along K and each

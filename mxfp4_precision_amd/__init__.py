@@ -35,7 +35,7 @@ MX_FP6_E3M2 = 3
 EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
             "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
             "mx_fp8_blob_bytes", "mx_quantize_fp8_tw", "mx_gemm_f8_tw",
-            "mx_fp6_blob_bytes", "mx_quantize_fp6", "mx_gemm_fp6",
+            "mx_fp6_blob_bytes", "mx_quantize_fp6", "mx_gemm_fp6", "mx_quantize_dual_mul",
             "mx_status_string", "mx_last_error")
 
 
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.mx_layout_convert_host.argtypes = [i32, i64, i64, vp, vp, vp, vp]
     L.mx_fp6_blob_bytes.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
     L.mx_quantize_fp6.argtypes = [vp, i64, i64, i64, i32, optp, i32, optp, i32, vp, vp, vp, vp, vp]
+    L.mx_quantize_dual_mul.argtypes = [vp, vp, i64, i64, i64, i64, optp, optp, i32, vp, vp, vp, vp, vp]
     L.mx_gemm_fp6.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     L.mx_device_supported.argtypes = [i32]
@@ -152,6 +153,12 @@ def mx_quantize_dual(x, M: int, N: int, ldx: int, row_opts, col_opts, layout: in
                      q_row, s_row, q_col, s_col, stream=None):
     _check(lib().mx_quantize_dual(_ptr(x), M, N, ldx, _opts(row_opts), _opts(col_opts), layout,
                                   _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+
+
+def mx_quantize_dual_mul(x, g, M: int, N: int, ldx: int, ldg: int, row_opts, col_opts, layout: int,
+                         q_row, s_row, q_col=None, s_col=None, stream=None):
+    _check(lib().mx_quantize_dual_mul(_ptr(x), _ptr(g), M, N, ldx, ldg, _opts(row_opts), _opts(col_opts), layout,
+                                      _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
 
 
 def mx_fp6_blob_bytes(rows: int, length: int, layout: int) -> Tuple[int, int]:

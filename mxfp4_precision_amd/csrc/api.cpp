@@ -174,6 +174,43 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, con
                         "mx_quantize_dual");
 }
 
+mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t N, int64_t ldx, int64_t ldg,
+                               const mx_quant_opts *row_opts, const mx_quant_opts *col_opts, mx_layout layout,
+                               void *q_row, void *s_row, void *q_col, void *s_col, void *stream) {
+    const bool dual = q_col || s_col;
+    MX_TRY(validate_x(x, M, N, ldx));
+    if (!g) return fail(MX_ERR_INVALID_ARGUMENT, "g is NULL");
+    if (ldg < N || ldg < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldg=%lld must be >= max(N, 1)", (long long)ldg);
+    if (!aligned16(g)) return fail(MX_ERR_MISALIGNED, "g must be 16-byte aligned");
+    if (ldg % 8) return fail(MX_ERR_MISALIGNED, "ldg=%lld must be a multiple of 8", (long long)ldg);
+    MX_TRY(check_opts(row_opts, "row"));
+    if (row_opts && row_opts->rht) return fail(MX_ERR_UNSUPPORTED, "row options: rht is not combined with the prologue");
+    if (dual) {
+        MX_TRY(check_opts(col_opts, "col"));
+        if (col_opts && col_opts->rht)
+            return fail(MX_ERR_UNSUPPORTED, "col options: rht is not combined with the prologue");
+    }
+    MX_TRY(check_layout(layout));
+    MX_TRY(validate_out(q_row, s_row, "row-wise"));
+    if (dual) MX_TRY(validate_out(q_col, s_col, "column-wise"));
+    if (M == 0 || N == 0) return MX_SUCCESS;
+    MX_TRY(check_device());
+    mx::QuantArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.g = static_cast<const uint16_t *>(g);
+    a.M = M; a.N = N; a.ldx = ldx; a.ldg = ldg;
+    a.M_pad = mx::padded(M); a.N_pad = mx::padded(N);
+    a.row = to_dir(row_opts);
+    if (dual) a.col = to_dir(col_opts);
+    a.sr_pairs = (dual && N % 16 == 0 && a.row.index_base % 16 == 0 && a.col.index_base % 16 == 0) ? 1u : 0u;
+    a.q_row = static_cast<uint8_t *>(q_row);
+    a.s_row = static_cast<uint8_t *>(s_row);
+    a.q_col = static_cast<uint8_t *>(q_col);
+    a.s_col = static_cast<uint8_t *>(s_col);
+    return check_launch(mx::launch_quantize_mul(a, dual, layout, static_cast<hipStream_t>(stream)),
+                        "mx_quantize_dual_mul");
+}
+
 mx_status mx_fp6_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *data_bytes,
                             size_t *scale_bytes) {
     if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");

@@ -28,6 +28,8 @@ struct DirOpts {
 struct QuantArgs {
     const uint16_t *x;
     int64_t M, N, ldx;
+    const uint16_t *g;          // second factor of the multiply prologue (same shape), or NULL
+    int64_t ldg;
     int64_t M_pad, N_pad;       // padded quantized axes (col blob, row blob)
     DirOpts row, col;
     uint32_t sr_pairs;          // 1: N and both index bases are multiples of 16
@@ -37,6 +39,7 @@ struct QuantArgs {
 // Kernel launchers (quantize.hip, gemm.hip, convert.hip, dequantize.hip).  They assume validated arguments.
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
 hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
+hipError_t launch_quantize_mul(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);
 hipError_t launch_gemm_fp6(int64_t M, int64_t N, int64_t K, int fmt_a, const uint8_t *A, const uint8_t *As,
                            int fmt_b, const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C, int64_t ldc,
                            hipStream_t stream);

@@ -80,6 +80,7 @@ __device__ __forceinline__ uint32_t code_sr(uint32_t u, uint32_t rbyte) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // 2^(c-127) as fp32 (c = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float scale_f32(uint32_t c) {
@@ -337,9 +338,22 @@ __device__ __forceinline__ void lds_put6(uint8_t *base, int o, uint32_t lo, uint
 // ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
 // options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
 // 64 bytes (FP4) or 96 bytes (FP6), padded by 16 bytes against bank conflicts.
-template <int ELEM, int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
+// bf16 pair x times bf16 pair y, each product in fp32 (IEEE, denormals kept)
+// and rounded to bf16 nearest-even: what a producer that multiplies in fp32
+// and stores bf16 would have written.
+__device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
+#pragma clang fp contract(off)
+    const f32x2_t p = {__uint_as_float(x << 16) * __uint_as_float(y << 16),
+                       __uint_as_float(x & 0xFFFF0000u) * __uint_as_float(y & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+}
+
+// MUL: the quantized tensor is bf16(x * g) elementwise (the prologue of
+// mx_quantize_dual_mul), formed in the staging read.
+template <int ELEM, int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT, bool MUL = false>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     static_assert(ELEM == 4 || (ELEM == 6 && !RHT), "element size");
+    static_assert(!MUL || (ELEM == 4 && !RHT), "prologue");
     constexpr int kLinePitch = ELEM == 4 ? 80 : 112;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -366,6 +380,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
                 uint32_t hi = (i < M && j0 + 2 * w + 1 < N) ? p[2 * w + 1] : 0u;
                 d[t][w] = lo | (hi << 16);
             }
+        }
+    }
+    if constexpr (MUL) {
+        // the second factor, same shape and bounds (positions past M or N read as 0)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t i = row0 + 8 * q + t;
+            const uint16_t *p = a.g + i * a.ldg + j0;
+            uint32_t e[4];
+            if (i < M && j0 + 8 <= N) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(p);
+                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t lo = (i < M && j0 + 2 * w < N) ? p[2 * w] : 0u;
+                    const uint32_t hi = (i < M && j0 + 2 * w + 1 < N) ? p[2 * w + 1] : 0u;
+                    e[w] = lo | (hi << 16);
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) d[t][w] = mul_bf16_pair(d[t][w], e[w]);
         }
     }
 
@@ -733,6 +769,24 @@ hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipS
                     : launch_rht<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
     return dual ? launch_rht<MX_LAYOUT_TILED, true>(a, grid, stream)
                 : launch_rht<MX_LAYOUT_TILED, false>(a, grid, stream);
+}
+
+template <int LAYOUT, bool DUAL>
+hipError_t launch_mul(const QuantArgs &a, dim3 grid, hipStream_t stream) {
+    const bool rs = a.row.use_sr != 0, cs = DUAL && a.col.use_sr != 0;
+    if (rs && cs) hipLaunchKernelGGL((quantize_kernel<4, LAYOUT, DUAL, true, true, false, true>), grid, dim3(256), 0, stream, a);
+    else if (rs) hipLaunchKernelGGL((quantize_kernel<4, LAYOUT, DUAL, true, false, false, true>), grid, dim3(256), 0, stream, a);
+    else if (cs) hipLaunchKernelGGL((quantize_kernel<4, LAYOUT, DUAL, false, true, false, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((quantize_kernel<4, LAYOUT, DUAL, false, false, false, true>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_mul(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
+    dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
+    if (layout == MX_LAYOUT_CANONICAL)
+        return dual ? launch_mul<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
+                    : launch_mul<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
+    return dual ? launch_mul<MX_LAYOUT_TILED, true>(a, grid, stream) : launch_mul<MX_LAYOUT_TILED, false>(a, grid, stream);
 }
 
 hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {

@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_gemm_fp6_entries.restype = _int
         L.oracle_fp6_to_tiled.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
         L.oracle_fp6_to_tiled.restype = _int
+        L.oracle_bf16_mul_array.argtypes = [_vp, _vp, _i64, _vp]
+        L.oracle_bf16_mul_array.restype = None
         _lib = L
     return _lib
 
@@ -364,3 +366,15 @@ def fp6_to_tiled(q: np.ndarray, s: np.ndarray, rows: int, length: int):
     s = np.ascontiguousarray(s, dtype=np.uint8)
     lib().oracle_fp6_to_tiled(_ptr(q), _ptr(s), rows, length, _ptr(qt), _ptr(st))
     return qt, st
+
+
+# ------------------------------------------------------- multiply prologue
+def bf16_mul(x: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """bf16(fp32(x * g)) elementwise on bf16 bit arrays of one shape: the tensor the
+    multiply prologue quantizes."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    g = np.ascontiguousarray(g, dtype=np.uint16)
+    assert x.shape == g.shape
+    out = np.empty_like(x)
+    lib().oracle_bf16_mul_array(_ptr(x), _ptr(g), x.size, _ptr(out))
+    return out

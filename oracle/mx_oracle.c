@@ -71,6 +71,8 @@ static double bf16_value(uint16_t b)
 
 static int bf16_is_finite(uint16_t b) { return ((b >> 7) & 0xFF) != 0xFF; }
 
+uint16_t oracle_bf16_from_double(double d);
+
 /* [OCP-MX] sec. 5.3.3: FP4 E2M1 magnitudes of the 3-bit codes 0..7. */
 static const double E2M1_MAGNITUDE[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
 
@@ -887,4 +889,21 @@ int oracle_fp6_to_tiled(const uint8_t *q, const uint8_t *s, int64_t R, int64_t L
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------ multiply prologue */
+/*
+ * The element the multiply prologue quantizes (reading of the page "Primus
+ * PR 1107": the packer forms the gradient in its staging read instead of
+ * reading back what the producer stored; the producer multiplies in fp32 and
+ * stores bf16): y = bf16(fp32(x * g)) -- the exact product of the two bf16
+ * values rounded to fp32 nearest-even (IEEE, subnormals kept), then to bf16
+ * nearest-even (oracle_bf16_from_double).
+ */
+void oracle_bf16_mul_array(const uint16_t *x, const uint16_t *g, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        float p = (float)(bf16_value(x[i]) * bf16_value(g[i]));
+        out[i] = oracle_bf16_from_double((double)p);
+    }
 }

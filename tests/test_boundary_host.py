@@ -201,3 +201,20 @@ def test_fp6_validation_and_sizes(L):
     assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, T, A16, A16, A16, None, 0) == mx.MX_ERR_INVALID_ARGUMENT
     assert _status(Q, A16, 4, 8, 8, 2, o, 3, o, 5, A16, A16, None, None, 0) == mx.MX_ERR_UNSUPPORTED
     assert _status(Q, A16, 0, 8, 8, 2, o, 3, o, T, A16, A16, None, None, 0) == mx.MX_SUCCESS
+
+
+def test_multiply_prologue_validation(L):
+    A16 = 1 << 20
+    T = mx.MX_LAYOUT_TILED
+    Q = mx.mx_quantize_dual_mul
+    o = mx.quant_opts()
+    no_device = (mx.MX_ERR_DEVICE_UNSUPPORTED, mx.MX_ERR_HIP)
+    assert _status(Q, A16, A16, 4, 8, 8, 8, o, o, T, A16, A16, A16, A16, 0) in no_device
+    assert _status(Q, A16, 0, 4, 8, 8, 8, o, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(Q, A16, A16 + 2, 4, 8, 8, 8, o, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(Q, A16, A16, 4, 8, 8, 12, o, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_MISALIGNED
+    assert _status(Q, A16, A16, 4, 8, 8, 4, o, o, T, A16, A16, A16, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(Q, A16, A16, 4, 8, 8, 8, mx.quant_opts(rht=3), o, T, A16, A16, A16, A16, 0) == \
+        mx.MX_ERR_UNSUPPORTED
+    assert _status(Q, A16, A16, 4, 8, 8, 8, o, o, T, A16, A16, None, None, 0) in no_device
+    assert _status(Q, A16, A16, 0, 8, 8, 8, o, o, T, A16, A16, None, None, 0) == mx.MX_SUCCESS

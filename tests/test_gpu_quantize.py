@@ -338,3 +338,60 @@ def test_fc2_full_size_rht_recipe(oracle_mod):
     ref = oracle_mod.gemm_entries(oqg, osg, oqx, osx, dout, din, T, ii, jj)
     rel = np.linalg.norm(got[ii, jj] - ref) / np.linalg.norm(ref)
     assert rel <= 1e-5, rel
+
+
+def check_mul(oracle_mod, x, g, layout, row_opts=None, col_opts=None, rkw=None, ckw=None, dual=True, ldx=None):
+    """mx_quantize_dual_mul(x, g) against the oracle's quantization of bf16(fp32(x * g))."""
+    M, N = x.shape
+    xd, ldx = to_dev_bf16(x, ldx)
+    gd, ldg = to_dev_bf16(g, (ldx or 8) + 8)
+    qr, sr = mx.empty_blob(M, N, layout)
+    qc = sc = None
+    if dual:
+        qc, sc = mx.empty_blob(N, M, layout)
+    mx.mx_quantize_dual_mul(xd, gd, M, N, ldx, ldg, row_opts or mx.quant_opts(), col_opts or mx.quant_opts(), layout,
+                            qr, sr, qc, sc)
+    y = oracle_mod.bf16_mul(x, g)
+    dirs = [(0, qr, sr, rkw, M, N)] + ([(1, qc, sc, ckw, N, M)] if dual else [])
+    for d, q, s, kw, rows, length in dirs:
+        qw, sw = oracle_mod.quantize(y, d, **(kw or {}))
+        q, s = host(q), host(s)
+        if layout == CANON:
+            q, s = canon_shape(oracle_mod, rows, length, q, s)
+        else:
+            qw, sw = oracle_mod.to_tiled(qw, sw, rows, length)
+        assert_equal_bytes(q, qw, "mul dir %d data %s" % (d, (M, N)))
+        assert_equal_bytes(s, sw, "mul dir %d scale %s" % (d, (M, N)))
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", [(1, 1), (33, 70), (127, 129), (200, 1000), (300, 136)])
+def test_multiply_prologue(oracle_mod, layout, shape):
+    """Quantizer prologue: bf16(x * g) formed in the staging read, both blobs
+    bit-exact against the oracle's quantization of the product; row-only too;
+    g has its own row stride."""
+    _require_gpu()
+    log("mul prologue %s layout %d" % (shape, layout))
+    x = synth.random_bf16(500 + shape[0], shape, std=1.0)
+    g = synth.random_bf16(600 + shape[1], shape, std=0.7)
+    check_mul(oracle_mod, x, g, layout)
+    check_mul(oracle_mod, x, g, layout, dual=False)
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_multiply_prologue_sr_2d_specials(oracle_mod, layout):
+    """SR on both directions (paired Philox path), 2D blocks, and factors that
+    make Inf, NaN (0 * Inf), subnormal and overflowing products."""
+    _require_gpu()
+    x = synth.random_bf16(77, (160, 256), std=0.3)
+    g = synth.random_bf16(78, (160, 256), std=4.0)
+    x[0, 3] = 0x7F80; g[0, 3] = 0x0000          # Inf * 0 = NaN
+    x[1, 9] = 0x7F7F; g[1, 9] = 0x4000          # overflow to Inf
+    x[2, :] = 0x0080; g[2, :] = 0x0100          # far below the fp32 normal range
+    x[3, 40] = 0xFF80; g[3, 40] = 0x3F80        # -Inf
+    ro = mx.quant_opts(use_sr=True, seed=11, tensor_id=4)
+    co = mx.quant_opts(use_sr=True, seed=12, tensor_id=5)
+    check_mul(oracle_mod, x, g, layout, ro, co, dict(use_sr=True, seed=11, tensor_id=4),
+              dict(use_sr=True, seed=12, tensor_id=5))
+    w2 = mx.quant_opts(use_2d_block=True)
+    check_mul(oracle_mod, x, g, layout, w2, w2, dict(use_2d=True), dict(use_2d=True))
