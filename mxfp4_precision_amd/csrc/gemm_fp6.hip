@@ -38,6 +38,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
@@ -298,7 +299,7 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
         if (tm0 + kBM <= M && tn0 + kBN <= N) {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 2; ++it)
-                *reinterpret_cast<uint4 *>(dst0 + 2 * it * ldc) = v[it];
+                __builtin_nontemporal_store(__builtin_bit_cast(v4u_t, v[it]), reinterpret_cast<v4u_t *>(dst0 + 2 * it * ldc));
         } else {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 2; ++it) {

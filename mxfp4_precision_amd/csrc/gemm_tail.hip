@@ -23,6 +23,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
 constexpr int kFmtFp4 = 4;                 // MFMA f8f6f4 format code for E2M1
 constexpr int kWaves = 4;
@@ -245,8 +246,8 @@ __device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[
 // acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4].
 // bf16: rounded (V_CVT_PK_BF16_F32, nearest even), staged in LDS, then
 // written as whole 256-byte row segments (each store instruction covers 4
-// rows with 16 bytes per lane); fp32: 16 bytes per lane straight from
-// registers.  Masked at the M/N edges.
+// rows with 16 bytes per lane; non-temporal, as C is not read again here);
+// fp32: 16 bytes per lane straight from registers.  Masked at the M/N edges.
 template <bool OUT_BF16>
 __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn, int64_t M, int64_t N, void *C,
                                            int64_t ldc, int wave, int lane) {
@@ -283,7 +284,7 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
         if (tm0 + kBM <= M && tn0 + kBN <= N) {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 4; ++it)
-                *reinterpret_cast<uint4 *>(dst0 + 4 * it * ldc) = v[it];
+                __builtin_nontemporal_store(__builtin_bit_cast(v4u_t, v[it]), reinterpret_cast<v4u_t *>(dst0 + 4 * it * ldc));
         } else {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 4; ++it) {
