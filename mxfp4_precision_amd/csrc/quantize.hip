@@ -319,6 +319,34 @@ __device__ __forceinline__ uint32_t code6(uint32_t x16, uint32_t c, const Fp6Dir
     }
     return c == 0xFFu ? 0u : (code | ((x16 >> 10) & 0x20u));
 }
+// One 32-element block (16 bf16 pairs, element e in half e%2 of w[e/2]) ->
+// scale byte and six dwords of codes by V_CVT_SCALEF32_PK32_FP6_BF16 /
+// _BF6_BF16 (E2M3 / E3M2), which divide by the fp32 scale and round to
+// nearest even with saturation; probed on MI355X against the add-and-shift
+// encode below for every finite bf16 at every scale byte a block can have:
+// no difference.  A block holding Inf/NaN gets scale 0xFF and zero codes.
+typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp6_block_hw(const u32x16_t &w, uint32_t fmt, uint32_t emax, u32x6_t &out) {
+    u16x2_t m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+    const uint32_t amax16 = m[0] > m[1] ? m[0] : m[1];
+    const uint32_t sc = scale_code_emax(amax16, emax);
+    const bf16x32_t x = __builtin_bit_cast(bf16x32_t, w);
+    const float sf = scale_f32(sc);
+    out = fmt == 2u ? __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(x, sf) : __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(x, sf);
+    if (sc == 0xFFu) out = u32x6_t{0u, 0u, 0u, 0u, 0u, 0u};
+    return sc;
+}
+__device__ __forceinline__ void lds_put24(uint8_t *p, const u32x6_t &v) {
+    *reinterpret_cast<uint2 *>(p) = uint2{v[0], v[1]};
+    *reinterpret_cast<uint2 *>(p + 8) = uint2{v[2], v[3]};
+    *reinterpret_cast<uint2 *>(p + 16) = uint2{v[4], v[5]};
+}
+
 // Eight 6-bit codes -> 48 bits, element e at bits [6e, 6e+6): lo = bits 0..31, hi = 32..47.
 __device__ __forceinline__ void pack6(const uint32_t (&k)[8], uint32_t &lo, uint32_t &hi) {
     lo = k[0] | (k[1] << 6) | (k[2] << 12) | (k[3] << 18) | (k[4] << 24) | (k[5] << 30);
@@ -479,6 +507,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
     // spread LDS banks; scales as 4 bytes per blob row.
     __shared__ __attribute__((aligned(16))) uint8_t s_data[2][kTileRows * kLinePitch];
     __shared__ __attribute__((aligned(16))) uint8_t s_scale[2][kTileRows * 4];
+    // MXFP6, round to nearest, 1D blocks: each 32-element block is gathered
+    // into one lane through this 128 x 128 bf16 buffer (rows, then columns)
+    // and encoded by the hardware converter.
+    constexpr int kXPitch = 272;
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[ELEM == 6 ? kTileRows * kXPitch : 16];
     const int r_loc0 = wave * kWaveRows + 8 * q;      // this lane's first tile row
 
     // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
@@ -513,6 +546,30 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             if (i >= M) packed = 0;
             *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
             if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+        }
+    } else if (ELEM == 6 && !ROW_SR && !a.row.use_2d) {
+        // the lane's 8 rows x 8 columns into the row-major buffer, then thread
+        // th encodes blocks 2(th%2), 2(th%2)+1 of tile row th/2
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            *reinterpret_cast<uint4 *>(&s_x[(r_loc0 + t) * kXPitch + 16 * c]) = uint4{d[t][0], d[t][1], d[t][2], d[t][3]};
+        __syncthreads();
+        const int th = (int)threadIdx.x, rl = th >> 1;
+        const uint32_t emax = a.row.fmt == 2u ? 2u : 4u;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            const int b = 2 * (th & 1) + bb;
+            const uint8_t *src = &s_x[rl * kXPitch + 64 * b];
+            u32x16_t w;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
+                w[4 * v] = x4.x; w[4 * v + 1] = x4.y; w[4 * v + 2] = x4.z; w[4 * v + 3] = x4.w;
+            }
+            u32x6_t codes;
+            const uint32_t sc = fp6_block_hw(w, a.row.fmt, emax, codes);
+            lds_put24(&s_data[0][rl * kLinePitch + 24 * b], codes);
+            s_scale[0][rl * 4 + b] = (uint8_t)sc;
         }
     } else if constexpr (ELEM == 6) {
         const Fp6Dir f = fp6_dir(a.row.fmt);
@@ -602,7 +659,37 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a) {
             camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
             camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
         }
-        if constexpr (ELEM == 6) {
+        if (ELEM == 6 && !COL_SR && !a.col.use_2d) {
+            // the lane's 8 columns x 8 rows into the buffer as columns (after
+            // every reader of the row pass is done), then thread th encodes
+            // blocks 2(th%2), 2(th%2)+1 of tile column th/2
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int w = u >> 1, h = u & 1;
+                *reinterpret_cast<uint4 *>(&s_x[(8 * c + u) * kXPitch + 2 * r_loc0]) =
+                    uint4{pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h), pair_of(d[4][w], d[5][w], h),
+                          pair_of(d[6][w], d[7][w], h)};
+            }
+            __syncthreads();
+            const int th = (int)threadIdx.x, cl = th >> 1;
+            const uint32_t emax = a.col.fmt == 2u ? 2u : 4u;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int b = 2 * (th & 1) + bb;
+                const uint8_t *src = &s_x[cl * kXPitch + 64 * b];
+                u32x16_t wv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
+                    wv[4 * v] = x4.x; wv[4 * v + 1] = x4.y; wv[4 * v + 2] = x4.z; wv[4 * v + 3] = x4.w;
+                }
+                u32x6_t codes;
+                const uint32_t sc = fp6_block_hw(wv, a.col.fmt, emax, codes);
+                lds_put24(&s_data[1][cl * kLinePitch + 24 * b], codes);
+                s_scale[1][cl * 4 + b] = (uint8_t)sc;
+            }
+        } else if constexpr (ELEM == 6) {
             const Fp6Dir f = fp6_dir(a.col.fmt);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
