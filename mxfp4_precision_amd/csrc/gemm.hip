@@ -641,8 +641,10 @@ __global__ void fill_kernel(T *C, int64_t M, int64_t N, int64_t ldc, const uint1
     else C[(idx / N) * ldc + j] = __uint_as_float((uint32_t)b << 16);
 }
 
+}  // namespace
+
 // Compute units of the current device (cached per device; 0 if unknown).
-int cu_count() {
+int device_cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -653,8 +655,6 @@ int cu_count() {
     }
     return n;
 }
-
-}  // namespace
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *As,
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
@@ -678,7 +678,7 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
     const int tiles = tiles_m * tiles_n;
     // Whole rounds of 256x256 tiles here; a last round that would fill at most
     // half of the CUs goes to the tail kernel as 128x128 tiles instead.
-    const int cus = cu_count();
+    const int cus = device_cu_count();
     const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
     auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_kernel<true, true> : gemm_a4w4_kernel<true, false>)
                                        : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);

@@ -502,9 +502,21 @@ hipError_t launch_gemm_fp6(int64_t M, int64_t N, int64_t K, int fmt_a, const uin
         cdiv(N, 16) * (K_pad / 128) * kAtomBytes >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
     const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-    dim3 grid((unsigned)(tiles_m * tiles_n));
+    const int tiles = tiles_m * tiles_n;
+    // whole rounds here; a last round that would fill at most a quarter of the
+    // CUs goes to the 128x128 tail kernel (gemm_fp6_tail.hip).  (Same-box A/B
+    // on the fc2 shapes: 64 leftover tiles -7.5%; 96 no gain; 128 +1%.)
+    const int cus = device_cu_count();
+    const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 4) ? tiles % cus : 0;
     auto kernel = out_dtype == MX_BF16 ? pick_kernel<true>(fmt_a, fmt_b) : pick_kernel<false>(fmt_a, fmt_b);
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, As, B, Bs, C, ldc);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles - tail)), dim3(kThreads), 0, stream, M, N, K_pad, tiles_m,
+                       tiles_n, A, As, B, Bs, C, ldc);
+    if (tail) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_gemm_fp6_tail(M, N, K_pad, tiles_m, tiles_n, tiles - tail, tail, fmt_a, A, As, fmt_b, B, Bs,
+                                    out_dtype, C, ldc, stream);
+    }
     return hipGetLastError();
 }
 

@@ -165,7 +165,8 @@ def run_gemm(oracle_mod, a, fa, b, fb, nsample=None, seed=0, what=""):
         ii, jj = ii.ravel(), jj.ravel()
     else:
         rng = np.random.default_rng(seed)
-        ii, jj = rng.integers(0, M, nsample), rng.integers(0, N, nsample)
+        ii = np.concatenate([rng.integers(0, M, nsample), [0, M - 1, M - 1, 0]])
+        jj = np.concatenate([rng.integers(0, N, nsample), [0, N - 1, 0, N - 1]])
     ref, sabs = oracle_mod.gemm_fp6_entries(oqa, osa, fa, oqb, osb, fb, M, N, K, ii, jj)
     tau = 2.0 ** -12 * sabs + 2.0 ** -22 * np.abs(ref)
     got_b = outs[mx.MX_BF16].view(np.uint16)[ii, jj]
@@ -218,3 +219,15 @@ def test_fp6_fc2_step_sampled(oracle_mod):
     log("fp6 fc2 wgrad")
     run_gemm(oracle_mod, np.ascontiguousarray(dY.T), E3M2, np.ascontiguousarray(X.T), E2M3, nsample=2048, seed=3,
              what="fp6 wgrad")
+
+
+def test_fp6_gemm_tail_tiles(oracle_mod):
+    """306 output tiles of 256x256 on 256 CUs: the last 50 (holding the ragged
+    last row and column of tiles) run as 200 tiles of 128x128 in the tail
+    kernel; sampled entries of both regions against the oracle."""
+    _require_gpu()
+    M, N, K = 4597, 4349, 384
+    log("fp6 gemm tail tiles %dx%dx%d" % (M, N, K))
+    a = synth.random_bf16(191, (M, K), std=1.0)
+    b = synth.random_bf16(192, (N, K), std=0.05)
+    run_gemm(oracle_mod, a, E3M2, b, E2M3, nsample=8192, seed=9, what="fp6 tail")
