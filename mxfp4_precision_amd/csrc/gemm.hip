@@ -76,6 +76,9 @@ constexpr int kXcds = 8;
 constexpr int kGroupM = 8;                 // tile rows per band in the tile order
 
 static_assert(kAtoms % kWaves == 0 && kLoads % 2 == 0, "DMA split");
+// 16-byte stores per wave per tile in the stream kernel's epilogue: kMA
+// passes of kWavesM * 32 rows of 512 bytes, 2 rows per store instruction
+constexpr int kEpiStoresPerTile = kMA * (kWavesM * 32 / kWaves) / 2;
 static_assert(kMA + kMB <= kSlots, "one operand read per slot");
 
 // Buffer resource over [p, p + bytes).  Loads address it with a per-lane
@@ -155,25 +158,38 @@ struct Regs {
 // the atom lands as zeros.
 template <int S, int V, class Ctx>
 __device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
+    using kint = typename Ctx::kint;
     if constexpr (V < kLoads) {
+        // atom kWaves*V + wave: an A atom for every wave or a B atom for every wave
+        constexpr bool isA = kWaves * (V + 1) <= kGA;
+        static_assert(isA || kWaves * V >= kGA, "A/B split falls on a DMA instruction");
         const int a = kWaves * V + c.wave;
-        uint32_t base = k < c.ksteps ? (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024) : kOutOfRange;
+        uint32_t base;
         if constexpr (Ctx::kStream) {
-            const typename Ctx::kint kn = k - c.kstream;
-            if (kn >= 0) base = kn < c.knext ? (uint32_t)c.ld_next[V] + (uint32_t)(kn * 1024) : kOutOfRange;
+            // steps of the tile, then the next tile's first steps
+            const bool cur = k < c.kstream;
+            const kint kk = cur ? k : k - c.kstream;
+            const int row = cur ? c.ld_row[V] : c.ld_next[V];
+            base = kk < (cur ? c.ksteps : c.knext) ? (uint32_t)row + (uint32_t)(kk * 1024) : kOutOfRange;
+        } else {
+            base = k < c.ksteps ? (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024) : kOutOfRange;
         }
-        const __amdgpu_buffer_rsrc_t rsrc = a < kGA ? c.rA : c.rB;
+        // (plain-typed locals: a builtin call on template-dependent operands
+        // does not resolve in the host compilation pass)
+        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rA : c.rB;
         const uint32_t off = base + (uint32_t)c.lane16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS(stage_buf<S>() + a * 1024), 16, off, 0, 0, 0);
     } else {
         constexpr int R = V - kLoads;
+        constexpr bool isA = kWaves * (R + 1) <= kGA;
+        static_assert(isA || kWaves * R >= kGA, "A/B split falls on a DMA instruction");
         const int a = kWaves * R + c.wave;
-        const typename Ctx::kint h = k / 4;
+        const kint h = k / 4;
         uint32_t base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
         // only step kstream (the next tile's first) opens a k-group past the tile
         if constexpr (Ctx::kStream)
             if (k >= c.kstream) base = c.knext > 0 ? (uint32_t)c.sc_next[R] : kOutOfRange;
-        const __amdgpu_buffer_rsrc_t rsrc = a < kGA ? c.rAs : c.rBs;
+        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rAs : c.rBs;
         const uint32_t off = base + (uint32_t)c.lane4;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS(scale_buf() + a * 256), 4, off, 0, 0, 0);
     }
@@ -202,19 +218,6 @@ __device__ __forceinline__ void dma_part(const Ctx &c, typename Ctx::kint k) {
     }
 }
 
-// DMA instructions issued in half H of a step for the step with stage DS.
-// One-tile kernel: half 0 issues part 1, half 1 part 0.  Stream kernel: a
-// step with stage 2 is issued whole in half 1 of the step before it (its
-// stage is free from that half on), so that at the end of a tile all three
-// prefetched steps of the next tile are in flight before the epilogue's
-// stores; the waits between halves stay the same.
-__host__ __device__ constexpr int half_ops(bool stream, int DS, int H) {
-    return !(stream && DS == 2) ? part_ops(DS) : H == 0 ? 0 : 2 * part_ops(DS);
-}
-__host__ __device__ constexpr int half_op(bool stream, int DS, int P, int n) {
-    return !(stream && DS == 2) ? part_op(DS, P, n) : n;   // stage 2 opens no k-group: data ops 0..3
-}
-
 template <int S>
 __device__ __forceinline__ void mfma_tile(v16f &acc, const uint4 &xb, const uint4 &xa, uint32_t sbv, uint32_t sav) {
     const v8i bop = {(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
@@ -239,7 +242,7 @@ struct Lds {
 //  - at S == 3, half 1 also reads the next k-group's scales, two per slot.
 //  - the DMA instructions this slot carries (half 0: part 1 of step k+2,
 //    half 1: part 0 of step k+3).
-template <int S, int H, int T, class Ctx>
+template <int S, int H, int T, bool FRESH, class Ctx>
 __device__ __forceinline__ void slot(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                      const Lds &l) {
     constexpr int i = T / kMA, j = T % kMA;
@@ -276,24 +279,25 @@ __device__ __forceinline__ void slot(const Ctx &c, typename Ctx::kint k, v16f (&
 
     constexpr int DS = H == 0 ? ((S + 2) & 3) : ((S + 3) & 3);
     constexpr int P = H == 0 ? 1 : 0;
-    constexpr bool kSt = Ctx::kStream;
-    constexpr int nv = half_ops(kSt, DS, H);
+    // FRESH (a tile's first k-step in the stream kernel): the second part of
+    // step 2 already went out before the previous tile's stores
+    constexpr int nv = (FRESH && S == 0 && H == 0) ? 0 : part_ops(DS);
     const typename Ctx::kint dk = H == 0 ? k + 2 : k + 3;
-    if constexpr (nv > 0 && dma_slot(0, nv) == T) dma_op<DS, half_op(kSt, DS, P, 0)>(c, dk);
-    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, half_op(kSt, DS, P, 1)>(c, dk);
-    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, half_op(kSt, DS, P, 2)>(c, dk);
-    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, half_op(kSt, DS, P, 3)>(c, dk);
-    static_assert(part_ops(0) <= 4 && 2 * part_ops(2) <= 4, "dma slots");
+    if constexpr (nv > 0 && dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0)>(c, dk);
+    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1)>(c, dk);
+    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2)>(c, dk);
+    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3)>(c, dk);
+    static_assert(part_ops(0) <= 4, "dma slots");
     // keep this slot's instructions in this slot
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S, int H, int T = 0, class Ctx>
+template <int S, int H, int T = 0, bool FRESH = false, class Ctx>
 __device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                           const Lds &l) {
     if constexpr (T < kSlots) {
-        slot<S, H, T>(c, k, acc, r, l);
-        half_step<S, H, T + 1>(c, k, acc, r, l);
+        slot<S, H, T, FRESH>(c, k, acc, r, l);
+        half_step<S, H, T + 1, FRESH>(c, k, acc, r, l);
     }
 }
 
@@ -302,18 +306,19 @@ __device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v1
 // wave, which publishes step k+1 and certifies that all reads of step k-1's
 // stage are done before half 1 starts overwriting it.  Vector memory
 // instructions complete in issue order (loads and stores alike), so the
-// count is exact.  STORES: instructions issued after step k+1's DMA beyond
-// those of step k+2 (the stream kernel's epilogue stores, in the first two
-// k-steps of a tile), which the wait then need not drain.
-template <int S, int STORES = 0, class Ctx>
+// count is exact.  FRESH: the first k-group of a tile in the stream kernel,
+// where the previous tile's kEpiStoresPerTile stores were issued after all of step
+// 2's DMA; the first two waits count past them instead of draining them.
+template <int S, bool FRESH = false, class Ctx>
 __device__ __forceinline__ void k_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                        const Lds &l) {
+    constexpr int kStores = FRESH && S < 2 ? kEpiStoresPerTile : 0;
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 0>(c, k, acc, r, l);
-    static_assert(issued_for((S + 2) & 3) + STORES <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3) + STORES) : "memory");
+    half_step<S, 0, 0, FRESH>(c, k, acc, r, l);
+    static_assert(issued_for((S + 2) & 3) + kStores <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3) + kStores) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 1>(c, k, acc, r, l);
+    half_step<S, 1, 0, FRESH>(c, k, acc, r, l);
     if constexpr (S == 3) {
 #pragma unroll
         for (int t = 0; t < kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
@@ -568,22 +573,26 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
 // kMA passes of 64 rows, pass p staging MFMA tile row j = p of every wave
 // (tile rows 32p + [0, 32) and 128 + 32p + [0, 32)), 512 bytes per row with
 // the same chunk swizzle as the one-tile epilogue.  Each wave issues exactly
-// kEpiStores 16-byte buffer stores per tile whatever the edges: a chunk past
+// kEpiStoresPerTile 16-byte buffer stores per tile whatever the edges: a chunk past
 // row M or column N gets an out-of-range offset, which the buffer range check
 // drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
 // what lets the next tile's first waits count past the stores instead of
-// draining them.
+// draining them.  Before the stores, the epilogue issues the second part of
+// the next tile's step 2 (its first k-step would otherwise issue it after
+// them), into stage 2, free since the tile's last k-step.
 constexpr int kPassRows = kWavesM * 32;                   // 64
 constexpr int kEpiRowsPerWave = kPassRows / kWaves;       // 8: 4 instructions of 2 rows
-constexpr int kEpiStores = kMA * kEpiRowsPerWave / 2;     // 16
+static_assert(kEpiStoresPerTile == kMA * kEpiRowsPerWave / 2, "store count");
 static_assert(kPassRows * kBN * 2 == kStageBytes, "one pass fills stage 3");
 
 __device__ __forceinline__ uint8_t *c_stage3(int r, int col) {
     return g_stage3 + r * (kBN * 2) + (((col >> 3) ^ (r & 31)) * 16) + (col & 7) * 2;
 }
 
-__device__ __forceinline__ void store_tile_stream(v16f (&acc)[kMB][kMA], int tm, int tn, int M, int N,
-                                                  __amdgpu_buffer_rsrc_t rC, int ldc, int wave, int lane) {
+__device__ __forceinline__ void store_tile_stream(const GemmCtxT<true> &c, v16f (&acc)[kMB][kMA], int tm, int tn,
+                                                  int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
+                                                  int lane) {
+    dma_part<2, 1>(c, c.kstream + 2);
     const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
     const int tm0 = tm * kBM;
@@ -626,7 +635,8 @@ __device__ __forceinline__ void store_tile_stream(v16f (&acc)[kMB][kMA], int tm,
 // already fetch the next tile's first three and its first operands and
 // scales, so the pipeline never drains between tiles; the epilogue's stores
 // then overlap the next tile's first k-steps (its first two waits count past
-// them, only the third one needs them done).  Needs N % 8 == 0 and
+// them, only the third one needs them done).  The k-loop is the one-tile
+// kernel's, DMA schedule included.  Needs N % 8 == 0 and
 // M * ldc * 2 < 2^31 (32-bit store offsets).
 __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N, int K_pad, int tiles_m, int tiles_n,
                                                                     int tiles, const uint8_t *__restrict__ A,
@@ -670,9 +680,10 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
 #pragma unroll
         for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
 
-    // Prologue: steps 0-2 whole, all landed before the first k-step, so the
-    // first tile's first two waits (which count past kEpiStores instructions
-    // that this tile does not have) wait for nothing.
+    // Prologue: steps 0-2 whole (a tile's first k-step does not issue step
+    // 2's second part), all landed before the first k-step, so the first
+    // tile's first two waits (which count past stores that this tile does not
+    // have) wait for nothing.
     dma_part<0, 0>(c, 0);
     dma_part<0, 1>(c, 0);
     dma_part<1, 0>(c, 1);
@@ -711,8 +722,8 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
 
     for (;;) {
         // first k-group: its first two waits count past the previous tile's stores
-        k_step<0, kEpiStores>(c, 0, acc, r, l);
-        k_step<1, kEpiStores>(c, 1, acc, r, l);
+        k_step<0, true>(c, 0, acc, r, l);
+        k_step<1, true>(c, 1, acc, r, l);
         k_step<2>(c, 2, acc, r, l);
         k_step<3>(c, 3, acc, r, l);
         for (int h = 1; h < c.kgroups; ++h) {
@@ -723,7 +734,7 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
             k_step<3>(c, k0 + 3, acc, r, l);
         }
         // r now holds the next tile's first operands and scales
-        store_tile_stream(acc, tm, tn, M, N, rC, ldc, wave, lane);
+        store_tile_stream(c, acc, tm, tn, M, N, rC, ldc, wave, lane);
         vb += P;
         if (vb >= tiles) break;
         tm = tm_next;
