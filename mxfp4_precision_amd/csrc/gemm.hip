@@ -307,12 +307,13 @@ __device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v1
 // stage are done before half 1 starts overwriting it.  Vector memory
 // instructions complete in issue order (loads and stores alike), so the
 // count is exact.  FRESH: the first k-group of a tile in the stream kernel,
-// where the previous tile's kEpiStoresPerTile stores were issued after all of step
-// 2's DMA; the first two waits count past them instead of draining them.
-template <int S, bool FRESH = false, class Ctx>
+// where EXTRA vector-memory instructions (the previous tile's stores and
+// this tile's bias loads) were issued after all of step 2's DMA; the first
+// two waits count past them instead of draining them.
+template <int S, bool FRESH = false, int EXTRA = 0, class Ctx>
 __device__ __forceinline__ void k_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                        const Lds &l) {
-    constexpr int kStores = FRESH && S < 2 ? kEpiStoresPerTile : 0;
+    constexpr int kStores = FRESH && S < 2 ? EXTRA : 0;
     __builtin_amdgcn_sched_barrier(0);
     half_step<S, 0, 0, FRESH>(c, k, acc, r, l);
     static_assert(issued_for((S + 2) & 3) + kStores <= 63, "vmcnt range");
@@ -629,21 +630,62 @@ __device__ __forceinline__ void store_tile_stream(const GemmCtxT<true> &c, v16f 
     }
 }
 
-// Persistent form of gemm_a4w4_kernel for bf16 output without bias:
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+
+// This lane's bias values for tile column tn: columns n0 + 32i + 8q +
+// 4(lane/32) + 0..3 of the tile, 4 bf16 per (i, q), one 8-byte buffer load
+// each (the range ends at the 16-byte boundary after the last entry; the
+// bias is 16-byte aligned, so that block is inside its allocation; columns
+// past it read 0 and are never stored).
+__device__ __forceinline__ void load_bias(__amdgpu_buffer_rsrc_t rb, int tn, int wn, int lane,
+                                          v2u_t (&bias_bits)[kMB * 4]) {
+    const int col0 = tn * kBN + wn * kWN + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
+}
+
+__device__ __forceinline__ void add_bias(v16f (&acc)[kMB][kMA], const v2u_t (&bias_bits)[kMB * 4]) {
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v2u_t bb = bias_bits[i * 4 + q];
+            const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
+            const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
+#pragma unroll
+            for (int j = 0; j < kMA; ++j) {
+                acc[i][j][4 * q] += b0;
+                acc[i][j][4 * q + 1] += b1;
+                acc[i][j][4 * q + 2] += b2;
+                acc[i][j][4 * q + 3] += b3;
+            }
+        }
+}
+
+// Persistent form of gemm_a4w4_kernel for bf16 output:
 // gridDim.x workgroups, block b runs tiles b, b + gridDim.x, ... of the first
 // `tiles` of the tile order as one stream of k-steps.  A tile's last k-steps
 // already fetch the next tile's first three and its first operands and
 // scales, so the pipeline never drains between tiles; the epilogue's stores
 // then overlap the next tile's first k-steps (its first two waits count past
 // them, only the third one needs them done).  The k-loop is the one-tile
-// kernel's, DMA schedule included.  Needs N % 8 == 0 and
-// M * ldc * 2 < 2^31 (32-bit store offsets).
+// kernel's, DMA schedule included.  BIAS: a tile's bias values are loaded
+// right after the previous tile's stores (8 more instructions for those
+// waits to count past).  Needs N % 8 == 0 and M * ldc * 2 < 2^31 (32-bit
+// store offsets).
+template <bool BIAS>
 __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N, int K_pad, int tiles_m, int tiles_n,
                                                                     int tiles, const uint8_t *__restrict__ A,
                                                                     const uint8_t *__restrict__ As,
                                                                     const uint8_t *__restrict__ B,
                                                                     const uint8_t *__restrict__ Bs,
+                                                                    const uint16_t *__restrict__ bias,
                                                                     void *__restrict__ C, int ldc) {
+    constexpr int kBiasLoads = BIAS ? kMB * 4 : 0;
+    constexpr int kFreshOps = kEpiStoresPerTile + kBiasLoads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % kWavesM, wn = wave / kWavesM;
@@ -662,6 +704,7 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
     c.rAs = make_rsrc(As, (int64_t)nGA * c.kgroups * 256);
     c.rBs = make_rsrc(Bs, (int64_t)nGB * c.kgroups * 256);
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (int64_t)M * ldc * 2);
+    const __amdgpu_buffer_rsrc_t rBias = make_rsrc(bias, BIAS ? ((int64_t)N * 2 + 15) / 16 * 16 : 0);
 
     int vb = blockIdx.x;
     int tm, tn, tm_next = 0, tn_next = 0;
@@ -679,6 +722,8 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
         for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+    v2u_t bias_bits[BIAS ? kMB * 4 : 1];
+    if constexpr (BIAS) load_bias(rBias, tn, wn, lane, bias_bits);
 
     // Prologue: steps 0-2 whole (a tile's first k-step does not issue step
     // 2's second part), all landed before the first k-step, so the first
@@ -721,9 +766,10 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
         r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
 
     for (;;) {
-        // first k-group: its first two waits count past the previous tile's stores
-        k_step<0, true>(c, 0, acc, r, l);
-        k_step<1, true>(c, 1, acc, r, l);
+        // first k-group: its first two waits count past the previous tile's
+        // stores and this tile's bias loads
+        k_step<0, true, kFreshOps>(c, 0, acc, r, l);
+        k_step<1, true, kFreshOps>(c, 1, acc, r, l);
         k_step<2>(c, 2, acc, r, l);
         k_step<3>(c, 3, acc, r, l);
         for (int h = 1; h < c.kgroups; ++h) {
@@ -734,7 +780,18 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
             k_step<3>(c, k0 + 3, acc, r, l);
         }
         // r now holds the next tile's first operands and scales
+        if constexpr (BIAS) add_bias(acc, bias_bits);
         store_tile_stream(c, acc, tm, tn, M, N, rC, ldc, wave, lane);
+        if constexpr (BIAS) {
+            // The next tile's bias, after the stores in issue order as the
+            // first waits assume.  It is loaded on every path (after the last
+            // tile it is unused), so that the compiler's own wait tracking
+            // sees one instruction sequence at the loop head.
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            load_bias(rBias, tn_next, wn, lane, bias_bits);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         vb += P;
         if (vb >= tiles) break;
         tm = tm_next;
@@ -757,6 +814,10 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
     }
     // drain the stores and the trailing (out-of-range) DMAs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // A use of the last bias load on the exit path (never taken: M > 0), so
+    // that the load is not sunk past the loop's exit test.
+    if constexpr (BIAS)
+        if (M < 0) reinterpret_cast<v2u_t *>(C)[lane] = bias_bits[0];
 }
 
 // ------------------------------------------------------------ FP8 (E5M2)
@@ -939,10 +1000,11 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
     // per CU.  Same-box timings at 18432 rows: the stream form takes 7% off at
     // 12-24 k-steps per tile and 3.5% at 48, ties at 96 and loses 1-2% at 144,
     // where the per-tile costs it hides are small next to the k-loop.
-    if (!bias && out_dtype == MX_BF16 && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 96 * 128 &&
-        cus > 0 && tiles - tail > cus) {
-        hipLaunchKernelGGL(gemm_a4w4_stream_kernel, dim3((unsigned)cus), dim3(kThreads), 0, stream, (int)M, (int)N,
-                           (int)K_pad, tiles_m, tiles_n, tiles - tail, A, As, B, Bs, C, (int)ldc);
+    if (out_dtype == MX_BF16 && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 96 * 128 && cus > 0 &&
+        tiles - tail > cus) {
+        auto kernel = bias ? gemm_a4w4_stream_kernel<true> : gemm_a4w4_stream_kernel<false>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)cus), dim3(kThreads), 0, stream, (int)M, (int)N, (int)K_pad,
+                           tiles_m, tiles_n, tiles - tail, A, As, B, Bs, bias, C, (int)ldc);
     } else {
         auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_kernel<true, true> : gemm_a4w4_kernel<true, false>)
                                            : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 import mxfp4_precision_amd as mx
 from mxfp4_precision_amd import synth
 
-from gpu_util import (bf16_bits_to_f64, check_gemm_bf16, gemm, host, log, quantize_dual, quantize_rowwise,
+from gpu_util import (check_gemm_bf16, gemm, host, log, quantize_dual, quantize_rowwise,
                       tau_bound, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -268,32 +268,51 @@ def test_tail_tiles_bias_every_entry_of_tail_rows(oracle_mod):
     log("tail-bias: %d/%d bf16 exact, fp32 rel %.3g" % (exact, ii.size, rel))
 
 
+def _rne_bf16_bits(f32):
+    """bf16 bits of finite fp32 values, round to nearest even."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 @pytest.mark.parametrize("K", [200, 700, 1536])
 def test_several_tiles_per_workgroup(oracle_mod, K):
     """5020x7640 output = 20x30 = 600 tiles of 256x256: two whole rounds on
     256 CUs, where each persistent workgroup runs two tiles back to back (the
     DMAs of the first tile's last k-steps fetch the second tile's first ones,
-    its stores overlap the second tile's first k-steps), plus an 88-tile
-    tail; ragged last row and column of tiles.  K 200 (fewer k-steps than the
-    pipeline depth), 700 (padded k-group) and 1536.  Sampled entries against
-    the oracle; bf16 output equal to that of the one-tile-per-workgroup kernel
-    (the bias form, with a zero bias), which accumulates in the same order;
-    nothing written past column N of the ldc-strided output."""
+    its stores overlap the second tile's first k-steps, the second tile's
+    bias loads follow them), plus an 88-tile tail; ragged last row and column
+    of tiles.  K 200 (fewer k-steps than the pipeline depth), 700 (padded
+    k-group) and 1536.  Without and with a bias: sampled entries against the
+    oracle, and the bf16 output (persistent kernel) equal to the round-to-
+    nearest-even of the fp32 output (one tile per workgroup), which
+    accumulates in the same order; nothing written past column N of the
+    ldc-strided output."""
     _require_gpu()
     M, N = 5020, 7640
     a = synth.random_bf16(101 + K, (M, K), std=1.0)
     b = synth.random_bf16(102 + K, (N, K), std=0.05)
+    bias = synth.random_bf16(103 + K, (N,), std=2.0)
     log("several tiles per workgroup %dx%dx%d" % (M, N, K))
     cb, cf = run_case(oracle_mod, a, b, full=False, nsample=8192, seed=K, what="stream-%d" % K)
+    assert np.array_equal(cb, _rne_bf16_bits(cf))
     ad, lda = to_dev_bf16(a)
     bd, ldb = to_dev_bf16(b)
     qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
     qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
-    zero = torch.zeros(((N + 7) // 8 * 8,), dtype=torch.int16, device="cuda")
-    ref_b = host(gemm_bias(qa, sa, qb, sb, M, N, K, zero, mx.MX_BF16))[:M, :N].view(np.uint16)
-    assert np.array_equal(bf16_bits_to_f64(cb), bf16_bits_to_f64(ref_b))
-    ref_f = host(gemm_bias(qa, sa, qb, sb, M, N, K, zero, mx.MX_F32))[:M, :N].astype(np.float64)
-    assert np.array_equal(cf, ref_f)
+    bias_d = torch.zeros(((N + 7) // 8 * 8,), dtype=torch.int16)
+    bias_d[:N] = torch.from_numpy(bias.view(np.int16))
+    bias_d = bias_d.cuda()
+    cbb = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_BF16))[:M, :N].view(np.uint16)
+    cfb = host(gemm_bias(qa, sa, qb, sb, M, N, K, bias_d, mx.MX_F32))[:M, :N]
+    assert np.array_equal(cbb, _rne_bf16_bits(cfb))
+    oqa, osa = oracle_mod.quantize(a, 0)
+    oqb, osb = oracle_mod.quantize(b, 0)
+    rng = np.random.default_rng(K + 1)
+    ii, jj = rng.integers(0, M, 4096), rng.integers(0, N, 4096)
+    ref = oracle_mod.gemm_bias_entries(oqa, osa, oqb, osb, M, N, K, bias, ii, jj)
+    tau = tau_bound(oracle_mod, oqa, osa, oqb, osb, M, N, K, ii, jj)
+    exact, _ = check_gemm_bf16(cbb[ii, jj], ref, tau, oracle_mod, "stream-bias-%d" % K)
+    log("stream-bias-%d: %d/%d bf16 exact" % (K, exact, ii.size))
     ldc = N + 24
     Cp = host(gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16, ldc=ldc)).view(np.uint16)
     assert np.array_equal(Cp[:M, :N], cb)
