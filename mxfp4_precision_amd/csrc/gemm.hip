@@ -574,9 +574,9 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
 // kMA passes of 64 rows, pass p staging MFMA tile row j = p of every wave
 // (tile rows 32p + [0, 32) and 128 + 32p + [0, 32)), 512 bytes per row with
 // the same chunk swizzle as the one-tile epilogue.  Each wave issues exactly
-// kEpiStoresPerTile 16-byte buffer stores per tile whatever the edges: a chunk past
-// row M or column N gets an out-of-range offset, which the buffer range check
-// drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
+// kEpiStoresPerTile 16-byte buffer stores per tile whatever the edges: a
+// chunk past row M or column N gets an out-of-range offset, which the buffer
+// range check drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
 // what lets the next tile's first waits count past the stores instead of
 // draining them.  Before the stores, the epilogue issues the second part of
 // the next tile's step 2 (its first k-step would otherwise issue it after
@@ -784,9 +784,11 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
         store_tile_stream(c, acc, tm, tn, M, N, rC, ldc, wave, lane);
         if constexpr (BIAS) {
             // The next tile's bias, after the stores in issue order as the
-            // first waits assume.  It is loaded on every path (after the last
-            // tile it is unused), so that the compiler's own wait tracking
-            // sees one instruction sequence at the loop head.
+            // first waits assume.  (The compiler moves these loads past the
+            // exit test below; its own wait before the first read of the
+            // next tile then merges the paths with and without them and
+            // comes out at 20-21 instead of 28, draining a few of the oldest
+            // stores: correct, slightly conservative.)
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
             load_bias(rBias, tn_next, wn, lane, bias_bits);
@@ -814,10 +816,6 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
     }
     // drain the stores and the trailing (out-of-range) DMAs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    // A use of the last bias load on the exit path (never taken: M > 0), so
-    // that the load is not sunk past the loop's exit test.
-    if constexpr (BIAS)
-        if (M < 0) reinterpret_cast<v2u_t *>(C)[lane] = bias_bits[0];
 }
 
 // ------------------------------------------------------------ FP8 (E5M2)
