@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true",
                    help="skip the timings of the options outside the step (RHT, bias epilogue, layout conversion)")
-    p.add_argument("--cpu-tokens", type=int, default=32,
+    p.add_argument("--cpu-tokens", type=int, default=96,
                    help="token slice of the step the CPU oracle is timed on")
     p.add_argument("--profile-copy-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size kernel "
