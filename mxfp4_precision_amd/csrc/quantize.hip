@@ -30,7 +30,7 @@
 // E2M1 subnormal step (0.5) with the fp32 subnormal range, so the code is
 // the truncation u >> 22 plus 1 iff the element's random byte is below the
 // next 8 bits (u >> 14) & 0xFF, which equal floor(256 (v-lo)/(hi-lo)); the
-// kernel gets that sum as one carry (see code_sr).
+// kernel gets that sum as one carry (see pack8_sr).
 
 // Random Hadamard transform (when a direction's rht seed is non-zero): the
 // page's dual-quantize op has an "rht" switch for the column-wise blobs of
@@ -65,20 +65,6 @@ __device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
     return e > 2u ? e - 2u : 0u;
 }
 
-// |x| * 2^(1-c) as fp32 bits (exact whenever the code can be non-zero).
-__device__ __forceinline__ uint32_t scaled_u(uint32_t x16, uint32_t c) {
-    float xf = __uint_as_float((x16 & 0x7FFFu) << 16);
-    return __float_as_uint(__builtin_ldexpf(xf, 1 - (int)c));
-}
-
-// u clamped at code 7 (6.0), plus (255 - byte) << 14: the carry into bit 22
-// happens iff the byte is below the 8 bits u >> 14 & 0xFF.
-__device__ __forceinline__ uint32_t code_sr(uint32_t u, uint32_t rbyte) {
-    const uint32_t top = 7u << 22;
-    u = u < top ? u : top;
-    return (u + ((255u - rbyte) << 14)) >> 22;
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
@@ -105,9 +91,37 @@ __device__ __forceinline__ uint32_t pair_of(uint32_t lo_word, uint32_t hi_word, 
     return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
 }
 
-__device__ __forceinline__ uint32_t nibble_sr(uint32_t x16, uint32_t c, uint32_t rbyte) {
-    if (c == 0xFFu) return 0u;
-    return code_sr(scaled_u(x16, c), rbyte) | ((x16 >> 12) & 8u);
+// Stochastic E2M1 nibbles of eight bf16 that share the scale byte c: element
+// e is half e%2 of pair word p[e/2] (nibble e of the result); nb(e) holds
+// 255 minus its random byte in bits 16..23 and zeros elsewhere.  With u
+// clamped at code 7, (u << 2) + nb(e) carries into bit 24 iff the byte is
+// below u's bits 14..21, and bits 24..26 are then the code.  Branch-free:
+// the magnitude comes from the ldexp's |.| source modifier, the sign bits
+// (bit 7 of bytes 1 and 3 of each pair) are gathered by four byte permutes,
+// and a block holding Inf/NaN (c = 0xFF) is zeroed once for all eight.
+template <typename NB>
+__device__ __forceinline__ uint32_t pack8_sr(const uint32_t (&p)[4], uint32_t c, NB nb) {
+    const int sh = 1 - (int)c;
+    constexpr uint32_t top = 7u << 22;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t xhi = (e & 1) ? (p[e >> 1] & 0xFFFF0000u) : (p[e >> 1] << 16);
+        uint32_t u = __float_as_uint(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(xhi)), sh));
+        u = u < top ? u : top;
+        codes |= (((u << 2) + nb(e)) >> 24) << (4 * e);
+    }
+    const uint32_t a = __builtin_amdgcn_perm(p[1], p[0], 0x07030501u);   // p0.b1 p1.b1 p0.b3 p1.b3
+    const uint32_t b = __builtin_amdgcn_perm(p[3], p[2], 0x07030501u);   // p2.b1 p3.b1 p2.b3 p3.b3
+    const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);      // sign of element 2i at bit 8i+7
+    const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);       // sign of element 2i+1 at bit 8i+7
+    const uint32_t signs = ((even >> 4) & 0x08080808u) | (odd & 0x80808080u);
+    return c == 0xFFu ? 0u : (codes | signs);
+}
+
+// Byte k of w moved to bits 16..23, zeros elsewhere (selector 0x0C gives 0x00).
+__device__ __forceinline__ uint32_t byte_to_b2(uint32_t w, int k) {
+    return __builtin_amdgcn_perm(0u, w, 0x0C000C0Cu | ((uint32_t)k << 16));
 }
 
 // ------------------------------------------------------------------ Philox
@@ -374,13 +388,16 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
 }
 
-// Dual stochastic rounding holds both directions' random bytes and needs
-// 150-230 VGPRs when unconstrained (two waves per SIMD); capping it at 168
-// (three waves) costs no spills and took 11% off the 18432x3072 dY quantize.
-// (With the Hadamard transform as well it would spill, so that form keeps
-// its registers.)
+// Dual stochastic rounding holds both directions' random bytes while the
+// staging loads are in flight.  Asking for at least two waves per SIMD (up to
+// 256 VGPRs) lets the compiler schedule it in 164 VGPRs without spills, so
+// three waves still fit a SIMD; asking for three (168 VGPRs) made it spill.
+// Same-box timings of the 18432x3072 dY quantize: 0.0637 ms, against 0.0688
+// ms with the spilling three-wave request and 0.0711 ms for the earlier form
+// that drew the bytes after the loads had landed.  (With the Hadamard
+// transform as well it would spill, so that form keeps its registers.)
 template <bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
-constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? 3 : 1;
+constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? 2 : 1;
 
 // ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
 // options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
@@ -423,59 +440,31 @@ __global__ __launch_bounds__(256) __attribute__((
             }
         }
     }
+    // the second factor of the prologue, same shape and bounds (positions past
+    // M or N read as 0); its loads are issued here and the products formed
+    // after the random bytes
+    uint32_t gl[MUL ? 8 : 1][4];
     if constexpr (MUL) {
-        // the second factor, same shape and bounds (positions past M or N read as 0)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int64_t i = row0 + 8 * q + t;
             const uint16_t *p = a.g + i * a.ldg + j0;
-            uint32_t e[4];
             if (i < M && j0 + 8 <= N) {
                 const v4u_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_t *>(p));
-                e[0] = v.x; e[1] = v.y; e[2] = v.z; e[3] = v.w;
+                gl[t][0] = v.x; gl[t][1] = v.y; gl[t][2] = v.z; gl[t][3] = v.w;
             } else {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t lo = (i < M && j0 + 2 * w < N) ? p[2 * w] : 0u;
                     const uint32_t hi = (i < M && j0 + 2 * w + 1 < N) ? p[2 * w + 1] : 0u;
-                    e[w] = lo | (hi << 16);
+                    gl[t][w] = lo | (hi << 16);
                 }
             }
-#pragma unroll
-            for (int w = 0; w < 4; ++w) d[t][w] = mul_bf16_pair(d[t][w], e[w]);
         }
     }
 
-    // ---- block amax, row direction: per row t over the lane's 8 columns, then lanes c^1, c^2
-    uint32_t ramax[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        uint32_t m = umax(umax(max_abs_pair(d[t][0]), max_abs_pair(d[t][1])),
-                          umax(max_abs_pair(d[t][2]), max_abs_pair(d[t][3])));
-        ramax[t] = m;
-    }
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-        uint32_t pk = ramax[t] | (ramax[t + 1] << 16);
-        uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 1, 64);
-        uint32_t lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu), hi = umax(pk >> 16, o1 >> 16);
-        pk = lo | (hi << 16);
-        uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 2, 64);
-        ramax[t] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
-        ramax[t + 1] = umax(pk >> 16, o2 >> 16);
-    }
-    // 32x32 tile amax (2D mode): rows of the lane, then the 4 q-lanes
-    uint32_t tile_amax = 0;
-    if (a.row.use_2d || (DUAL && a.col.use_2d)) {
-        uint32_t m = 0;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) m = umax(m, ramax[t]);
-        m = xor_max(m, 16);
-        m = xor_max(m, 32);
-        tile_amax = m;
-    }
-
-    // ---- stochastic-rounding bytes.  One Philox block covers 16 consecutive
+    // ---- stochastic-rounding bytes, computed while the loads above are in
+    // flight (they do not depend on x).  One Philox block covers 16 consecutive
     // row-major elements: the columns of lanes c and c^1.  When both
     // directions round stochastically and every group starts on a lane pair
     // (N and both index bases multiples of 16), lane c&1 == d computes the
@@ -512,6 +501,42 @@ __global__ __launch_bounds__(256) __attribute__((
             if (DUAL && COL_SR)
                 rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
         }
+    }
+
+    if constexpr (MUL) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) d[t][w] = mul_bf16_pair(d[t][w], gl[t][w]);
+    }
+
+    // ---- block amax, row direction: per row t over the lane's 8 columns, then lanes c^1, c^2
+    uint32_t ramax[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        uint32_t m = umax(umax(max_abs_pair(d[t][0]), max_abs_pair(d[t][1])),
+                          umax(max_abs_pair(d[t][2]), max_abs_pair(d[t][3])));
+        ramax[t] = m;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        uint32_t pk = ramax[t] | (ramax[t + 1] << 16);
+        uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 1, 64);
+        uint32_t lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu), hi = umax(pk >> 16, o1 >> 16);
+        pk = lo | (hi << 16);
+        uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 2, 64);
+        ramax[t] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
+        ramax[t + 1] = umax(pk >> 16, o2 >> 16);
+    }
+    // 32x32 tile amax (2D mode): rows of the lane, then the 4 q-lanes
+    uint32_t tile_amax = 0;
+    if (a.row.use_2d || (DUAL && a.col.use_2d)) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) m = umax(m, ramax[t]);
+        m = xor_max(m, 16);
+        m = xor_max(m, 32);
+        tile_amax = m;
     }
 
     // ---- encode both directions into LDS, then write whole 16-byte slices.
@@ -610,12 +635,8 @@ __global__ __launch_bounds__(256) __attribute__((
         const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
         uint32_t packed = 0;
         if (ROW_SR) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                uint32_t rb = ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu;
-                packed |= nibble_sr(x16, sc, rb) << (4 * e);
-            }
+            const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
+            packed = pack8_sr(d[t], sc, [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); });
         } else {
             packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
         }
@@ -728,12 +749,11 @@ __global__ __launch_bounds__(256) __attribute__((
             const uint32_t sc = j < N ? scale_code(a.col.use_2d ? tile_amax : camax[u]) : 0u;
             uint32_t packed = 0;
             if (COL_SR) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-                    uint32_t rb = ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu;
-                    packed |= nibble_sr(x16, sc, rb) << (4 * t);
-                }
+                // element t of the column = row t: pairs (rows 2i, 2i+1) of this column's half
+                const int w = u >> 1, h = u & 1;
+                const uint32_t pr[4] = {pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
+                                        pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h)};
+                packed = pack8_sr(pr, sc, [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); });
             } else {
                 const int w = u >> 1, h = u & 1;
                 packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
