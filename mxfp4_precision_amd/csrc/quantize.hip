@@ -396,8 +396,10 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 // ms with the spilling three-wave request and 0.0711 ms for the earlier form
 // that drew the bytes after the loads had landed.  (With the Hadamard
 // transform as well it would spill, so that form keeps its registers.)
-template <bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
-constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? 2 : 1;
+// MXFP6 draws its bytes after the loads have landed and fits three waves
+// (168 VGPRs) without spills.
+template <int ELEM, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
+constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? (ELEM == 6 ? 3 : 2) : 1;
 
 // ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
 // options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
@@ -406,7 +408,7 @@ constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? 2 : 1;
 // mx_quantize_dual_mul), formed in the staging read.
 template <int ELEM, int LAYOUT, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT, bool MUL = false>
 __global__ __launch_bounds__(256) __attribute__((
-    amdgpu_waves_per_eu(kMinWaves<DUAL, ROW_SR, COL_SR, RHT>, 8))) void quantize_kernel(QuantArgs a) {
+    amdgpu_waves_per_eu(kMinWaves<ELEM, DUAL, ROW_SR, COL_SR, RHT>, 8))) void quantize_kernel(QuantArgs a) {
     static_assert(ELEM == 4 || (ELEM == 6 && !RHT), "element size");
     static_assert(!MUL || (ELEM == 4 && !RHT), "prologue");
     constexpr int kLinePitch = ELEM == 4 ? 80 : 112;
@@ -463,45 +465,52 @@ __global__ __launch_bounds__(256) __attribute__((
         }
     }
 
-    // ---- stochastic-rounding bytes, computed while the loads above are in
-    // flight (they do not depend on x).  One Philox block covers 16 consecutive
-    // row-major elements: the columns of lanes c and c^1.  When both
+    // ---- stochastic-rounding bytes.  They do not depend on x, so MXFP4 draws
+    // them while the staging loads above are in flight; MXFP6 draws them after
+    // the amax reductions (with its encode, holding the bytes across the loads
+    // costs occupancy or spills: same-box SR dual quantize of an 18432x3072
+    // gradient 0.078-0.080 ms late, 0.086-0.090 ms early).  One Philox block
+    // covers 16 consecutive row-major elements: the columns of lanes c and
+    // c^1.  When both
     // directions round stochastically and every group starts on a lane pair
     // (N and both index bases multiples of 16), lane c&1 == d computes the
     // blocks of direction d for its 8 rows and the pair swaps the halves it
     // does not need, halving the Philox work; otherwise each lane computes
     // its own 8-byte windows.
     uint32_t rrow_lo[8], rrow_hi[8], rcol_lo[8], rcol_hi[8];
-    if (ROW_SR && COL_SR && a.sr_pairs) {
-        const uint32_t p = (uint32_t)(c & 1);
-        const DirOpts &o = p ? a.col : a.row;
-        const uint64_t jpair = (uint64_t)(col0 + 16 * (c >> 1));
+    auto draw_sr = [&]() {
+        if (ROW_SR && COL_SR && a.sr_pairs) {
+            const uint32_t p = (uint32_t)(c & 1);
+            const DirOpts &o = p ? a.col : a.row;
+            const uint64_t jpair = (uint64_t)(col0 + 16 * (c >> 1));
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int64_t i = row0 + 8 * q + t;
-            const uint64_t g = (o.index_base + (uint64_t)i * (uint64_t)N + jpair) >> 4;
-            uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p;
-            philox10(w0, w1, w2, w3, o.key0, o.key1);
-            const uint32_t r0 = (uint32_t)__shfl_xor((int)(p ? w0 : w2), 1, 64);
-            const uint32_t r1 = (uint32_t)__shfl_xor((int)(p ? w1 : w3), 1, 64);
-            rrow_lo[t] = p ? r0 : w0;
-            rrow_hi[t] = p ? r1 : w1;
-            rcol_lo[t] = p ? w2 : r0;
-            rcol_hi[t] = p ? w3 : r1;
-        }
-    } else {
+            for (int t = 0; t < 8; ++t) {
+                const int64_t i = row0 + 8 * q + t;
+                const uint64_t g = (o.index_base + (uint64_t)i * (uint64_t)N + jpair) >> 4;
+                uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p;
+                philox10(w0, w1, w2, w3, o.key0, o.key1);
+                const uint32_t r0 = (uint32_t)__shfl_xor((int)(p ? w0 : w2), 1, 64);
+                const uint32_t r1 = (uint32_t)__shfl_xor((int)(p ? w1 : w3), 1, 64);
+                rrow_lo[t] = p ? r0 : w0;
+                rrow_hi[t] = p ? r1 : w1;
+                rcol_lo[t] = p ? w2 : r0;
+                rcol_hi[t] = p ? w3 : r1;
+            }
+        } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int64_t i = row0 + 8 * q + t;
-            rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
-            // pads too: after a Hadamard transform they carry values (otherwise they are 0 and
-            // round to 0 with any byte)
-            if (ROW_SR)
-                rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
-            if (DUAL && COL_SR)
-                rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
+            for (int t = 0; t < 8; ++t) {
+                const int64_t i = row0 + 8 * q + t;
+                rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
+                // pads too: after a Hadamard transform they carry values (otherwise they are 0 and
+                // round to 0 with any byte)
+                if (ROW_SR)
+                    rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
+                if (DUAL && COL_SR)
+                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
+            }
         }
-    }
+    };
+    if constexpr (ELEM == 4) draw_sr();
 
     if constexpr (MUL) {
 #pragma unroll
@@ -538,6 +547,8 @@ __global__ __launch_bounds__(256) __attribute__((
         m = xor_max(m, 32);
         tile_amax = m;
     }
+
+    if constexpr (ELEM == 6) draw_sr();
 
     // ---- encode both directions into LDS, then write whole 16-byte slices.
     // Staging: one 64-byte line per blob row of this workgroup's tile (128 blob
