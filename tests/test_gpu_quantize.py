@@ -157,6 +157,66 @@ def test_exhaustive_element_sweep(oracle_mod):
     check_dual(oracle_mod, X[:4096], CANON)
 
 
+def _special_tensor(seed, shape):
+    x = synth.random_bf16(seed, shape, std=1.0)
+    x[0, 5] = 0x7F80        # +Inf
+    x[1, 40] = 0xFFC0       # NaN
+    x[40, 100] = 0xFF80     # -Inf (column block too)
+    x[2, :32] = 0x8000      # -0 block
+    x[3, 32:64] = 0x0001    # subnormal block (amax subnormal -> scale 0)
+    x[4, 64:96] = np.array([0x0080 + k for k in range(32)], dtype=np.uint16)  # min-normal region
+    x[5, :] = 0x7F7F        # bf16 max
+    x[6, 0] = 0x0001
+    x[6, 1:32] = 0
+    x[64:96, 200:232] = 0   # zero 32x32 tile
+    return x
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_special_values_stochastic(oracle_mod, layout):
+    """The special blocks of test_special_values with stochastic rounding in both
+    directions: Inf/NaN blocks (scale 0xFF, zero codes), -0, subnormal amax
+    (scale 0), bf16 max; N = 256 takes the paired Philox path, N = 250 the
+    unpaired one."""
+    _require_gpu()
+    sr = mx.quant_opts(use_sr=True, seed=11, tensor_id=4)
+    kw = dict(use_sr=True, seed=11, tensor_id=4)
+    x = _special_tensor(9, (96, 256))
+    check_dual(oracle_mod, x, layout, sr, sr, kw, kw)
+    check_dual(oracle_mod, np.ascontiguousarray(x[:, :250]), layout, sr, sr, kw, kw)
+
+
+def test_exhaustive_element_sweep_stochastic(oracle_mod):
+    """Every finite bf16 magnitude at every scale that can hold it, both signs,
+    with stochastic rounding: row-wise over the whole sweep, dual on a slice
+    (paired Philox path), and row-wise on a slice 31 columns wide (unpaired)."""
+    _require_gpu()
+    mags = np.arange(0x7F80, dtype=np.uint16)
+    mval = (mags.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    blocks = []
+    for e in range(-127, 126):
+        sel = mval < 8.0 * 2.0 ** e
+        if e > -120:
+            sel &= mval >= 2.0 ** (e - 10)
+        xs = mags[sel]
+        xs = np.concatenate([xs, xs | np.uint16(0x8000)])
+        per = 31
+        nrow = -(-xs.size // per)
+        blk = np.zeros((nrow, 32), dtype=np.uint16)
+        blk[:, 0] = synth.bf16_bits(np.float32(4.0 * 2.0 ** e))
+        flat = np.zeros(nrow * per, dtype=np.uint16)
+        flat[: xs.size] = xs
+        blk[:, 1:] = flat.reshape(nrow, per)
+        blocks.append(blk)
+    X = np.tile(np.concatenate(blocks), (1, 2))     # 64 columns: two blocks per row
+    sr = mx.quant_opts(use_sr=True, seed=5, tensor_id=3)
+    kw = dict(use_sr=True, seed=5, tensor_id=3)
+    log("exhaustive SR sweep rows %d" % X.shape[0])
+    check_rowwise(oracle_mod, X, CANON, sr, kw)
+    check_dual(oracle_mod, X[:4096], CANON, sr, sr, kw, kw)
+    check_rowwise(oracle_mod, np.ascontiguousarray(X[:, :31]), CANON, sr, kw)
+
+
 @pytest.mark.parametrize("layout", [CANON, TILED])
 def test_stochastic_rounding(oracle_mod, layout):
     """SR with Philox bytes keyed by (seed, tensor_id, direction, element index), both directions."""
