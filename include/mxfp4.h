@@ -201,7 +201,10 @@ mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t 
  * nearest even; overflow to +-Inf) or MX_F32.  A NaN scale byte yields NaN in
  * the affected outputs (hardware-defined propagation).  M == 0 or N == 0 is a
  * no-op; K == 0 writes zeros.
- * Requires 16-byte aligned pointers and ldc % 8 == 0.
+ * Requires 16-byte aligned pointers and ldc % 8 == 0.  Each operand's tiled
+ * data blob (cdiv(rows,16)*16 * K_pad/2 bytes) must stay below 2 GiB: the
+ * kernels address it with 32-bit buffer offsets (MX_ERR_UNSUPPORTED
+ * otherwise, before anything is launched; split the product instead).
  */
 mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K,
                        const void *A, const void *A_scale,
@@ -269,7 +272,8 @@ mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, m
  * bf16 (RNE) or fp32 output.  a_scale_inv / b_scale_inv: device pointers to
  * the inverse scales (the [1] entries of the quantizer's info), read by the
  * kernel, so no host synchronization.  Arguments and errors otherwise as
- * mx_gemm_a4w4.
+ * mx_gemm_a4w4 (each FP8 operand blob, cdiv(rows,16)*16 * K_pad bytes, must
+ * stay below 2 GiB).
  */
 mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
                         const void *A, const float *a_scale_inv,
@@ -336,8 +340,8 @@ mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx,
  *   C[i][j] = sum_k A[i][k] * B[j][k],  element = fp6(code) * 2^(scale-127)
  * with A in fmt_a and B in fmt_b (MX_FP6_E2M3 or MX_FP6_E3M2, mixed allowed).
  * Arguments, layout (MX_LAYOUT_TILED of the MXFP6 blobs), output and errors
- * as mx_gemm_a4w4; MX_ERR_UNSUPPORTED also for an unknown format, MX_ERR_HIP
- * when an operand blob reaches 2 GiB.  The matrix instruction's sum of 64
+ * as mx_gemm_a4w4; MX_ERR_UNSUPPORTED also for an unknown format and when an
+ * operand blob (cdiv(rows,16)*16 * K_pad*3/4 bytes) reaches 2 GiB.  The matrix instruction's sum of 64
  * E3M2 x E3M2 products keeps fewer bits than fp32 (measured on MI355X: error
  * up to about 2^-14 of the sum of |products|); E2M3 operands sum exactly.
  */

@@ -100,6 +100,19 @@ mx_status validate_out(const void *q, const void *s, const char *name) {
     return MX_SUCCESS;
 }
 
+// The GEMM kernels address each operand blob with 32-bit buffer offsets: a
+// tiled blob of `rows` rows must stay below 2 GiB.  row_bytes is one row's
+// data bytes along the padded K.
+mx_status check_blob_limit(const char *name, const char *which, int64_t rows, int64_t row_bytes) {
+    const int64_t bytes = mx::cdiv(rows, 16) * 16 * row_bytes;
+    if (bytes >= (int64_t(1) << 31))
+        return fail(MX_ERR_UNSUPPORTED,
+                    "%s: operand %s blob is %lld bytes; operand blobs are addressed with 32-bit offsets and must "
+                    "stay below 2 GiB (split the product along M, N or K)",
+                    name, which, (long long)bytes);
+    return MX_SUCCESS;
+}
+
 #define MX_TRY(expr)                     \
     do {                                 \
         mx_status _st = (expr);          \
@@ -298,6 +311,11 @@ mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64
         (want_bias && !aligned16(bias)))
         return fail(MX_ERR_MISALIGNED, "operands, bias and C must be 16-byte aligned");
     if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
+    {
+        const int64_t K_pad = mx::padded(K);
+        MX_TRY(check_blob_limit(name, "A", M, fp6_a ? K_pad / 4 * 3 : K_pad / 2));
+        MX_TRY(check_blob_limit(name, "B", N, fp6_b ? K_pad / 4 * 3 : K_pad / 2));
+    }
     if (M == 0 || N == 0) return MX_SUCCESS;
     MX_TRY(check_device());
     if (fp6_a)
@@ -383,6 +401,8 @@ mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
     if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
         return fail(MX_ERR_MISALIGNED, "operands and C must be 16-byte aligned");
     if (ldc % 8) return fail(MX_ERR_MISALIGNED, "ldc=%lld must be a multiple of 8", (long long)ldc);
+    MX_TRY(check_blob_limit("mx_gemm_f8_tw", "A", M, mx::padded(K)));
+    MX_TRY(check_blob_limit("mx_gemm_f8_tw", "B", N, mx::padded(K)));
     if (M == 0 || N == 0) return MX_SUCCESS;
     MX_TRY(check_device());
     return check_launch(mx::launch_gemm_fp8(M, N, K, static_cast<const uint8_t *>(A), a_scale_inv,

@@ -985,8 +985,9 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
                                ldc, bias);
         return hipGetLastError();
     }
-    // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
-    if (cdiv(M, 16) * K_pad / 2 >= (int64_t(1) << 31) || cdiv(N, 16) * K_pad / 2 >= (int64_t(1) << 31))
+    // buffer offsets are 32-bit: each operand blob (16-row groups of K_pad/2
+    // bytes per row) must stay below 2 GiB
+    if (cdiv(M, 16) * 16 * (K_pad / 2) >= (int64_t(1) << 31) || cdiv(N, 16) * 16 * (K_pad / 2) >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
     const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
     const int tiles = tiles_m * tiles_n;

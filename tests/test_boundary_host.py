@@ -121,6 +121,31 @@ def test_gemm_validation(L):
     assert _status(G, 0, 1, 0, 4, 4, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_SUCCESS
 
 
+def test_gemm_operand_blob_limit(L):
+    """Operand blobs are addressed with 32-bit buffer offsets: a tiled blob of
+    2 GiB or more is refused before anything is launched (here with no GPU:
+    the check runs ahead of the device query).  2^20 rows x K 4096 is exactly
+    2 GiB of E2M1 data (a guard on cdiv(rows, 16) * K_pad / 2 would pass it)."""
+    A16 = 1 << 20
+    T = mx.MX_LAYOUT_TILED
+    G = mx.mx_gemm_a4w4
+    big, K = 1 << 20, 4096
+    assert _status(G, 0, 1, big, 4, K, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    assert "2 GiB" in mx.mx_last_error() and "operand A" in mx.mx_last_error()
+    assert _status(G, 0, 1, 4, big, K, A16, A16, A16, A16, T, 0, A16, big, 0) == mx.MX_ERR_UNSUPPORTED
+    assert "operand B" in mx.mx_last_error()
+    # one 16-row group less is below the limit: validation passes and the call
+    # reaches the device check (which fails here for want of a GPU)
+    assert _status(G, 0, 1, big - 16, 4, K, A16, A16, A16, A16, T, 0, A16, 8, 0) != mx.MX_ERR_UNSUPPORTED
+    # FP6: 3/4 byte per element, FP8: one byte per element
+    F6 = mx.mx_gemm_fp6
+    assert _status(F6, 0, 1, 1 << 19, 4, 8192, mx.MX_FP6_E2M3, A16, A16, mx.MX_FP6_E2M3, A16, A16, T, 0,
+                   A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    F8 = mx.mx_gemm_f8_tw
+    assert _status(F8, 0, 1, 1 << 19, 4, 4096, A16, A16, A16, A16, T, 0, A16, 8, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(F8, 0, 1, (1 << 19) - 16, 4, 4096, A16, A16, A16, A16, T, 0, A16, 8, 0) != mx.MX_ERR_UNSUPPORTED
+
+
 def test_dequantize_validation(L):
     A16 = 1 << 20
     assert _status(mx.mx_dequantize, A16, A16, -1, 4, 0, A16, 4, 0) == mx.MX_ERR_INVALID_ARGUMENT
