@@ -178,6 +178,8 @@ def main():
 
     extras = None if args.no_extras else time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout,
                                                       Xr, Xrs, Wr, Wrs, qb, flops["gemm_fwd"])
+    if extras is not None:
+        extras["other_workloads"] = time_other_workloads(mx, torch, dev, stream, synth)
 
     out = {
         "metric": METRIC,
@@ -324,6 +326,94 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
     out["layout_convert_to_canonical"] = {"ms": round(ms, 5),
                                           "GB/s": round(2.0 * (d_bytes + s_bytes) / (ms * 1e-3) / 1e9, 1),
                                           "what": "X row-wise blob %dx%d, tiled -> canonical" % (tokens, din)}
+    return out
+
+
+def time_other_workloads(mx, torch, dev, stream, synth, reps=20):
+    """The other seeded workloads of the suite, timed like the extras (event pair
+    around `reps` back-to-back launches on the launch stream, inputs resident):
+    the 4600x3072 dual quantize (M not a multiple of 128, outliers, zero
+    blocks), the QKV forward (4608 x 9216 x 3072) and the MLP fc1 step
+    (9216 tokens, 3072 -> 12288: three dual quantizes, fwd, dgrad, wgrad)."""
+    T = mx.MX_LAYOUT_TILED
+    plain = mx.quant_opts()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev)
+
+    def dual_bytes(M, N):
+        d1, s1 = mx.mx_blob_bytes(M, N, T)
+        d2, s2 = mx.mx_blob_bytes(N, M, T)
+        return 2.0 * M * N + d1 + s1 + d2 + s2
+
+    def quant_entry(ms, nbytes, what):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "what": what}
+
+    def gemm_entry(ms, M, N, K, what):
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1), "frac_fp4_peak": round(tf / PEAK_FP4_TFLOPS, 4),
+                "what": what}
+
+    out = {}
+    # dual quantize only, 4600 x 3072
+    x = dev_bf16(synth.dual()["X"])
+    M, N = x.shape
+    qr, qrs = mx.empty_blob(M, N, T, dev); qc, qcs = mx.empty_blob(N, M, T, dev)
+    ms = timed(lambda: mx.mx_quantize_dual(x, M, N, N, plain, plain, T, qr, qrs, qc, qcs, stream))
+    out["dual_4600x3072"] = quant_entry(ms, dual_bytes(M, N), "dual quantize 4600x3072 (outliers, zero blocks)")
+    del x, qr, qrs, qc, qcs
+    # QKV forward
+    d = synth.qkv()
+    a, w = dev_bf16(d["A"]), dev_bf16(d["W"])
+    (M, K), N = a.shape, w.shape[0]
+    ar, ars = mx.empty_blob(M, K, T, dev); wr, wrs = mx.empty_blob(N, K, T, dev)
+    ms_a = timed(lambda: mx.mx_quantize_rowwise(a, M, K, K, plain, T, ar, ars, stream))
+    ms_w = timed(lambda: mx.mx_quantize_rowwise(w, N, K, K, plain, T, wr, wrs, stream))
+    C = torch.empty((M, N), dtype=torch.int16, device=dev)
+    ms = timed(lambda: mx.mx_gemm_a4w4(0, 1, M, N, K, ar, ars, wr, wrs, T, mx.MX_BF16, C, N, stream))
+    rb = lambda r, k: 2.0 * r * k + sum(mx.mx_blob_bytes(r, k, T))
+    out["qkv_quant_A_rowwise"] = quant_entry(ms_a, rb(M, K), "A 4608x3072 row-wise")
+    out["qkv_quant_W_rowwise"] = quant_entry(ms_w, rb(N, K), "W 9216x3072 row-wise")
+    out["qkv_gemm_fwd"] = gemm_entry(ms, M, N, K, "QKV forward 4608 x 9216 x 3072")
+    del a, w, ar, ars, wr, wrs, C, d
+    # MLP fc1 training step
+    d = synth.fc1()
+    X, W, G = dev_bf16(d["X"]), dev_bf16(d["W"]), dev_bf16(d["dY"])
+    del d
+    (Tk, din), dout = X.shape, W.shape[0]
+    blobs = {}
+    tot = 0.0
+    for name, t in (("X", X), ("W", W), ("dY", G)):
+        M, N = t.shape
+        b = mx.empty_blob(M, N, T, dev) + mx.empty_blob(N, M, T, dev)
+        ms = timed(lambda: mx.mx_quantize_dual(t, M, N, N, plain, plain, T, *b, stream))
+        out["fc1_quant_" + name] = quant_entry(ms, dual_bytes(M, N), "%s %dx%d dual" % (name, M, N))
+        blobs[name] = b
+        tot += ms
+    Y = torch.empty((Tk, dout), dtype=torch.int16, device=dev)
+    dX = torch.empty((Tk, din), dtype=torch.int16, device=dev)
+    dW = torch.empty((dout, din), dtype=torch.int16, device=dev)
+    xb, wb, gb = blobs["X"], blobs["W"], blobs["dY"]
+    for name, (M, N, K, A_, As_, B_, Bs_, C_, ldc) in (
+            ("fwd", (Tk, dout, din, xb[0], xb[1], wb[0], wb[1], Y, dout)),
+            ("dgrad", (Tk, din, dout, gb[0], gb[1], wb[2], wb[3], dX, din)),
+            ("wgrad", (dout, din, Tk, gb[2], gb[3], xb[2], xb[3], dW, din))):
+        ms = timed(lambda: mx.mx_gemm_a4w4(0, 1, M, N, K, A_, As_, B_, Bs_, T, mx.MX_BF16, C_, ldc, stream))
+        out["fc1_gemm_" + name] = gemm_entry(ms, M, N, K, "fc1 %s %d x %d x %d" % (name, M, N, K))
+        tot += ms
+    out["fc1_step_sum_ms"] = round(tot, 5)
     return out
 
 
