@@ -2,10 +2,11 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
 ``libmxfp4.so``.  Functions carry the C ABI's names (``include/mxfp4.h``) and
-take device pointers as ints or torch tensors (their ``data_ptr()``), sizes as
-ints, and a stream as a ``torch.cuda.Stream``, an int handle, or None (torch's
-current stream).  A non-zero status raises ``MXError``; if the shared library
-is missing, the first call raises: there is no fallback.
+take device pointers as ints or GPU torch tensors (their ``data_ptr()``; host
+tensors and arrays are refused before any call), sizes as ints, and a stream
+as a ``torch.cuda.Stream``, an int handle, or None (torch's current stream).
+A non-zero status raises ``MXError``; if the shared library is missing, the
+first call raises: there is no fallback.
 
 Build the library with ``python -m mxfp4_precision_amd.build``.
 """
@@ -91,10 +92,9 @@ def lib() -> ctypes.CDLL:
     L.mx_status_string.restype = ctypes.c_char_p
     L.mx_last_error.argtypes = []
     L.mx_last_error.restype = ctypes.c_char_p
-    for name in ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm_a4w4", "mx_gemm_a4w4_bias",
-                 "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_fp8_blob_bytes",
-                 "mx_quantize_fp8_tw", "mx_gemm_f8_tw"):
-        getattr(L, name).restype = i32
+    for name in EXPORTED:
+        if name not in ("mx_device_supported", "mx_status_string", "mx_last_error"):
+            getattr(L, name).restype = i32     # mx_status
     _lib = L
     return L
 
@@ -111,16 +111,31 @@ def _check(st: int):
         raise MXError(st, lib().mx_last_error().decode())
 
 
-def _ptr(p) -> Optional[int]:
-    if p is None:
-        return None
-    if isinstance(p, int):
+def _dptr(p) -> Optional[int]:
+    """A device-pointer argument.  Ints pass through (the caller vouches for
+    them); a tensor must live on a GPU.  Host tensors and arrays are refused
+    here: a kernel that dereferences a host address faults the device."""
+    if p is None or isinstance(p, int):
         return p
     if hasattr(p, "data_ptr"):
+        if not getattr(p, "is_cuda", False):
+            raise TypeError("a device pointer is required, got a tensor on %s" % p.device)
         return p.data_ptr()
-    if hasattr(p, "ctypes"):          # numpy array (host pointer)
+    raise TypeError("a device pointer is required, got %r (host arrays are not accepted)" % type(p))
+
+
+def _hptr(p) -> Optional[int]:
+    """A host-pointer argument (the host layout converter): numpy arrays, CPU
+    tensors or ints; device tensors are refused."""
+    if p is None or isinstance(p, int):
+        return p
+    if hasattr(p, "data_ptr"):
+        if getattr(p, "is_cuda", False):
+            raise TypeError("a host pointer is required, got a tensor on %s" % p.device)
+        return p.data_ptr()
+    if hasattr(p, "ctypes"):          # numpy array
         return p.ctypes.data
-    raise TypeError("expected a pointer, tensor or array, got %r" % type(p))
+    raise TypeError("expected a host array, tensor or int, got %r" % type(p))
 
 
 def _stream(s) -> Optional[int]:
@@ -145,20 +160,21 @@ def mx_blob_bytes(rows: int, length: int, layout: int) -> Tuple[int, int]:
 
 
 def mx_quantize_rowwise(x, M: int, N: int, ldx: int, opts, layout: int, q, s, stream=None):
-    _check(lib().mx_quantize_rowwise(_ptr(x), M, N, ldx, _opts(opts), layout, _ptr(q), _ptr(s),
+    _check(lib().mx_quantize_rowwise(_dptr(x), M, N, ldx, _opts(opts), layout, _dptr(q), _dptr(s),
                                      _stream(stream)))
 
 
 def mx_quantize_dual(x, M: int, N: int, ldx: int, row_opts, col_opts, layout: int,
                      q_row, s_row, q_col, s_col, stream=None):
-    _check(lib().mx_quantize_dual(_ptr(x), M, N, ldx, _opts(row_opts), _opts(col_opts), layout,
-                                  _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+    _check(lib().mx_quantize_dual(_dptr(x), M, N, ldx, _opts(row_opts), _opts(col_opts), layout,
+                                  _dptr(q_row), _dptr(s_row), _dptr(q_col), _dptr(s_col), _stream(stream)))
 
 
 def mx_quantize_dual_mul(x, g, M: int, N: int, ldx: int, ldg: int, row_opts, col_opts, layout: int,
                          q_row, s_row, q_col=None, s_col=None, stream=None):
-    _check(lib().mx_quantize_dual_mul(_ptr(x), _ptr(g), M, N, ldx, ldg, _opts(row_opts), _opts(col_opts), layout,
-                                      _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+    _check(lib().mx_quantize_dual_mul(_dptr(x), _dptr(g), M, N, ldx, ldg, _opts(row_opts), _opts(col_opts),
+                                      layout, _dptr(q_row), _dptr(s_row), _dptr(q_col), _dptr(s_col),
+                                      _stream(stream)))
 
 
 def mx_fp6_blob_bytes(rows: int, length: int, layout: int) -> Tuple[int, int]:
@@ -169,26 +185,26 @@ def mx_fp6_blob_bytes(rows: int, length: int, layout: int) -> Tuple[int, int]:
 
 def mx_quantize_fp6(x, M: int, N: int, ldx: int, row_fmt: int, row_opts, col_fmt: int, col_opts,
                     layout: int, q_row, s_row, q_col=None, s_col=None, stream=None):
-    _check(lib().mx_quantize_fp6(_ptr(x), M, N, ldx, row_fmt, _opts(row_opts), col_fmt, _opts(col_opts), layout,
-                                 _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+    _check(lib().mx_quantize_fp6(_dptr(x), M, N, ldx, row_fmt, _opts(row_opts), col_fmt, _opts(col_opts),
+                                 layout, _dptr(q_row), _dptr(s_row), _dptr(q_col), _dptr(s_col), _stream(stream)))
 
 
 def mx_gemm_fp6(transA: int, transB: int, M: int, N: int, K: int, fmt_a: int, A, A_scale, fmt_b: int, B, B_scale,
                 layout: int, out_dtype: int, C, ldc: int, stream=None):
-    _check(lib().mx_gemm_fp6(transA, transB, M, N, K, fmt_a, _ptr(A), _ptr(A_scale), fmt_b, _ptr(B), _ptr(B_scale),
-                             layout, out_dtype, _ptr(C), ldc, _stream(stream)))
+    _check(lib().mx_gemm_fp6(transA, transB, M, N, K, fmt_a, _dptr(A), _dptr(A_scale), fmt_b, _dptr(B),
+                             _dptr(B_scale), layout, out_dtype, _dptr(C), ldc, _stream(stream)))
 
 
 def mx_gemm_a4w4(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B, B_scale,
                  layout: int, out_dtype: int, C, ldc: int, stream=None):
-    _check(lib().mx_gemm_a4w4(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
-                              layout, out_dtype, _ptr(C), ldc, _stream(stream)))
+    _check(lib().mx_gemm_a4w4(transA, transB, M, N, K, _dptr(A), _dptr(A_scale), _dptr(B), _dptr(B_scale),
+                              layout, out_dtype, _dptr(C), ldc, _stream(stream)))
 
 
 def mx_gemm_a4w4_bias(transA: int, transB: int, M: int, N: int, K: int, A, A_scale, B, B_scale,
                       layout: int, out_dtype: int, bias, C, ldc: int, stream=None):
-    _check(lib().mx_gemm_a4w4_bias(transA, transB, M, N, K, _ptr(A), _ptr(A_scale), _ptr(B), _ptr(B_scale),
-                                   layout, out_dtype, _ptr(bias), _ptr(C), ldc, _stream(stream)))
+    _check(lib().mx_gemm_a4w4_bias(transA, transB, M, N, K, _dptr(A), _dptr(A_scale), _dptr(B), _dptr(B_scale),
+                                   layout, out_dtype, _dptr(bias), _dptr(C), ldc, _stream(stream)))
 
 
 def mx_fp8_blob_bytes(rows: int, length: int, layout: int) -> int:
@@ -198,28 +214,28 @@ def mx_fp8_blob_bytes(rows: int, length: int, layout: int) -> int:
 
 
 def mx_quantize_fp8_tw(x, M: int, N: int, ldx: int, layout: int, q_row, q_col, info, stream=None):
-    _check(lib().mx_quantize_fp8_tw(_ptr(x), M, N, ldx, layout, _ptr(q_row), _ptr(q_col), _ptr(info),
+    _check(lib().mx_quantize_fp8_tw(_dptr(x), M, N, ldx, layout, _dptr(q_row), _dptr(q_col), _dptr(info),
                                     _stream(stream)))
 
 
 def mx_gemm_f8_tw(transA: int, transB: int, M: int, N: int, K: int, A, a_scale_inv, B, b_scale_inv,
                   layout: int, out_dtype: int, C, ldc: int, stream=None):
-    _check(lib().mx_gemm_f8_tw(transA, transB, M, N, K, _ptr(A), _ptr(a_scale_inv), _ptr(B), _ptr(b_scale_inv),
-                               layout, out_dtype, _ptr(C), ldc, _stream(stream)))
+    _check(lib().mx_gemm_f8_tw(transA, transB, M, N, K, _dptr(A), _dptr(a_scale_inv), _dptr(B),
+                               _dptr(b_scale_inv), layout, out_dtype, _dptr(C), ldc, _stream(stream)))
 
 
 def mx_layout_convert(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst, stream=None):
-    _check(lib().mx_layout_convert(to_tiled, rows, length, _ptr(q_src), _ptr(s_src), _ptr(q_dst), _ptr(s_dst),
-                                   _stream(stream)))
+    _check(lib().mx_layout_convert(to_tiled, rows, length, _dptr(q_src), _dptr(s_src), _dptr(q_dst),
+                                   _dptr(s_dst), _stream(stream)))
 
 
 def mx_layout_convert_host(to_tiled: int, rows: int, length: int, q_src, s_src, q_dst, s_dst):
-    _check(lib().mx_layout_convert_host(to_tiled, rows, length, _ptr(q_src), _ptr(s_src),
-                                        _ptr(q_dst), _ptr(s_dst)))
+    _check(lib().mx_layout_convert_host(to_tiled, rows, length, _hptr(q_src), _hptr(s_src),
+                                        _hptr(q_dst), _hptr(s_dst)))
 
 
 def mx_dequantize(q, s, rows: int, length: int, layout: int, out_f32, ldo: int, stream=None):
-    _check(lib().mx_dequantize(_ptr(q), _ptr(s), rows, length, layout, _ptr(out_f32), ldo,
+    _check(lib().mx_dequantize(_dptr(q), _dptr(s), rows, length, layout, _dptr(out_f32), ldo,
                                _stream(stream)))
 
 

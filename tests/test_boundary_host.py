@@ -146,6 +146,25 @@ def test_gemm_operand_blob_limit(L):
     assert _status(F8, 0, 1, (1 << 19) - 16, 4, 4096, A16, A16, A16, A16, T, 0, A16, 8, 0) != mx.MX_ERR_UNSUPPORTED
 
 
+def test_host_objects_refused_as_device_pointers(L):
+    """Device entry points refuse CPU tensors and numpy arrays before calling
+    into the library (a kernel given a host address would fault the GPU); the
+    host converter takes them."""
+    import numpy as np
+    torch = pytest.importorskip("torch")
+    host_t = torch.zeros(64, dtype=torch.uint8)
+    host_a = np.zeros(64, dtype=np.uint8)
+    T = mx.MX_LAYOUT_TILED
+    for bad in (host_t, host_a):
+        with pytest.raises(TypeError, match="device pointer"):
+            mx.mx_gemm_a4w4(0, 1, 4, 4, 4, bad, bad, bad, bad, T, 0, bad, 8, 0)
+        with pytest.raises(TypeError, match="device pointer"):
+            mx.mx_quantize_dual(bad, 4, 8, 8, None, None, T, bad, bad, bad, bad, 0)
+    # ints pass through untouched (validation then answers for them)
+    with pytest.raises(mx.MXError):
+        mx.mx_gemm_a4w4(0, 0, 4, 4, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, T, 0, 1 << 20, 8, 0)
+
+
 def test_dequantize_validation(L):
     A16 = 1 << 20
     assert _status(mx.mx_dequantize, A16, A16, -1, 4, 0, A16, 4, 0) == mx.MX_ERR_INVALID_ARGUMENT
