@@ -176,10 +176,31 @@ def main():
     # Dual quantizer roofline on the largest launch (X: 18432 x 12288).
     qx_gbs = qb["quant_X"] / (per["quant_X"] * 1e-3) / 1e9
 
+    def enqueue_us(fn, n=200):
+        """Host time per call (Python binding + C-ABI validation + launch), no sync per call."""
+        torch.cuda.synchronize()
+        t = []
+        for i in range(n):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+            if i % 20 == 19:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return round(float(np.median(t)) * 1e6, 2)
+
+    host_enqueue = None if args.no_extras else {
+        "mx_quantize_dual_us": enqueue_us(lambda: mx.mx_quantize_dual(X, tokens, din, din, o_plain, o_plain, T, Xr,
+                                                                      Xrs, Xc, Xcs, stream)),
+        "mx_gemm_a4w4_us": enqueue_us(lambda: mx.mx_gemm_a4w4(0, 1, tokens, dout, din, Xr, Xrs, Wr, Wrs, T,
+                                                              mx.MX_BF16, Y, dout, stream)),
+        "what": "median host time per call through the Python binding (ctypes) and the C ABI, no "
+                "synchronization per call"}
     extras = None if args.no_extras else time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout,
                                                       Xr, Xrs, Wr, Wrs, qb, flops["gemm_fwd"])
     if extras is not None:
         extras["other_workloads"] = time_other_workloads(mx, torch, dev, stream, synth)
+        extras["host_enqueue"] = host_enqueue
 
     out = {
         "metric": METRIC,
@@ -330,11 +351,13 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
 
 
 def time_other_workloads(mx, torch, dev, stream, synth, reps=20):
-    """The other seeded workloads of the suite, timed like the extras (event pair
-    around `reps` back-to-back launches on the launch stream, inputs resident):
-    the 4600x3072 dual quantize (M not a multiple of 128, outliers, zero
-    blocks), the QKV forward (4608 x 9216 x 3072) and the MLP fc1 step
-    (9216 tokens, 3072 -> 12288: three dual quantizes, fwd, dgrad, wgrad)."""
+    """The other seeded workloads of the suite: the 4600x3072 dual quantize (M
+    not a multiple of 128, outliers, zero blocks) and the QKV forward (4608 x
+    9216 x 3072, its two row-wise quantizes and the GEMM), each over rotating
+    buffer sets larger than twice the Infinity Cache, median and minimum of 30
+    batches of 20 launches; the MLP fc1 step (9216 tokens, 3072 -> 12288: three
+    dual quantizes, fwd, dgrad, wgrad; tensors of 56-226 MB), timed like the
+    extras (event pair around `reps` back-to-back launches, inputs resident)."""
     T = mx.MX_LAYOUT_TILED
     plain = mx.quant_opts()
 
@@ -367,27 +390,69 @@ def time_other_workloads(mx, torch, dev, stream, synth, reps=20):
                 "what": what}
 
     out = {}
+    # The two small workloads move 43 MB and ~110 MB per call, less than the
+    # 256 MB Infinity Cache, so they cycle through enough buffer sets (inputs
+    # and outputs) to exceed twice its size and report the median and the
+    # minimum over batches of launches.
+    MALL = 256 << 20
+
+    def batch_stats(fn_i, nsets, batches, per):
+        for i in range(2 * nsets):
+            fn_i(i % nsets)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t = []
+        for b in range(batches):
+            ev[0].record(stream)
+            for j in range(per):
+                fn_i((b * per + j) % nsets)
+            ev[1].record(stream)
+            ev[1].synchronize()
+            t.append(ev[0].elapsed_time(ev[1]) / per)
+        return float(np.median(t)), float(np.min(t))
+
+    def with_stats(entry, med, mn, nsets):
+        entry["min_ms"] = round(mn, 5)
+        entry["buffer_sets"] = nsets
+        entry["timing"] = "median of 30 batches of 20 launches, rotating buffer sets"
+        return entry
+
     # dual quantize only, 4600 x 3072
-    x = dev_bf16(synth.dual()["X"])
-    M, N = x.shape
-    qr, qrs = mx.empty_blob(M, N, T, dev); qc, qcs = mx.empty_blob(N, M, T, dev)
-    ms = timed(lambda: mx.mx_quantize_dual(x, M, N, N, plain, plain, T, qr, qrs, qc, qcs, stream))
-    out["dual_4600x3072"] = quant_entry(ms, dual_bytes(M, N), "dual quantize 4600x3072 (outliers, zero blocks)")
-    del x, qr, qrs, qc, qcs
-    # QKV forward
+    x0 = dev_bf16(synth.dual()["X"])
+    M, N = x0.shape
+    set_bytes = dual_bytes(M, N)
+    nsets = max(2, -(-2 * MALL // int(set_bytes)) + 1)
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    outs = [mx.empty_blob(M, N, T, dev) + mx.empty_blob(N, M, T, dev) for _ in range(nsets)]
+    med, mn = batch_stats(lambda i: mx.mx_quantize_dual(xs[i], M, N, N, plain, plain, T, *outs[i], stream),
+                          nsets, 30, 20)
+    out["dual_4600x3072"] = with_stats(quant_entry(med, set_bytes, "dual quantize 4600x3072 (outliers, zero blocks)"),
+                                       med, mn, nsets)
+    del x0, xs, outs
+    # QKV forward: both row-wise quantizes and the GEMM, each over rotating sets
     d = synth.qkv()
-    a, w = dev_bf16(d["A"]), dev_bf16(d["W"])
-    (M, K), N = a.shape, w.shape[0]
-    ar, ars = mx.empty_blob(M, K, T, dev); wr, wrs = mx.empty_blob(N, K, T, dev)
-    ms_a = timed(lambda: mx.mx_quantize_rowwise(a, M, K, K, plain, T, ar, ars, stream))
-    ms_w = timed(lambda: mx.mx_quantize_rowwise(w, N, K, K, plain, T, wr, wrs, stream))
-    C = torch.empty((M, N), dtype=torch.int16, device=dev)
-    ms = timed(lambda: mx.mx_gemm_a4w4(0, 1, M, N, K, ar, ars, wr, wrs, T, mx.MX_BF16, C, N, stream))
+    a0, w0 = dev_bf16(d["A"]), dev_bf16(d["W"])
+    (M, K), N = a0.shape, w0.shape[0]
     rb = lambda r, k: 2.0 * r * k + sum(mx.mx_blob_bytes(r, k, T))
-    out["qkv_quant_A_rowwise"] = quant_entry(ms_a, rb(M, K), "A 4608x3072 row-wise")
-    out["qkv_quant_W_rowwise"] = quant_entry(ms_w, rb(N, K), "W 9216x3072 row-wise")
-    out["qkv_gemm_fwd"] = gemm_entry(ms, M, N, K, "QKV forward 4608 x 9216 x 3072")
-    del a, w, ar, ars, wr, wrs, C, d
+    na = max(2, -(-2 * MALL // int(rb(M, K))) + 1)
+    nw = max(2, -(-2 * MALL // int(rb(N, K))) + 1)
+    a_s = [a0] + [a0.clone() for _ in range(na - 1)]
+    w_s = [w0] + [w0.clone() for _ in range(nw - 1)]
+    ab = [mx.empty_blob(M, K, T, dev) for _ in range(na)]
+    wb = [mx.empty_blob(N, K, T, dev) for _ in range(nw)]
+    med, mn = batch_stats(lambda i: mx.mx_quantize_rowwise(a_s[i], M, K, K, plain, T, *ab[i], stream), na, 30, 20)
+    out["qkv_quant_A_rowwise"] = with_stats(quant_entry(med, rb(M, K), "A 4608x3072 row-wise"), med, mn, na)
+    med, mn = batch_stats(lambda i: mx.mx_quantize_rowwise(w_s[i], N, K, K, plain, T, *wb[i], stream), nw, 30, 20)
+    out["qkv_quant_W_rowwise"] = with_stats(quant_entry(med, rb(N, K), "W 9216x3072 row-wise"), med, mn, nw)
+    # GEMM sets: operand blobs + C; the blobs are copies of the quantized ones
+    g_set = sum(t.numel() for t in ab[0] + wb[0]) + 2.0 * M * N
+    ng = max(2, -(-2 * MALL // int(g_set)) + 1)
+    ga = [ab[0]] + [tuple(t.clone() for t in ab[0]) for _ in range(ng - 1)]
+    gw = [wb[0]] + [tuple(t.clone() for t in wb[0]) for _ in range(ng - 1)]
+    Cs = [torch.empty((M, N), dtype=torch.int16, device=dev) for _ in range(ng)]
+    med, mn = batch_stats(lambda i: mx.mx_gemm_a4w4(0, 1, M, N, K, ga[i][0], ga[i][1], gw[i][0], gw[i][1], T,
+                                                    mx.MX_BF16, Cs[i], N, stream), ng, 30, 20)
+    out["qkv_gemm_fwd"] = with_stats(gemm_entry(med, M, N, K, "QKV forward 4608 x 9216 x 3072"), med, mn, ng)
+    del a0, w0, a_s, w_s, ab, wb, ga, gw, Cs, d
     # MLP fc1 training step
     d = synth.fc1()
     X, W, G = dev_bf16(d["X"]), dev_bf16(d["W"]), dev_bf16(d["dY"])
@@ -458,11 +523,83 @@ def cpu_baseline(data, ct, din, dout):
     dt = time.perf_counter() - t0
     fl = 2.0 * ct * din * dout * 3
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": "fc2 step on a %d-token slice (X %dx%d, W %dx%d, dY %dx%d): oracle dual "
-                      "quantize of all three + the slice's fwd, dgrad and wgrad GEMMs in fp64"
-                      % (ct, ct, din, dout, din, ct, dout)}
+    out = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 2),
+           "sample": "fc2 step on a %d-token slice (X %dx%d, W %dx%d, dY %dx%d): oracle dual "
+                     "quantize of all three + the slice's fwd, dgrad and wgrad GEMMs in fp64"
+                     % (ct, ct, din, dout, din, ct, dout)}
+    out.update(host_description())
+    out["components"] = cpu_components(data, ct, 16)
+    return out
+
+
+def host_description():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "cpus_available": avail}
+
+
+def oracle_components(x, w, rows):
+    """Oracle rates on two pieces of the step, comparable across thread counts:
+    the dual quantize of x (bytes read + both blobs written) and the forward
+    GEMM over its first `rows` token rows (against all of W)."""
+    import oracle
+    M, N = x.shape
+    t0 = time.perf_counter()
+    xr = oracle.quantize(x, 0)
+    xc = oracle.quantize(x, 1)
+    dq = time.perf_counter() - t0
+    qbytes = 2.0 * M * N + sum(a.nbytes for a in xr + xc)
+    wr = oracle.quantize(w, 0, use_2d=True, tensor_id=1)
+    t0 = time.perf_counter()
+    oracle.gemm_rows(xr[0], xr[1], wr[0], wr[1], M, w.shape[0], N, 0, rows)
+    dg = time.perf_counter() - t0
+    return {"quantize_GB/s": round(qbytes / dq / 1e9, 4),
+            "gemm_GFLOP/s": round(2.0 * rows * w.shape[0] * N / dg / 1e9, 4)}
+
+
+# oracle_components in a child process with one OpenMP thread (an OpenMP
+# runtime fixes its thread count when it starts)
+_ONE_CORE = r"""
+import json, sys
+import numpy as np
+sys.path.insert(0, sys.argv[1])
+import bench
+d = np.load(sys.argv[2])
+print(json.dumps(bench.oracle_components(d["x"], d["w"], int(sys.argv[3]))))
+"""
+
+
+def cpu_components(data, ct, rows):
+    """oracle_components on all cores (this process) and on one core (a child)."""
+    import subprocess
+    import tempfile
+    x = np.ascontiguousarray(data["X"][:ct])
+    w = data["W"]
+    out = {"all_cores": oracle_components(x, w, rows)}
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "slice.npz")
+        np.savez(path, x=x, w=w)
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, "-c", _ONE_CORE, ROOT, path, str(rows)], env=env, capture_output=True,
+                           text=True, timeout=600)
+    if r.returncode == 0:
+        out["one_core"] = json.loads(r.stdout.strip().splitlines()[-1])
+    else:
+        out["one_core_error"] = r.stderr.strip().splitlines()[-1] if r.stderr.strip() else "exit %d" % r.returncode
+    out["what"] = ("oracle dual quantize of X[:%d] (GB/s of bytes read and written) and its forward GEMM over "
+                   "%d token rows (GFLOP/s), on all cores and with OMP_NUM_THREADS=1" % (ct, rows))
+    return out
 
 
 if __name__ == "__main__":
