@@ -189,6 +189,44 @@ def main():
         torch.cuda.synchronize()
         return round(float(np.median(t)) * 1e6, 2)
 
+    def measured_ceilings():
+        """What this chip sustains with no algorithm around it: the FP4 matrix
+        instruction's rate on the step's own X codes and on uniform random codes
+        (mx_measure_mfma_fp4), and a plain 1 GiB device copy."""
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        iters, reps = 20000, 5
+        out_buf = torch.empty((cus * 512,), dtype=torch.float32, device=dev)
+        gen = torch.Generator(device="cpu").manual_seed(11)
+        patterns = {"x_codes": Xr[:16384],
+                    "uniform_codes": torch.randint(0, 256, (16384,), generator=gen, dtype=torch.uint8).to(dev)}
+        res = {}
+        for name, ops in patterns.items():
+            mx.mx_measure_mfma_fp4(ops, cus, iters, out_buf, stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                mx.mx_measure_mfma_fp4(ops, cus, iters, out_buf, stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / reps
+            res["mfma_fp4_%s_TFLOP/s" % name] = round(cus * 64.0 * iters * 131072 / (ms * 1e-3) / 1e12, 1)
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res["copy_1GiB_GB/s"] = round(2.0 * (1 << 30) / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9, 1)
+        del src, dst
+        res["what"] = ("MFMA-only loop (8 waves per CU, 8 accumulator chains, operands switching every instruction) "
+                       "on the fc2 X blob's first 16 KB of E2M1 codes and on uniform random codes; torch device copy "
+                       "of 1 GiB (read + write bytes)")
+        return res
+
+    ceilings = None if args.no_extras else measured_ceilings()
     host_enqueue = None if args.no_extras else {
         "mx_quantize_dual_us": enqueue_us(lambda: mx.mx_quantize_dual(X, tokens, din, din, o_plain, o_plain, T, Xr,
                                                                       Xrs, Xc, Xcs, stream)),
@@ -234,6 +272,10 @@ def main():
     if extras is not None:
         out["extras"] = extras
 
+    if ceilings is not None:
+        ceilings["gemm_frac_of_x_codes_rate"] = round(gemm_achieved / ceilings["mfma_fp4_x_codes_TFLOP/s"], 4)
+        ceilings["quant_X_frac_of_copy"] = round(qx_gbs / ceilings["copy_1GiB_GB/s"], 4)
+        out["measured_ceilings"] = ceilings
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(data, args.cpu_tokens, din, dout)
     print(json.dumps(out), flush=True)

@@ -439,6 +439,18 @@ mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t leng
                         "mx_dequantize");
 }
 
+mx_status mx_measure_mfma_fp4(const void *operands, int workgroups, int64_t iters, float *out, void *stream) {
+    if (!operands || !out) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
+    if (workgroups < 1 || iters < 1)
+        return fail(MX_ERR_INVALID_ARGUMENT, "workgroups=%d and iters=%lld must be >= 1", workgroups,
+                    (long long)iters);
+    if (!aligned16(operands) || !aligned16(out))
+        return fail(MX_ERR_MISALIGNED, "operands and out must be 16-byte aligned");
+    MX_TRY(check_device());
+    return check_launch(mx::launch_measure_mfma_fp4(operands, workgroups, iters, out, static_cast<hipStream_t>(stream)),
+                        "mx_measure_mfma_fp4");
+}
+
 int mx_device_supported(int device) {
     if (device < 0 || device >= kMaxDevices) return 0;
     return query_supported(device);

@@ -165,6 +165,15 @@ def test_host_objects_refused_as_device_pointers(L):
         mx.mx_gemm_a4w4(0, 0, 4, 4, 4, 1 << 20, 1 << 20, 1 << 20, 1 << 20, T, 0, 1 << 20, 8, 0)
 
 
+def test_measure_mfma_validation(L):
+    A16 = 1 << 20
+    M = mx.mx_measure_mfma_fp4
+    assert _status(M, 0, 4, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, A16, 0, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, A16, 4, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, A16 + 4, 4, 10, A16, 0) == mx.MX_ERR_MISALIGNED
+
+
 def test_dequantize_validation(L):
     A16 = 1 << 20
     assert _status(mx.mx_dequantize, A16, A16, -1, 4, 0, A16, 4, 0) == mx.MX_ERR_INVALID_ARGUMENT
