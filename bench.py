@@ -226,7 +226,81 @@ def main():
                        "of 1 GiB (read + write bytes)")
         return res
 
+    def telemetry(nsteps=60):
+        """Power cap, memory clock, the clock table with its current level, and the
+        power drawn (hwmon power1_input sampled every ~2 ms by a host thread) while
+        the step runs back to back and while the MFMA-only loop runs, from the
+        card's sysfs files; empty if they are not readable."""
+        import glob
+        import threading
+        cards = [d for d in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(d + "/pp_dpm_sclk")]
+        if len(cards) != 1:
+            return {"note": "%d cards with clock tables visible; not sampled" % len(cards)}
+        dev_dir = cards[0]
+        hw = sorted(glob.glob(dev_dir + "/hwmon/hwmon*"))
+
+        def read(path):
+            try:
+                return open(path).read().strip()
+            except OSError:
+                return None
+
+        res = {}
+        cap = read(hw[0] + "/power1_cap") if hw else None
+        if cap:
+            res["power_cap_W"] = round(int(cap) / 1e6, 1)
+        mclk = [l for l in (read(dev_dir + "/pp_dpm_mclk") or "").splitlines() if l.endswith("*")]
+        if mclk:
+            res["mclk"] = mclk[0].split(":", 1)[1].strip(" *")
+        res["sclk_levels"] = ", ".join(l.strip() for l in (read(dev_dir + "/pp_dpm_sclk") or "").splitlines())
+        if not hw or read(hw[0] + "/power1_input") is None:
+            return res
+        def sampled(run):
+            samples, sclk, stop = [], [], threading.Event()
+
+            def sampler():
+                while not stop.is_set():
+                    v = read(hw[0] + "/power1_input")
+                    if v:
+                        samples.append(int(v) / 1e6)
+                    cur = [l for l in (read(dev_dir + "/pp_dpm_sclk") or "").splitlines() if l.endswith("*")]
+                    if cur:
+                        try:
+                            sclk.append(int(cur[0].split(":", 1)[1].strip(" *").lower().replace("mhz", "")))
+                        except ValueError:
+                            pass
+                    time.sleep(0.002)
+            run()
+            torch.cuda.synchronize()
+            th = threading.Thread(target=sampler)
+            th.start()
+            run()
+            torch.cuda.synchronize()
+            stop.set()
+            th.join()
+            if not samples:
+                return None
+            return {"power_W_mean": round(float(np.mean(samples)), 1), "power_W_max": round(float(np.max(samples)), 1),
+                    "sclk_MHz_min_max": [min(sclk), max(sclk)] if sclk else None, "samples": len(samples)}
+
+        def steps():
+            for _ in range(nsteps):
+                step()
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        ops = torch.randint(0, 256, (16384,), generator=torch.Generator(device="cpu").manual_seed(11),
+                            dtype=torch.uint8).to(dev)
+        obuf = torch.empty((cus * 512,), dtype=torch.float32, device=dev)
+
+        def mfma_loop():
+            for _ in range(10):
+                mx.mx_measure_mfma_fp4(ops, cus, 20000, obuf, stream)
+        res["during_steps"] = sampled(steps)
+        res["during_mfma_only_loop"] = sampled(mfma_loop)
+        return res
+
     ceilings = None if args.no_extras else measured_ceilings()
+    if ceilings is not None:
+        ceilings["telemetry"] = telemetry()
     host_enqueue = None if args.no_extras else {
         "mx_quantize_dual_us": enqueue_us(lambda: mx.mx_quantize_dual(X, tokens, din, din, o_plain, o_plain, T, Xr,
                                                                       Xrs, Xc, Xcs, stream)),
