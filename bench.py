@@ -192,27 +192,15 @@ def main():
     def measured_ceilings():
         """What this chip sustains with no algorithm around it: the FP4 matrix
         instruction's rate on the step's own X codes and on uniform random codes
-        (mx_measure_mfma_fp4), and a plain 1 GiB device copy."""
-        cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        iters, reps = 20000, 5
-        out_buf = torch.empty((cus * 512,), dtype=torch.float32, device=dev)
+        (mx_measure_mfma, E2M1 x E2M1), and a plain 1 GiB device copy."""
         gen = torch.Generator(device="cpu").manual_seed(11)
-        patterns = {"x_codes": Xr[:16384],
-                    "uniform_codes": torch.randint(0, 256, (16384,), generator=gen, dtype=torch.uint8).to(dev)}
-        res = {}
-        for name, ops in patterns.items():
-            mx.mx_measure_mfma_fp4(ops, cus, iters, out_buf, stream)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            for _ in range(reps):
-                mx.mx_measure_mfma_fp4(ops, cus, iters, out_buf, stream)
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            ms = ev[0].elapsed_time(ev[1]) / reps
-            res["mfma_fp4_%s_TFLOP/s" % name] = round(cus * 64.0 * iters * 131072 / (ms * 1e-3) / 1e12, 1)
+        uniform = torch.randint(0, 256, (16384,), generator=gen, dtype=torch.uint8).to(dev)
+        res = {"mfma_fp4_x_codes_TFLOP/s": mfma_rate(mx, torch, dev, stream, 4, 4, Xr),
+               "mfma_fp4_uniform_codes_TFLOP/s": mfma_rate(mx, torch, dev, stream, 4, 4, uniform)}
         src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
+        reps = 5
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
         for _ in range(reps):
@@ -221,7 +209,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_1GiB_GB/s"] = round(2.0 * (1 << 30) / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9, 1)
         del src, dst
-        res["what"] = ("MFMA-only loop (8 waves per CU, 8 accumulator chains, operands switching every instruction) "
+        res["what"] = ("MFMA-only loop (8 waves per CU, 4 accumulator chains, operands switching every instruction) "
                        "on the fc2 X blob's first 16 KB of E2M1 codes and on uniform random codes; torch device copy "
                        "of 1 GiB (read + write bytes)")
         return res
@@ -293,7 +281,7 @@ def main():
 
         def mfma_loop():
             for _ in range(10):
-                mx.mx_measure_mfma_fp4(ops, cus, 20000, obuf, stream)
+                mx.mx_measure_mfma(4, 4, ops, cus, 40000, obuf, stream)
         res["during_steps"] = sampled(steps)
         res["during_mfma_only_loop"] = sampled(mfma_loop)
         return res
@@ -412,6 +400,10 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
     out["fp8_gemm_wgrad"] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
                              "frac_fp8_peak": round(fl / (ms * 1e-3) / 1e12 / 5000.0, 4),
                              "what": "hybrid backward wgrad dY^T . X, tensorwise E5M2"}
+    c8 = mfma_rate(mx, torch, dev, stream, 1, 1, gr8)
+    out["fp8_mfma_ceiling"] = {"TFLOP/s": c8, "gemm_dgrad_frac": round(out["fp8_gemm_dgrad"]["TFLOP/s"] / c8, 4),
+                               "gemm_wgrad_frac": round(out["fp8_gemm_wgrad"]["TFLOP/s"] / c8, 4),
+                               "what": "MFMA-only loop, E5M2 x E5M2, on the dY FP8 blob's codes"}
     # quantizer prologue: dual quantize of bf16(dY * g) with the product formed in the staging read,
     # against the unfused pair (torch's bf16 multiply writing the product, then the quantizer)
     gfac = torch.empty_like(dY)
@@ -456,6 +448,13 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
                                           stream))
         out[name] = {"ms": round(ms, 5), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 1),
                      "frac_fp6_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4), "what": what}
+    c22 = mfma_rate(mx, torch, dev, stream, E2M3, E2M3, x6r[0])
+    c32 = mfma_rate(mx, torch, dev, stream, E3M2, E2M3, g6r[0])
+    out["fp6_mfma_ceiling"] = {"E2M3xE2M3_TFLOP/s": c22, "E3M2xE2M3_TFLOP/s": c32,
+                               "gemm_fwd_frac": round(out["fp6_gemm_fwd"]["TFLOP/s"] / c22, 4),
+                               "gemm_dgrad_frac": round(out["fp6_gemm_dgrad"]["TFLOP/s"] / c32, 4),
+                               "gemm_wgrad_frac": round(out["fp6_gemm_wgrad"]["TFLOP/s"] / c32, 4),
+                               "what": "MFMA-only loop on the X (E2M3) and dY (E3M2) FP6 blobs' codes"}
     d_bytes, s_bytes = mx.mx_blob_bytes(tokens, din, mx.MX_LAYOUT_CANONICAL)
     cq = torch.empty((d_bytes,), dtype=torch.uint8, device=dev)
     cs = torch.empty((s_bytes,), dtype=torch.uint8, device=dev)
@@ -464,6 +463,23 @@ def time_extras(mx, torch, dev, stream, X, W, dY, tokens, din, dout, Xr, Xrs, Wr
                                           "GB/s": round(2.0 * (d_bytes + s_bytes) / (ms * 1e-3) / 1e9, 1),
                                           "what": "X row-wise blob %dx%d, tiled -> canonical" % (tokens, din)}
     return out
+
+
+def mfma_rate(mx, torch, dev, stream, fmt_a, fmt_b, ops, iters=40000, reps=5):
+    """TFLOP/s of the MFMA-only loop (mx_measure_mfma) on the first 16 KB of
+    `ops` (uint8 device tensor of element codes), one workgroup of 8 waves per CU."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty((cus * 512,), dtype=torch.float32, device=dev)
+    ops = ops[:16384]
+    mx.mx_measure_mfma(fmt_a, fmt_b, ops, cus, iters, out, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        mx.mx_measure_mfma(fmt_a, fmt_b, ops, cus, iters, out, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    return round(cus * 32.0 * iters * 131072 / (ms * 1e-3) / 1e12, 1)
 
 
 def time_other_workloads(mx, torch, dev, stream, synth, reps=20):

@@ -389,25 +389,28 @@ mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t leng
 
 /*
  * Measurement aid (not a step of the path): the sustained rate of the
- * block-scaled FP4 matrix instruction the GEMM issues
- * (V_MFMA_SCALE_F32_32X32X64_F8F6F4, E2M1 x E2M1, unit scales) with no memory
- * traffic in its loop, i.e. the ceiling that power and clock leave for FP4
- * GEMMs on operands like the given ones (the dense spec, 10.1 PF/s, assumes
- * 2.4 GHz throughout).
+ * block-scaled matrix instruction the GEMMs issue
+ * (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with unit scales) for element formats
+ * fmt_a x fmt_b (0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1: the instruction's own
+ * codes), with no memory traffic in its loop, i.e. the ceiling that the
+ * chip's clock under matrix work leaves for GEMMs on operands like the given
+ * ones (the dense specs assume 2.4 GHz throughout).
  *   operands: device buffer of 64 x 64 uint32 words (16 KB, caller-owned,
- *     16-byte aligned) of E2M1 codes: lane L of every wave uses words
- *     [64 L, 64 L + 64) as 8 operand pairs (pair k: A = words 8k..8k+3,
- *     B = words 8k+4..8k+7), one per accumulator chain.
+ *     16-byte aligned): lane L of every wave uses words [64 L, 64 L + 64) as
+ *     4 operand pairs (pair k: A = words 16k..16k+7, B = words 16k+8..16k+15;
+ *     an E2M1 operand uses the first 4 words of its 8, an FP6 one the first 6),
+ *     one per accumulator chain.
  *   workgroups: >= 1 workgroups of 8 waves (two per SIMD); each wave issues
- *     8 * iters instructions, so one launch performs
- *     workgroups * 8 * 8 * iters * 131072 flops.
+ *     4 * iters instructions, so one launch performs
+ *     workgroups * 8 * 4 * iters * 131072 flops.
  *   out: device float[workgroups * 512] (caller-owned): one sum per lane,
  *     stored so that the work is kept.
- * Asynchronous on `stream`.  Errors: MX_ERR_INVALID_ARGUMENT (NULL,
- * workgroups < 1, iters < 1), MX_ERR_MISALIGNED, MX_ERR_DEVICE_UNSUPPORTED,
- * MX_ERR_HIP.
+ * Asynchronous on `stream`.  Errors: MX_ERR_UNSUPPORTED (format code),
+ * MX_ERR_INVALID_ARGUMENT (NULL, workgroups < 1, iters < 1),
+ * MX_ERR_MISALIGNED, MX_ERR_DEVICE_UNSUPPORTED, MX_ERR_HIP.
  */
-mx_status mx_measure_mfma_fp4(const void *operands, int workgroups, int64_t iters, float *out, void *stream);
+mx_status mx_measure_mfma(int fmt_a, int fmt_b, const void *operands, int workgroups, int64_t iters, float *out,
+                          void *stream);
 
 /* 1 if device `device` is gfx950 (the only target), else 0. */
 int mx_device_supported(int device);

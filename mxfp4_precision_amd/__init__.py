@@ -37,7 +37,7 @@ EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm
             "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
             "mx_fp8_blob_bytes", "mx_quantize_fp8_tw", "mx_gemm_f8_tw",
             "mx_fp6_blob_bytes", "mx_quantize_fp6", "mx_gemm_fp6", "mx_quantize_dual_mul",
-            "mx_measure_mfma_fp4", "mx_status_string", "mx_last_error")
+            "mx_measure_mfma", "mx_status_string", "mx_last_error")
 
 
 class MXError(RuntimeError):
@@ -86,7 +86,7 @@ def lib() -> ctypes.CDLL:
     L.mx_quantize_dual_mul.argtypes = [vp, vp, i64, i64, i64, i64, optp, optp, i32, vp, vp, vp, vp, vp]
     L.mx_gemm_fp6.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
-    L.mx_measure_mfma_fp4.argtypes = [vp, i32, i64, vp, vp]
+    L.mx_measure_mfma.argtypes = [i32, i32, vp, i32, i64, vp, vp]
     L.mx_device_supported.argtypes = [i32]
     L.mx_device_supported.restype = i32
     L.mx_status_string.argtypes = [i32]
@@ -240,8 +240,8 @@ def mx_dequantize(q, s, rows: int, length: int, layout: int, out_f32, ldo: int, 
                                _stream(stream)))
 
 
-def mx_measure_mfma_fp4(operands, workgroups: int, iters: int, out, stream=None):
-    _check(lib().mx_measure_mfma_fp4(_dptr(operands), workgroups, iters, _dptr(out), _stream(stream)))
+def mx_measure_mfma(fmt_a: int, fmt_b: int, operands, workgroups: int, iters: int, out, stream=None):
+    _check(lib().mx_measure_mfma(fmt_a, fmt_b, _dptr(operands), workgroups, iters, _dptr(out), _stream(stream)))
 
 
 def mx_device_supported(device: int) -> bool:

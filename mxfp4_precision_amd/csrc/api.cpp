@@ -439,7 +439,11 @@ mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t leng
                         "mx_dequantize");
 }
 
-mx_status mx_measure_mfma_fp4(const void *operands, int workgroups, int64_t iters, float *out, void *stream) {
+mx_status mx_measure_mfma(int fmt_a, int fmt_b, const void *operands, int workgroups, int64_t iters, float *out,
+                          void *stream) {
+    if (fmt_a < 0 || fmt_a > 4 || fmt_b < 0 || fmt_b > 4)
+        return fail(MX_ERR_UNSUPPORTED, "element formats %d, %d (valid: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1)",
+                    fmt_a, fmt_b);
     if (!operands || !out) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (workgroups < 1 || iters < 1)
         return fail(MX_ERR_INVALID_ARGUMENT, "workgroups=%d and iters=%lld must be >= 1", workgroups,
@@ -447,8 +451,9 @@ mx_status mx_measure_mfma_fp4(const void *operands, int workgroups, int64_t iter
     if (!aligned16(operands) || !aligned16(out))
         return fail(MX_ERR_MISALIGNED, "operands and out must be 16-byte aligned");
     MX_TRY(check_device());
-    return check_launch(mx::launch_measure_mfma_fp4(operands, workgroups, iters, out, static_cast<hipStream_t>(stream)),
-                        "mx_measure_mfma_fp4");
+    return check_launch(mx::launch_measure_mfma(fmt_a, fmt_b, operands, workgroups, iters, out,
+                                                static_cast<hipStream_t>(stream)),
+                        "mx_measure_mfma");
 }
 
 int mx_device_supported(int device) {

@@ -62,6 +62,7 @@ hipError_t launch_layout_convert(bool to_tiled, int64_t rows, int64_t length, co
                                  const uint8_t *s_src, uint8_t *q_dst, uint8_t *s_dst, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t length,
                              mx_layout layout, float *out, int64_t ldo, hipStream_t stream);
-hipError_t launch_measure_mfma_fp4(const void *ops, int workgroups, int64_t iters, float *out, hipStream_t stream);
+hipError_t launch_measure_mfma(int fmt_a, int fmt_b, const void *ops, int workgroups, int64_t iters, float *out,
+                               hipStream_t stream);
 
 }  // namespace mx

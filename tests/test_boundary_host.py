@@ -167,11 +167,13 @@ def test_host_objects_refused_as_device_pointers(L):
 
 def test_measure_mfma_validation(L):
     A16 = 1 << 20
-    M = mx.mx_measure_mfma_fp4
-    assert _status(M, 0, 4, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
-    assert _status(M, A16, 0, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
-    assert _status(M, A16, 4, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
-    assert _status(M, A16 + 4, 4, 10, A16, 0) == mx.MX_ERR_MISALIGNED
+    M = mx.mx_measure_mfma
+    assert _status(M, 5, 4, A16, 4, 10, A16, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(M, 4, -1, A16, 4, 10, A16, 0) == mx.MX_ERR_UNSUPPORTED
+    assert _status(M, 4, 4, 0, 4, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, 4, 4, A16, 0, 10, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, 4, 4, A16, 4, 0, A16, 0) == mx.MX_ERR_INVALID_ARGUMENT
+    assert _status(M, 4, 4, A16 + 4, 4, 10, A16, 0) == mx.MX_ERR_MISALIGNED
 
 
 def test_dequantize_validation(L):
