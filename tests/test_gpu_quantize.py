@@ -11,6 +11,7 @@ torch = pytest.importorskip("torch")
 import mxfp4_precision_amd as mx
 from mxfp4_precision_amd import synth
 
+import input_digests
 from gpu_util import canon_shape, host, log, quantize_dual, quantize_rowwise, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -258,7 +259,9 @@ def test_fc2_full_size_dual(oracle_mod):
     """Full-size 18432x12288 GELU activation (seed 4), dual, tiled layout, every byte."""
     _require_gpu()
     log("fc2 X 18432x12288 dual")
-    x = synth.fc2()["X"]
+    d = synth.fc2()
+    input_digests.check("fc2", d)
+    x = d["X"]
     check_dual(oracle_mod, x, TILED)
 
 

@@ -17,6 +17,7 @@ torch = pytest.importorskip("torch")
 import mxfp4_precision_amd as mx
 from mxfp4_precision_amd import synth
 
+import input_digests
 from gpu_util import check_gemm_bf16, gemm, host, log, quantize_dual, tau_bound, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +92,7 @@ def test_fc1_step_full_size(oracle_mod):
     X N(0,1), W N(0,0.02), dY N(0,1e-3), round to nearest, 1D blocks."""
     _require_gpu()
     d = synth.fc1()
+    input_digests.check("fc1", d)
     log("fc1 step X %s W %s dY %s" % (d["X"].shape, d["W"].shape, d["dY"].shape))
     _step(oracle_mod, d["X"], d["W"], d["dY"], tag="fc1-")
 
