@@ -396,10 +396,11 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 // ms with the spilling three-wave request and 0.0711 ms for the earlier form
 // that drew the bytes after the loads had landed.  (With the Hadamard
 // transform as well it would spill, so that form keeps its registers.)
-// MXFP6 draws its bytes after the loads have landed and fits three waves
-// (168 VGPRs) without spills.
+// MXFP6 draws its bytes after the loads have landed; with both directions
+// stochastic it fits three waves (168 VGPRs) without spills, with one
+// direction stochastic (the mixed-options forms) two.
 template <int ELEM, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
-constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? (ELEM == 6 ? 3 : 2) : 1;
+constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? (ELEM == 6 ? (ROW_SR && COL_SR ? 3 : 2) : 2) : 1;
 
 // ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
 // options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
