@@ -570,24 +570,27 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
 }
 
 // Epilogue of the stream kernel (bf16 output).  Stages 0-2 already hold the
-// next tile's first k-steps, so only stage 3 is free: the tile goes out in
-// kMA passes of 64 rows, pass p staging MFMA tile row j = p of every wave
-// (tile rows 32p + [0, 32) and 128 + 32p + [0, 32)), 512 bytes per row with
-// the same chunk swizzle as the one-tile epilogue.  Each wave issues exactly
-// kEpiStoresPerTile 16-byte buffer stores per tile whatever the edges: a
-// chunk past row M or column N gets an out-of-range offset, which the buffer
-// range check drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
-// what lets the next tile's first waits count past the stores instead of
-// draining them.  Before the stores, the epilogue issues the second part of
-// the next tile's step 2 (its first k-step would otherwise issue it after
-// them), into stage 2, free since the tile's last k-step.
-constexpr int kPassRows = kWavesM * 32;                   // 64
-constexpr int kEpiRowsPerWave = kPassRows / kWaves;       // 8: 4 instructions of 2 rows
-static_assert(kEpiStoresPerTile == kMA * kEpiRowsPerWave / 2, "store count");
-static_assert(kPassRows * kBN * 2 == kStageBytes, "one pass fills stage 3");
+// next tile's first k-steps, so only stage 3 is free.  Each wave takes a
+// 4 KB slot of it: in pass p (kMA passes) the wave stages its own 32 x 64
+// block (MFMA row tile p: tile rows 128 wm + 32p + [0, 32), columns
+// 64 wn + [0, 64)), 128 bytes per row with 16-byte chunk c of row r at c ^
+// (r % 8), and reads it back as whole 128-byte row segments, 8 rows per store
+// instruction.  After the first barrier (every wave done with stage 3's last
+// k-step) no wave waits for another: a wave's LDS operations complete in
+// order, so its next pass may overwrite the slot it has just read.  Each wave
+// issues exactly kEpiStoresPerTile 16-byte buffer stores per tile whatever
+// the edges: a chunk past row M or column N gets an out-of-range offset, which
+// the buffer range check drops (N % 8 == 0, so a chunk is all in or all out).
+// The fixed count is what lets the next tile's first waits count past the
+// stores instead of draining them.  Before the stores, the epilogue issues
+// the second part of the next tile's step 2 (its first k-step would otherwise
+// issue it after them), into stage 2, free since the tile's last k-step.
+constexpr int kSlotBytes = 32 * kWN * 2;                  // 4 KB per wave
+static_assert(kSlotBytes * kWaves == kStageBytes, "one slot per wave fills stage 3");
+static_assert(kEpiStoresPerTile == kMA * 4, "store count: 4 instructions of 8 rows per pass");
 
-__device__ __forceinline__ uint8_t *c_stage3(int r, int col) {
-    return g_stage3 + r * (kBN * 2) + (((col >> 3) ^ (r & 31)) * 16) + (col & 7) * 2;
+__device__ __forceinline__ uint8_t *c_slot(int wave, int r, int chunk) {
+    return g_stage3 + wave * kSlotBytes + r * (kWN * 2) + ((chunk ^ (r & 7)) * 16);
 }
 
 __device__ __forceinline__ void store_tile_stream(const GemmCtxT<true> &c, v16f (&acc)[kMB][kMA], int tm, int tn,
@@ -596,34 +599,28 @@ __device__ __forceinline__ void store_tile_stream(const GemmCtxT<true> &c, v16f 
     dma_part<2, 1>(c, c.kstream + 2);
     const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
-    const int tm0 = tm * kBM;
-    const int cl = (lane & 31) * 8;
-    const int col = tn * kBN + cl;
+    const int row_w = tm * kBM + kWM * wm;                     // first C row of this wave's block
+    const int col = tn * kBN + kWN * wn + 8 * (lane & 7);      // this lane's 8 columns on the way out
+    // every wave is done reading stage 3 (the tile's last k-step); a bare
+    // barrier: a __syncthreads() fence would also wait for the next tile's DMAs
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int p = 0; p < kMA; ++p) {
-        // Stage 3 is free: every wave is done with the tile's last k-step
-        // (p = 0) or with reading the previous pass.  A bare barrier: a
-        // __syncthreads() fence would also wait for the next tile's DMAs.
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
         for (int i = 0; i < kMB; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int rl = wm * 32 + lrow, cw = wn * kWN + 32 * i + 8 * q + 4 * lhi;
                 const uint32_t p01 = __builtin_bit_cast(
                     uint32_t, __builtin_convertvector((f32x2_t{acc[i][p][4 * q], acc[i][p][4 * q + 1]}), bf16x2_t));
                 const uint32_t p23 = __builtin_bit_cast(
                     uint32_t, __builtin_convertvector((f32x2_t{acc[i][p][4 * q + 2], acc[i][p][4 * q + 3]}), bf16x2_t));
-                *reinterpret_cast<uint2 *>(c_stage3(rl, cw)) = uint2{p01, p23};
+                *reinterpret_cast<uint2 *>(c_slot(wave, lrow, 4 * i + q) + 8 * lhi) = uint2{p01, p23};
             }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // staged row lr is tile row 32p + lr (lr < 32) or 128 + 32p + lr - 32
-        const int lr0 = kEpiRowsPerWave * wave + lhi;
-        const int row0 = tm0 + 32 * p + lr0 + (lr0 >= 32 ? kBM / 2 - 32 : 0);
 #pragma unroll
-        for (int it = 0; it < kEpiRowsPerWave / 2; ++it) {
-            const v4u_t v = *reinterpret_cast<const v4u_t *>(c_stage3(kEpiRowsPerWave * wave + 2 * it + lhi, cl));
-            const int row = row0 + 2 * it;
+        for (int s = 0; s < 4; ++s) {
+            const int r = 8 * s + (lane >> 3);
+            const v4u_t v = *reinterpret_cast<const v4u_t *>(c_slot(wave, r, lane & 7));
+            const int row = row_w + 32 * p + r;
             const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
         }
