@@ -144,7 +144,8 @@ def main():
     for k in range(args.steps):
         step(evsets[k])
     torch.cuda.synchronize()
-    per = {n: float(np.mean([evs[i].elapsed_time(evs[i + 1]) for evs in evsets])) for i, n in enumerate(names)}
+    samples = {n: [evs[i].elapsed_time(evs[i + 1]) for evs in evsets] for i, n in enumerate(names)}
+    per = {n: float(np.mean(v)) for n, v in samples.items()}
 
     gemm_shapes = {"gemm_fwd": (tokens, dout, din), "gemm_dgrad": (tokens, din, dout),
                    "gemm_wgrad": (dout, din, tokens)}
@@ -160,7 +161,8 @@ def main():
 
     kernels = {}
     for n in names:
-        entry = {"ms": round(per[n], 5)}
+        entry = {"ms": round(per[n], 5), "ms_median": round(float(np.median(samples[n])), 5),
+                 "ms_min": round(float(np.min(samples[n])), 5)}
         if n in flops:
             entry["TFLOP/s"] = round(flops[n] / (per[n] * 1e-3) / 1e12, 1)
             entry["frac_fp4_peak"] = round(flops[n] / (per[n] * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)
