@@ -77,8 +77,9 @@ constexpr int kGroupM = 8;                 // tile rows per band in the tile ord
 
 static_assert(kAtoms % kWaves == 0 && kLoads % 2 == 0, "DMA split");
 // 16-byte stores per wave per tile in the stream kernel's epilogue: kMA
-// passes of kWavesM * 32 rows of 512 bytes, 2 rows per store instruction
-constexpr int kEpiStoresPerTile = kMA * (kWavesM * 32 / kWaves) / 2;
+// passes of the wave's own 32 rows x kWN bf16 columns, 64 lanes x 16 bytes
+// per store instruction
+constexpr int kEpiStoresPerTile = kMA * (32 * kWN * 2) / (64 * 16);
 static_assert(kMA + kMB <= kSlots, "one operand read per slot");
 
 // Buffer resource over [p, p + bytes).  Loads address it with a per-lane
