@@ -993,11 +993,13 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
     // half of the CUs goes to the tail kernel as 128x128 tiles instead.
     const int cus = device_cu_count();
     const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
-    // Several tiles per workgroup with a short K: one persistent workgroup
-    // per CU.  Same-box timings at 18432 rows: the stream form takes 7% off at
-    // 12-24 k-steps per tile and 3.5% at 48, ties at 96 and loses 1-2% at 144,
-    // where the per-tile costs it hides are small next to the k-loop.
-    if (out_dtype == MX_BF16 && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 96 * 128 && cus > 0 &&
+    // Several tiles per workgroup: one persistent workgroup per CU.  Same-box
+    // timings at 18432 rows: the stream form takes 7% off at 12-24 k-steps per
+    // tile and 3.5% at 48, ties at 96, and with its wave-private epilogue
+    // takes 0.9% off at 144 (the fc2 wgrad; with the earlier epilogue it lost
+    // 1-2% there).  Longer K is not measured, so it keeps one tile per
+    // workgroup.
+    if (out_dtype == MX_BF16 && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 144 * 128 && cus > 0 &&
         tiles - tail > cus) {
         auto kernel = bias ? gemm_a4w4_stream_kernel<true> : gemm_a4w4_stream_kernel<false>;
         hipLaunchKernelGGL(kernel, dim3((unsigned)cus), dim3(kThreads), 0, stream, (int)M, (int)N, (int)K_pad,
