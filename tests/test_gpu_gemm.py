@@ -172,11 +172,18 @@ def _fc2_operands(which):
 def test_fc2_full_size_sampled(oracle_mod, which):
     """The three GEMMs of the fc2 training step at full size (18432 tokens,
     12288 -> 3072), sampled entries, in the launch configuration the benchmark
-    times (864, 3456 and 576 output tiles)."""
+    times (864, 3456 and 576 output tiles).  Every entry of the bf16 output
+    (persistent kernel plus tail kernel, 96, 24 and 144 k-steps per tile, the
+    last being the longest K the persistent kernel takes) equals the
+    round-to-nearest-even of the fp32 output (one tile per workgroup, the
+    same accumulation order)."""
     _require_gpu()
     a, b = _fc2_operands(which)
     log("fc2 %s %dx%dx%d" % (which, a.shape[0], b.shape[0], a.shape[1]))
-    run_case(oracle_mod, a, b, full=False, nsample=4096, seed=5, what="fc2-" + which)
+    cb, cf = run_case(oracle_mod, a, b, full=False, nsample=4096, seed=5, what="fc2-" + which)
+    bad = np.count_nonzero(cb != _rne_bf16_bits(cf))
+    assert bad == 0, ("fc2-" + which, bad)
+    log("fc2-%s: all %d bf16 entries equal RNE of the fp32 output" % (which, cb.size))
 
 
 def gemm_bias(A, As, B, Bs, M, N, K, bias, out_dtype=mx.MX_BF16):
@@ -274,7 +281,7 @@ def _rne_bf16_bits(f32):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("K", [200, 700, 1536])
+@pytest.mark.parametrize("K", [200, 700, 1536, 18560])
 def test_several_tiles_per_workgroup(oracle_mod, K):
     """5020x7640 output = 20x30 = 600 tiles of 256x256: two whole rounds on
     256 CUs, where each persistent workgroup runs two tiles back to back (the
@@ -282,7 +289,9 @@ def test_several_tiles_per_workgroup(oracle_mod, K):
     its stores overlap the second tile's first k-steps, the second tile's
     bias loads follow them), plus an 88-tile tail; ragged last row and column
     of tiles.  K 200 (fewer k-steps than the pipeline depth), 700 (padded
-    k-group) and 1536.  Without and with a bias: sampled entries against the
+    k-group), 1536, and 18560 (145 k-steps, one past the longest K the
+    persistent kernel takes, so the bf16 output comes from one tile per
+    workgroup too).  Without and with a bias: sampled entries against the
     oracle, and the bf16 output (persistent kernel) equal to the round-to-
     nearest-even of the fp32 output (one tile per workgroup), which
     accumulates in the same order; nothing written past column N of the
