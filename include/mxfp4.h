@@ -15,8 +15,8 @@
  * Conventions shared by every entry point:
  *  - All tensors live in device memory the caller owns; the library allocates
  *    nothing and keeps no state between calls.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *    runs asynchronously.  Returned status reflects argument validation and
+ *  - Work is enqueued on `stream` (NULL = the null stream) and runs
+ *    asynchronously.  Returned status reflects argument validation and
  *    the launch only; kernels never report errors after launch.
  *  - Validation happens before any launch.  Nothing is written on error, and
  *    there is no fallback path: an unsupported request is an error.
@@ -34,6 +34,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h>   /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -126,8 +128,8 @@ typedef struct mx_quant_opts {
     uint32_t use_sr;
     uint64_t seed;
     uint32_t tensor_id;
+    uint64_t index_base;   /* global element-index offset of x (shards, chunks) */
     uint32_t rht;          /* random Hadamard transform seed, 0 = off */
-    uint64_t index_base;
 } mx_quant_opts;
 
 /*
@@ -152,7 +154,7 @@ mx_status mx_blob_bytes(int64_t rows, int64_t length, mx_layout layout,
  */
 mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx,
                               const mx_quant_opts *opts, mx_layout layout,
-                              void *q, void *s, void *stream);
+                              void *q, void *s, hipStream_t stream);
 
 /*
  * Dual quantization: the row-wise blob (R = M, L = N) and the column-wise blob
@@ -164,7 +166,7 @@ mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx,
 mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx,
                            const mx_quant_opts *row_opts, const mx_quant_opts *col_opts,
                            mx_layout layout, void *q_row, void *s_row,
-                           void *q_col, void *s_col, void *stream);
+                           void *q_col, void *s_col, hipStream_t stream);
 
 /*
  * Quantizer with a multiply prologue: quantizes y = bf16(x * g) (elementwise,
@@ -184,7 +186,7 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx,
 mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t N, int64_t ldx, int64_t ldg,
                                const mx_quant_opts *row_opts, const mx_quant_opts *col_opts,
                                mx_layout layout, void *q_row, void *s_row,
-                               void *q_col, void *s_col, void *stream);
+                               void *q_col, void *s_col, hipStream_t stream);
 
 /*
  * Block-scaled FP4 x FP4 GEMM with fp32 accumulation:
@@ -210,7 +212,7 @@ mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K,
                        const void *A, const void *A_scale,
                        const void *B, const void *B_scale,
                        mx_layout layout, mx_dtype out_dtype,
-                       void *C, int64_t ldc, void *stream);
+                       void *C, int64_t ldc, hipStream_t stream);
 
 /*
  * mx_gemm_a4w4 with the linear layer's bias added in the epilogue:
@@ -227,7 +229,7 @@ mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_
                             const void *A, const void *A_scale,
                             const void *B, const void *B_scale,
                             mx_layout layout, mx_dtype out_dtype, const void *bias,
-                            void *C, int64_t ldc, void *stream);
+                            void *C, int64_t ldc, hipStream_t stream);
 
 /*
  * ---- Hybrid backward: tensorwise FP8 (E5M2) ----
@@ -263,7 +265,7 @@ mx_status mx_fp8_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size
  * MX_ERR_HIP.  M == 0 or N == 0 is a no-op.
  */
 mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, mx_layout layout,
-                             void *q_row, void *q_col, float *info, void *stream);
+                             void *q_row, void *q_col, float *info, hipStream_t stream);
 
 /*
  * C = (A . B^T) * a_scale_inv[0] * b_scale_inv[0] on tensorwise E5M2 blobs
@@ -279,7 +281,7 @@ mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
                         const void *A, const float *a_scale_inv,
                         const void *B, const float *b_scale_inv,
                         mx_layout layout, mx_dtype out_dtype,
-                        void *C, int64_t ldc, void *stream);
+                        void *C, int64_t ldc, hipStream_t stream);
 
 /* ------------------------------------------------------------------ MXFP6
  *
@@ -333,7 +335,7 @@ mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx,
                           int row_fmt, const mx_quant_opts *row_opts,
                           int col_fmt, const mx_quant_opts *col_opts,
                           mx_layout layout, void *q_row, void *s_row,
-                          void *q_col, void *s_col, void *stream);
+                          void *q_col, void *s_col, hipStream_t stream);
 
 /*
  * Block-scaled FP6 x FP6 GEMM with fp32 accumulation on tiled MXFP6 blobs:
@@ -349,7 +351,7 @@ mx_status mx_gemm_fp6(int transA, int transB, int64_t M, int64_t N, int64_t K,
                       int fmt_a, const void *A, const void *A_scale,
                       int fmt_b, const void *B, const void *B_scale,
                       mx_layout layout, mx_dtype out_dtype,
-                      void *C, int64_t ldc, void *stream);
+                      void *C, int64_t ldc, hipStream_t stream);
 
 /*
  * Device-side layout conversion of one blob (rows, length) between the two
@@ -366,7 +368,7 @@ mx_status mx_gemm_fp6(int transA, int transB, int64_t M, int64_t N, int64_t K,
  * length == 0 is a no-op.
  */
 mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const void *q_src,
-                            const void *s_src, void *q_dst, void *s_dst, void *stream);
+                            const void *s_src, void *q_dst, void *s_dst, hipStream_t stream);
 
 /*
  * Host-side layout conversion of one blob (rows, length) between the two
@@ -385,7 +387,7 @@ mx_status mx_layout_convert_host(int to_tiled, int64_t rows, int64_t length,
  * emit more for finite input); byte 0xFF gives NaN.
  */
 mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t length,
-                        mx_layout layout, void *out_f32, int64_t ldo, void *stream);
+                        mx_layout layout, void *out_f32, int64_t ldo, hipStream_t stream);
 
 /*
  * Measurement aid (not a step of the path): the sustained rate of the
@@ -410,10 +412,30 @@ mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t leng
  * MX_ERR_MISALIGNED, MX_ERR_DEVICE_UNSUPPORTED, MX_ERR_HIP.
  */
 mx_status mx_measure_mfma(int fmt_a, int fmt_b, const void *operands, int workgroups, int64_t iters, float *out,
-                          void *stream);
+                          hipStream_t stream);
 
-/* 1 if device `device` is gfx950 (the only target), else 0. */
+/*
+ * 1 if device `device` is gfx950 (the only target), else 0.  The page
+ * "primus_turbo_mxfp4_local.py" has check_mxfp4_support() decide, when a
+ * layer is built, whether the FP4 path can run at all, and refuses to build
+ * the layer otherwise; this is that check.  Every entry point that launches
+ * work repeats it (cached per device) and returns MX_ERR_DEVICE_UNSUPPORTED
+ * instead of launching on another device.
+ */
 int mx_device_supported(int device);
+
+/*
+ * Test aid: replaces the device query of every entry point by a fixed
+ * architecture name, so that the failure paths can be exercised on any
+ * machine.  arch = NULL restores the real query.  With a name other than
+ * "gfx950", calls fail with MX_ERR_DEVICE_UNSUPPORTED after validation; with
+ * "gfx950" on a machine whose runtime has no usable device, the launch fails
+ * and the call returns MX_ERR_HIP with HIP's error text.  The name applies to
+ * every device index and to mx_device_supported.  Process-wide; not for use
+ * while other threads call the library.  Errors: MX_ERR_INVALID_ARGUMENT (a
+ * name of 64 characters or more).
+ */
+mx_status mx_set_device_arch_override(const char *arch);
 
 /* Static name of a status code. */
 const char *mx_status_string(mx_status status);

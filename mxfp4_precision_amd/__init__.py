@@ -17,7 +17,9 @@ import os
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxfp4.so")
+# MXFP4_LIB names another build of the same library (the sanitizer build of
+# the host code that the CPU tests run); the default is the in-tree build.
+LIB_PATH = os.environ.get("MXFP4_LIB") or os.path.join(_HERE, "libmxfp4.so")
 
 MX_SUCCESS = 0
 MX_ERR_INVALID_ARGUMENT = 1
@@ -37,7 +39,7 @@ EXPORTED = ("mx_blob_bytes", "mx_quantize_rowwise", "mx_quantize_dual", "mx_gemm
             "mx_layout_convert", "mx_layout_convert_host", "mx_dequantize", "mx_device_supported",
             "mx_fp8_blob_bytes", "mx_quantize_fp8_tw", "mx_gemm_f8_tw",
             "mx_fp6_blob_bytes", "mx_quantize_fp6", "mx_gemm_fp6", "mx_quantize_dual_mul",
-            "mx_measure_mfma", "mx_status_string", "mx_last_error")
+            "mx_measure_mfma", "mx_set_device_arch_override", "mx_status_string", "mx_last_error")
 
 
 class MXError(RuntimeError):
@@ -49,12 +51,12 @@ class MXError(RuntimeError):
 class mx_quant_opts(ctypes.Structure):
     _fields_ = [("use_2d_block", ctypes.c_uint32), ("use_sr", ctypes.c_uint32),
                 ("seed", ctypes.c_uint64), ("tensor_id", ctypes.c_uint32),
-                ("rht", ctypes.c_uint32), ("index_base", ctypes.c_uint64)]
+                ("index_base", ctypes.c_uint64), ("rht", ctypes.c_uint32)]
 
 
 def quant_opts(use_2d_block: bool = False, use_sr: bool = False, seed: int = 0,
                tensor_id: int = 0, index_base: int = 0, rht: int = 0) -> mx_quant_opts:
-    return mx_quant_opts(int(use_2d_block), int(use_sr), seed, tensor_id, rht, index_base)
+    return mx_quant_opts(int(use_2d_block), int(use_sr), seed, tensor_id, index_base, rht)
 
 
 _lib = None
@@ -87,6 +89,7 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm_fp6.argtypes = [i32, i32, i64, i64, i64, i32, vp, vp, i32, vp, vp, i32, i32, vp, i64, vp]
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, vp, i64, vp]
     L.mx_measure_mfma.argtypes = [i32, i32, vp, i32, i64, vp, vp]
+    L.mx_set_device_arch_override.argtypes = [ctypes.c_char_p]
     L.mx_device_supported.argtypes = [i32]
     L.mx_device_supported.restype = i32
     L.mx_status_string.argtypes = [i32]
@@ -246,6 +249,11 @@ def mx_measure_mfma(fmt_a: int, fmt_b: int, operands, workgroups: int, iters: in
 
 def mx_device_supported(device: int) -> bool:
     return bool(lib().mx_device_supported(device))
+
+
+def mx_set_device_arch_override(arch: Optional[str]):
+    """Test aid: fixed architecture name in place of the device query (None restores it)."""
+    _check(lib().mx_set_device_arch_override(None if arch is None else arch.encode()))
 
 
 def mx_status_string(status: int) -> str:

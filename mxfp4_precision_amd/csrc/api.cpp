@@ -29,13 +29,30 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_ok[kMaxDevices];
 
+// The architecture name that replaces the device query (a test aid, set by
+// mx_set_device_arch_override); empty = query the device.
+char g_arch_override[64] = "";
+std::atomic<bool> g_has_override{false};
+
+bool arch_is_gfx950(const char *name) {
+    // "gfx950" possibly followed by target features (":sramecc+:xnack-")
+    return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
+}
+
 int query_supported(int dev) {
+    if (g_has_override.load(std::memory_order_acquire)) return arch_is_gfx950(g_arch_override) ? 1 : 0;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-    return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    return arch_is_gfx950(prop.gcnArchName) ? 1 : 0;
 }
 
 mx_status check_device() {
+    if (g_has_override.load(std::memory_order_acquire)) {
+        if (!arch_is_gfx950(g_arch_override))
+            return fail(MX_ERR_DEVICE_UNSUPPORTED, "device is %s, not gfx950 (MI355X) (architecture override)",
+                        g_arch_override);
+        return MX_SUCCESS;
+    }
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -143,7 +160,7 @@ mx_status mx_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size_t *
 }
 
 mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx, const mx_quant_opts *opts,
-                              mx_layout layout, void *q, void *s, void *stream) {
+                              mx_layout layout, void *q, void *s, hipStream_t stream) {
     MX_TRY(validate_x(x, M, N, ldx));
     MX_TRY(check_opts(opts, "row"));
     MX_TRY(check_layout(layout));
@@ -157,13 +174,13 @@ mx_status mx_quantize_rowwise(const void *x, int64_t M, int64_t N, int64_t ldx, 
     a.row = to_dir(opts);
     a.q_row = static_cast<uint8_t *>(q);
     a.s_row = static_cast<uint8_t *>(s);
-    return check_launch(mx::launch_quantize(a, false, layout, static_cast<hipStream_t>(stream)),
+    return check_launch(mx::launch_quantize(a, false, layout, stream),
                         "mx_quantize_rowwise");
 }
 
 mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, const mx_quant_opts *row_opts,
                            const mx_quant_opts *col_opts, mx_layout layout, void *q_row, void *s_row,
-                           void *q_col, void *s_col, void *stream) {
+                           void *q_col, void *s_col, hipStream_t stream) {
     MX_TRY(validate_x(x, M, N, ldx));
     MX_TRY(check_opts(row_opts, "row"));
     MX_TRY(check_opts(col_opts, "col"));
@@ -183,13 +200,13 @@ mx_status mx_quantize_dual(const void *x, int64_t M, int64_t N, int64_t ldx, con
     a.s_row = static_cast<uint8_t *>(s_row);
     a.q_col = static_cast<uint8_t *>(q_col);
     a.s_col = static_cast<uint8_t *>(s_col);
-    return check_launch(mx::launch_quantize(a, true, layout, static_cast<hipStream_t>(stream)),
+    return check_launch(mx::launch_quantize(a, true, layout, stream),
                         "mx_quantize_dual");
 }
 
 mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t N, int64_t ldx, int64_t ldg,
                                const mx_quant_opts *row_opts, const mx_quant_opts *col_opts, mx_layout layout,
-                               void *q_row, void *s_row, void *q_col, void *s_col, void *stream) {
+                               void *q_row, void *s_row, void *q_col, void *s_col, hipStream_t stream) {
     const bool dual = q_col || s_col;
     MX_TRY(validate_x(x, M, N, ldx));
     if (!g) return fail(MX_ERR_INVALID_ARGUMENT, "g is NULL");
@@ -220,7 +237,7 @@ mx_status mx_quantize_dual_mul(const void *x, const void *g, int64_t M, int64_t 
     a.s_row = static_cast<uint8_t *>(s_row);
     a.q_col = static_cast<uint8_t *>(q_col);
     a.s_col = static_cast<uint8_t *>(s_col);
-    return check_launch(mx::launch_quantize_mul(a, dual, layout, static_cast<hipStream_t>(stream)),
+    return check_launch(mx::launch_quantize_mul(a, dual, layout, stream),
                         "mx_quantize_dual_mul");
 }
 
@@ -250,7 +267,7 @@ mx_status check_fp6_opts(const mx_quant_opts *o, const char *which) {
 
 mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx, int row_fmt,
                           const mx_quant_opts *row_opts, int col_fmt, const mx_quant_opts *col_opts,
-                          mx_layout layout, void *q_row, void *s_row, void *q_col, void *s_col, void *stream) {
+                          mx_layout layout, void *q_row, void *s_row, void *q_col, void *s_col, hipStream_t stream) {
     const bool dual = q_col || s_col;
     MX_TRY(validate_x(x, M, N, ldx));
     MX_TRY(check_fp6_fmt(row_fmt, "row"));
@@ -279,7 +296,7 @@ mx_status mx_quantize_fp6(const void *x, int64_t M, int64_t N, int64_t ldx, int 
     a.s_row = static_cast<uint8_t *>(s_row);
     a.q_col = static_cast<uint8_t *>(q_col);
     a.s_col = static_cast<uint8_t *>(s_col);
-    return check_launch(mx::launch_quantize_fp6(a, dual, layout, static_cast<hipStream_t>(stream)),
+    return check_launch(mx::launch_quantize_fp6(a, dual, layout, stream),
                         "mx_quantize_fp6");
 }
 
@@ -287,7 +304,7 @@ namespace {
 
 mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
                       const void *A_scale, const void *B, const void *B_scale, mx_layout layout, mx_dtype out_dtype,
-                      const void *bias, bool want_bias, void *C, int64_t ldc, void *stream, int fp6_a = 0,
+                      const void *bias, bool want_bias, void *C, int64_t ldc, hipStream_t stream, int fp6_a = 0,
                       int fp6_b = 0) {
     if (transA != 0 || transB != 1)
         return fail(MX_ERR_UNSUPPORTED,
@@ -322,13 +339,13 @@ mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64
         return check_launch(mx::launch_gemm_fp6(M, N, K, fp6_a, static_cast<const uint8_t *>(A),
                                                 static_cast<const uint8_t *>(A_scale), fp6_b,
                                                 static_cast<const uint8_t *>(B), static_cast<const uint8_t *>(B_scale),
-                                                out_dtype, C, ldc, static_cast<hipStream_t>(stream)),
+                                                out_dtype, C, ldc, stream),
                             name);
     return check_launch(mx::launch_gemm(M, N, K, static_cast<const uint8_t *>(A),
                                         static_cast<const uint8_t *>(A_scale), static_cast<const uint8_t *>(B),
                                         static_cast<const uint8_t *>(B_scale),
                                         want_bias ? static_cast<const uint16_t *>(bias) : nullptr, out_dtype, C,
-                                        ldc, static_cast<hipStream_t>(stream)),
+                                        ldc, stream),
                         name);
 }
 
@@ -336,21 +353,21 @@ mx_status gemm_common(const char *name, int transA, int transB, int64_t M, int64
 
 mx_status mx_gemm_a4w4(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
                        const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
-                       mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+                       mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream) {
     return gemm_common("mx_gemm_a4w4", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype, nullptr,
                        false, C, ldc, stream);
 }
 
 mx_status mx_gemm_a4w4_bias(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
                             const void *A_scale, const void *B, const void *B_scale, mx_layout layout,
-                            mx_dtype out_dtype, const void *bias, void *C, int64_t ldc, void *stream) {
+                            mx_dtype out_dtype, const void *bias, void *C, int64_t ldc, hipStream_t stream) {
     return gemm_common("mx_gemm_a4w4_bias", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype,
                        bias, true, C, ldc, stream);
 }
 
 mx_status mx_gemm_fp6(int transA, int transB, int64_t M, int64_t N, int64_t K, int fmt_a, const void *A,
                       const void *A_scale, int fmt_b, const void *B, const void *B_scale, mx_layout layout,
-                      mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+                      mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream) {
     MX_TRY(check_fp6_fmt(fmt_a, "A"));
     MX_TRY(check_fp6_fmt(fmt_b, "B"));
     return gemm_common("mx_gemm_fp6", transA, transB, M, N, K, A, A_scale, B, B_scale, layout, out_dtype, nullptr,
@@ -366,7 +383,7 @@ mx_status mx_fp8_blob_bytes(int64_t rows, int64_t length, mx_layout layout, size
 }
 
 mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, mx_layout layout, void *q_row,
-                             void *q_col, float *info, void *stream) {
+                             void *q_col, float *info, hipStream_t stream) {
     MX_TRY(validate_x(x, M, N, ldx));
     MX_TRY(check_layout(layout));
     if (!q_row && !q_col) return fail(MX_ERR_INVALID_ARGUMENT, "q_row and q_col are both NULL");
@@ -377,13 +394,13 @@ mx_status mx_quantize_fp8_tw(const void *x, int64_t M, int64_t N, int64_t ldx, m
     MX_TRY(check_device());
     return check_launch(mx::launch_quantize_fp8(static_cast<const uint16_t *>(x), M, N, ldx, layout,
                                                 static_cast<uint8_t *>(q_row), static_cast<uint8_t *>(q_col), info,
-                                                static_cast<hipStream_t>(stream)),
+                                                stream),
                         "mx_quantize_fp8_tw");
 }
 
 mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K, const void *A,
                         const float *a_scale_inv, const void *B, const float *b_scale_inv, mx_layout layout,
-                        mx_dtype out_dtype, void *C, int64_t ldc, void *stream) {
+                        mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream) {
     if (transA != 0 || transB != 1)
         return fail(MX_ERR_UNSUPPORTED, "transA=%d transB=%d: only transA=0, transB=1 (C = A . B^T) is supported",
                     transA, transB);
@@ -407,12 +424,12 @@ mx_status mx_gemm_f8_tw(int transA, int transB, int64_t M, int64_t N, int64_t K,
     MX_TRY(check_device());
     return check_launch(mx::launch_gemm_fp8(M, N, K, static_cast<const uint8_t *>(A), a_scale_inv,
                                             static_cast<const uint8_t *>(B), b_scale_inv, out_dtype, C, ldc,
-                                            static_cast<hipStream_t>(stream)),
+                                            stream),
                         "mx_gemm_f8_tw");
 }
 
 mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const void *q_src, const void *s_src,
-                            void *q_dst, void *s_dst, void *stream) {
+                            void *q_dst, void *s_dst, hipStream_t stream) {
     if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
     if (!q_src || !s_src || !q_dst || !s_dst) return fail(MX_ERR_INVALID_ARGUMENT, "NULL pointer");
     if (!aligned16(q_src) || !aligned16(q_dst) || !aligned16(s_src) || !aligned16(s_dst))
@@ -421,12 +438,12 @@ mx_status mx_layout_convert(int to_tiled, int64_t rows, int64_t length, const vo
     MX_TRY(check_device());
     return check_launch(mx::launch_layout_convert(to_tiled != 0, rows, length, static_cast<const uint8_t *>(q_src),
                                                   static_cast<const uint8_t *>(s_src), static_cast<uint8_t *>(q_dst),
-                                                  static_cast<uint8_t *>(s_dst), static_cast<hipStream_t>(stream)),
+                                                  static_cast<uint8_t *>(s_dst), stream),
                         "mx_layout_convert");
 }
 
 mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t length, mx_layout layout,
-                        void *out_f32, int64_t ldo, void *stream) {
+                        void *out_f32, int64_t ldo, hipStream_t stream) {
     if (rows < 0 || length < 0) return fail(MX_ERR_INVALID_ARGUMENT, "negative blob shape");
     MX_TRY(check_layout(layout));
     if (ldo < length || ldo < 1) return fail(MX_ERR_INVALID_ARGUMENT, "ldo must be >= max(length, 1)");
@@ -435,12 +452,12 @@ mx_status mx_dequantize(const void *q, const void *s, int64_t rows, int64_t leng
     MX_TRY(check_device());
     return check_launch(mx::launch_dequantize(static_cast<const uint8_t *>(q), static_cast<const uint8_t *>(s),
                                               rows, length, layout, static_cast<float *>(out_f32), ldo,
-                                              static_cast<hipStream_t>(stream)),
+                                              stream),
                         "mx_dequantize");
 }
 
 mx_status mx_measure_mfma(int fmt_a, int fmt_b, const void *operands, int workgroups, int64_t iters, float *out,
-                          void *stream) {
+                          hipStream_t stream) {
     if (fmt_a < 0 || fmt_a > 4 || fmt_b < 0 || fmt_b > 4)
         return fail(MX_ERR_UNSUPPORTED, "element formats %d, %d (valid: 0 E4M3, 1 E5M2, 2 E2M3, 3 E3M2, 4 E2M1)",
                     fmt_a, fmt_b);
@@ -452,13 +469,27 @@ mx_status mx_measure_mfma(int fmt_a, int fmt_b, const void *operands, int workgr
         return fail(MX_ERR_MISALIGNED, "operands and out must be 16-byte aligned");
     MX_TRY(check_device());
     return check_launch(mx::launch_measure_mfma(fmt_a, fmt_b, operands, workgroups, iters, out,
-                                                static_cast<hipStream_t>(stream)),
+                                                stream),
                         "mx_measure_mfma");
 }
 
 int mx_device_supported(int device) {
     if (device < 0 || device >= kMaxDevices) return 0;
     return query_supported(device);
+}
+
+mx_status mx_set_device_arch_override(const char *arch) {
+    if (!arch) {
+        g_has_override.store(false, std::memory_order_release);
+        return MX_SUCCESS;
+    }
+    if (std::strlen(arch) >= sizeof g_arch_override)
+        return fail(MX_ERR_INVALID_ARGUMENT, "architecture name longer than %d characters",
+                    (int)sizeof g_arch_override - 1);
+    g_has_override.store(false, std::memory_order_release);
+    std::snprintf(g_arch_override, sizeof g_arch_override, "%s", arch);
+    g_has_override.store(true, std::memory_order_release);
+    return MX_SUCCESS;
 }
 
 const char *mx_status_string(mx_status status) {

@@ -25,6 +25,29 @@ def L():
     return mx.lib()
 
 
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.fixture(autouse=True)
+def _no_launch_on_a_gpu(L):
+    """These tests pass fake (never dereferenced) addresses.  On a machine with
+    a GPU, a call whose arguments pass validation would launch a kernel on
+    them, so the device query is replaced by a non-gfx950 name there and every
+    such call stops at the device check instead.  Without a GPU the real query
+    runs (and fails with MX_ERR_HIP)."""
+    if _gpu_present():
+        mx.mx_set_device_arch_override("gfx000")
+        yield
+        mx.mx_set_device_arch_override(None)
+    else:
+        yield
+
+
 def declared_functions():
     names = []
     inc = os.path.join(ROOT, "include")
@@ -214,10 +237,80 @@ def test_device_layout_convert_validation(L):
 
 def test_device_supported_without_gpu(L):
     # no GPU in a CPU-only container: the query reports unsupported instead of crashing
-    import torch
-    if torch.cuda.is_available():
+    if _gpu_present():
         pytest.skip("GPU present")
     assert mx.mx_device_supported(0) is False
+
+
+def _every_launching_call(A16):
+    """One valid-argument call of every entry point that launches work."""
+    T = mx.MX_LAYOUT_TILED
+    o = mx.quant_opts()
+    return {
+        "mx_quantize_rowwise": lambda: mx.mx_quantize_rowwise(A16, 4, 8, 8, o, T, A16, A16, 0),
+        "mx_quantize_dual": lambda: mx.mx_quantize_dual(A16, 4, 8, 8, o, o, T, A16, A16, A16, A16, 0),
+        "mx_quantize_dual_mul": lambda: mx.mx_quantize_dual_mul(A16, A16, 4, 8, 8, 8, o, o, T, A16, A16, A16,
+                                                                A16, 0),
+        "mx_gemm_a4w4": lambda: mx.mx_gemm_a4w4(0, 1, 4, 8, 128, A16, A16, A16, A16, T, mx.MX_BF16, A16, 8, 0),
+        "mx_gemm_a4w4_bias": lambda: mx.mx_gemm_a4w4_bias(0, 1, 4, 8, 128, A16, A16, A16, A16, T, mx.MX_F32, A16,
+                                                          A16, 8, 0),
+        "mx_quantize_fp6": lambda: mx.mx_quantize_fp6(A16, 4, 8, 8, mx.MX_FP6_E2M3, o, mx.MX_FP6_E3M2, o, T, A16,
+                                                      A16, A16, A16, 0),
+        "mx_gemm_fp6": lambda: mx.mx_gemm_fp6(0, 1, 4, 8, 128, mx.MX_FP6_E2M3, A16, A16, mx.MX_FP6_E3M2, A16, A16,
+                                              T, mx.MX_BF16, A16, 8, 0),
+        "mx_quantize_fp8_tw": lambda: mx.mx_quantize_fp8_tw(A16, 4, 8, 8, T, A16, A16, A16, 0),
+        "mx_gemm_f8_tw": lambda: mx.mx_gemm_f8_tw(0, 1, 4, 8, 128, A16, A16, A16, A16, T, mx.MX_BF16, A16, 8, 0),
+        "mx_layout_convert": lambda: mx.mx_layout_convert(1, 4, 8, A16, A16, A16, A16, 0),
+        "mx_dequantize": lambda: mx.mx_dequantize(A16, A16, 4, 8, T, A16, 8, 0),
+        "mx_measure_mfma": lambda: mx.mx_measure_mfma(4, 4, A16, 1, 1, A16, 0),
+    }
+
+
+def test_forced_unsupported_device(L):
+    """The device check of every launching entry point, forced to see another
+    architecture through the query hook: MX_ERR_DEVICE_UNSUPPORTED naming it,
+    after validation and before any launch (fail loudly, as the page
+    "primus_turbo_mxfp4_local.py" has check_mxfp4_support() refuse to build
+    an FP4 layer on an unsupported device)."""
+    try:
+        mx.mx_set_device_arch_override("gfx942")
+        assert mx.mx_device_supported(0) is False and mx.mx_device_supported(5) is False
+        for name, call in _every_launching_call(1 << 20).items():
+            with pytest.raises(mx.MXError) as e:
+                call()
+            assert e.value.status == mx.MX_ERR_DEVICE_UNSUPPORTED, name
+            assert "gfx942" in mx.mx_last_error(), name
+        # validation still answers first
+        assert _status(mx.mx_quantize_rowwise, 0, 4, 8, 8, None, 1, 1 << 20, 1 << 20, 0) == \
+            mx.MX_ERR_INVALID_ARGUMENT
+        mx.mx_set_device_arch_override("gfx950:sramecc+:xnack-")
+        assert mx.mx_device_supported(0) is True
+        mx.mx_set_device_arch_override("gfx9500")
+        assert mx.mx_device_supported(0) is False
+        with pytest.raises(mx.MXError) as e:
+            mx.mx_set_device_arch_override("g" * 64)
+        assert e.value.status == mx.MX_ERR_INVALID_ARGUMENT
+    finally:
+        mx.mx_set_device_arch_override("gfx000" if _gpu_present() else None)
+
+
+def test_forced_launch_failure_reports_hip_error(L):
+    """With the device check forced to pass on a machine whose runtime has no
+    device, every launching entry point gets as far as the launch, which
+    fails: MX_ERR_HIP with HIP's own error text, no crash, no fallback."""
+    if _gpu_present():
+        pytest.skip("needs a machine without a GPU (the fake addresses would reach a real launch)")
+    try:
+        mx.mx_set_device_arch_override("gfx950")
+        assert mx.mx_device_supported(0) is True
+        for name, call in _every_launching_call(1 << 20).items():
+            with pytest.raises(mx.MXError) as e:
+                call()
+            assert e.value.status == mx.MX_ERR_HIP, name
+            msg = mx.mx_last_error()
+            assert "launch failed" in msg and name in msg, (name, msg)
+    finally:
+        mx.mx_set_device_arch_override(None)
 
 
 def test_fp8_validation_and_sizes(L):
