@@ -55,7 +55,140 @@ def parse():
     p.add_argument("--profile-copy-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size kernel "
                         "that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    p.add_argument("--workload", default="fc2_step", choices=["fc2_step"] + sorted(WORKLOADS),
+                   help="fc2_step (default): the bench line.  Any other: only that workload's kernels, "
+                        "--steps passes of them after --warmup, per-kernel event timings in one JSON line "
+                        "(for rocprofv3 runs of one configuration)")
     return p.parse_args()
+
+
+# Workloads other than the fc2 step, by name: what each pass runs.  Small
+# inputs cycle through buffer sets larger than twice the 256 MB Infinity Cache
+# so that every pass reads from HBM.
+WORKLOADS = {
+    "dual_4600x3072": "dual quantize 4600x3072 (N(0,1), 0.1% outliers x100, a zero 32x32 tile per 1024 rows)",
+    "qkv": "QKV forward: A 4608x3072 and W 9216x3072 row-wise quantize, GEMM 4608 x 9216 x 3072",
+    "fc1_step": "MLP fc1 step: X 9216x3072, W 12288x3072, dY 9216x12288 dual quantize; fwd, dgrad, wgrad",
+    "fc2_w2d": "fc2 weight 3072x12288 dual quantize with 32x32 blocks",
+}
+
+
+def run_workload(args):
+    """--workload NAME: that workload's kernels only, `steps` passes after
+    `warmup`, per-kernel mean of HIP events on the launch stream."""
+    import torch
+    import mxfp4_precision_amd as mx
+    from mxfp4_precision_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mx.lib()
+    dev = torch.device("cuda:0")
+    T = mx.MX_LAYOUT_TILED
+    plain = mx.quant_opts()
+    stream = torch.cuda.current_stream()
+    MALL = 256 << 20
+
+    def dev_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev)
+
+    def dual_bytes(M, N):
+        d1, s1 = mx.mx_blob_bytes(M, N, T)
+        d2, s2 = mx.mx_blob_bytes(N, M, T)
+        return 2.0 * M * N + d1 + s1 + d2 + s2
+
+    def row_bytes(M, N):
+        return 2.0 * M * N + sum(mx.mx_blob_bytes(M, N, T))
+
+    def sets_for(nbytes):
+        return max(2, -(-2 * MALL // int(nbytes)) + 1)
+
+    kernels = []   # (name, fn(i), nsets, bytes or None, flops or None)
+    if args.workload in ("dual_4600x3072", "fc2_w2d"):
+        if args.workload == "dual_4600x3072":
+            x0, opts = dev_bf16(synth.dual()["X"]), plain
+        else:
+            x0, opts = dev_bf16(synth.fc2()["W"]), mx.quant_opts(use_2d_block=True, tensor_id=1)
+        M, N = x0.shape
+        n = sets_for(dual_bytes(M, N))
+        xs = [x0] + [x0.clone() for _ in range(n - 1)]
+        outs = [mx.empty_blob(M, N, T, dev) + mx.empty_blob(N, M, T, dev) for _ in range(n)]
+        kernels.append(("quant_dual", lambda i: mx.mx_quantize_dual(xs[i], M, N, N, opts, opts, T, *outs[i], stream),
+                        n, dual_bytes(M, N), None))
+    elif args.workload == "qkv":
+        d = synth.qkv()
+        a0, w0 = dev_bf16(d["A"]), dev_bf16(d["W"])
+        (M, K), N = a0.shape, w0.shape[0]
+        na, nw = sets_for(row_bytes(M, K)), sets_for(row_bytes(N, K))
+        a_s = [a0] + [a0.clone() for _ in range(na - 1)]
+        w_s = [w0] + [w0.clone() for _ in range(nw - 1)]
+        ab = [mx.empty_blob(M, K, T, dev) for _ in range(na)]
+        wb = [mx.empty_blob(N, K, T, dev) for _ in range(nw)]
+        kernels.append(("quant_A", lambda i: mx.mx_quantize_rowwise(a_s[i], M, K, K, plain, T, *ab[i], stream),
+                        na, row_bytes(M, K), None))
+        kernels.append(("quant_W", lambda i: mx.mx_quantize_rowwise(w_s[i], N, K, K, plain, T, *wb[i], stream),
+                        nw, row_bytes(N, K), None))
+        for i in range(na):
+            mx.mx_quantize_rowwise(a_s[i], M, K, K, plain, T, *ab[i], stream)
+        for i in range(nw):
+            mx.mx_quantize_rowwise(w_s[i], N, K, K, plain, T, *wb[i], stream)
+        ng = sets_for(sum(t.numel() for t in ab[0] + wb[0]) + 2.0 * M * N)
+        Cs = [torch.empty((M, N), dtype=torch.int16, device=dev) for _ in range(ng)]
+        kernels.append(("gemm_fwd", lambda i: mx.mx_gemm_a4w4(0, 1, M, N, K, *ab[i % na], *wb[i % nw], T, mx.MX_BF16,
+                                                              Cs[i], N, stream), ng, None, 2.0 * M * N * K))
+    elif args.workload == "fc1_step":
+        d = synth.fc1()
+        X, W, G = dev_bf16(d["X"]), dev_bf16(d["W"]), dev_bf16(d["dY"])
+        (Tk, din), dout = X.shape, W.shape[0]
+        bl = {}
+        for name, t in (("X", X), ("W", W), ("dY", G)):
+            M, N = t.shape
+            bl[name] = mx.empty_blob(M, N, T, dev) + mx.empty_blob(N, M, T, dev)
+            kernels.append(("quant_" + name, (lambda t, M, N, b: lambda i: mx.mx_quantize_dual(
+                t, M, N, N, plain, plain, T, *b, stream))(t, M, N, bl[name]), 1, dual_bytes(M, N), None))
+        Y = torch.empty((Tk, dout), dtype=torch.int16, device=dev)
+        dX = torch.empty((Tk, din), dtype=torch.int16, device=dev)
+        dW = torch.empty((dout, din), dtype=torch.int16, device=dev)
+        xb, wb, gb = bl["X"], bl["W"], bl["dY"]
+        for name, (M, N, K, A_, As_, B_, Bs_, C_, ldc) in (
+                ("fwd", (Tk, dout, din, xb[0], xb[1], wb[0], wb[1], Y, dout)),
+                ("dgrad", (Tk, din, dout, gb[0], gb[1], wb[2], wb[3], dX, din)),
+                ("wgrad", (dout, din, Tk, gb[2], gb[3], xb[2], xb[3], dW, din))):
+            kernels.append(("gemm_" + name, (lambda M, N, K, A_, As_, B_, Bs_, C_, ldc: lambda i: mx.mx_gemm_a4w4(
+                0, 1, M, N, K, A_, As_, B_, Bs_, T, mx.MX_BF16, C_, ldc, stream))(M, N, K, A_, As_, B_, Bs_, C_, ldc),
+                1, None, 2.0 * M * N * K))
+
+    def one_pass(p, ev=None):
+        for k, (_, fn, nsets, _, _) in enumerate(kernels):
+            if ev is not None:
+                ev[k].record(stream)
+            fn(p % nsets)
+        if ev is not None:
+            ev[len(kernels)].record(stream)
+
+    for p in range(args.warmup):
+        one_pass(p)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
+    for p in range(args.steps):
+        one_pass(p, evs[p])
+    torch.cuda.synchronize()
+    res = {}
+    for k, (name, _, nsets, nbytes, fl) in enumerate(kernels):
+        t = [e[k].elapsed_time(e[k + 1]) for e in evs]
+        ms = float(np.mean(t))
+        entry = {"ms": round(ms, 5), "ms_median": round(float(np.median(t)), 5), "ms_min": round(float(np.min(t)), 5),
+                 "buffer_sets": nsets}
+        if nbytes:
+            entry["GB/s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            entry["frac_hbm_peak"] = round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        if fl:
+            entry["TFLOP/s"] = round(fl / (ms * 1e-3) / 1e12, 1)
+            entry["frac_fp4_peak"] = round(fl / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)
+        res[name] = entry
+    print(json.dumps({"workload": args.workload, "what": WORKLOADS[args.workload], "steps": args.steps,
+                      "warmup": args.warmup, "kernels": res}), flush=True)
 
 
 def main():
@@ -64,6 +197,9 @@ def main():
         print("bench.py measures one GPU only: libmxfp4 has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.workload != "fc2_step":
+        run_workload(args)
+        return
 
     import torch
     import mxfp4_precision_amd as mx

@@ -193,6 +193,22 @@ def gemm_rows(qa, sa, qb, sb, M: int, N: int, K: int, i0: int, i1: int) -> np.nd
     return out
 
 
+def gemm_dense(qa, sa, qb, sb, M: int, N: int, K: int):
+    """Whole C = deq(A) . deq(B)^T over the padded K and S = |deq(A)| . |deq(B)|^T
+    (the sum of |products| each entry's error bar is scaled by), both fp64 M x N:
+    the oracle's exact dequantization, then numpy's float64 matrix product (a
+    library routine standing in for the sum; its rounding, ~K 2^-53 S, is far
+    below any bar it is used for).  Used where the entry-by-entry sum would
+    take too long (full-size products)."""
+    da = dequantize(qa, sa, M, K)
+    db = dequantize(qb, sb, N, K)
+    C = da @ db.T
+    np.abs(da, out=da)
+    np.abs(db, out=db)
+    S = da @ db.T
+    return C, S
+
+
 def e5m2_value(code: int) -> float:
     """Exact value of an FP8 E5M2 code (OFP8)."""
     return float(lib().oracle_e5m2_value(code))

@@ -72,13 +72,43 @@ def _gemm_checked(oracle_mod, what, A, B, oA, oB, M, N, K, nsample, seed):
         % (what, M, N, K, exact, ii.size, tau_only, rel))
 
 
-def _step(oracle_mod, X, W, dY, wopts=None, wkw=None, gopts=None, gkw=None, nsample=4096, tag=""):
+def _gemm_full_checked(oracle_mod, what, A, B, oA, oB, M, N, K):
+    """Every entry: the bf16 output (the launch the step uses) within the bf16
+    bar of the oracle's product, the fp32 output within tau + 2^-24 |C| of it
+    elementwise and within 1e-5 relative Frobenius.  The oracle's whole product
+    is its dequantization times a float64 matmul (gemm_dense)."""
+    (qa, sa), (qb, sb) = A, B
+    (oqa, osa), (oqb, osb) = oA, oB
+    cb = host(gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16))[:M, :N].view(np.uint16)
+    cf = host(gemm(qa, sa, qb, sb, M, N, K, mx.MX_F32))[:M, :N].astype(np.float64)
+    ref, sabs = oracle_mod.gemm_dense(oqa, osa, oqb, osb, M, N, K)
+    tau = (oracle_mod.padded(K) / 32) * 2.0 ** -24 * sabs
+    del sabs
+    exact, tau_only = check_gemm_bf16(cb, ref, tau, oracle_mod, what)
+    del cb
+    err = np.abs(cf - ref)
+    bad = ~(err <= tau + 2.0 ** -24 * np.abs(ref))
+    assert not bad.any(), "%s: %d fp32 entries beyond tau, first at %s" % (what, int(bad.sum()),
+                                                                          np.argwhere(bad)[:3].tolist())
+    rel = np.linalg.norm(cf - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-5, (what, rel)
+    log("%s %dx%dx%d: every entry checked; %d/%d bf16 exact, %d tau-floor only, fp32 rel %.3g, "
+        "fp32 max err/tau %.3g" % (what, M, N, K, exact, ref.size, tau_only, rel,
+                                    float((err / np.maximum(tau, 1e-300)).max())))
+
+
+def _step(oracle_mod, X, W, dY, wopts=None, wkw=None, gopts=None, gkw=None, nsample=4096, tag="", full=False):
     T, din = X.shape
     dout = W.shape[0]
     assert W.shape == (dout, din) and dY.shape == (T, dout)
     (xr, xrs, xc, xcs), (oxr, oxc) = _dual_checked(oracle_mod, tag + "X", X)
     (wr, wrs, wc, wcs), (owr, owc) = _dual_checked(oracle_mod, tag + "W", W, wopts, wkw)
     (gr, grs, gc, gcs), (ogr, ogc) = _dual_checked(oracle_mod, tag + "dY", dY, gopts, gkw)
+    if full:
+        _gemm_full_checked(oracle_mod, tag + "fwd", (xr, xrs), (wr, wrs), oxr, owr, T, dout, din)
+        _gemm_full_checked(oracle_mod, tag + "dgrad", (gr, grs), (wc, wcs), ogr, owc, T, din, dout)
+        _gemm_full_checked(oracle_mod, tag + "wgrad", (gc, gcs), (xc, xcs), ogc, oxc, dout, din, T)
+        return
     # forward Y = X W^T: (T x dout), K = din
     _gemm_checked(oracle_mod, tag + "fwd", (xr, xrs), (wr, wrs), oxr, owr, T, dout, din, nsample, 11)
     # dgrad dX = dY W: A = dY_row (T rows, K = dout), B = W_col (din rows, K = dout)
@@ -110,3 +140,22 @@ def test_fc2_recipe_step_ragged(oracle_mod):
     sr = mx.quant_opts(use_sr=True, seed=7, tensor_id=2)
     _step(oracle_mod, X, W, dY, w2, dict(use_2d=True, tensor_id=1), sr, dict(use_sr=True, seed=7, tensor_id=2),
           nsample=8192, tag="fc2-ragged-")
+
+
+def test_fc2_step_full_size_every_entry(oracle_mod):
+    """The MLP fc2 training step exactly as the benchmark runs it, at full size
+    (18432 tokens, 12288 -> 3072; seed 4): X GELU(N(0,1)) plain, W N(0,0.02)
+    with 32x32 blocks in both directions, dY N(0,1e-3) with stochastic
+    rounding in both directions (seed 7, tensor id 2).  Every byte of the six
+    blobs against the oracle; fwd X_row . W_row^T, dgrad dY_row . W_col^T and
+    wgrad dY_col . X_col^T from those blobs, every entry of each product
+    (bf16 output from the persistent and tail kernels the step launches, and
+    fp32 output) against the oracle's product of its own blobs."""
+    _require_gpu()
+    d = synth.fc2()
+    input_digests.check("fc2", d)
+    log("fc2 step X %s W %s dY %s" % (d["X"].shape, d["W"].shape, d["dY"].shape))
+    w2 = mx.quant_opts(use_2d_block=True, tensor_id=1)
+    sr = mx.quant_opts(use_sr=True, seed=7, tensor_id=2)
+    _step(oracle_mod, d["X"], d["W"], d["dY"], w2, dict(use_2d=True, tensor_id=1), sr,
+          dict(use_sr=True, seed=7, tensor_id=2), tag="fc2-", full=True)

@@ -67,6 +67,33 @@ def test_gemm_against_numpy_matmul(oracle_mod):
     assert np.linalg.norm(C - ref) <= 1e-12 * np.linalg.norm(ref)
 
 
+def test_gemm_dense_matches_entry_sums(oracle_mod):
+    """gemm_dense (dequantize + float64 matmul) against the oracle's own
+    entry-by-entry sum on every entry of a ragged shape with outliers and zero
+    blocks, and its |product| sums against a direct sum; then a transposed
+    operand (a plausible wiring mistake) must fail the same comparison."""
+    M, N, K = 70, 45, 777
+    a = synth.random_bf16(37, (M, K), std=1.0)
+    b = synth.random_bf16(38, (N, K), std=0.02)
+    a[3, :64] = 0
+    a[5, 10] = synth.bf16_bits(np.array([3e3], np.float32))[0]
+    qa, sa = oracle_mod.quantize(a, 0)
+    qb, sb = oracle_mod.quantize(b, 0)
+    C, S = oracle_mod.gemm_dense(qa, sa, qb, sb, M, N, K)
+    ref = oracle_mod.gemm_rows(qa, sa, qb, sb, M, N, K, 0, M)
+    assert C.shape == (M, N) and S.shape == (M, N)
+    assert np.abs(C - ref).max() <= 1e-13 * S.max()
+    da = oracle_mod.dequantize(qa, sa, M, K)
+    db = oracle_mod.dequantize(qb, sb, N, K)
+    i, j = 5, 7
+    assert abs(S[i, j] - sum(abs(da[i, k] * db[j, k]) for k in range(da.shape[1]))) <= 1e-12 * S[i, j]
+    assert (S >= np.abs(C) - 1e-12 * S).all()
+    Ct, _ = oracle_mod.gemm_dense(qb, sb, qa, sa, N, M, K)
+    assert np.abs(Ct.T - C).max() <= 1e-13 * S.max()                   # the product's own symmetry
+    Cw, _ = oracle_mod.gemm_dense(qa, sa, qa[:N], sa[:N], M, N, K)   # wrong B operand: must differ
+    assert np.abs(Cw - ref).max() > 1e-3 * np.abs(ref).max()
+
+
 def test_gemm_hand_dot_product(oracle_mod):
     """K = 32 of 1.0 against 0.5 (unit-scale blocks): 32 * 0.5 = 16 in every entry."""
     a = synth.bf16_bits(np.ones((2, 32), np.float32) * 4.0)   # amax 4 -> scale 2^0, code 6
