@@ -55,8 +55,13 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(_LIB_PATH)
+        # MX_ORACLE_LIB names another build of mx_oracle.c (the sanitizer build
+        # the CPU tests run); the default is the build next to this file.
+        path = os.environ.get("MX_ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB_PATH
+        L = ctypes.CDLL(path)
         L.oracle_quantize.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _u64, _u32, _u64, _u32, _vp, _vp]
         L.oracle_quantize.restype = _int
         L.oracle_dequantize.argtypes = [_vp, _vp, _i64, _i64, _vp]
