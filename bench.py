@@ -74,8 +74,8 @@ WORKLOADS = {
 
 
 def run_workload(args):
-    """--workload NAME: that workload's kernels only, `steps` passes after
-    `warmup`, per-kernel mean of HIP events on the launch stream."""
+    """--workload NAME: that workload's kernels only, each timed over `steps`
+    batches of back-to-back launches with HIP events on the launch stream."""
     import torch
     import mxfp4_precision_amd as mx
     from mxfp4_precision_amd import synth
@@ -159,26 +159,27 @@ def run_workload(args):
                 0, 1, M, N, K, A_, As_, B_, Bs_, T, mx.MX_BF16, C_, ldc, stream))(M, N, K, A_, As_, B_, Bs_, C_, ldc),
                 1, None, 2.0 * M * N * K))
 
-    def one_pass(p, ev=None):
-        for k, (_, fn, nsets, _, _) in enumerate(kernels):
-            if ev is not None:
-                ev[k].record(stream)
-            fn(p % nsets)
-        if ev is not None:
-            ev[len(kernels)].record(stream)
-
-    for p in range(args.warmup):
-        one_pass(p)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
-    for p in range(args.steps):
-        one_pass(p, evs[p])
-    torch.cuda.synchronize()
+    # Each kernel timed on its own: batches of 20 back-to-back launches (rotating
+    # buffer sets) between two events on the launch stream, so that host
+    # enqueue time never shows between launches; median, mean and minimum
+    # over `steps` batches after `warmup` untimed launches.
+    per = 20
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     res = {}
-    for k, (name, _, nsets, nbytes, fl) in enumerate(kernels):
-        t = [e[k].elapsed_time(e[k + 1]) for e in evs]
-        ms = float(np.mean(t))
-        entry = {"ms": round(ms, 5), "ms_median": round(float(np.median(t)), 5), "ms_min": round(float(np.min(t)), 5),
+    for name, fn, nsets, nbytes, fl in kernels:
+        for i in range(max(args.warmup, 2 * nsets)):
+            fn(i % nsets)
+        torch.cuda.synchronize()
+        t = []
+        for b in range(args.steps):
+            ev[0].record(stream)
+            for j in range(per):
+                fn((b * per + j) % nsets)
+            ev[1].record(stream)
+            ev[1].synchronize()
+            t.append(ev[0].elapsed_time(ev[1]) / per)
+        ms = float(np.median(t))
+        entry = {"ms": round(ms, 5), "ms_mean": round(float(np.mean(t)), 5), "ms_min": round(float(np.min(t)), 5),
                  "buffer_sets": nsets}
         if nbytes:
             entry["GB/s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
@@ -187,8 +188,8 @@ def run_workload(args):
             entry["TFLOP/s"] = round(fl / (ms * 1e-3) / 1e12, 1)
             entry["frac_fp4_peak"] = round(fl / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)
         res[name] = entry
-    print(json.dumps({"workload": args.workload, "what": WORKLOADS[args.workload], "steps": args.steps,
-                      "warmup": args.warmup, "kernels": res}), flush=True)
+    print(json.dumps({"workload": args.workload, "what": WORKLOADS[args.workload], "batches": args.steps,
+                      "launches_per_batch": per, "warmup": args.warmup, "kernels": res}), flush=True)
 
 
 def main():
