@@ -10,6 +10,13 @@
 // pipeline and slot schedule as the main kernel, scaled down: 4 waves of
 // 64x64 (2x2 MFMA tiles), 16 atoms (16 KB) per LDS stage, so two workgroups
 // fit one CU and each SIMD still interleaves two waves.
+//
+// When the leftover tiles give at most one 128x128 tile per CU (the fc2 and
+// fc1 wgrad: 64 leftover 256x256 tiles on 256 CUs), a lone 4-wave workgroup
+// would leave each SIMD one wave with nothing to hide its waits behind.  The
+// split form then runs two groups of 4 waves per workgroup on the same tile,
+// each group the pipeline above over one half of K (its own LDS stages), and
+// adds the two fp32 partial tiles through LDS before the epilogue.
 
 #include <type_traits>
 
@@ -66,12 +73,21 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kStageBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_scale[kAtoms * 256];
+// the second K group's pipeline (split form only)
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage4[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage5[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage6[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage7[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_scale1[kAtoms * 256];
 
-template <int S>
+// stage S of K group G (G = 0 in the plain form)
+template <int S, int G = 0>
 __device__ __forceinline__ uint8_t *stage_buf() {
-    return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+    if constexpr (G == 0) return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
+    else return S == 0 ? g_stage4 : S == 1 ? g_stage5 : S == 2 ? g_stage6 : g_stage7;
 }
-__device__ __forceinline__ uint8_t *scale_buf() { return g_scale; }
+template <int G = 0>
+__device__ __forceinline__ uint8_t *scale_buf() { return G == 0 ? g_scale : g_scale1; }
 __device__ __forceinline__ uint8_t *stage_dyn(int s) {
     return s == 0 ? g_stage0 : s == 1 ? g_stage1 : s == 2 ? g_stage2 : g_stage3;
 }
@@ -104,19 +120,19 @@ struct Regs {
 // atom kWaves*V + wave; V >= kLoads (only when k opens a k-group) copies scale
 // atom kWaves*(V - kLoads) + wave.  Past K_pad the offset is out of range and
 // the atom lands as zeros.
-template <int S, int V>
+template <int S, int V, int G>
 __device__ __forceinline__ void dma_op(const GemmCtx &c, int64_t k) {
     if constexpr (V < kLoads) {
         const int a = kWaves * V + c.wave;
         const uint32_t base = k < c.ksteps ? (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS(stage_buf<S>() + a * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS((stage_buf<S, G>() + a * 1024)), 16,
                                                  base + c.lane16, 0, 0, 0);
     } else {
         constexpr int R = V - kLoads;
         const int a = kWaves * R + c.wave;
         const int64_t h = k / 4;
         const uint32_t base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(scale_buf() + a * 256), 4,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rAs : c.rBs, MX_LDS(scale_buf<G>() + a * 256), 4,
                                                  base + c.lane4, 0, 0, 0);
     }
 }
@@ -136,11 +152,11 @@ __host__ __device__ constexpr int dma_slot(int n, int nv) {
     return s > kSlots - 1 ? kSlots - 1 : s;
 }
 
-template <int S, int P, int n = 0>
+template <int S, int P, int G, int n = 0>
 __device__ __forceinline__ void dma_part(const GemmCtx &c, int64_t k) {
     if constexpr (n < part_ops(S)) {
-        dma_op<S, part_op(S, P, n)>(c, k);
-        dma_part<S, P, n + 1>(c, k);
+        dma_op<S, part_op(S, P, n), G>(c, k);
+        dma_part<S, P, G, n + 1>(c, k);
     }
 }
 
@@ -168,7 +184,7 @@ struct Lds {
 //  - at S == 3, half 1 also reads the next k-group's scales, two per slot.
 //  - the DMA instructions this slot carries (half 0: part 1 of step k+2,
 //    half 1: part 0 of step k+3).
-template <int S, int H, int T>
+template <int S, int H, int T, int G>
 __device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
     constexpr int i = T / kMA, j = T % kMA;
     if constexpr (H == 0) mfma_tile<S>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
@@ -177,7 +193,7 @@ __device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kM
     if constexpr (T < kMA + kMB) {
         constexpr int RS = H == 0 ? S : ((S + 1) & 3);
         constexpr int RH = H == 0 ? 1 : 0;
-        const uint8_t *st = stage_buf<RS>() + l.frag_off + RH * 512;
+        const uint8_t *st = stage_buf<RS, G>() + l.frag_off + RH * 512;
         if constexpr (T == 0 || T > kMA) {
             constexpr int bi = T == 0 ? 0 : T - kMA;
             const uint4 v = *reinterpret_cast<const uint4 *>(st + (l.b_atom0 + 2 * bi) * 1024);
@@ -195,10 +211,10 @@ __device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kM
             const int q = 2 * (T - kScStart) + e;
             const int hh = q & 1, t = q >> 1;
             if (t < kMA)
-                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf<G>() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
             else
                 r.sb_n[t - kMA][hh] =
-                    *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
+                    *reinterpret_cast<const uint32_t *>(scale_buf<G>() + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
         }
     }
 
@@ -206,20 +222,20 @@ __device__ __forceinline__ void slot(const GemmCtx &c, int64_t k, v16f (&acc)[kM
     constexpr int P = H == 0 ? 1 : 0;
     constexpr int nv = part_ops(DS);
     const int64_t dk = H == 0 ? k + 2 : k + 3;
-    if constexpr (dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0)>(c, dk);
-    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1)>(c, dk);
-    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2)>(c, dk);
-    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3)>(c, dk);
+    if constexpr (dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0), G>(c, dk);
+    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1), G>(c, dk);
+    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2), G>(c, dk);
+    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3), G>(c, dk);
     static_assert(part_ops(0) <= 4, "dma slots");
     // keep this slot's instructions in this slot
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S, int H, int T = 0>
+template <int S, int H, int G, int T = 0>
 __device__ __forceinline__ void half_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
     if constexpr (T < kSlots) {
-        slot<S, H, T>(c, k, acc, r, l);
-        half_step<S, H, T + 1>(c, k, acc, r, l);
+        slot<S, H, T, G>(c, k, acc, r, l);
+        half_step<S, H, G, T + 1>(c, k, acc, r, l);
     }
 }
 
@@ -227,13 +243,13 @@ __device__ __forceinline__ void half_step(const GemmCtx &c, int64_t k, v16f (&ac
 // (only step k+2's instructions may still be outstanding) and then for every
 // wave, which publishes step k+1 and certifies that all reads of step k-1's
 // stage are done before half 1 starts overwriting it.
-template <int S>
+template <int S, int G>
 __device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], Regs &r, const Lds &l) {
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 0>(c, k, acc, r, l);
+    half_step<S, 0, G>(c, k, acc, r, l);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3)) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 1>(c, k, acc, r, l);
+    half_step<S, 1, G>(c, k, acc, r, l);
     if constexpr (S == 3) {
 #pragma unroll
         for (int t = 0; t < kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
@@ -248,9 +264,12 @@ __device__ __forceinline__ void k_step(const GemmCtx &c, int64_t k, v16f (&acc)[
 // written as whole 256-byte row segments (each store instruction covers 4
 // rows with 16 bytes per lane; non-temporal, as C is not read again here);
 // fp32: 16 bytes per lane straight from registers.  Masked at the M/N edges.
-template <bool OUT_BF16>
+// NG K groups share the workgroup: group 0 holds the summed accumulators
+// (wave = its index in the group); all NG * kWaves waves (index wave_all)
+// take part in the bf16 stores.
+template <bool OUT_BF16, int NG>
 __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn, int64_t M, int64_t N, void *C,
-                                           int64_t ldc, int wave, int lane) {
+                                           int64_t ldc, int group, int wave, int wave_all, int lane) {
     const int wm = wave % kWavesM, wn = wave / kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
     const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
@@ -259,28 +278,32 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
         // them have landed and every stage read is done before the tile
         // overwrites the stages.
         __syncthreads();
+        if (group == 0) {
 #pragma unroll
-        for (int j = 0; j < kMA; ++j)
+            for (int j = 0; j < kMA; ++j)
 #pragma unroll
-            for (int i = 0; i < kMB; ++i)
+                for (int i = 0; i < kMB; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
-                    const uint32_t p01 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
-                    const uint32_t p23 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
-                    *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
+                        const uint32_t p01 = __builtin_bit_cast(
+                            uint32_t,
+                            __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
+                        const uint32_t p23 = __builtin_bit_cast(
+                            uint32_t,
+                            __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
+                        *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
+                    }
+        }
         __syncthreads();
-        constexpr int kRowsPerWave = kBM / kWaves;        // 32: 8 instructions of 4 rows
+        constexpr int kRowsPerWave = kBM / (kWaves * NG);   // 32 or 16: instructions of 4 rows
         const int cl = (lane & 15) * 8;
         const int64_t col = tn0 + cl;
         uint4 v[kRowsPerWave / 4];
 #pragma unroll
         for (int it = 0; it < kRowsPerWave / 4; ++it)
-            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave + 4 * it + (lane >> 4), cl));
-        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave + (lane >> 4)) * ldc + col;
+            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave_all + 4 * it + (lane >> 4), cl));
+        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave_all + (lane >> 4)) * ldc + col;
         if (tm0 + kBM <= M && tn0 + kBN <= N) {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 4; ++it)
@@ -288,7 +311,7 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
         } else {
 #pragma unroll
             for (int it = 0; it < kRowsPerWave / 4; ++it) {
-                const int64_t row = tm0 + kRowsPerWave * wave + 4 * it + (lane >> 4);
+                const int64_t row = tm0 + kRowsPerWave * wave_all + 4 * it + (lane >> 4);
                 if (row >= M || col >= N) continue;
                 uint16_t *dst = dst0 + 4 * it * ldc;
                 if (col + 7 < N) {
@@ -302,6 +325,7 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
             }
         }
     } else {
+        if (group != 0) return;
         const int64_t m0 = tm0 + wm * kWM, n0 = tn0 + wn * kWN;
 #pragma unroll
         for (int j = 0; j < kMA; ++j) {
@@ -327,20 +351,77 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
     }
 }
 
+// The k-loop of K group G: prologue DMAs, then `iters` k-groups of 4 k-steps
+// (k-steps at or past c.ksteps land as zeros), then the drain of the trailing
+// DMAs.  Every wave of the workgroup runs the same number of k-steps, so the
+// per-step barriers line up across groups.
+template <int G>
+__device__ __forceinline__ void run_k(const GemmCtx &c, v16f (&acc)[kMB][kMA], const Lds &l, int64_t iters) {
+    // Prologue: steps 0 and 1 whole, the first part of step 2 (its second
+    // part goes out in step 0's first half).
+    dma_part<0, 0, G>(c, 0);
+    dma_part<0, 1, G>(c, 0);
+    dma_part<1, 0, G>(c, 1);
+    dma_part<1, 1, G>(c, 1);
+    dma_part<2, 0, G>(c, 2);
+
+    Regs r;
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + part_ops(2)) : "memory");
+#pragma unroll
+    for (int t = 0; t < kMA; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            r.sa[t][hh] =
+                *reinterpret_cast<const uint32_t *>(scale_buf<G>() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+#pragma unroll
+    for (int t = 0; t < kMB; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            r.sb[t][hh] =
+                *reinterpret_cast<const uint32_t *>(scale_buf<G>() + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+#pragma unroll
+    for (int t = 0; t < kMA; ++t)
+        r.a0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0, G>() + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
+#pragma unroll
+    for (int t = 0; t < kMB; ++t)
+        r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0, G>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
+
+    for (int64_t h = 0; h < iters; ++h) {
+        const int64_t k0 = 4 * h;
+        k_step<0, G>(c, k0, acc, r, l);
+        k_step<1, G>(c, k0 + 1, acc, r, l);
+        k_step<2, G>(c, k0 + 2, acc, r, l);
+        k_step<3, G>(c, k0 + 3, acc, r, l);
+    }
+    // drain the trailing (out-of-range) DMAs before LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Split form: 4 KB of the second group's stages per accumulator tile of a
+// wave (wave w of the group owns stage 4 + w), float e of lane L at
+// (e * 64 + L) * 4, so consecutive lanes touch consecutive banks.
+__device__ __forceinline__ float *partial_slot(int wave, int tile) {
+    uint8_t *base = wave == 0 ? g_stage4 : wave == 1 ? g_stage5 : wave == 2 ? g_stage6 : g_stage7;
+    return reinterpret_cast<float *>(base + tile * 4096);
+}
+
 // BIAS: C[i][j] = (sum) + bias[j], bias a bf16 vector of N, added in fp32
 // before the output rounding.
 // Workgroup b computes quarter b % 4 of 256x256 tile first + b / 4 of the
 // main kernel's tile order (tiles_m x tiles_n 256x256 tiles, bands of 8 rows).
-template <bool OUT_BF16, bool BIAS>
-__global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
-                                                                  int tiles_n, int first, const uint8_t *__restrict__ A,
-                                                             const uint8_t *__restrict__ As,
-                                                             const uint8_t *__restrict__ B,
-                                                             const uint8_t *__restrict__ Bs,
-                                                             const uint16_t *__restrict__ bias,
-                                                             void *__restrict__ C, int64_t ldc) {
+// SPLIT: 8 waves, K group g = wave / 4 takes k-groups [g * kg0, ...) of the
+// tile (kg0 = half of them, rounded up); group 1's partial tile is added into
+// group 0's through LDS before the epilogue.
+template <bool OUT_BF16, bool BIAS, bool SPLIT>
+__global__ __launch_bounds__(SPLIT ? 2 * kThreads : kThreads) void gemm_a4w4_tail_kernel(
+    int64_t M, int64_t N, int64_t K_pad, int tiles_m, int tiles_n, int first, const uint8_t *__restrict__ A,
+    const uint8_t *__restrict__ As, const uint8_t *__restrict__ B, const uint8_t *__restrict__ Bs,
+    const uint16_t *__restrict__ bias, void *__restrict__ C, int64_t ldc) {
+    constexpr int NG = SPLIT ? 2 : 1;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int group = SPLIT ? wave_all / kWaves : 0;
+    const int wave = wave_all % kWaves;
     const int wm = wave % kWavesM, wn = wave / kWavesM;
 
     // ---- which 128x128 tile: quarter of a leftover 256x256 tile of the main order
@@ -351,18 +432,22 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
     const int tm = 2 * (first_m + (id % band) % gsz) + (quarter >> 1);
     const int tn = 2 * ((id % band) / gsz) + (quarter & 1);
 
+    const int64_t ksteps = K_pad / 128, kgroups = cdiv(K_pad, 512);
+    // k-groups of group 0 (all of them without the split); group 1 starts at k-group kg0
+    const int64_t kg0 = SPLIT ? (kgroups + 1) / 2 : kgroups;
+    const int64_t kfirst = group ? 4 * kg0 : 0;
     GemmCtx c;
-    c.ksteps = K_pad / 128;
-    c.kgroups = cdiv(K_pad, 512);
+    c.ksteps = group ? ksteps - kfirst : (SPLIT ? (ksteps < 4 * kg0 ? ksteps : 4 * kg0) : ksteps);
+    c.kgroups = group ? kgroups - kg0 : kg0;
     c.wave = wave;
     c.lane16 = lane * 16;
     c.lane4 = lane * 4;
     const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);   // row groups present in memory
     const int64_t gA0 = (int64_t)tm * kGA, gB0 = (int64_t)tn * kGB;
-    c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
-    c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
-    c.rAs = make_rsrc(As, nGA * c.kgroups * 256);
-    c.rBs = make_rsrc(Bs, nGB * c.kgroups * 256);
+    c.rA = make_rsrc(A, nGA * ksteps * 1024);
+    c.rB = make_rsrc(B, nGB * ksteps * 1024);
+    c.rAs = make_rsrc(As, nGA * kgroups * 256);
+    c.rBs = make_rsrc(Bs, nGB * kgroups * 256);
 
     // This lane's bias values (columns n0 + 32i + 8q + 4(lane/32) + 0..3 of its
     // tile, 4 bf16 per (i, q)), loaded before the k-loop so they have long
@@ -383,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
                 bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
     }
     // Row groups past an operand are clamped to its last group: those rows of C
-    // are never stored, so their contents do not matter.
+    // are never stored, so their contents do not matter.  A group's offsets
+    // start at its first k-step.
 #pragma unroll
     for (int r = 0; r < kLoads; ++r) {
         const int a = kWaves * r + wave;
@@ -391,8 +477,8 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
         int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
         const int64_t gmax = (isA ? nGA : nGB) - 1;
         g = g < gmax ? g : gmax;
-        c.ld_row[r] = (int)(g * c.ksteps * 1024);
-        c.sc_row[r] = (int)(g * c.kgroups * 256);
+        c.ld_row[r] = (int)((g * ksteps + kfirst) * 1024);
+        c.sc_row[r] = (int)((g * kgroups + kfirst / 4) * 256);
     }
 
     v16f acc[kMB][kMA];
@@ -400,14 +486,6 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
     for (int i = 0; i < kMB; ++i)
 #pragma unroll
         for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
-
-    // Prologue: steps 0 and 1 whole, the first part of step 2 (its second
-    // part goes out in step 0's first half).
-    dma_part<0, 0>(c, 0);
-    dma_part<0, 1>(c, 0);
-    dma_part<1, 0>(c, 1);
-    dma_part<1, 1>(c, 1);
-    dma_part<2, 0>(c, 2);
 
     // Lane L of a 32-row operand tile takes row L%32, k-block 2*half + L/32:
     // atom (L%32)/16, slice (L%16) + 16*(2*half + L/32).  Its scale is byte
@@ -419,54 +497,56 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
     l.a_atom0 = wm * kTA;
     l.b_atom0 = kGA + wn * kTB;
 
-    Regs r;
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + part_ops(2)) : "memory");
-#pragma unroll
-    for (int t = 0; t < kMA; ++t)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-#pragma unroll
-    for (int t = 0; t < kMB; ++t)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-#pragma unroll
-    for (int t = 0; t < kMA; ++t)
-        r.a0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
-#pragma unroll
-    for (int t = 0; t < kMB; ++t)
-        r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
+    if (SPLIT && group == 1) run_k<1>(c, acc, l, kg0);
+    else run_k<0>(c, acc, l, kg0);
 
-    for (int64_t h = 0; h < c.kgroups; ++h) {
-        const int64_t k0 = 4 * h;
-        k_step<0>(c, k0, acc, r, l);
-        k_step<1>(c, k0 + 1, acc, r, l);
-        k_step<2>(c, k0 + 2, acc, r, l);
-        k_step<3>(c, k0 + 3, acc, r, l);
+    if constexpr (SPLIT) {
+        // every wave is past its last stage read; group 1's stages take its partial tile
+        __syncthreads();
+        if (group == 1) {
+#pragma unroll
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < kMA; ++j) {
+                    float *p = partial_slot(wave, i * kMA + j) + lane;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) p[e * 64] = acc[i][j][e];
+                }
+        }
+        __syncthreads();
+        if (group == 0) {
+#pragma unroll
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < kMA; ++j) {
+                    const float *p = partial_slot(wave, i * kMA + j) + lane;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += p[e * 64];
+                }
+        }
     }
-    // drain the trailing (out-of-range) DMAs before LDS is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue
     if constexpr (BIAS) {
+        if (group == 0) {
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+            for (int i = 0; i < kMB; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v2u bb = bias_bits[i * 4 + q];
-                const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
-                const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
+                for (int q = 0; q < 4; ++q) {
+                    const v2u bb = bias_bits[i * 4 + q];
+                    const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
+                    const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
 #pragma unroll
-                for (int j = 0; j < kMA; ++j) {
-                    acc[i][j][4 * q] += b0;
-                    acc[i][j][4 * q + 1] += b1;
-                    acc[i][j][4 * q + 2] += b2;
-                    acc[i][j][4 * q + 3] += b3;
+                    for (int j = 0; j < kMA; ++j) {
+                        acc[i][j][4 * q] += b0;
+                        acc[i][j][4 * q + 1] += b1;
+                        acc[i][j][4 * q + 2] += b2;
+                        acc[i][j][4 * q + 3] += b3;
+                    }
                 }
-            }
+        }
     }
-    store_tile<OUT_BF16>(acc, tm, tn, M, N, C, ldc, wave, lane);
+    store_tile<OUT_BF16, NG>(acc, tm, tn, M, N, C, ldc, group, wave, wave_all, lane);
 }
 
 }  // namespace
@@ -474,10 +554,16 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_tail_kernel(int64_t M, int
 hipError_t launch_gemm_tail(int64_t M, int64_t N, int64_t K_pad, int tiles_m, int tiles_n, int first, int count,
                             const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs,
                             const uint16_t *bias, mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream) {
-    auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_tail_kernel<true, true> : gemm_a4w4_tail_kernel<true, false>)
-                                       : (bias ? gemm_a4w4_tail_kernel<false, true> : gemm_a4w4_tail_kernel<false, false>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * count)), dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n,
-                       first, A, As, B, Bs, bias, C, ldc);
+    // at most one 128x128 tile per CU (and K long enough to halve): the split form
+    const int cus = device_cu_count();
+    const bool split = cus > 0 && 4 * count <= cus && K_pad >= 8 * 128;
+    const bool bf = out_dtype == MX_BF16;
+    auto kernel = split ? (bf ? (bias ? gemm_a4w4_tail_kernel<true, true, true> : gemm_a4w4_tail_kernel<true, false, true>)
+                              : (bias ? gemm_a4w4_tail_kernel<false, true, true> : gemm_a4w4_tail_kernel<false, false, true>))
+                        : (bf ? (bias ? gemm_a4w4_tail_kernel<true, true, false> : gemm_a4w4_tail_kernel<true, false, false>)
+                              : (bias ? gemm_a4w4_tail_kernel<false, true, false> : gemm_a4w4_tail_kernel<false, false, false>));
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * count)), dim3(split ? 2 * kThreads : kThreads), 0, stream, M, N,
+                       K_pad, tiles_m, tiles_n, first, A, As, B, Bs, bias, C, ldc);
     return hipGetLastError();
 }
 

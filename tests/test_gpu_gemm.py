@@ -240,16 +240,21 @@ def test_bias_k_zero_writes_bias(oracle_mod):
     assert (cf.astype(np.float64) == oracle_mod.bf16_to_double(bias)[None, :]).all()
 
 
-def test_tail_tiles_bias_every_entry_of_tail_rows(oracle_mod):
+@pytest.mark.parametrize("K", [384, 1100, 2048])
+def test_tail_tiles_bias_every_entry_of_tail_rows(oracle_mod, K):
     """Tile count past one round on 256 CUs with a small last round: the last
     round runs as 128x128 tiles (4597x4349 -> 18x17 = 306 tiles of 256x256; the
     last 50 of the tile order, which hold the ragged last row and column of
-    tiles, become 200 tiles of 128x128).  With a bias, in bf16 and fp32: every
-    entry of rows in the main and the tail region, against the oracle."""
+    tiles, become 200 tiles of 128x128).  K 384: one workgroup of 4 waves per
+    small tile; K 1100 (3 k-groups: 2 + 1, the second group's last steps past
+    K) and 2048 (4 k-groups: 2 + 2): at most one small tile per CU, so each
+    runs as two K groups of 4 waves summed through LDS.  With a bias, in bf16
+    and fp32: every entry of rows in the main and the tail region, against
+    the oracle, and the bf16 output equal to the rounding of the fp32 one."""
     _require_gpu()
-    M, N, K = 4597, 4349, 384
-    a = synth.random_bf16(91, (M, K), std=1.0)
-    b = synth.random_bf16(92, (N, K), std=0.05)
+    M, N = 4597, 4349
+    a = synth.random_bf16(91 + K, (M, K), std=1.0)
+    b = synth.random_bf16(92 + K, (N, K), std=0.05)
     bias = synth.random_bf16(93, (N,), std=2.0)
     log("tail tiles with bias %dx%dx%d" % (M, N, K))
     ad, lda = to_dev_bf16(a)
@@ -271,8 +276,8 @@ def test_tail_tiles_bias_every_entry_of_tail_rows(oracle_mod):
     exact, _ = check_gemm_bf16(cb[ii, jj], ref, tau, oracle_mod, "tail-bias")
     rel = np.linalg.norm(cf[ii, jj] - ref) / max(np.linalg.norm(ref), 1e-300)
     assert rel <= 1e-5, rel
-    assert (cb[:, N:] if cb.shape[1] > N else cb[:0]).size == 0
-    log("tail-bias: %d/%d bf16 exact, fp32 rel %.3g" % (exact, ii.size, rel))
+    assert np.array_equal(cb, _rne_bf16_bits(cf))
+    log("tail-bias K %d: %d/%d bf16 exact, fp32 rel %.3g" % (K, exact, ii.size, rel))
 
 
 def _rne_bf16_bits(f32):
