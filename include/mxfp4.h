@@ -117,8 +117,11 @@ typedef enum mx_dtype {
  *   Walsh-Hadamard transform over position bits 0..4, each (a, b) -> (a + b,
  *   a - b) rounded to fp32; c = fp32(1/sqrt(32)).  Pads count as +0 before
  *   the transform, so pad positions of a block that holds real elements get
- *   codes too (their SR byte uses the same index formula on padded
- *   coordinates).  Both operands of a GEMM must be transformed with the same
+ *   codes too.  With use_sr their byte uses the same index formula on padded
+ *   coordinates in a counter space of their own: counter word 3 is 2 + dir,
+ *   so no pad shares a byte with a real element (and, for the row-wise blob
+ *   with N >= 64 and for the column-wise blob, with another pad).  Both
+ *   operands of a GEMM must be transformed with the same
  *   rht value along the shared K axis: (H D)^T (H D) c^2 ~= I leaves the
  *   product unchanged.  Not combined with use_2d_block (MX_ERR_UNSUPPORTED).
  * The scale never depends on use_sr.  NULL options = all zero.

@@ -488,7 +488,11 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int t = 0; t < 8; ++t) {
                 const int64_t i = row0 + 8 * q + t;
                 const uint64_t g = (o.index_base + (uint64_t)i * (uint64_t)N + jpair) >> 4;
-                uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p;
+                // pads draw from counter word 3 = 2 + dir: the row blob's pads
+                // are columns past N (whole 16-blocks, N % 16 == 0 here), the
+                // column blob's rows past M
+                const bool pad = p ? i >= M : (int64_t)jpair >= N;
+                uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p + (pad ? 2u : 0u);
                 philox10(w0, w1, w2, w3, o.key0, o.key1);
                 const uint32_t r0 = (uint32_t)__shfl_xor((int)(p ? w0 : w2), 1, 64);
                 const uint32_t r1 = (uint32_t)__shfl_xor((int)(p ? w1 : w3), 1, 64);
@@ -503,11 +507,25 @@ __global__ __launch_bounds__(256) __attribute__((
                 const int64_t i = row0 + 8 * q + t;
                 rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
                 // pads too: after a Hadamard transform they carry values (otherwise they are 0 and
-                // round to 0 with any byte)
-                if (ROW_SR)
-                    rand8(a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
+                // round to 0 with any byte); they draw from counter word 3 = 2 + dir
+                if (ROW_SR) {
+                    const uint64_t n0 = a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0;
+                    rand8(n0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
+                    if (j0 + 8 > N) {
+                        // columns past N among the lane's 8: take their bytes from the pad space
+                        uint32_t plo, phi;
+                        rand8(n0, a.row, 2u, plo, phi);
+                        const int64_t nreal = N - j0;          // real columns of the lane (may be <= 0)
+                        const uint64_t keep = nreal <= 0 ? 0ull : (~0ull >> (64 - 8 * nreal));
+                        const uint64_t v = (((uint64_t)rrow_hi[t] << 32) | rrow_lo[t]) & keep;
+                        const uint64_t w = (((uint64_t)phi << 32) | plo) & ~keep;
+                        rrow_lo[t] = (uint32_t)(v | w);
+                        rrow_hi[t] = (uint32_t)((v | w) >> 32);
+                    }
+                }
                 if (DUAL && COL_SR)
-                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, 1u, rcol_lo[t], rcol_hi[t]);
+                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, i >= M ? 3u : 1u,
+                          rcol_lo[t], rcol_hi[t]);
             }
         }
     };

@@ -161,7 +161,8 @@ void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t
  * The random byte of logical element n (row-major index into the unpadded
  * M x N tensor, plus the caller's index_base) for one direction:
  * counter = (lo32(n>>4), hi32(n>>4), tensor_id, dir), key = (lo32(seed), hi32(seed)),
- * byte n%16 of the four output words taken little-endian.
+ * byte n%16 of the four output words taken little-endian.  (Pad positions,
+ * which carry values only after a Hadamard transform, pass dir + 2.)
  */
 unsigned oracle_sr_byte(uint64_t seed, uint32_t tensor_id, uint32_t dir, uint64_t n)
 {
@@ -297,7 +298,11 @@ int oracle_quantize(const uint16_t *x, int64_t M, int64_t N, int64_t ldx, int di
                             int64_t i = dir == 0 ? r : k;
                             int64_t j = dir == 0 ? k : r;
                             uint64_t n = index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j;
-                            code = sr_code(v, oracle_sr_byte(seed, tensor_id, (uint32_t)dir, n));
+                            /* pad positions (k >= L) draw from their own counter space,
+                             * counter word 3 = 2 + dir, so they never share a byte with a
+                             * real element */
+                            uint32_t word3 = (uint32_t)dir + (k >= L ? 2u : 0u);
+                            code = sr_code(v, oracle_sr_byte(seed, tensor_id, word3, n));
                         } else {
                             code = rne_code(v);
                         }

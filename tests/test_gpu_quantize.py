@@ -358,6 +358,22 @@ def test_rht_both_directions_stochastic(oracle_mod, layout, shape):
                dict(use_sr=True, seed=6, tensor_id=2, index_base=7, rht=78))
 
 
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", [(200, 80), (97, 160)])
+def test_rht_stochastic_paired_lanes_with_pads(oracle_mod, layout, shape):
+    """RHT and stochastic rounding on both blobs with N and both index bases
+    multiples of 16 (neighbouring lanes share Philox blocks, one per
+    direction), M and N short of the 128-padding: pad blocks of the row blob
+    (columns past N) and pad rows of the column blob draw from their own
+    counter space."""
+    _require_gpu()
+    x = synth.random_bf16(450 + shape[0] + shape[1], shape, std=0.3)
+    row = mx.quant_opts(use_sr=True, seed=15, tensor_id=2, index_base=32, rht=91)
+    col = mx.quant_opts(use_sr=True, seed=16, tensor_id=2, index_base=4096, rht=92)
+    check_dual(oracle_mod, x, layout, row, col, dict(use_sr=True, seed=15, tensor_id=2, index_base=32, rht=91),
+               dict(use_sr=True, seed=16, tensor_id=2, index_base=4096, rht=92))
+
+
 def test_rht_rowwise_and_specials(oracle_mod):
     """Row-wise RHT through mx_quantize_rowwise, with Inf/NaN blocks (scale 0xFF,
     zero codes), signed zeros and large/small magnitudes in other blocks."""

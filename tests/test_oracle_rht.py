@@ -138,30 +138,71 @@ def test_rht_rejects_2d(oracle_mod):
         oracle_mod.quantize(x, 1, use_2d=True, rht=3)
 
 
+def _sr_code(v, r):
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    lo = max(k for k in range(8) if grid[k] <= v) if v < 6 else 7
+    tt = int(np.floor(256 * (v - grid[lo]) / (grid[lo + 1] - grid[lo]))) if lo < 7 else 0
+    return min(lo + (1 if r < tt else 0), 7)
+
+
 def test_rht_sr_bytes_follow_the_index_formula(oracle_mod):
     """With stochastic rounding the transformed element at padded coordinates
-    (i, j) rounds with byte sr_byte(seed, tensor_id, dir, index_base + i N + j):
-    re-deriving each code from the transformed value and that byte."""
-    M, N = 40, 5
+    (i, j) rounds with byte sr_byte(seed, tensor_id, w, index_base + i N + j),
+    w = dir for a real element and 2 + dir for a pad: re-deriving every code
+    of both blobs (column blob: 40 rows = 8 real + 24 pad rows in the second
+    block; row blob: N = 70, pads at columns 70..127) from the transformed
+    value and that byte.  The old rule (pads on w = dir) must fail somewhere."""
+    M, N = 40, 70
     x = synth.random_bf16(21, (M, N), std=1.0)
-    q, s = oracle_mod.quantize(x, 1, use_sr=True, seed=77, tensor_id=3, index_base=1000, rht=5)
-    signs = oracle_mod.rht_signs(5)
-    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
     xf = synth.bf16_to_f32(x)
-    for j in range(N):
-        for blk in range(2):
-            col = np.zeros(32, np.float32)
-            n_real = min(32, M - 32 * blk)
-            col[:n_real] = xf[32 * blk: 32 * blk + n_real, j]
-            y = oracle_mod.rht32(col, signs)
-            e = int(s[j, blk]) - 127
-            for t in range(32):
-                i = 32 * blk + t
-                v = abs(float(y[t])) * 2.0 ** -e
-                r = oracle_mod.sr_byte(77, 3, 1, 1000 + i * N + j)
-                lo = max(k for k in range(8) if grid[k] <= v) if v < 6 else 7
-                tt = int(np.floor(256 * (v - grid[lo]) / (grid[lo + 1] - grid[lo]))) if lo < 7 else 0
-                code = min(lo + (1 if r < tt else 0), 7)
-                b = q[j, i // 2]
-                nib = (b >> 4) if i % 2 else (b & 15)
-                assert (nib & 7) == code and (nib >> 3) == (1 if np.signbit(y[t]) else 0)
+    signs = oracle_mod.rht_signs(5)
+    for direction in (1, 0):
+        q, s = oracle_mod.quantize(x, direction, use_sr=True, seed=77, tensor_id=3, index_base=1000, rht=5)
+        rows, length = (N, M) if direction == 1 else (M, N)
+        old_rule_fails = 0
+        for r in range(rows):
+            for blk in range((length + 127) // 128 * 4):
+                vec = np.zeros(32, np.float32)
+                k0 = 32 * blk
+                n_real = max(0, min(32, length - k0))
+                if direction == 1:
+                    vec[:n_real] = xf[k0:k0 + n_real, r]
+                else:
+                    vec[:n_real] = xf[r, k0:k0 + n_real]
+                y = oracle_mod.rht32(vec, signs)
+                e = int(s[r, blk]) - 127
+                for t in range(32):
+                    k = k0 + t
+                    i, j = (k, r) if direction == 1 else (r, k)
+                    v = abs(float(y[t])) * 2.0 ** -e
+                    pad = k >= length
+                    n = 1000 + i * N + j
+                    byte = oracle_mod.sr_byte(77, 3, direction + (2 if pad else 0), n)
+                    b = q[r, k // 2]
+                    nib = (b >> 4) if k % 2 else (b & 15)
+                    assert (nib & 7) == _sr_code(v, byte), (direction, r, k)
+                    assert (nib >> 3) == (1 if np.signbit(y[t]) else 0)
+                    if pad and (nib & 7) != _sr_code(v, oracle_mod.sr_byte(77, 3, direction, n)):
+                        old_rule_fails += 1
+        assert old_rule_fails > 0, direction
+
+
+@pytest.mark.parametrize("M,N", [(40, 70), (200, 64), (130, 300)])
+def test_sr_counter_positions_are_distinct(M, N):
+    """Every position that draws a stochastic-rounding byte -- the M x N real
+    elements and, after a Hadamard transform, the pads of each direction up to
+    the 128-padded axis -- gets its own (counter, byte) pair: real elements use
+    counter word 3 = dir with n = i N + j, pads word 3 = 2 + dir with the same
+    formula on padded coordinates.  (Row-blob pads would share bytes only for
+    N < 64, where a row's pad run is longer than a row.)"""
+    Mp, Np = -(-M // 128) * 128, -(-N // 128) * 128
+    keys = set()
+    count = 0
+    for direction in (0, 1):
+        for i in range(Mp if direction == 1 else M):
+            for j in range(Np if direction == 0 else N):
+                pad = (j >= N) if direction == 0 else (i >= M)
+                n = i * N + j
+                keys.add((direction + (2 if pad else 0), n >> 4, n & 15))
+                count += 1
+    assert len(keys) == count
