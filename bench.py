@@ -104,6 +104,14 @@ def run_workload(args):
     def sets_for(nbytes):
         return max(2, -(-2 * MALL // int(nbytes)) + 1)
 
+    if args.profile_copy_mib:
+        n = args.profile_copy_mib << 20
+        src = torch.ones(n // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     kernels = []   # (name, fn(i), nsets, bytes or None, flops or None)
     if args.workload in ("dual_4600x3072", "fc2_w2d"):
         if args.workload == "dual_4600x3072":
