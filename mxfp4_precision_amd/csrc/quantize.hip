@@ -488,10 +488,12 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int t = 0; t < 8; ++t) {
                 const int64_t i = row0 + 8 * q + t;
                 const uint64_t g = (o.index_base + (uint64_t)i * (uint64_t)N + jpair) >> 4;
-                // pads draw from counter word 3 = 2 + dir: the row blob's pads
-                // are columns past N (whole 16-blocks, N % 16 == 0 here), the
-                // column blob's rows past M
-                const bool pad = p ? i >= M : (int64_t)jpair >= N;
+                // after a Hadamard transform pads carry values and draw from
+                // counter word 3 = 2 + dir: the row blob's pads are columns past
+                // N (whole 16-blocks, N % 16 == 0 here), the column blob's rows
+                // past M (without the transform pads are 0 and round to 0 with
+                // any byte, so those kernels skip the distinction)
+                const bool pad = RHT && (p ? i >= M : (int64_t)jpair >= N);
                 uint32_t w0 = (uint32_t)g, w1 = (uint32_t)(g >> 32), w2 = o.tensor_id, w3 = p + (pad ? 2u : 0u);
                 philox10(w0, w1, w2, w3, o.key0, o.key1);
                 const uint32_t r0 = (uint32_t)__shfl_xor((int)(p ? w0 : w2), 1, 64);
@@ -506,12 +508,12 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int t = 0; t < 8; ++t) {
                 const int64_t i = row0 + 8 * q + t;
                 rrow_lo[t] = rrow_hi[t] = rcol_lo[t] = rcol_hi[t] = 0;
-                // pads too: after a Hadamard transform they carry values (otherwise they are 0 and
-                // round to 0 with any byte); they draw from counter word 3 = 2 + dir
+                // pads too: after a Hadamard transform they carry values and draw from
+                // counter word 3 = 2 + dir (otherwise they are 0 and round to 0 with any byte)
                 if (ROW_SR) {
                     const uint64_t n0 = a.row.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0;
                     rand8(n0, a.row, 0u, rrow_lo[t], rrow_hi[t]);
-                    if (j0 + 8 > N) {
+                    if (RHT && j0 + 8 > N) {
                         // columns past N among the lane's 8: take their bytes from the pad space
                         uint32_t plo, phi;
                         rand8(n0, a.row, 2u, plo, phi);
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((
                     }
                 }
                 if (DUAL && COL_SR)
-                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, i >= M ? 3u : 1u,
+                    rand8(a.col.index_base + (uint64_t)i * (uint64_t)N + (uint64_t)j0, a.col, RHT && i >= M ? 3u : 1u,
                           rcol_lo[t], rcol_hi[t]);
             }
         }
