@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "a4w4 GEMM TFLOP/s + dual-quantize GB/s (% roofline), Flux-12B-shaped linears"
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+VALU_ISSUE_PEAK_G = 1024 * 2.4 / 4   # G wave64 VALU instructions/s: 256 CUs x 4 SIMDs, 16 lanes/clock, 2.4 GHz
 
 
 def parse():
@@ -478,6 +479,21 @@ def main():
         "kernels": kernels,
         "input_gen_s": round(gen_s, 1),
     }
+    # The stochastic-rounding dual quantize is bound by its VALU work (Philox
+    # rounds and the encode), not by HBM: its wave-level VALU instructions per
+    # launch (SQ_INSTS_VALU from the committed counter profile, valid while
+    # the sources match) over the live event-timed duration, against the
+    # chip's VALU issue ceiling: 1024 SIMDs x one wave64 instruction per 4
+    # cycles (16 lanes per clock) at 2.4 GHz.
+    if traffic and traffic.get("quant_dY_valu_insts"):
+        insts = traffic["quant_dY_valu_insts"]
+        rate = insts / (per["quant_dY"] * 1e-3) / 1e9
+        out["roofline_quantize_sr"] = {
+            "kernel": "mx_quantize_dual (dY %dx%d, stochastic rounding both blobs)" % (tokens, dout),
+            "bound": "alu", "achieved": round(rate, 1), "peak": VALU_ISSUE_PEAK_G, "unit": "G VALU wave-instructions/s",
+            "frac": round(rate / VALU_ISSUE_PEAK_G, 4),
+            "valu_insts_per_element": round(insts / (tokens * dout), 4),
+            "hbm_frac": kernels["quant_dY"]["frac_hbm_peak"]}
     if extras is not None:
         out["extras"] = extras
 
@@ -775,7 +791,11 @@ def load_traffic():
                 return None
         L = rec["launches"]
         gemm = sum(L[n]["hbm_bytes"] for n in ("gemm_fwd", "gemm_dgrad", "gemm_wgrad")) / 3.0
-        return {"gemm": int(gemm), "quant_X": int(L["quant_X"]["hbm_bytes"])}
+        out = {"gemm": int(gemm), "quant_X": int(L["quant_X"]["hbm_bytes"])}
+        valu = rec.get("valu", {}).get("quant_dY", {})
+        if "SQ_INSTS_VALU_per_launch" in valu:
+            out["quant_dY_valu_insts"] = float(valu["SQ_INSTS_VALU_per_launch"])
+        return out
     except (OSError, KeyError, ValueError):
         return None
 
