@@ -156,8 +156,11 @@ struct Regs {
 // DMA instruction V of k-step k into stage S = k % 4: V < kLoads copies data
 // atom kWaves*V + wave; V >= kLoads (only when k opens a k-group) copies scale
 // atom kWaves*(V - kLoads) + wave.  Past K_pad the offset is out of range and
-// the atom lands as zeros.
-template <int S, int V, class Ctx>
+// the atom lands as zeros.  INNER: the caller guarantees k < ksteps (a step
+// of the current tile inside K_pad), so the offset is the row's plus k's
+// with no test: a wave issues its instructions in order, and the tests and
+// selects in front of every DMA otherwise hold back its next MFMA.
+template <int S, int V, bool INNER = false, class Ctx>
 __device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
     using kint = typename Ctx::kint;
     if constexpr (V < kLoads) {
@@ -166,7 +169,9 @@ __device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
         static_assert(isA || kWaves * V >= kGA, "A/B split falls on a DMA instruction");
         const int a = kWaves * V + c.wave;
         uint32_t base;
-        if constexpr (Ctx::kStream) {
+        if constexpr (INNER) {
+            base = (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024);
+        } else if constexpr (Ctx::kStream) {
             // steps of the tile, then the next tile's first steps
             const bool cur = k < c.kstream;
             const kint kk = cur ? k : k - c.kstream;
@@ -186,10 +191,15 @@ __device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
         static_assert(isA || kWaves * R >= kGA, "A/B split falls on a DMA instruction");
         const int a = kWaves * R + c.wave;
         const kint h = k / 4;
-        uint32_t base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
-        // only step kstream (the next tile's first) opens a k-group past the tile
-        if constexpr (Ctx::kStream)
-            if (k >= c.kstream) base = c.knext > 0 ? (uint32_t)c.sc_next[R] : kOutOfRange;
+        uint32_t base;
+        if constexpr (INNER) {
+            base = (uint32_t)c.sc_row[R] + (uint32_t)(h * 256);
+        } else {
+            base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
+            // only step kstream (the next tile's first) opens a k-group past the tile
+            if constexpr (Ctx::kStream)
+                if (k >= c.kstream) base = c.knext > 0 ? (uint32_t)c.sc_next[R] : kOutOfRange;
+        }
         const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rAs : c.rBs;
         const uint32_t off = base + (uint32_t)c.lane4;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS(scale_buf() + a * 256), 4, off, 0, 0, 0);
@@ -242,8 +252,8 @@ struct Lds {
 //    first use (b[0], a[0..kMA), b[1..kMB)).
 //  - at S == 3, half 1 also reads the next k-group's scales, two per slot.
 //  - the DMA instructions this slot carries (half 0: part 1 of step k+2,
-//    half 1: part 0 of step k+3).
-template <int S, int H, int T, bool FRESH, class Ctx>
+//    half 1: part 0 of step k+3); INNER: both steps lie inside the tile's K.
+template <int S, int H, int T, bool FRESH, bool INNER, class Ctx>
 __device__ __forceinline__ void slot(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                      const Lds &l) {
     constexpr int i = T / kMA, j = T % kMA;
@@ -284,21 +294,21 @@ __device__ __forceinline__ void slot(const Ctx &c, typename Ctx::kint k, v16f (&
     // step 2 already went out before the previous tile's stores
     constexpr int nv = (FRESH && S == 0 && H == 0) ? 0 : part_ops(DS);
     const typename Ctx::kint dk = H == 0 ? k + 2 : k + 3;
-    if constexpr (nv > 0 && dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0)>(c, dk);
-    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1)>(c, dk);
-    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2)>(c, dk);
-    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3)>(c, dk);
+    if constexpr (nv > 0 && dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0), INNER>(c, dk);
+    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1), INNER>(c, dk);
+    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2), INNER>(c, dk);
+    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3), INNER>(c, dk);
     static_assert(part_ops(0) <= 4, "dma slots");
     // keep this slot's instructions in this slot
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S, int H, int T = 0, bool FRESH = false, class Ctx>
+template <int S, int H, int T = 0, bool FRESH = false, bool INNER = false, class Ctx>
 __device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                           const Lds &l) {
     if constexpr (T < kSlots) {
-        slot<S, H, T, FRESH>(c, k, acc, r, l);
-        half_step<S, H, T + 1, FRESH>(c, k, acc, r, l);
+        slot<S, H, T, FRESH, INNER>(c, k, acc, r, l);
+        half_step<S, H, T + 1, FRESH, INNER>(c, k, acc, r, l);
     }
 }
 
@@ -310,17 +320,18 @@ __device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v1
 // count is exact.  FRESH: the first k-group of a tile in the stream kernel,
 // where EXTRA vector-memory instructions (the previous tile's stores and
 // this tile's bias loads) were issued after all of step 2's DMA; the first
-// two waits count past them instead of draining them.
-template <int S, bool FRESH = false, int EXTRA = 0, class Ctx>
+// two waits count past them instead of draining them.  INNER: steps k+2 and
+// k+3 are both below ksteps (see dma_op).
+template <int S, bool FRESH = false, int EXTRA = 0, bool INNER = false, class Ctx>
 __device__ __forceinline__ void k_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
                                        const Lds &l) {
     constexpr int kStores = FRESH && S < 2 ? EXTRA : 0;
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 0, 0, FRESH>(c, k, acc, r, l);
+    half_step<S, 0, 0, FRESH, INNER>(c, k, acc, r, l);
     static_assert(issued_for((S + 2) & 3) + kStores <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3) + kStores) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 1, 0, FRESH>(c, k, acc, r, l);
+    half_step<S, 1, 0, FRESH, INNER>(c, k, acc, r, l);
     if constexpr (S == 3) {
 #pragma unroll
         for (int t = 0; t < kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
@@ -539,7 +550,16 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t 
     for (int t = 0; t < kMB; ++t)
         r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
 
-    for (int64_t h = 0; h < c.kgroups; ++h) {
+    // k-group h fetches steps 4h+2 .. 4h+6: inside K while 4h+6 < ksteps
+    int64_t h = 0;
+    for (; 4 * h + 6 < c.ksteps; ++h) {
+        const int64_t k0 = 4 * h;
+        k_step<0, false, 0, true>(c, k0, acc, r, l);
+        k_step<1, false, 0, true>(c, k0 + 1, acc, r, l);
+        k_step<2, false, 0, true>(c, k0 + 2, acc, r, l);
+        k_step<3, false, 0, true>(c, k0 + 3, acc, r, l);
+    }
+    for (; h < c.kgroups; ++h) {
         const int64_t k0 = 4 * h;
         k_step<0>(c, k0, acc, r, l);
         k_step<1>(c, k0 + 1, acc, r, l);
@@ -770,7 +790,17 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
         k_step<1, true, kFreshOps>(c, 1, acc, r, l);
         k_step<2>(c, 2, acc, r, l);
         k_step<3>(c, 3, acc, r, l);
-        for (int h = 1; h < c.kgroups; ++h) {
+        // k-group h fetches steps 4h+2 .. 4h+6: all of this tile while
+        // 4h+6 < ksteps; the last group (or two) also fetch the next tile's
+        int h = 1;
+        for (; 4 * h + 6 < c.ksteps; ++h) {
+            const int k0 = 4 * h;
+            k_step<0, false, 0, true>(c, k0, acc, r, l);
+            k_step<1, false, 0, true>(c, k0 + 1, acc, r, l);
+            k_step<2, false, 0, true>(c, k0 + 2, acc, r, l);
+            k_step<3, false, 0, true>(c, k0 + 3, acc, r, l);
+        }
+        for (; h < c.kgroups; ++h) {
             const int k0 = 4 * h;
             k_step<0>(c, k0, acc, r, l);
             k_step<1>(c, k0 + 1, acc, r, l);
