@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["api.cpp", "layout.cpp", "quantize.hip", "quantize_fp8.hip", "gemm.hip", "gemm_tail.hip", "gemm_fp6.hip", "gemm_fp6_tail.hip", "convert.hip",
+SOURCES = ["api.cpp", "layout.cpp", "quantize.hip", "quantize_fp8.hip", "gemm.hip", "convert.hip",
            "dequantize.hip", "measure.hip"]
 ARCH = "gfx950"
 

@@ -1,34 +1,45 @@
-// Block-scaled FP4 x FP4 GEMM (C = A . B^T) for gfx950 on tiled-layout blobs.
+// Block-scaled GEMMs (C = A . B^T) for gfx950: one software pipeline for
+// MXFP4 (E2M1) and MXFP6 (E2M3 / E3M2) operands in the tiled blob layout,
+// instantiated per element format and workgroup tile shape, plus the
+// tensorwise-scaled FP8 (E5M2) product of the hybrid backward.
 //
-// C[i][j] = sum_k e2m1(A[i][k]) 2^(sa[i][k/32]-127) * e2m1(B[j][k]) 2^(sb[j][k/32]-127),
+// C[i][j] = sum_k e(A[i][k]) 2^(sa[i][k/32]-127) * e(B[j][k]) 2^(sb[j][k/32]-127),
 // fp32 accumulation, bf16 (RNE) or fp32 output: the NT product that the
 // forward, dgrad and wgrad of the MXFP4 linear on the page
-// "primus_turbo_mxfp4_local.py" compute.
+// "primus_turbo_mxfp4_local.py" compute (and its MXFP6 variant, with the
+// element formats of OCP MX v1.0 sec. 5.3.2).
 //
-// MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both formats FP4.  Lane L of a
-// 32-row operand tile supplies 16 bytes (32 elements) of row L%32, k-block
-// 2*half + L/32 of a 128-wide k-step, and that block's E8M0 scale as the byte
-// of a VGPR that OPSEL picks.  The tiled layout puts exactly those 16 bytes at
-// a fixed slice of a 1 KB atom (16 rows x 128 k) and a lane's scales for 4
-// consecutive k-steps in one dword of a 256-byte scale atom, so operands move
-// as whole atoms and are read from LDS with conflict-free ds_read_b128.
+// MFMA: V_MFMA_SCALE_F32_32X32X64_F8F6F4.  Lane L of a 32-row operand tile
+// supplies the 32 elements of row L%32, k-block 2*half + L/32 of a 128-wide
+// k-step (16 bytes for FP4, 24 for FP6), and that block's E8M0 scale as the
+// byte of a VGPR that OPSEL picks.  The tiled layout puts exactly those bytes
+// at a fixed slice of an atom (16 rows x 128 k: 1 KB for FP4; 1536 bytes for
+// FP6, each lane's first 16 bytes in the atom's first kilobyte and the last 8
+// in the remaining 512 bytes) and a lane's scales for 4 consecutive k-steps
+// in one dword of a 256-byte scale atom, so operands move as whole atoms and
+// are read from LDS with conflict-free ds_read_b128 (plus ds_read_b64 for the
+// FP6 high parts).
 //
-// Workgroup: 8 waves (two per SIMD), 256x256 tile of C; wave w owns the
-// 128x64 block at rows 128*(w%2), columns 64*(w/2): 4x2 MFMA tiles, 128 fp32
-// accumulators per lane, under 256 registers so two waves share each SIMD.
-// Every LDS read or DMA instruction a wave issues stalls that wave's MFMA
-// stream for tens of cycles; with two waves per SIMD the other wave's MFMAs
-// fill that gap.
+// Workgroup shapes: 256x256 tiles with 8 waves of 128x64 (4x2 MFMA tiles,
+// 128 fp32 accumulators per lane, two waves per SIMD), and 128x128 tiles
+// with 4 waves of 64x64 for the leftover tiles of a last round, alone or as
+// two K groups of 4 waves that each run the pipeline over half of K and add
+// their partial tiles through LDS.  Every LDS read or DMA instruction a wave
+// issues stalls that wave's MFMA stream for tens of cycles; with two waves
+// per SIMD the other wave's MFMAs fill that gap.
 //
-// Pipeline: LDS holds 4 k-step stages of 32 atoms (16 A + 16 B, 32 KB) and one
-// k-group (4 steps) of scale atoms.  Atoms travel global -> LDS by DMA
-// (buffer_load ... lds, no registers); step k+3 is in flight while step k
-// computes.  Each k-step is two halves of 8 MFMAs per wave; one slot = one
-// MFMA plus, in fixed order, the LDS read of an operand of the next half and
-// the DMA instructions assigned to that slot, so memory instructions are
-// spread evenly between MFMAs.  Half 0 of step k issues the second part of
-// step k+2's DMA, half 1 the first part of step k+3's; the barrier between
-// the halves publishes step k+1 and frees the stage of step k-1.
+// Pipeline: LDS holds kStages k-step stages (FP4: 4 of 32 atoms, 32 KB each;
+// FP6: 3 of 48 KB) and one k-group (4 steps) of scale atoms.  Atoms travel
+// global -> LDS by DMA (buffer_load ... lds, no registers).  Each k-step is
+// two halves of kSlots MFMAs per wave; one slot = one MFMA plus, in fixed
+// order, the LDS read of an operand of the next half and the DMA
+// instructions assigned to that slot, so memory instructions are spread
+// evenly between MFMAs.  Half 0 of step k issues the second part of step
+// k+2's DMA, half 1 the first part of step k+3's; the barrier between the
+// halves publishes step k+1 and frees the stage that step k+3 lands in
+// (step k-1's with four stages, step k's own with three).  The stage index
+// runs mod kStages and the position in the 4-step scale group mod 4, so the
+// unrolled k-loop body is kPeriod = lcm(kStages, 4) steps.
 //
 // The MFMA is issued with B as the "A" operand, so each lane's accumulators
 // are 4 consecutive columns of one row of C.  Workgroups are ordered so that
@@ -50,75 +61,15 @@ namespace mx {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t v6u __attribute__((ext_vector_type(6)));   // one lane's FP6 operand
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
 
-constexpr int kFmtFp4 = 4;                 // MFMA f8f6f4 format code for E2M1
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBM = 256, kBN = 256;        // workgroup tile
-constexpr int kWM = 128, kWN = 64;         // wave tile
-constexpr int kWavesM = kBM / kWM;         // wave grid 2 x 4
-constexpr int kGA = kBM / 16;              // A atoms (16-row groups) per k-step per workgroup
-constexpr int kGB = kBN / 16;
-constexpr int kTA = kWM / 16;              // A atoms per wave
-constexpr int kTB = kWN / 16;
-constexpr int kMA = kWM / 32;              // 32x32 MFMA tiles per wave along M (A rows)
-constexpr int kMB = kWN / 32;              // ... along N (B rows)
-constexpr int kAtoms = kGA + kGB;          // atoms per stage
-constexpr int kLoads = kAtoms / kWaves;    // data DMAs per wave per k-step
-constexpr int kHalfLoads = kLoads / 2;
-constexpr int kSlots = kMA * kMB;          // MFMAs per wave per half-step
 constexpr int kXcds = 8;
-constexpr int kGroupM = 8;                 // tile rows per band in the tile order
-
-static_assert(kAtoms % kWaves == 0 && kLoads % 2 == 0, "DMA split");
-// 16-byte stores per wave per tile in the stream kernel's epilogue: kMA
-// passes of the wave's own 32 rows x kWN bf16 columns, 64 lanes x 16 bytes
-// per store instruction
-constexpr int kEpiStoresPerTile = kMA * (32 * kWN * 2) / (64 * 16);
-static_assert(kMA + kMB <= kSlots, "one operand read per slot");
-
-// Buffer resource over [p, p + bytes).  Loads address it with a per-lane
-// byte offset; an offset at or past `bytes` reads zeros (the hardware range
-// check of raw buffers), which is how k-steps past K_pad become zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// LDS: 4 k-step stages of 32 atoms and one k-group of scale atoms, as
-// separate arrays so that the compiler can tell a DMA into one stage from a
-// read of another.  After the k-loop the stages hold the bf16 C tile: rows
-// [64s, 64s + 64) in stage s, 512 bytes per row, 16-byte chunk c of row r at
-// chunk c ^ (r % 32) so that reads and writes of a column of rows spread
-// over all banks.
-constexpr int kStageBytes = kAtoms * 1024;
-static_assert(kBN * 2 * (kBM / 4) == kStageBytes, "a quarter of the bf16 C tile fills one stage");
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage2[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage3[kStageBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_scale[kAtoms * 256];
-
-template <int S>
-__device__ __forceinline__ uint8_t *stage_buf() {
-    return S == 0 ? g_stage0 : S == 1 ? g_stage1 : S == 2 ? g_stage2 : g_stage3;
-}
-__device__ __forceinline__ uint8_t *scale_buf() { return g_scale; }
-__device__ __forceinline__ uint8_t *stage_dyn(int s) {
-    return s == 0 ? g_stage0 : s == 1 ? g_stage1 : s == 2 ? g_stage2 : g_stage3;
-}
-// byte address of bf16 C element (r, col) of the staged tile, col % 4 == 0
-__device__ __forceinline__ uint8_t *c_stage(int r, int col) {
-    const int chunk = (col >> 3) ^ (r & 31);
-    return stage_dyn(r >> 6) + (r & 63) * (kBN * 2) + chunk * 16 + (col & 7) * 2;
-}
-
-#define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
-
 // Offset that lies past every operand buffer: a buffer load there returns 0.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // buffer-store cache policy: non-temporal (C is not read again by the kernel)
@@ -127,69 +78,304 @@ constexpr int kCachePolicyNT = 2;
 // maxima (no wait): vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Buffer resource over [p, p + bytes).  Loads address it with a per-lane
+// byte offset; an offset at or past `bytes` reads zeros (the hardware range
+// check of raw buffers), which is how k-steps past K_pad become zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+#define MX_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// ------------------------------------------------------------ element formats
+// MFMA f8f6f4 format codes: 2 = E2M3, 3 = E3M2, 4 = E2M1.
+struct Fp4Fmt {
+    static constexpr int kFa = 4, kFb = 4;    // formats of A and B
+    static constexpr bool kHi = false;        // an operand is one 16-byte slice
+    static constexpr int kStepBytes = 1024;   // blob bytes of one 16-row group per k-step
+    static constexpr int kStages = 4;
+    static constexpr int kPeriod = 4;
+    // the next k-group's scales go to a spare register set during the
+    // group's last step (12 VGPRs that the FP4 operands leave room for)
+    static constexpr bool kScaleAhead = true;
+    // a separate copy of the k-loop for the steps whose DMAs all fall inside
+    // the tile's K, without range tests (see dma_op)
+    static constexpr bool kInner = true;
+    static constexpr bool kStream = true;   // persistent form for bf16 output
+    typedef uint4 Op;
+};
+template <int FA, int FB>
+struct Fp6Fmt {
+    static constexpr int kFa = FA, kFb = FB;
+    static constexpr bool kHi = true;         // 16 bytes in the atom's first KB + 8 in its high part
+    static constexpr int kStepBytes = 1536;
+    static constexpr int kStages = 3;
+    static constexpr int kPeriod = 12;
+    // each half's scale entries are replaced while that half's MFMAs are not
+    // running (the 6-register operands leave no room for a second set)
+    static constexpr bool kScaleAhead = false;
+    // one copy of the 12-step loop body: a second one costs spills
+    static constexpr bool kInner = false;
+    // The persistent form with its stores written straight from registers
+    // (no stage is free for staging) measured 1.3-2.7x slower than one tile
+    // per workgroup on the fc2 shapes: each 8-byte store instruction touches
+    // 32 rows.
+    static constexpr bool kStream = false;
+    typedef v6u Op;
+};
+
+// ------------------------------------------------------------ tile shapes
+// BM x BN workgroup tile of C, WM x WN wave tile, KG K groups (1, or 2 for
+// the split form: waves [0, W) run the first half of K, [W, 2W) the second).
+template <int BM, int BN, int WM, int WN, int KG>
+struct Shape {
+    static constexpr int kBM = BM, kBN = BN, kWM = WM, kWN = WN, kKG = KG;
+    static constexpr int kWavesM = BM / WM;               // wave grid kWavesM x (BN / WN)
+    static constexpr int kWaves = (BM / WM) * (BN / WN);  // waves of one K group
+    static constexpr int kThreads = kWaves * KG * 64;
+};
+using MainShape = Shape<256, 256, 128, 64, 1>;
+using TailShape = Shape<128, 128, 64, 64, 1>;
+using SplitShape = Shape<128, 128, 64, 64, 2>;
+
+template <class F, class S>
+struct Cfg {
+    using Fmt = F;
+    using Op = typename F::Op;
+    static constexpr int kStages = F::kStages, kPeriod = F::kPeriod;
+    static constexpr int kBM = S::kBM, kBN = S::kBN, kWM = S::kWM, kWN = S::kWN, kKG = S::kKG;
+    static constexpr int kWaves = S::kWaves, kWavesM = S::kWavesM, kThreads = S::kThreads;
+    static constexpr int kGA = kBM / 16, kGB = kBN / 16;  // A / B atoms (16-row groups) per k-step
+    static constexpr int kAtoms = kGA + kGB;
+    static constexpr int kTA = kWM / 16, kTB = kWN / 16;  // atoms per wave tile
+    static constexpr int kMA = kWM / 32, kMB = kWN / 32;  // 32x32 MFMA tiles per wave along M (A) / N (B)
+    static constexpr int kSlots = kMA * kMB;              // MFMAs per wave per half-step
+    // DMA units per wave and k-step: one 1 KB unit per atom (FP4: the atom;
+    // FP6: its first KB), and for FP6 one per two atoms holding both high
+    // parts, interleaved in 16-byte chunks (chunk c of atom 2h+a at position
+    // 2c+a); scale atoms, 256 bytes each, when a step opens a k-group
+    static constexpr int kLoLoads = kAtoms / kWaves;
+    static constexpr int kHiLoads = F::kHi ? kAtoms / 2 / kWaves : 0;
+    static constexpr int kLoads = kLoLoads + kHiLoads;
+    static constexpr int kScaleLoads = kAtoms / kWaves;
+    static constexpr int kHalfLoads = kLoads / 2, kHalfScale = kScaleLoads / 2;
+    static constexpr int kHiBase = kAtoms * 1024;         // high-part units follow the first KBs
+    static constexpr int kStageBytes = kAtoms * (F::kHi ? 1536 : 1024);
+    static_assert(kAtoms % kWaves == 0 && kLoads % 2 == 0 && kScaleLoads % 2 == 0, "DMA split");
+    static_assert(!F::kHi || kAtoms % (2 * kWaves) == 0, "whole high-part units per wave");
+    static_assert(kMA + kMB <= kSlots, "one operand read per slot");
+
+    // A k-step's DMA is issued in two parts: part P holds data units
+    // [P*kHalfLoads, (P+1)*kHalfLoads) and, when the step opens a k-group
+    // (k-group position SG == 0), scale units [P*kHalfScale, (P+1)*kHalfScale).
+    static constexpr int part_ops(int SG) { return SG == 0 ? kHalfLoads + kHalfScale : kHalfLoads; }
+    static constexpr int part_op(int P, int n) {
+        return n < kHalfLoads ? kHalfLoads * P + n : kLoads + kHalfScale * P + (n - kHalfLoads);
+    }
+    // vector-memory instructions a wave issues for a k-step at k-group position SG
+    static constexpr int issued_for(int SG) { return 2 * part_ops(SG); }
+    // slot of the n-th of nv DMA instructions in a half-step
+    static constexpr int dma_slot(int n, int nv) {
+        const int s = 1 + (n * kSlots) / nv;
+        return s > kSlots - 1 ? kSlots - 1 : s;
+    }
+    static_assert(part_ops(0) <= 5, "dma slots");
+};
+
+// LDS.  Each stage (and the scale k-group) is an array of its own, so that
+// the compiler can tell a DMA into one stage from a read of another; K group
+// G of the split form has its own set.
+// ID: stage index (0..3) or 4 for the scale k-group, plus 8 per K group.
+template <int BYTES, int ID>
+__shared__ __attribute__((aligned(1024))) uint8_t g_lds[BYTES];
+template <class C, int S, int G>
+__device__ __forceinline__ uint8_t *stage_buf() {
+    return g_lds<C::kStageBytes, 8 * G + S>;
+}
+template <class C, int G>
+__device__ __forceinline__ uint8_t *scale_buf() {
+    return g_lds<C::kAtoms * 256, 8 * G + 4>;
+}
+template <class C, int G = 0>
+__device__ __forceinline__ uint8_t *stage_dyn(int s) {
+    if constexpr (C::kStages == 4)
+        return s == 0 ? stage_buf<C, 0, G>() : s == 1 ? stage_buf<C, 1, G>() : s == 2 ? stage_buf<C, 2, G>()
+                                                                                     : stage_buf<C, 3, G>();
+    else
+        return s == 0 ? stage_buf<C, 0, G>() : s == 1 ? stage_buf<C, 1, G>() : stage_buf<C, 2, G>();
+}
+
+// After the k-loop the stages hold the bf16 C tile: kCRows rows per stage,
+// kBN * 2 bytes per row, 16-byte chunk c of row r at chunk c ^ (r % chunks
+// per row), so that reads and writes of a column of rows spread over all
+// banks.  Byte address of bf16 element (r, col), col % 4 == 0.
+template <class C>
+__device__ __forceinline__ uint8_t *c_stage(int r, int col) {
+    constexpr int kCRows = C::kStageBytes / (C::kBN * 2);
+    constexpr int kChunks = C::kBN * 2 / 16;
+    static_assert(kCRows * C::kStages >= C::kBM, "the bf16 C tile fits the stages");
+    const int s = r / kCRows, rr = r - s * kCRows;
+    const int chunk = (col >> 3) ^ (r & (kChunks - 1));
+    return stage_dyn<C>(s) + rr * (C::kBN * 2) + chunk * 16 + (col & 7) * 2;
+}
+
+// ------------------------------------------------------------ pipeline state
 // STREAM: the workgroup runs several output tiles back to back as one stream
-// of k-steps; a tile occupies kstream = 4 * kgroups steps of it, and a DMA
-// for step kstream + j (j < 3) fetches step j of the next tile (ld_next /
-// sc_next; knext = its k-steps, 0 when there is none).
-template <bool STREAM>
-struct GemmCtxT {
+// of k-steps; a tile occupies kstream steps of it, and a DMA for step kstream
+// + j (j < 3) fetches step j of the next tile (*_next; knext = its k-steps, 0
+// when there is none).
+template <class C, bool STREAM>
+struct Ctx {
     static constexpr bool kStream = STREAM;
     // k-step counter type: the stream kernel keeps k-steps in 32 bits (operand
     // blobs stay below 2 GiB, so K_pad / 128 < 2^24) to spare scalar registers
     using kint = typename std::conditional<STREAM, int, int64_t>::type;
     __amdgpu_buffer_rsrc_t rA, rB, rAs, rBs;
-    int ld_row[kLoads];    // byte offset of this wave's r-th atom row (k-step 0)
-    int sc_row[kLoads];    // byte offset of this wave's r-th scale-atom row (k-group 0)
+    int lo_row[C::kLoLoads];      // byte offsets of this wave's unit rows at k-step 0 (wave-uniform)
+    uint32_t hi_off[C::kHiLoads > 0 ? C::kHiLoads : 1];   // FP6 high-part units: per lane, lane part included
+    int sc_row[C::kScaleLoads];   // byte offsets of this wave's scale-atom rows at k-group 0
     kint ksteps, kgroups;
     int wave, lane16, lane4;
-    int ld_next[STREAM ? kLoads : 1], sc_next[STREAM ? kLoads : 1];
+    int lo_next[STREAM ? C::kLoLoads : 1];
+    uint32_t hi_next[STREAM && C::kHiLoads > 0 ? C::kHiLoads : 1];
+    int sc_next[STREAM ? C::kScaleLoads : 1];
     kint kstream, knext;
 };
-using GemmCtx = GemmCtxT<false>;
 
+template <class C>
 struct Regs {
-    uint4 a0[kMA], b0[kMB], a1[kMA], b1[kMB];       // operands of half 0 / half 1
-    uint32_t sa[kMA][2], sb[kMB][2];                // scales of the current k-group
-    uint32_t sa_n[kMA][2], sb_n[kMB][2];            // ... of the next one
+    using Op = typename C::Op;
+    static constexpr bool kAhead = C::Fmt::kScaleAhead;
+    Op a0[C::kMA], b0[C::kMB], a1[C::kMA], b1[C::kMB];   // operands of half 0 / half 1
+    uint32_t sa[C::kMA][2], sb[C::kMB][2];                // scales of the k-group in use, per half
+    uint32_t sa_n[kAhead ? C::kMA : 1][2], sb_n[kAhead ? C::kMB : 1][2];   // ... of the next one
 };
 
-// DMA instruction V of k-step k into stage S = k % 4: V < kLoads copies data
-// atom kWaves*V + wave; V >= kLoads (only when k opens a k-group) copies scale
-// atom kWaves*(V - kLoads) + wave.  Past K_pad the offset is out of range and
-// the atom lands as zeros.  INNER: the caller guarantees k < ksteps (a step
-// of the current tile inside K_pad), so the offset is the row's plus k's
-// with no test: a wave issues its instructions in order, and the tests and
-// selects in front of every DMA otherwise hold back its next MFMA.
-template <int S, int V, bool INNER = false, class Ctx>
-__device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
-    using kint = typename Ctx::kint;
-    if constexpr (V < kLoads) {
-        // atom kWaves*V + wave: an A atom for every wave or a B atom for every wave
-        constexpr bool isA = kWaves * (V + 1) <= kGA;
-        static_assert(isA || kWaves * V >= kGA, "A/B split falls on a DMA instruction");
-        const int a = kWaves * V + c.wave;
+// Per-lane LDS byte offsets of this wave's first A and B operand tiles (half
+// 0), with the wave-dependent part folded in, so every read adds only a
+// compile-time constant (tile, half) that fits the instruction's offset field.
+struct Lds {
+    int lo_a, lo_b;   // 16 bytes in a stage's first-KB region
+    int hi_a, hi_b;   // FP6: 8 bytes in the interleaved high-part units
+    int sc_a, sc_b;   // scale dword in the scale atoms
+};
+
+template <class C>
+__device__ __forceinline__ Lds lds_offsets(int wave, int lane) {
+    // lane L of a 32-row tile: row L%32 = atom (L%32)/16, slice s = L%16 + 16*(L/32) (half 0)
+    const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int sl = (lrow & 15) + 16 * lhi;
+    const int frag_off = ((lrow >> 4) * 1024) + sl * 16;
+    // high parts: slice s of atom 2t + a at chunk position 2(s/2) + a, 8 bytes in per s%2
+    const int frag_hi = 32 * (sl >> 1) + 16 * (lrow >> 4) + 8 * (sl & 1);
+    // the slice's scale is byte (k-step % 4) of the dword at the same slice of the scale atom
+    const int sc_off = ((lrow >> 4) * 256) + sl * 4;
+    const int a0 = wm * C::kTA, b0 = C::kGA + wn * C::kTB;   // first atoms of the wave's A and B tiles
+    Lds l;
+    l.lo_a = frag_off + a0 * 1024;
+    l.lo_b = frag_off + b0 * 1024;
+    l.hi_a = frag_hi + (a0 / 2) * 1024;
+    l.hi_b = frag_hi + (b0 / 2) * 1024;
+    l.sc_a = sc_off + a0 * 256;
+    l.sc_b = sc_off + b0 * 256;
+    // Hide the bases' known zero bits: otherwise the compiler turns base +
+    // constant into an OR, which the LDS instructions' offset field does not
+    // take, and gives every read an address register of its own.
+    asm volatile("" : "+v"(l.lo_a), "+v"(l.lo_b), "+v"(l.sc_a), "+v"(l.sc_b));
+    if constexpr (C::Fmt::kHi) asm volatile("" : "+v"(l.hi_a), "+v"(l.hi_b));
+    return l;
+}
+
+// Operand of one 32-row tile: 16 bytes from the first-KB region (plus 8 from
+// the high part for FP6).
+template <class C>
+__device__ __forceinline__ typename C::Op read_op(const uint8_t *lo, const uint8_t *hi) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(lo);
+    if constexpr (C::Fmt::kHi) {
+        const uint2 h = *reinterpret_cast<const uint2 *>(hi);
+        return v6u{v.x, v.y, v.z, v.w, h.x, h.y};
+    } else {
+        return v;
+    }
+}
+
+template <class C, int SG>
+__device__ __forceinline__ void mfma_tile(v16f &acc, const typename C::Op &xb, const typename C::Op &xa, uint32_t sbv,
+                                          uint32_t sav) {
+    v8i bop, aop;
+    if constexpr (C::Fmt::kHi) {
+        bop = v8i{(int)xb[0], (int)xb[1], (int)xb[2], (int)xb[3], (int)xb[4], (int)xb[5], 0, 0};
+        aop = v8i{(int)xa[0], (int)xa[1], (int)xa[2], (int)xa[3], (int)xa[4], (int)xa[5], 0, 0};
+    } else {
+        bop = v8i{(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
+        aop = v8i{(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
+    }
+    // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C);
+    // OPSEL SG picks the k-step's byte of each scale dword
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc, C::Fmt::kFb, C::Fmt::kFa, SG, (int)sbv, SG,
+                                                          (int)sav);
+}
+
+// DMA instruction V of k-step k into stage S of K group G: V < kLoLoads
+// copies the first KB of atom kWaves*V + wave; V < kLoads (FP6) the high
+// parts of atoms 2h, 2h+1 (h = kWaves*(V - kLoLoads) + wave; lane p fetches
+// chunk p/2 of atom 2h + p%2); otherwise (only when k opens a k-group) scale
+// atom kWaves*(V - kLoads) + wave.  Past the operand's K the offset is out
+// of range and the unit lands as zeros.  INNER: the caller guarantees k <
+// ksteps (a step of the current tile inside K), so the offset is the row's
+// plus k's with no test: a wave issues its instructions in order, and the
+// tests and selects in front of every DMA otherwise hold back its next MFMA.
+template <class C, int S, int V, int G, bool INNER, class X>
+__device__ __forceinline__ void dma_op(const X &c, typename X::kint k) {
+    using kint = typename X::kint;
+    constexpr uint32_t kStep = C::Fmt::kStepBytes;
+    if constexpr (V < C::kLoLoads) {
+        // unit kWaves*V + wave: an A atom for every wave or a B atom for every wave
+        constexpr bool isA = C::kWaves * (V + 1) <= C::kGA;
+        static_assert(isA || C::kWaves * V >= C::kGA, "A/B split falls on a DMA instruction");
+        const int a = C::kWaves * V + c.wave;
         uint32_t base;
         if constexpr (INNER) {
-            base = (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024);
-        } else if constexpr (Ctx::kStream) {
+            base = (uint32_t)c.lo_row[V] + (uint32_t)k * kStep;
+        } else if constexpr (X::kStream) {
             // steps of the tile, then the next tile's first steps
             const bool cur = k < c.kstream;
             const kint kk = cur ? k : k - c.kstream;
-            const int row = cur ? c.ld_row[V] : c.ld_next[V];
-            base = kk < (cur ? c.ksteps : c.knext) ? (uint32_t)row + (uint32_t)(kk * 1024) : kOutOfRange;
+            const int row = cur ? c.lo_row[V] : c.lo_next[V];
+            base = kk < (cur ? c.ksteps : c.knext) ? (uint32_t)row + (uint32_t)kk * kStep : kOutOfRange;
         } else {
-            base = k < c.ksteps ? (uint32_t)c.ld_row[V] + (uint32_t)(k * 1024) : kOutOfRange;
+            base = k < c.ksteps ? (uint32_t)c.lo_row[V] + (uint32_t)k * kStep : kOutOfRange;
         }
         // (plain-typed locals: a builtin call on template-dependent operands
         // does not resolve in the host compilation pass)
         const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rA : c.rB;
         const uint32_t off = base + (uint32_t)c.lane16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS(stage_buf<S>() + a * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((stage_buf<C, S, G>() + a * 1024)), 16, off, 0, 0, 0);
+    } else if constexpr (V < C::kLoads) {
+        constexpr int R = V - C::kLoLoads;
+        constexpr bool isA = 2 * C::kWaves * (R + 1) <= C::kGA;
+        static_assert(isA || 2 * C::kWaves * R >= C::kGA, "A/B split falls on a DMA instruction");
+        const int h = C::kWaves * R + c.wave;
+        uint32_t off;
+        if constexpr (INNER) {
+            off = c.hi_off[R] + (uint32_t)k * kStep;
+        } else if constexpr (X::kStream) {
+            const bool cur = k < c.kstream;
+            const kint kk = cur ? k : k - c.kstream;
+            const uint32_t row = cur ? c.hi_off[R] : c.hi_next[R];
+            off = kk < (cur ? c.ksteps : c.knext) ? row + (uint32_t)kk * kStep : kOutOfRange;
+        } else {
+            off = k < c.ksteps ? c.hi_off[R] + (uint32_t)k * kStep : kOutOfRange;
+        }
+        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rA : c.rB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((stage_buf<C, S, G>() + C::kHiBase + h * 1024)), 16,
+                                                 off, 0, 0, 0);
     } else {
-        constexpr int R = V - kLoads;
-        constexpr bool isA = kWaves * (R + 1) <= kGA;
-        static_assert(isA || kWaves * R >= kGA, "A/B split falls on a DMA instruction");
-        const int a = kWaves * R + c.wave;
+        constexpr int R = V - C::kLoads;
+        constexpr bool isA = C::kWaves * (R + 1) <= C::kGA;
+        static_assert(isA || C::kWaves * R >= C::kGA, "A/B split falls on a DMA instruction");
+        const int a = C::kWaves * R + c.wave;
         const kint h = k / 4;
         uint32_t base;
         if constexpr (INNER) {
@@ -197,198 +383,325 @@ __device__ __forceinline__ void dma_op(const Ctx &c, typename Ctx::kint k) {
         } else {
             base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
             // only step kstream (the next tile's first) opens a k-group past the tile
-            if constexpr (Ctx::kStream)
+            if constexpr (X::kStream)
                 if (k >= c.kstream) base = c.knext > 0 ? (uint32_t)c.sc_next[R] : kOutOfRange;
         }
         const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rAs : c.rBs;
         const uint32_t off = base + (uint32_t)c.lane4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS(scale_buf() + a * 256), 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((scale_buf<C, G>() + a * 256)), 4, off, 0, 0, 0);
     }
 }
 
-// A k-step's DMA is issued in two parts: part P holds data atoms
-// [P*kHalfLoads, (P+1)*kHalfLoads) and, when the step opens a k-group, the
-// scale atoms with the same indices.
-__host__ __device__ constexpr int part_ops(int S) { return S == 0 ? 2 * kHalfLoads : kHalfLoads; }
-__host__ __device__ constexpr int part_op(int S, int P, int n) {
-    return n < kHalfLoads ? kHalfLoads * P + n : kLoads + kHalfLoads * P + (n - kHalfLoads);
-}
-// vector-memory instructions a wave issues for a k-step with stage S
-__host__ __device__ constexpr int issued_for(int S) { return 2 * part_ops(S); }
-// slot of the n-th of nv DMA instructions in a half-step
-__host__ __device__ constexpr int dma_slot(int n, int nv) {
-    const int s = 1 + (n * kSlots) / nv;
-    return s > kSlots - 1 ? kSlots - 1 : s;
-}
-
-template <int S, int P, int n = 0, class Ctx>
-__device__ __forceinline__ void dma_part(const Ctx &c, typename Ctx::kint k) {
-    if constexpr (n < part_ops(S)) {
-        dma_op<S, part_op(S, P, n)>(c, k);
-        dma_part<S, P, n + 1>(c, k);
+// Part P of the DMA of k-step k (stage S, k-group position SG).
+template <class C, int S, int SG, int P, int G, int n = 0, class X>
+__device__ __forceinline__ void dma_part(const X &c, typename X::kint k) {
+    if constexpr (n < C::part_ops(SG)) {
+        dma_op<C, S, C::part_op(P, n), G, false>(c, k);
+        dma_part<C, S, SG, P, G, n + 1>(c, k);
     }
 }
 
-template <int S>
-__device__ __forceinline__ void mfma_tile(v16f &acc, const uint4 &xb, const uint4 &xa, uint32_t sbv, uint32_t sav) {
-    const v8i bop = {(int)xb.x, (int)xb.y, (int)xb.z, (int)xb.w, 0, 0, 0, 0};
-    const v8i aop = {(int)xa.x, (int)xa.y, (int)xa.z, (int)xa.w, 0, 0, 0, 0};
-    // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C)
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc, kFmtFp4, kFmtFp4, S, (int)sbv, S,
-                                                          (int)sav);
-}
-
-struct Lds {
-    int frag_off;   // this lane's slice within a 32-row pair of atoms (half 0)
-    int sc_off;     // ... within a pair of scale atoms
-    int a_atom0;    // first A atom of this wave's rows
-    int b_atom0;    // first B atom of this wave's columns
-};
-
-// Slot T of half H of the k-step with stage S.
+// Slot T of half H of the k-step with stage S and k-group position SG.
 //  - MFMA T: tile (i, j) = (T / kMA, T % kMA) with the operands of half H.
 //  - LDS read T (T < kMA + kMB) of the other operand set: half 0 reads the
 //    second half of stage S, half 1 the first half of stage S+1, in order of
 //    first use (b[0], a[0..kMA), b[1..kMB)).
-//  - at S == 3, half 1 also reads the next k-group's scales, two per slot.
+//  - scales: kScaleAhead: at SG == 3, half 1 reads the next k-group's
+//    scales, two per slot, into the spare set; otherwise half 1 at SG == 3
+//    and half 0 at SG == 0 replace the entries of the half whose MFMAs are
+//    not running (the scale atoms stay in LDS until step 1 of the group
+//    issues the next group's DMA).
 //  - the DMA instructions this slot carries (half 0: part 1 of step k+2,
-//    half 1: part 0 of step k+3); INNER: both steps lie inside the tile's K.
-template <int S, int H, int T, bool FRESH, bool INNER, class Ctx>
-__device__ __forceinline__ void slot(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
+//    half 1: part 0 of step k+3).  FRESH (a tile's first k-step in the
+//    stream kernel): the second part of step 2 already went out before the
+//    previous tile's stores.  INNER: both steps lie inside the tile's K.
+template <class C, int S, int SG, int H, int T, bool FRESH, bool INNER, int G, class X>
+__device__ __forceinline__ void slot(const X &c, typename X::kint k, v16f (&acc)[C::kMB][C::kMA], Regs<C> &r,
                                      const Lds &l) {
-    constexpr int i = T / kMA, j = T % kMA;
-    if constexpr (H == 0) mfma_tile<S>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
-    else mfma_tile<S>(acc[i][j], r.b1[i], r.a1[j], r.sb[i][1], r.sa[j][1]);
+    constexpr int i = T / C::kMA, j = T % C::kMA;
+    if constexpr (H == 0) mfma_tile<C, SG>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
+    else mfma_tile<C, SG>(acc[i][j], r.b1[i], r.a1[j], r.sb[i][1], r.sa[j][1]);
 
-    if constexpr (T < kMA + kMB) {
-        constexpr int RS = H == 0 ? S : ((S + 1) & 3);
+    if constexpr (T < C::kMA + C::kMB) {
+        constexpr int RS = H == 0 ? S : (S + 1) % C::kStages;
         constexpr int RH = H == 0 ? 1 : 0;
-        const uint8_t *st = stage_buf<RS>() + l.frag_off + RH * 512;
-        if constexpr (T == 0 || T > kMA) {
-            constexpr int bi = T == 0 ? 0 : T - kMA;
-            const uint4 v = *reinterpret_cast<const uint4 *>(st + (l.b_atom0 + 2 * bi) * 1024);
+        const uint8_t *st = stage_buf<C, RS, G>();
+        if constexpr (T == 0 || T > C::kMA) {
+            constexpr int bi = T == 0 ? 0 : T - C::kMA;
+            const typename C::Op v = read_op<C>(st + l.lo_b + (2 * bi * 1024 + RH * 512),
+                                                st + C::kHiBase + l.hi_b + (bi * 1024 + RH * 512));
             if constexpr (H == 0) r.b1[bi] = v; else r.b0[bi] = v;
         } else {
             constexpr int ai = T - 1;
-            const uint4 v = *reinterpret_cast<const uint4 *>(st + (l.a_atom0 + 2 * ai) * 1024);
+            const typename C::Op v = read_op<C>(st + l.lo_a + (2 * ai * 1024 + RH * 512),
+                                                st + C::kHiBase + l.hi_a + (ai * 1024 + RH * 512));
             if constexpr (H == 0) r.a1[ai] = v; else r.a0[ai] = v;
         }
     }
-    constexpr int kScStart = kSlots - (kMA + kMB);
-    if constexpr (H == 1 && S == 3 && T >= kScStart) {
+    constexpr int kScStart = C::kSlots - (C::kMA + C::kMB);
+    const uint8_t *scb = scale_buf<C, G>();
+    if constexpr (C::Fmt::kScaleAhead) {
+        if constexpr (H == 1 && SG == 3 && T >= kScStart) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int q = 2 * (T - kScStart) + e;
-            const int hh = q & 1, t = q >> 1;
-            if (t < kMA)
-                r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-            else
-                r.sb_n[t - kMA][hh] =
-                    *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * (t - kMA)) * 256 + l.sc_off + hh * 128);
+            for (int e = 0; e < 2; ++e) {
+                const int q = 2 * (T - kScStart) + e;
+                const int hh = q & 1, t = q >> 1;
+                if (t < C::kMA)
+                    r.sa_n[t][hh] = *reinterpret_cast<const uint32_t *>(scb + l.sc_a + 2 * t * 256 + hh * 128);
+                else
+                    r.sb_n[t - C::kMA][hh] =
+                        *reinterpret_cast<const uint32_t *>(scb + l.sc_b + 2 * (t - C::kMA) * 256 + hh * 128);
+            }
         }
+    } else if constexpr (((H == 1 && SG == 3) || (H == 0 && SG == 0)) && T >= kScStart) {
+        constexpr int t = T - kScStart, hh = 1 - H;   // the half whose MFMAs are not running
+        if constexpr (t < C::kMA)
+            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scb + l.sc_a + (2 * t * 256 + hh * 128));
+        else
+            r.sb[t - C::kMA][hh] =
+                *reinterpret_cast<const uint32_t *>(scb + l.sc_b + (2 * (t - C::kMA) * 256 + hh * 128));
     }
 
-    constexpr int DS = H == 0 ? ((S + 2) & 3) : ((S + 3) & 3);
+    constexpr int DS = H == 0 ? (S + 2) % C::kStages : (S + 3) % C::kStages;
+    constexpr int DG = H == 0 ? (SG + 2) % 4 : (SG + 3) % 4;
     constexpr int P = H == 0 ? 1 : 0;
-    // FRESH (a tile's first k-step in the stream kernel): the second part of
-    // step 2 already went out before the previous tile's stores
-    constexpr int nv = (FRESH && S == 0 && H == 0) ? 0 : part_ops(DS);
-    const typename Ctx::kint dk = H == 0 ? k + 2 : k + 3;
-    if constexpr (nv > 0 && dma_slot(0, nv) == T) dma_op<DS, part_op(DS, P, 0), INNER>(c, dk);
-    if constexpr (nv > 1 && dma_slot(1, nv) == T) dma_op<DS, part_op(DS, P, 1), INNER>(c, dk);
-    if constexpr (nv > 2 && dma_slot(2, nv) == T) dma_op<DS, part_op(DS, P, 2), INNER>(c, dk);
-    if constexpr (nv > 3 && dma_slot(3, nv) == T) dma_op<DS, part_op(DS, P, 3), INNER>(c, dk);
-    static_assert(part_ops(0) <= 4, "dma slots");
+    constexpr int nv = (FRESH && SG == 0 && H == 0) ? 0 : C::part_ops(DG);
+    const typename X::kint dk = H == 0 ? k + 2 : k + 3;
+    if constexpr (nv > 0 && C::dma_slot(0, nv) == T) dma_op<C, DS, C::part_op(P, 0), G, INNER>(c, dk);
+    if constexpr (nv > 1 && C::dma_slot(1, nv) == T) dma_op<C, DS, C::part_op(P, 1), G, INNER>(c, dk);
+    if constexpr (nv > 2 && C::dma_slot(2, nv) == T) dma_op<C, DS, C::part_op(P, 2), G, INNER>(c, dk);
+    if constexpr (nv > 3 && C::dma_slot(3, nv) == T) dma_op<C, DS, C::part_op(P, 3), G, INNER>(c, dk);
+    if constexpr (nv > 4 && C::dma_slot(4, nv) == T) dma_op<C, DS, C::part_op(P, 4), G, INNER>(c, dk);
     // keep this slot's instructions in this slot
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int S, int H, int T = 0, bool FRESH = false, bool INNER = false, class Ctx>
-__device__ __forceinline__ void half_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
+template <class C, int S, int SG, int H, bool FRESH, bool INNER, int G, int T = 0, class X>
+__device__ __forceinline__ void half_step(const X &c, typename X::kint k, v16f (&acc)[C::kMB][C::kMA], Regs<C> &r,
                                           const Lds &l) {
-    if constexpr (T < kSlots) {
-        slot<S, H, T, FRESH, INNER>(c, k, acc, r, l);
-        half_step<S, H, T + 1, FRESH, INNER>(c, k, acc, r, l);
+    if constexpr (T < C::kSlots) {
+        slot<C, S, SG, H, T, FRESH, INNER, G>(c, k, acc, r, l);
+        half_step<C, S, SG, H, FRESH, INNER, G, T + 1>(c, k, acc, r, l);
     }
 }
 
 // One 128-wide k-step.  The barrier waits for this wave's DMA of step k+1
 // (only step k+2's instructions may still be outstanding) and then for every
-// wave, which publishes step k+1 and certifies that all reads of step k-1's
-// stage are done before half 1 starts overwriting it.  Vector memory
-// instructions complete in issue order (loads and stores alike), so the
-// count is exact.  FRESH: the first k-group of a tile in the stream kernel,
-// where EXTRA vector-memory instructions (the previous tile's stores and
-// this tile's bias loads) were issued after all of step 2's DMA; the first
-// two waits count past them instead of draining them.  INNER: steps k+2 and
-// k+3 are both below ksteps (see dma_op).
-template <int S, bool FRESH = false, int EXTRA = 0, bool INNER = false, class Ctx>
-__device__ __forceinline__ void k_step(const Ctx &c, typename Ctx::kint k, v16f (&acc)[kMB][kMA], Regs &r,
+// wave, which publishes step k+1 and certifies that every read of the stage
+// that half 1 starts overwriting is done.  Vector memory instructions
+// complete in issue order (loads and stores alike), so the count is exact.
+// FRESH: the first k-steps of a tile in the stream kernel, where EXTRA
+// vector-memory instructions (the previous tile's stores and this tile's
+// bias loads) were issued after all of step 2's DMA; the first two waits
+// count past them instead of draining them.
+template <class C, int S, int SG, bool FRESH, int EXTRA, bool INNER, int G, class X>
+__device__ __forceinline__ void k_step(const X &c, typename X::kint k, v16f (&acc)[C::kMB][C::kMA], Regs<C> &r,
                                        const Lds &l) {
-    constexpr int kStores = FRESH && S < 2 ? EXTRA : 0;
+    constexpr int kStores = FRESH && SG < 2 ? EXTRA : 0;
+    // with a 12-step loop body an opaque step index keeps the compiler from
+    // precomputing every step's addresses into registers
+    if constexpr (C::kPeriod > 4) asm volatile("" : "+s"(k));
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 0, 0, FRESH, INNER>(c, k, acc, r, l);
-    static_assert(issued_for((S + 2) & 3) + kStores <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for((S + 2) & 3) + kStores) : "memory");
+    half_step<C, S, SG, 0, FRESH, INNER, G>(c, k, acc, r, l);
+    static_assert(C::issued_for((SG + 2) & 3) + kStores <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::issued_for((SG + 2) & 3) + kStores) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    half_step<S, 1, 0, FRESH, INNER>(c, k, acc, r, l);
-    if constexpr (S == 3) {
+    half_step<C, S, SG, 1, FRESH, INNER, G>(c, k, acc, r, l);
+    if constexpr (C::Fmt::kScaleAhead && SG == 3) {
 #pragma unroll
-        for (int t = 0; t < kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
+        for (int t = 0; t < C::kMA; ++t) { r.sa[t][0] = r.sa_n[t][0]; r.sa[t][1] = r.sa_n[t][1]; }
 #pragma unroll
-        for (int t = 0; t < kMB; ++t) { r.sb[t][0] = r.sb_n[t][0]; r.sb[t][1] = r.sb_n[t][1]; }
+        for (int t = 0; t < C::kMB; ++t) { r.sb[t][0] = r.sb_n[t][0]; r.sb[t][1] = r.sb_n[t][1]; }
     }
 }
 
-// Epilogue: write the 256x256 tile (tm, tn) of C from the accumulators;
+// kPeriod consecutive k-steps from k0 (stage and k-group position 0 at k0).
+// FRESH applies to the first two.
+template <class C, bool FRESH, int EXTRA, bool INNER, int G, int s = 0, class X>
+__device__ __forceinline__ void period(const X &c, typename X::kint k0, v16f (&acc)[C::kMB][C::kMA], Regs<C> &r,
+                                       const Lds &l) {
+    if constexpr (s < C::kPeriod) {
+        k_step<C, s % C::kStages, s % 4, FRESH && s < 2, EXTRA, INNER, G>(c, k0 + s, acc, r, l);
+        period<C, FRESH, EXTRA, INNER, G, s + 1>(c, k0, acc, r, l);
+    }
+}
+
+// Scales of k-group 0 (both halves) and the operands of step 0's half 0,
+// once the prologue's DMA has landed for every wave.
+template <class C, int G>
+__device__ __forceinline__ void first_operands(Regs<C> &r, const Lds &l) {
+    const uint8_t *scb = scale_buf<C, G>();
+    const uint8_t *st = stage_buf<C, 0, G>();
+#pragma unroll
+    for (int t = 0; t < C::kMA; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scb + l.sc_a + t * 512 + hh * 128);
+#pragma unroll
+    for (int t = 0; t < C::kMB; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(scb + l.sc_b + t * 512 + hh * 128);
+#pragma unroll
+    for (int t = 0; t < C::kMA; ++t)
+        r.a0[t] = read_op<C>(st + l.lo_a + t * 2048, st + C::kHiBase + l.hi_a + t * 1024);
+#pragma unroll
+    for (int t = 0; t < C::kMB; ++t)
+        r.b0[t] = read_op<C>(st + l.lo_b + t * 2048, st + C::kHiBase + l.hi_b + t * 1024);
+}
+
+// ------------------------------------------------------------ tile order
+// Position `id` of the tile order: bands of group_m tile rows, walked column
+// by column.
+__device__ __forceinline__ void tile_at(int id, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+    const int band = group_m * tiles_n;
+    const int first_m = (id / band) * group_m;
+    const int gsz = min(tiles_m - first_m, group_m);
+    tm = first_m + (id % band) % gsz;
+    tn = (id % band) / gsz;
+}
+
+// Tile of block index b in a launch of nb blocks: XCD-contiguous ranges of
+// the tile order (blocks are dispatched to the XCDs round-robin).
+__device__ __forceinline__ void tile_of(int b, int nb, int tiles_m, int tiles_n, int group_m, int &tm, int &tn) {
+    const int xcd = b % kXcds, local = b / kXcds;
+    const int per = nb / kXcds, rem = nb % kXcds;
+    tile_at(xcd * per + (xcd < rem ? xcd : rem) + local, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// Byte offsets of this wave's unit rows and scale-atom rows for tile (tm,
+// tn), starting at k-step kfirst (a multiple of 4).  Row groups past an
+// operand are clamped to its last group: those rows of C are never stored,
+// so their contents do not matter.
+template <class C, class X>
+__device__ __forceinline__ void tile_rows(const X &c, int tm, int tn, int64_t nGA, int64_t nGB, int64_t ksteps,
+                                          int64_t kgroups, int64_t kfirst, int lane, int (&lo)[C::kLoLoads],
+                                          uint32_t (&hi)[C::kHiLoads > 0 ? C::kHiLoads : 1],
+                                          int (&sc)[C::kScaleLoads]) {
+    const int64_t gA0 = (int64_t)tm * C::kGA, gB0 = (int64_t)tn * C::kGB;
+    auto group_of = [&](int a) -> int64_t {
+        const bool isA = a < C::kGA;
+        const int64_t g = isA ? gA0 + a : gB0 + (a - C::kGA);
+        const int64_t gmax = (isA ? nGA : nGB) - 1;
+        return g < gmax ? g : gmax;
+    };
+    constexpr int64_t kStep = C::Fmt::kStepBytes;
+#pragma unroll
+    for (int r = 0; r < C::kLoLoads; ++r)
+        lo[r] = (int)((group_of(C::kWaves * r + c.wave) * ksteps + kfirst) * kStep);
+    if constexpr (C::kHiLoads > 0) {
+#pragma unroll
+        for (int r = 0; r < C::kHiLoads; ++r) {
+            const int h = C::kWaves * r + c.wave;
+            hi[r] = (uint32_t)((group_of(2 * h + (lane & 1)) * ksteps + kfirst) * kStep) + 1024u +
+                    (uint32_t)((lane >> 1) * 16);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < C::kScaleLoads; ++r)
+        sc[r] = (int)((group_of(C::kWaves * r + c.wave) * kgroups + kfirst / 4) * 256);
+}
+
+// ------------------------------------------------------------ bias
+// This lane's bias values for tile column tn: columns n0 + 32i + 8q +
+// 4(lane/32) + 0..3 of its wave tile, 4 bf16 per (i, q), one 8-byte buffer
+// load each, issued before the k-loop so they have long arrived by the
+// epilogue.  The range check of a buffer load zeroes whole dwords, so the
+// range ends at the 16-byte boundary after the last entry (the bias is
+// 16-byte aligned, so that block is inside its allocation's last page);
+// columns past it read 0, columns past N are never stored.
+template <class C>
+__device__ __forceinline__ void load_bias(__amdgpu_buffer_rsrc_t rb, int tn, int wn, int lane,
+                                          v2u_t (&bias_bits)[C::kMB * 4]) {
+    const int col0 = tn * C::kBN + wn * C::kWN + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
+}
+
+// C[i][j] = (sum) + bias[j], added in fp32 before the output rounding.
+template <class C>
+__device__ __forceinline__ void add_bias(v16f (&acc)[C::kMB][C::kMA], const v2u_t (&bias_bits)[C::kMB * 4]) {
+#pragma unroll
+    for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v2u_t bb = bias_bits[i * 4 + q];
+            const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
+            const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
+#pragma unroll
+            for (int j = 0; j < C::kMA; ++j) {
+                acc[i][j][4 * q] += b0;
+                acc[i][j][4 * q + 1] += b1;
+                acc[i][j][4 * q + 2] += b2;
+                acc[i][j][4 * q + 3] += b3;
+            }
+        }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
+// ------------------------------------------------------------ epilogues
+// Write the tile (tm, tn) of C from the accumulators;
 // acc[i][j][r] = C[m0 + 32j + lane%32][n0 + 32i + 8(r/4) + 4(lane/32) + r%4].
 // bf16: rounded (V_CVT_PK_BF16_F32, nearest even), staged in LDS, then
-// written as whole 512-byte row segments (each store instruction covers 2
-// rows with 16 bytes per lane; non-temporal, as C is not read again here);
-// fp32: 16 bytes per lane straight from registers.  Masked at the M/N edges.
-template <bool OUT_BF16>
-__device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn, int64_t M, int64_t N, void *C,
-                                           int64_t ldc, int wave, int lane) {
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
+// written as whole row segments (16 bytes per lane; non-temporal, as C is
+// not read again here); fp32: 16 bytes per lane straight from registers.
+// Masked at the M/N edges.  With two K groups, group 0 holds the summed
+// accumulators (wave = its index in the group); all waves (index wave_all)
+// take part in the bf16 stores.
+template <class C, bool OUT_BF16>
+__device__ __forceinline__ void store_tile(v16f (&acc)[C::kMB][C::kMA], int tm, int tn, int64_t M, int64_t N,
+                                           void *Cout, int64_t ldc, int group, int wave, int wave_all, int lane) {
+    const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
-    const int64_t tm0 = (int64_t)tm * kBM, tn0 = (int64_t)tn * kBN;
+    const int64_t tm0 = (int64_t)tm * C::kBM, tn0 = (int64_t)tn * C::kBN;
     if (OUT_BF16) {
         // Every wave waited for its own DMAs; the barrier makes sure all of
         // them have landed and every stage read is done before the tile
         // overwrites the stages.
         __syncthreads();
+        if (group == 0) {
 #pragma unroll
-        for (int j = 0; j < kMA; ++j)
+            for (int j = 0; j < C::kMA; ++j)
 #pragma unroll
-            for (int i = 0; i < kMB; ++i)
+                for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int rl = wm * kWM + 32 * j + lrow, cl = wn * kWN + 32 * i + 8 * q + 4 * lhi;
-                    const uint32_t p01 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}), bf16x2_t));
-                    const uint32_t p23 = __builtin_bit_cast(
-                        uint32_t, __builtin_convertvector((f32x2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}), bf16x2_t));
-                    *reinterpret_cast<uint2 *>(c_stage(rl, cl)) = uint2{p01, p23};
-                }
+                    for (int q = 0; q < 4; ++q) {
+                        const int rl = wm * C::kWM + 32 * j + lrow, cl = wn * C::kWN + 32 * i + 8 * q + 4 * lhi;
+                        *reinterpret_cast<uint2 *>(c_stage<C>(rl, cl)) =
+                            uint2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                  pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                    }
+        }
         __syncthreads();
-        constexpr int kRowsPerWave = kBM / kWaves;        // 32: 16 instructions of 2 rows
-        const int cl = (lane & 31) * 8;
+        constexpr int kLanesPerRow = C::kBN * 2 / 16;        // 32 (256 columns) or 16 (128)
+        constexpr int kRowsPerInst = 64 / kLanesPerRow;
+        constexpr int kRowsPerWave = C::kBM / (C::kWaves * C::kKG);
+        constexpr int kInst = kRowsPerWave / kRowsPerInst;
+        const int cl = (lane % kLanesPerRow) * 8;
         const int64_t col = tn0 + cl;
-        uint4 v[kRowsPerWave / 2];
+        const int rsub = lane / kLanesPerRow;
+        uint4 v[kInst];
 #pragma unroll
-        for (int it = 0; it < kRowsPerWave / 2; ++it)
-            v[it] = *reinterpret_cast<const uint4 *>(c_stage(kRowsPerWave * wave + 2 * it + (lane >> 5), cl));
-        uint16_t *dst0 = reinterpret_cast<uint16_t *>(C) + (tm0 + kRowsPerWave * wave + (lane >> 5)) * ldc + col;
-        if (tm0 + kBM <= M && tn0 + kBN <= N) {
+        for (int it = 0; it < kInst; ++it)
+            v[it] = *reinterpret_cast<const uint4 *>(c_stage<C>(kRowsPerWave * wave_all + kRowsPerInst * it + rsub, cl));
+        uint16_t *dst0 = reinterpret_cast<uint16_t *>(Cout) + (tm0 + kRowsPerWave * wave_all + rsub) * ldc + col;
+        if (tm0 + C::kBM <= M && tn0 + C::kBN <= N) {
 #pragma unroll
-            for (int it = 0; it < kRowsPerWave / 2; ++it)
-                __builtin_nontemporal_store(__builtin_bit_cast(v4u_t, v[it]), reinterpret_cast<v4u_t *>(dst0 + 2 * it * ldc));
+            for (int it = 0; it < kInst; ++it)
+                __builtin_nontemporal_store(__builtin_bit_cast(v4u_t, v[it]),
+                                            reinterpret_cast<v4u_t *>(dst0 + kRowsPerInst * it * ldc));
         } else {
 #pragma unroll
-            for (int it = 0; it < kRowsPerWave / 2; ++it) {
-                const int64_t row = tm0 + kRowsPerWave * wave + 2 * it + (lane >> 5);
+            for (int it = 0; it < kInst; ++it) {
+                const int64_t row = tm0 + kRowsPerWave * wave_all + kRowsPerInst * it + rsub;
                 if (row >= M || col >= N) continue;
-                uint16_t *dst = dst0 + 2 * it * ldc;
+                uint16_t *dst = dst0 + kRowsPerInst * it * ldc;
                 if (col + 7 < N) {
                     *reinterpret_cast<uint4 *>(dst) = v[it];
                 } else {
@@ -400,18 +713,19 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
             }
         }
     } else {
-        const int64_t m0 = tm0 + wm * kWM, n0 = tn0 + wn * kWN;
+        if (group != 0) return;
+        const int64_t m0 = tm0 + wm * C::kWM, n0 = tn0 + wn * C::kWN;
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) {
+        for (int j = 0; j < C::kMA; ++j) {
             const int64_t row = m0 + 32 * j + lrow;
             if (row >= M) continue;
 #pragma unroll
-            for (int i = 0; i < kMB; ++i) {
+            for (int i = 0; i < C::kMB; ++i) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int64_t col = n0 + 32 * i + 8 * q + 4 * lhi;
                     const v4f v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    float *dst = reinterpret_cast<float *>(C) + row * ldc + col;
+                    float *dst = reinterpret_cast<float *>(Cout) + row * ldc + col;
                     if (col + 3 < N) {
                         *reinterpret_cast<v4f *>(dst) = v;
                     } else {
@@ -425,291 +739,251 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[kMB][kMA], int tm, int tn
     }
 }
 
-// Tile of block index b in a launch of nb blocks: XCD-contiguous ranges of
-// the tile order (blocks are dispatched to the XCDs round-robin), the order
-// walking bands of kGroupM tile rows column by column.
-__device__ __forceinline__ void tile_of(int b, int nb, int tiles_m, int tiles_n, int &tm, int &tn) {
-    const int xcd = b % kXcds, local = b / kXcds;
-    const int per = nb / kXcds, rem = nb % kXcds;
-    const int id = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int band = kGroupM * tiles_n;
-    const int first_m = (id / band) * kGroupM;
-    const int gsz = min(tiles_m - first_m, kGroupM);
-    tm = first_m + (id % band) % gsz;
-    tn = (id % band) / gsz;
+// Epilogue of the stream kernel (bf16 output).  Every wave issues exactly
+// epi_stores<C>() buffer stores per tile whatever the edges: a chunk past row
+// M or column N gets an out-of-range offset, which the buffer range check
+// drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
+// what lets the next tile's first waits count past the stores instead of
+// draining them.  Before the stores, the epilogue issues the second part of
+// the next tile's step 2 (its first k-step would otherwise issue it after
+// them), into stage 2, free since the tile's last k-step.
+//  - Four stages (FP4): stages 0-2 already hold the next tile's first
+//    k-steps, so only stage 3 is free.  Each wave takes a 4 KB slot of it:
+//    in pass p (kMA passes) the wave stages its own 32 x 64 block (MFMA row
+//    tile p: tile rows 128 wm + 32p + [0, 32), columns 64 wn + [0, 64)), 128
+//    bytes per row with 16-byte chunk c of row r at c ^ (r % 8), and reads
+//    it back as whole 128-byte row segments, 8 rows per store instruction.
+//    After the first barrier (every wave done with stage 3's last k-step) no
+//    wave waits for another: a wave's LDS operations complete in order, so
+//    its next pass may overwrite the slot it has just read.
+//  - Three stages (FP6): the next tile's first steps occupy every stage, so
+//    each lane writes its 4 consecutive bf16 of each (i, j, q) straight from
+//    registers (8-byte stores; lanes L and L+32 cover 16 bytes of a row).
+template <class C>
+__host__ __device__ constexpr int epi_stores() {
+    return C::kStages == 4 ? C::kMA * 4 : C::kMA * C::kMB * 4;
 }
 
-// Byte offsets of this wave's atom rows and scale-atom rows for tile (tm, tn).
-// Row groups past an operand are clamped to its last group: those rows of C
-// are never stored, so their contents do not matter.
-template <class Ctx>
-__device__ __forceinline__ void tile_rows(const Ctx &c, int tm, int tn, int64_t nGA, int64_t nGB, int (&ld)[kLoads],
-                                          int (&sc)[kLoads]) {
-    const int64_t gA0 = (int64_t)tm * kGA, gB0 = (int64_t)tn * kGB;
+template <class C>
+__device__ __forceinline__ void store_tile_stream(const Ctx<C, true> &c, v16f (&acc)[C::kMB][C::kMA], int tm, int tn,
+                                                  int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
+                                                  int lane) {
+    dma_part<C, 2, 2, 1, 0>(c, c.kstream + 2);
+    const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int row_w = tm * C::kBM + C::kWM * wm;   // first C row of this wave's block
+    if constexpr (C::kStages == 4) {
+        constexpr int kSlotBytes = 32 * C::kWN * 2;   // 4 KB per wave
+        static_assert(kSlotBytes * C::kWaves == C::kStageBytes, "one slot per wave fills stage 3");
+        static_assert(C::kWN == 64, "8 lanes per 128-byte row");
+        uint8_t *slot_base = stage_buf<C, 3, 0>() + wave * kSlotBytes;
+        auto c_slot = [&](int r, int chunk) { return slot_base + r * (C::kWN * 2) + ((chunk ^ (r & 7)) * 16); };
+        const int col = tn * C::kBN + C::kWN * wn + 8 * (lane & 7);   // this lane's 8 columns on the way out
+        // every wave is done reading stage 3 (the tile's last k-step); a bare
+        // barrier: a __syncthreads() fence would also wait for the next tile's DMAs
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-        const int a = kWaves * r + c.wave;
-        const bool isA = a < kGA;
-        int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
-        const int64_t gmax = (isA ? nGA : nGB) - 1;
-        g = g < gmax ? g : gmax;
-        ld[r] = (int)(g * c.ksteps * 1024);
-        sc[r] = (int)(g * c.kgroups * 256);
+        for (int p = 0; p < C::kMA; ++p) {
+#pragma unroll
+            for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2 *>(c_slot(lrow, 4 * i + q) + 8 * lhi) =
+                        uint2{pack_bf16x2(acc[i][p][4 * q], acc[i][p][4 * q + 1]),
+                              pack_bf16x2(acc[i][p][4 * q + 2], acc[i][p][4 * q + 3])};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int r = 8 * s + (lane >> 3);
+                const v4u_t v = *reinterpret_cast<const v4u_t *>(c_slot(r, lane & 7));
+                const int row = row_w + 32 * p + r;
+                const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
+            }
+        }
+    } else {
+        const int col0 = tn * C::kBN + C::kWN * wn + 4 * lhi;
+#pragma unroll
+        for (int j = 0; j < C::kMA; ++j) {
+            const int row = row_w + 32 * j + lrow;
+#pragma unroll
+            for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int col = col0 + 32 * i + 8 * q;
+                    const v2u_t v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+                    const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, kCachePolicyNT);
+                }
+        }
     }
 }
 
-// BIAS: C[i][j] = (sum) + bias[j], bias a bf16 vector of N, added in fp32
-// before the output rounding.
-template <bool OUT_BF16, bool BIAS>
-__global__ __launch_bounds__(kThreads) void gemm_a4w4_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
-                                                             int tiles_n, const uint8_t *__restrict__ A,
-                                                             const uint8_t *__restrict__ As,
-                                                             const uint8_t *__restrict__ B,
-                                                             const uint8_t *__restrict__ Bs,
-                                                             const uint16_t *__restrict__ bias,
-                                                             void *__restrict__ C, int64_t ldc) {
+// ------------------------------------------------------------ kernels
+// The k-loop of K group G over `steps` k-steps (a multiple of 4; steps at or
+// past c.ksteps land as zeros): prologue DMAs, whole periods, then the drain
+// of the trailing DMAs.
+template <class C, int G, class X>
+__device__ __forceinline__ void run_tile(const X &c, v16f (&acc)[C::kMB][C::kMA], const Lds &l, int64_t steps) {
+    // Prologue: steps 0 and 1 whole, the first part of step 2 (its second
+    // part goes out in step 0's first half).
+    dma_part<C, 0, 0, 0, G>(c, 0);
+    dma_part<C, 0, 0, 1, G>(c, 0);
+    dma_part<C, 1, 1, 0, G>(c, 1);
+    dma_part<C, 1, 1, 1, G>(c, 1);
+    dma_part<C, 2, 2, 0, G>(c, 2);
+    Regs<C> r;
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::issued_for(1) + C::part_ops(2)) : "memory");
+    first_operands<C, G>(r, l);
+    // a period from k0 fetches steps k0+2 .. k0+kPeriod+2: inside K while
+    // k0 + kPeriod + 2 < ksteps
+    int64_t k0 = 0;
+    if constexpr (C::Fmt::kInner)
+        for (; k0 < steps && k0 + C::kPeriod + 2 < c.ksteps; k0 += C::kPeriod)
+            period<C, false, 0, true, G>(c, k0, acc, r, l);
+    for (; k0 < steps; k0 += C::kPeriod) period<C, false, 0, false, G>(c, k0, acc, r, l);
+    // drain the trailing (out-of-range) DMAs before LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Split form: 4 KB of the second group's stages per accumulator tile of a
+// wave (block w * kSlots + t), float e of lane L at (e * 64 + L) * 4, so
+// consecutive lanes touch consecutive banks.
+template <class C>
+__device__ __forceinline__ float *partial_slot(int wave, int tile) {
+    constexpr int kPerStage = C::kStageBytes / 4096;
+    static_assert(C::kStageBytes % 4096 == 0 && C::kWaves * C::kSlots <= kPerStage * C::kStages, "partials fit");
+    const int b = wave * C::kSlots + tile;
+    return reinterpret_cast<float *>(stage_dyn<C, 1>(b / kPerStage) + (b % kPerStage) * 4096);
+}
+
+// One output tile per workgroup.  256x256 (the main order: workgroup b takes
+// tile b of the XCD-remapped order) or 128x128 (the tail: workgroup b
+// computes quarter b % 4 of 256x256 tile first + b / 4 of the main order).
+// Two K groups (split form): group g = wave / 4 takes k-groups [g * kg0, ...)
+// of the tile (kg0 = half of them, rounded up); group 1's partial tile is
+// added into group 0's through LDS before the epilogue.  Every wave runs the
+// same number of k-steps (group 1's past its K land as zeros), so the
+// per-step barriers line up across groups.
+// BIAS: C[i][j] = (sum) + bias[j], bias a bf16 vector of N.
+template <class C, bool OUT_BF16, bool BIAS>
+__global__ __launch_bounds__(C::kThreads) void gemm_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
+                                                           int tiles_n, int group_m, int first,
+                                                           const uint8_t *__restrict__ A,
+                                                           const uint8_t *__restrict__ As,
+                                                           const uint8_t *__restrict__ B,
+                                                           const uint8_t *__restrict__ Bs,
+                                                           const uint16_t *__restrict__ bias, void *__restrict__ Cout,
+                                                           int64_t ldc) {
+    constexpr bool kSplit = C::kKG == 2;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int group = kSplit ? wave_all / C::kWaves : 0;
+    const int wave = wave_all % C::kWaves;
+    const int wn = wave / C::kWavesM;
 
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    if constexpr (C::kBM == 256) {
+        tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    } else {
+        const int quarter = (int)(blockIdx.x & 3);
+        tile_at(first + (int)(blockIdx.x >> 2), tiles_m, tiles_n, group_m, tm, tn);
+        tm = 2 * tm + (quarter >> 1);
+        tn = 2 * tn + (quarter & 1);
+    }
 
-    GemmCtx c;
-    c.ksteps = K_pad / 128;
-    c.kgroups = cdiv(K_pad, 512);
+    const int64_t ksteps = K_pad / 128, kgroups = cdiv(K_pad, 512);
+    // k-groups of group 0 (all of them without the split); group 1 starts at k-group kg0
+    const int64_t kg0 = kSplit ? (kgroups + 1) / 2 : kgroups;
+    const int64_t kfirst = group ? 4 * kg0 : 0;
+    Ctx<C, false> c;
+    c.ksteps = group ? ksteps - kfirst : (kSplit ? (ksteps < 4 * kg0 ? ksteps : 4 * kg0) : ksteps);
+    c.kgroups = group ? kgroups - kg0 : kg0;
     c.wave = wave;
     c.lane16 = lane * 16;
     c.lane4 = lane * 4;
     const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);   // row groups present in memory
-    c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
-    c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
-    c.rAs = make_rsrc(As, nGA * c.kgroups * 256);
-    c.rBs = make_rsrc(Bs, nGB * c.kgroups * 256);
+    constexpr int64_t kStep = C::Fmt::kStepBytes;
+    c.rA = make_rsrc(A, nGA * ksteps * kStep);
+    c.rB = make_rsrc(B, nGB * ksteps * kStep);
+    c.rAs = make_rsrc(As, nGA * kgroups * 256);
+    c.rBs = make_rsrc(Bs, nGB * kgroups * 256);
 
-    // This lane's bias values (columns n0 + 32i + 8q + 4(lane/32) + 0..3 of its
-    // tile, 4 bf16 per (i, q)), loaded before the k-loop so they have long
-    // arrived by the epilogue.  The range check of a buffer load zeroes whole
-    // dwords, so the range ends at the 16-byte boundary after the last entry
-    // (the bias is 16-byte aligned, so that block is inside the caller's
-    // allocation's last page); columns past it read 0, columns past N are
-    // never stored.
-    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-    v2u bias_bits[BIAS ? kMB * 4 : 1];
-    if constexpr (BIAS) {
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bias, cdiv(N * 2, 16) * 16);
-        const int col0 = tn * kBN + wn * kWN + 4 * (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
-    }
-    tile_rows(c, tm, tn, nGA, nGB, c.ld_row, c.sc_row);
+    v2u_t bias_bits[BIAS ? C::kMB * 4 : 1];
+    if constexpr (BIAS) load_bias<C>(make_rsrc(bias, cdiv(N * 2, 16) * 16), tn, wn, lane, bias_bits);
+    // a group's offsets start at its first k-step
+    tile_rows<C>(c, tm, tn, nGA, nGB, ksteps, kgroups, kfirst, lane, c.lo_row, c.hi_off, c.sc_row);
 
-    v16f acc[kMB][kMA];
+    v16f acc[C::kMB][C::kMA];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i)
+    for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
 
-    // Prologue: steps 0 and 1 whole, the first part of step 2 (its second
-    // part goes out in step 0's first half).
-    dma_part<0, 0>(c, 0);
-    dma_part<0, 1>(c, 0);
-    dma_part<1, 0>(c, 1);
-    dma_part<1, 1>(c, 1);
-    dma_part<2, 0>(c, 2);
+    const Lds l = lds_offsets<C>(wave, lane);
+    const int64_t steps = 4 * kg0;   // k-steps every wave runs
+    if (kSplit && group == 1) run_tile<C, 1>(c, acc, l, steps);
+    else run_tile<C, 0>(c, acc, l, steps);
 
-    // Lane L of a 32-row operand tile takes row L%32, k-block 2*half + L/32:
-    // atom (L%32)/16, slice (L%16) + 16*(2*half + L/32).  Its scale is byte
-    // (k-step % 4) of the dword at the same slice of the scale atom.
-    const int lrow = lane & 31, lhi = lane >> 5;
-    Lds l;
-    l.frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;
-    l.sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;
-    l.a_atom0 = wm * kTA;
-    l.b_atom0 = kGA + wn * kTB;
-
-    Regs r;
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(issued_for(1) + part_ops(2)) : "memory");
+    if constexpr (kSplit) {
+        // every wave is past its last stage read; group 1's stages take its partial tile
+        __syncthreads();
+        if (group == 1) {
 #pragma unroll
-    for (int t = 0; t < kMA; ++t)
+            for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
+                for (int j = 0; j < C::kMA; ++j) {
+                    float *p = partial_slot<C>(wave, i * C::kMA + j) + lane;
 #pragma unroll
-    for (int t = 0; t < kMB; ++t)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-#pragma unroll
-    for (int t = 0; t < kMA; ++t)
-        r.a0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
-#pragma unroll
-    for (int t = 0; t < kMB; ++t)
-        r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
-
-    // k-group h fetches steps 4h+2 .. 4h+6: inside K while 4h+6 < ksteps
-    int64_t h = 0;
-    for (; 4 * h + 6 < c.ksteps; ++h) {
-        const int64_t k0 = 4 * h;
-        k_step<0, false, 0, true>(c, k0, acc, r, l);
-        k_step<1, false, 0, true>(c, k0 + 1, acc, r, l);
-        k_step<2, false, 0, true>(c, k0 + 2, acc, r, l);
-        k_step<3, false, 0, true>(c, k0 + 3, acc, r, l);
-    }
-    for (; h < c.kgroups; ++h) {
-        const int64_t k0 = 4 * h;
-        k_step<0>(c, k0, acc, r, l);
-        k_step<1>(c, k0 + 1, acc, r, l);
-        k_step<2>(c, k0 + 2, acc, r, l);
-        k_step<3>(c, k0 + 3, acc, r, l);
-    }
-    // drain the trailing (out-of-range) DMAs before LDS is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // ---- epilogue
-    if constexpr (BIAS) {
-#pragma unroll
-        for (int i = 0; i < kMB; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v2u bb = bias_bits[i * 4 + q];
-                const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
-                const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
-#pragma unroll
-                for (int j = 0; j < kMA; ++j) {
-                    acc[i][j][4 * q] += b0;
-                    acc[i][j][4 * q + 1] += b1;
-                    acc[i][j][4 * q + 2] += b2;
-                    acc[i][j][4 * q + 3] += b3;
+                    for (int e = 0; e < 16; ++e) p[e * 64] = acc[i][j][e];
                 }
-            }
-    }
-    store_tile<OUT_BF16>(acc, tm, tn, M, N, C, ldc, wave, lane);
-}
-
-// Epilogue of the stream kernel (bf16 output).  Stages 0-2 already hold the
-// next tile's first k-steps, so only stage 3 is free.  Each wave takes a
-// 4 KB slot of it: in pass p (kMA passes) the wave stages its own 32 x 64
-// block (MFMA row tile p: tile rows 128 wm + 32p + [0, 32), columns
-// 64 wn + [0, 64)), 128 bytes per row with 16-byte chunk c of row r at c ^
-// (r % 8), and reads it back as whole 128-byte row segments, 8 rows per store
-// instruction.  After the first barrier (every wave done with stage 3's last
-// k-step) no wave waits for another: a wave's LDS operations complete in
-// order, so its next pass may overwrite the slot it has just read.  Each wave
-// issues exactly kEpiStoresPerTile 16-byte buffer stores per tile whatever
-// the edges: a chunk past row M or column N gets an out-of-range offset, which
-// the buffer range check drops (N % 8 == 0, so a chunk is all in or all out).
-// The fixed count is what lets the next tile's first waits count past the
-// stores instead of draining them.  Before the stores, the epilogue issues
-// the second part of the next tile's step 2 (its first k-step would otherwise
-// issue it after them), into stage 2, free since the tile's last k-step.
-constexpr int kSlotBytes = 32 * kWN * 2;                  // 4 KB per wave
-static_assert(kSlotBytes * kWaves == kStageBytes, "one slot per wave fills stage 3");
-static_assert(kEpiStoresPerTile == kMA * 4, "store count: 4 instructions of 8 rows per pass");
-
-__device__ __forceinline__ uint8_t *c_slot(int wave, int r, int chunk) {
-    return g_stage3 + wave * kSlotBytes + r * (kWN * 2) + ((chunk ^ (r & 7)) * 16);
-}
-
-__device__ __forceinline__ void store_tile_stream(const GemmCtxT<true> &c, v16f (&acc)[kMB][kMA], int tm, int tn,
-                                                  int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
-                                                  int lane) {
-    dma_part<2, 1>(c, c.kstream + 2);
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
-    const int lrow = lane & 31, lhi = lane >> 5;
-    const int row_w = tm * kBM + kWM * wm;                     // first C row of this wave's block
-    const int col = tn * kBN + kWN * wn + 8 * (lane & 7);      // this lane's 8 columns on the way out
-    // every wave is done reading stage 3 (the tile's last k-step); a bare
-    // barrier: a __syncthreads() fence would also wait for the next tile's DMAs
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        __syncthreads();
+        if (group == 0) {
 #pragma unroll
-    for (int p = 0; p < kMA; ++p) {
+            for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+                for (int j = 0; j < C::kMA; ++j) {
+                    const float *p = partial_slot<C>(wave, i * C::kMA + j) + lane;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t p01 = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector((f32x2_t{acc[i][p][4 * q], acc[i][p][4 * q + 1]}), bf16x2_t));
-                const uint32_t p23 = __builtin_bit_cast(
-                    uint32_t, __builtin_convertvector((f32x2_t{acc[i][p][4 * q + 2], acc[i][p][4 * q + 3]}), bf16x2_t));
-                *reinterpret_cast<uint2 *>(c_slot(wave, lrow, 4 * i + q) + 8 * lhi) = uint2{p01, p23};
-            }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int r = 8 * s + (lane >> 3);
-            const v4u_t v = *reinterpret_cast<const v4u_t *>(c_slot(wave, r, lane & 7));
-            const int row = row_w + 32 * p + r;
-            const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += p[e * 64];
+                }
         }
     }
+    if constexpr (BIAS)
+        if (group == 0) add_bias<C>(acc, bias_bits);
+    store_tile<C, OUT_BF16>(acc, tm, tn, M, N, Cout, ldc, group, wave, wave_all, lane);
 }
 
-typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
-
-// This lane's bias values for tile column tn: columns n0 + 32i + 8q +
-// 4(lane/32) + 0..3 of the tile, 4 bf16 per (i, q), one 8-byte buffer load
-// each (the range ends at the 16-byte boundary after the last entry; the
-// bias is 16-byte aligned, so that block is inside its allocation; columns
-// past it read 0 and are never stored).
-__device__ __forceinline__ void load_bias(__amdgpu_buffer_rsrc_t rb, int tn, int wn, int lane,
-                                          v2u_t (&bias_bits)[kMB * 4]) {
-    const int col0 = tn * kBN + wn * kWN + 4 * (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < kMB; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            bias_bits[i * 4 + q] = __builtin_amdgcn_raw_buffer_load_b64(rb, (col0 + 32 * i + 8 * q) * 2, 0, 0);
-}
-
-__device__ __forceinline__ void add_bias(v16f (&acc)[kMB][kMA], const v2u_t (&bias_bits)[kMB * 4]) {
-#pragma unroll
-    for (int i = 0; i < kMB; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const v2u_t bb = bias_bits[i * 4 + q];
-            const float b0 = __uint_as_float(bb[0] << 16), b1 = __uint_as_float(bb[0] & 0xFFFF0000u);
-            const float b2 = __uint_as_float(bb[1] << 16), b3 = __uint_as_float(bb[1] & 0xFFFF0000u);
-#pragma unroll
-            for (int j = 0; j < kMA; ++j) {
-                acc[i][j][4 * q] += b0;
-                acc[i][j][4 * q + 1] += b1;
-                acc[i][j][4 * q + 2] += b2;
-                acc[i][j][4 * q + 3] += b3;
-            }
-        }
-}
-
-// Persistent form of gemm_a4w4_kernel for bf16 output:
-// gridDim.x workgroups, block b runs tiles b, b + gridDim.x, ... of the first
-// `tiles` of the tile order as one stream of k-steps.  A tile's last k-steps
-// already fetch the next tile's first three and its first operands and
-// scales, so the pipeline never drains between tiles; the epilogue's stores
-// then overlap the next tile's first k-steps (its first two waits count past
-// them, only the third one needs them done).  The k-loop is the one-tile
-// kernel's, DMA schedule included.  BIAS: a tile's bias values are loaded
-// right after the previous tile's stores (8 more instructions for those
-// waits to count past).  Needs N % 8 == 0 and M * ldc * 2 < 2^31 (32-bit
-// store offsets).
-template <bool BIAS>
-__global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N, int K_pad, int tiles_m, int tiles_n,
-                                                                    int tiles, const uint8_t *__restrict__ A,
-                                                                    const uint8_t *__restrict__ As,
-                                                                    const uint8_t *__restrict__ B,
-                                                                    const uint8_t *__restrict__ Bs,
-                                                                    const uint16_t *__restrict__ bias,
-                                                                    void *__restrict__ C, int ldc) {
-    constexpr int kBiasLoads = BIAS ? kMB * 4 : 0;
-    constexpr int kFreshOps = kEpiStoresPerTile + kBiasLoads;
+// Persistent form of gemm_kernel (256x256 tiles, bf16 output): gridDim.x
+// workgroups, block b runs tiles b, b + gridDim.x, ... of the first `tiles`
+// of the tile order as one stream of k-steps.  A tile's last k-steps already
+// fetch the next tile's first three and its first operands and scales, so
+// the pipeline never drains between tiles; the epilogue's stores then
+// overlap the next tile's first k-steps (its first two waits count past
+// them, only the third one needs them done).  A tile is kstream = 4 *
+// kgroups steps of the stream, a multiple of kPeriod, so every tile starts
+// at stage 0.  BIAS: a tile's bias values are loaded right after the
+// previous tile's stores (kMB * 4 more instructions for those waits to count
+// past).  Needs N % 8 == 0 and M * ldc * 2 < 2^31 (32-bit store offsets).
+template <class C, bool BIAS>
+__global__ __launch_bounds__(C::kThreads) void gemm_stream_kernel(int M, int N, int K_pad, int tiles_m, int tiles_n,
+                                                                  int group_m, int tiles,
+                                                                  const uint8_t *__restrict__ A,
+                                                                  const uint8_t *__restrict__ As,
+                                                                  const uint8_t *__restrict__ B,
+                                                                  const uint8_t *__restrict__ Bs,
+                                                                  const uint16_t *__restrict__ bias,
+                                                                  void *__restrict__ Cout, int ldc) {
+    static_assert(C::kKG == 1 && C::kBM == 256, "stream form: main tiles");
+    constexpr int kBiasLoads = BIAS ? C::kMB * 4 : 0;
+    constexpr int kFreshOps = epi_stores<C>() + kBiasLoads;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int wn = wave / C::kWavesM;
     const int P = gridDim.x;
 
-    GemmCtxT<true> c;
+    Ctx<C, true> c;
     c.ksteps = K_pad / 128;
     c.kgroups = (K_pad + 511) / 512;
     c.kstream = 4 * c.kgroups;
@@ -717,109 +991,77 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
     c.lane16 = lane * 16;
     c.lane4 = lane * 4;
     const int nGA = (M + 15) / 16, nGB = (N + 15) / 16;
-    c.rA = make_rsrc(A, (int64_t)nGA * c.ksteps * 1024);
-    c.rB = make_rsrc(B, (int64_t)nGB * c.ksteps * 1024);
+    constexpr int64_t kStep = C::Fmt::kStepBytes;
+    c.rA = make_rsrc(A, (int64_t)nGA * c.ksteps * kStep);
+    c.rB = make_rsrc(B, (int64_t)nGB * c.ksteps * kStep);
     c.rAs = make_rsrc(As, (int64_t)nGA * c.kgroups * 256);
     c.rBs = make_rsrc(Bs, (int64_t)nGB * c.kgroups * 256);
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(C, (int64_t)M * ldc * 2);
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(Cout, (int64_t)M * ldc * 2);
     const __amdgpu_buffer_rsrc_t rBias = make_rsrc(bias, BIAS ? ((int64_t)N * 2 + 15) / 16 * 16 : 0);
 
     int vb = blockIdx.x;
     int tm, tn, tm_next = 0, tn_next = 0;
-    tile_of(vb, tiles, tiles_m, tiles_n, tm, tn);
-    tile_rows(c, tm, tn, nGA, nGB, c.ld_row, c.sc_row);
+    tile_of(vb, tiles, tiles_m, tiles_n, group_m, tm, tn);
+    tile_rows<C>(c, tm, tn, nGA, nGB, c.ksteps, c.kgroups, 0, lane, c.lo_row, c.hi_off, c.sc_row);
     c.knext = 0;
     if (vb + P < tiles) {
-        tile_of(vb + P, tiles, tiles_m, tiles_n, tm_next, tn_next);
-        tile_rows(c, tm_next, tn_next, nGA, nGB, c.ld_next, c.sc_next);
+        tile_of(vb + P, tiles, tiles_m, tiles_n, group_m, tm_next, tn_next);
+        tile_rows<C>(c, tm_next, tn_next, nGA, nGB, c.ksteps, c.kgroups, 0, lane, c.lo_next, c.hi_next, c.sc_next);
         c.knext = c.ksteps;
     }
 
-    v16f acc[kMB][kMA];
+    v16f acc[C::kMB][C::kMA];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i)
+    for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
-    v2u_t bias_bits[BIAS ? kMB * 4 : 1];
-    if constexpr (BIAS) load_bias(rBias, tn, wn, lane, bias_bits);
+        for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
+    v2u_t bias_bits[BIAS ? C::kMB * 4 : 1];
+    if constexpr (BIAS) load_bias<C>(rBias, tn, wn, lane, bias_bits);
 
     // Prologue: steps 0-2 whole (a tile's first k-step does not issue step
     // 2's second part), all landed before the first k-step, so the first
     // tile's first two waits (which count past stores that this tile does not
     // have) wait for nothing.
-    dma_part<0, 0>(c, 0);
-    dma_part<0, 1>(c, 0);
-    dma_part<1, 0>(c, 1);
-    dma_part<1, 1>(c, 1);
-    dma_part<2, 0>(c, 2);
-    dma_part<2, 1>(c, 2);
+    dma_part<C, 0, 0, 0, 0>(c, 0);
+    dma_part<C, 0, 0, 1, 0>(c, 0);
+    dma_part<C, 1, 1, 0, 0>(c, 1);
+    dma_part<C, 1, 1, 1, 0>(c, 1);
+    dma_part<C, 2, 2, 0, 0>(c, 2);
+    dma_part<C, 2, 2, 1, 0>(c, 2);
 
-    const int lrow = lane & 31, lhi = lane >> 5;
-    Lds l;
-    l.frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 16 * lhi) * 16;
-    l.sc_off = ((lrow >> 4) * 256) + ((lrow & 15) + 16 * lhi) * 4;
-    l.a_atom0 = wm * kTA;
-    l.b_atom0 = kGA + wn * kTB;
-
-    Regs r;
+    const Lds l = lds_offsets<C>(wave, lane);
+    Regs<C> r;
     // vmcnt(0) as a builtin (not asm), so that the compiler's own wait
     // tracking also knows that nothing is outstanding past this point
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int t = 0; t < kMA; ++t)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sa[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.a_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-#pragma unroll
-    for (int t = 0; t < kMB; ++t)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            r.sb[t][hh] = *reinterpret_cast<const uint32_t *>(scale_buf() + (l.b_atom0 + 2 * t) * 256 + l.sc_off + hh * 128);
-#pragma unroll
-    for (int t = 0; t < kMA; ++t)
-        r.a0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.a_atom0 + 2 * t) * 1024 + l.frag_off);
-#pragma unroll
-    for (int t = 0; t < kMB; ++t)
-        r.b0[t] = *reinterpret_cast<const uint4 *>(stage_buf<0>() + (l.b_atom0 + 2 * t) * 1024 + l.frag_off);
+    first_operands<C, 0>(r, l);
 
     for (;;) {
-        // first k-group: its first two waits count past the previous tile's
+        // first period: its first two waits count past the previous tile's
         // stores and this tile's bias loads
-        k_step<0, true, kFreshOps>(c, 0, acc, r, l);
-        k_step<1, true, kFreshOps>(c, 1, acc, r, l);
-        k_step<2>(c, 2, acc, r, l);
-        k_step<3>(c, 3, acc, r, l);
-        // k-group h fetches steps 4h+2 .. 4h+6: all of this tile while
-        // 4h+6 < ksteps; the last group (or two) also fetch the next tile's
-        int h = 1;
-        for (; 4 * h + 6 < c.ksteps; ++h) {
-            const int k0 = 4 * h;
-            k_step<0, false, 0, true>(c, k0, acc, r, l);
-            k_step<1, false, 0, true>(c, k0 + 1, acc, r, l);
-            k_step<2, false, 0, true>(c, k0 + 2, acc, r, l);
-            k_step<3, false, 0, true>(c, k0 + 3, acc, r, l);
-        }
-        for (; h < c.kgroups; ++h) {
-            const int k0 = 4 * h;
-            k_step<0>(c, k0, acc, r, l);
-            k_step<1>(c, k0 + 1, acc, r, l);
-            k_step<2>(c, k0 + 2, acc, r, l);
-            k_step<3>(c, k0 + 3, acc, r, l);
-        }
+        period<C, true, kFreshOps, false, 0>(c, 0, acc, r, l);
+        // a period from k0 fetches steps k0+2 .. k0+kPeriod+2: all of this
+        // tile while k0 + kPeriod + 2 < ksteps; the last one (or two) also
+        // fetch the next tile's
+        int k0 = C::kPeriod;
+        if constexpr (C::Fmt::kInner)
+            for (; k0 < c.kstream && k0 + C::kPeriod + 2 < c.ksteps; k0 += C::kPeriod)
+                period<C, false, 0, true, 0>(c, k0, acc, r, l);
+        for (; k0 < c.kstream; k0 += C::kPeriod) period<C, false, 0, false, 0>(c, k0, acc, r, l);
         // r now holds the next tile's first operands and scales
-        if constexpr (BIAS) add_bias(acc, bias_bits);
-        store_tile_stream(c, acc, tm, tn, M, N, rC, ldc, wave, lane);
+        if constexpr (BIAS) add_bias<C>(acc, bias_bits);
+        store_tile_stream<C>(c, acc, tm, tn, M, N, rC, ldc, wave, lane);
         if constexpr (BIAS) {
             // The next tile's bias, after the stores in issue order as the
             // first waits assume.  (The compiler moves these loads past the
             // exit test below; its own wait before the first read of the
             // next tile then merges the paths with and without them and
-            // comes out at 20-21 instead of 28, draining a few of the oldest
+            // comes out below the count, draining a few of the oldest
             // stores: correct, slightly conservative.)
             asm volatile("" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            load_bias(rBias, tn_next, wn, lane, bias_bits);
+            load_bias<C>(rBias, tn_next, wn, lane, bias_bits);
             __builtin_amdgcn_sched_barrier(0);
         }
         vb += P;
@@ -827,20 +1069,24 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
         tm = tm_next;
         tn = tn_next;
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) {
-            c.ld_row[q] = c.ld_next[q];
-            c.sc_row[q] = c.sc_next[q];
+        for (int q = 0; q < C::kLoLoads; ++q) c.lo_row[q] = c.lo_next[q];
+        if constexpr (C::kHiLoads > 0) {
+#pragma unroll
+            for (int q = 0; q < C::kHiLoads; ++q) c.hi_off[q] = c.hi_next[q];
         }
+#pragma unroll
+        for (int q = 0; q < C::kScaleLoads; ++q) c.sc_row[q] = c.sc_next[q];
         c.knext = 0;
         if (vb + P < tiles) {
-            tile_of(vb + P, tiles, tiles_m, tiles_n, tm_next, tn_next);
-            tile_rows(c, tm_next, tn_next, nGA, nGB, c.ld_next, c.sc_next);
+            tile_of(vb + P, tiles, tiles_m, tiles_n, group_m, tm_next, tn_next);
+            tile_rows<C>(c, tm_next, tn_next, nGA, nGB, c.ksteps, c.kgroups, 0, lane, c.lo_next, c.hi_next,
+                         c.sc_next);
             c.knext = c.ksteps;
         }
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+        for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-            for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+            for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
     }
     // drain the stores and the trailing (out-of-range) DMAs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -854,49 +1100,54 @@ __global__ __launch_bounds__(kThreads) void gemm_a4w4_stream_kernel(int M, int N
 // scales (127): lane L of a 32-row operand tile supplies 32 bytes, row L%32,
 // elements [32*(L/32), 32*(L/32) + 32) of the 64-wide step = two 16-byte
 // slices of the atom, 256 bytes apart.  Same workgroup, wave tiles, XCD
-// order and LDS stages as the FP4 kernel; a k-step is 64 elements, its 32
-// atoms fill one 32 KB stage, step k+3 is in flight while step k computes.
+// order, LDS stages and epilogue as the FP4 main tiles; a k-step is 64
+// elements, its 32 atoms fill one 32 KB stage, step k+3 is in flight while
+// step k computes.
+using Fp8Cfg = Cfg<Fp4Fmt, MainShape>;
 constexpr int kFmtBf8 = 1;          // MFMA f8f6f4 format code for E5M2
 constexpr int kUnitScale = 127;     // E8M0 2^0
 
 template <int S>
-__device__ __forceinline__ void fp8_dma_step(const GemmCtx &c, int64_t k) {
+__device__ __forceinline__ void fp8_dma_step(const Ctx<Fp8Cfg, false> &c, int64_t k) {
+    using C = Fp8Cfg;
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-        const int a = kWaves * r + c.wave;
-        const uint32_t base = k < c.ksteps ? (uint32_t)c.ld_row[r] + (uint32_t)(k * 1024) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < kGA ? c.rA : c.rB, MX_LDS(stage_buf<S>() + a * 1024), 16,
-                                                 base + c.lane16, 0, 0, 0);
+    for (int r = 0; r < C::kLoLoads; ++r) {
+        const int a = C::kWaves * r + c.wave;
+        const uint32_t base = k < c.ksteps ? (uint32_t)c.lo_row[r] + (uint32_t)(k * 1024) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < C::kGA ? c.rA : c.rB, MX_LDS((stage_buf<C, S, 0>() + a * 1024)),
+                                                 16, base + c.lane16, 0, 0, 0);
     }
 }
 
 template <int S>
-__device__ __forceinline__ void fp8_step(const GemmCtx &c, int64_t k, v16f (&acc)[kMB][kMA], int frag_off,
-                                         int a_atom0, int b_atom0) {
+__device__ __forceinline__ void fp8_step(const Ctx<Fp8Cfg, false> &c, int64_t k,
+                                         v16f (&acc)[Fp8Cfg::kMB][Fp8Cfg::kMA], int frag_off, int a_atom0,
+                                         int b_atom0) {
+    using C = Fp8Cfg;
     // step k landed for every wave (only steps k+1, k+2 may still be in flight),
     // and every wave is done reading step k-1's stage
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * kLoads) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * C::kLoLoads) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *st = stage_buf<S>() + frag_off;
-    uint4 b[kMB][2], a[kMA][2];
+    const uint8_t *st = stage_buf<C, S, 0>() + frag_off;
+    uint4 b[C::kMB][2], a[C::kMA][2];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) {
+    for (int i = 0; i < C::kMB; ++i) {
         b[i][0] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024);
         b[i][1] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024 + 256);
     }
 #pragma unroll
-    for (int j = 0; j < kMA; ++j) {
+    for (int j = 0; j < C::kMA; ++j) {
         a[j][0] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024);
         a[j][1] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024 + 256);
     }
     fp8_dma_step<(S + 3) & 3>(c, k + 3);
 #pragma unroll
-    for (int i = 0; i < kMB; ++i) {
+    for (int i = 0; i < C::kMB; ++i) {
         const v8i bop = {(int)b[i][0].x, (int)b[i][0].y, (int)b[i][0].z, (int)b[i][0].w,
                          (int)b[i][1].x, (int)b[i][1].y, (int)b[i][1].z, (int)b[i][1].w};
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) {
+        for (int j = 0; j < C::kMA; ++j) {
             const v8i aop = {(int)a[j][0].x, (int)a[j][0].y, (int)a[j][0].z, (int)a[j][0].w,
                              (int)a[j][1].x, (int)a[j][1].y, (int)a[j][1].z, (int)a[j][1].w};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc[i][j], kFmtBf8, kFmtBf8, 0,
@@ -905,27 +1156,29 @@ __device__ __forceinline__ void fp8_step(const GemmCtx &c, int64_t k, v16f (&acc
     }
     // reads first (the MFMAs need them), each DMA after an MFMA
 #pragma unroll
-    for (int t = 0; t < kLoads; ++t) {
+    for (int t = 0; t < C::kLoLoads; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMA * kMB - kLoads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, C::kMA * C::kMB - C::kLoLoads, 0);
 }
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
-                                                            int tiles_n, const uint8_t *__restrict__ A,
-                                                            const float *__restrict__ a_scale_inv,
-                                                            const uint8_t *__restrict__ B,
-                                                            const float *__restrict__ b_scale_inv,
-                                                            void *__restrict__ C, int64_t ldc) {
+__global__ __launch_bounds__(Fp8Cfg::kThreads) void gemm_fp8_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
+                                                                    int tiles_n, int group_m,
+                                                                    const uint8_t *__restrict__ A,
+                                                                    const float *__restrict__ a_scale_inv,
+                                                                    const uint8_t *__restrict__ B,
+                                                                    const float *__restrict__ b_scale_inv,
+                                                                    void *__restrict__ Cout, int64_t ldc) {
+    using C = Fp8Cfg;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave % kWavesM, wn = wave / kWavesM;
+    const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
 
-    GemmCtx c;
+    Ctx<C, false> c;
     c.ksteps = K_pad / 64;
     c.kgroups = 0;
     c.wave = wave;
@@ -934,30 +1187,30 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(int64_t M, int64_t N
     const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);
     c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
     c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
-    const int64_t gA0 = (int64_t)tm * kGA, gB0 = (int64_t)tn * kGB;
+    const int64_t gA0 = (int64_t)tm * C::kGA, gB0 = (int64_t)tn * C::kGB;
 #pragma unroll
-    for (int r = 0; r < kLoads; ++r) {
-        const int a = kWaves * r + wave;
-        const bool isA = a < kGA;
-        int64_t g = isA ? gA0 + a : gB0 + (a - kGA);
+    for (int r = 0; r < C::kLoLoads; ++r) {
+        const int a = C::kWaves * r + wave;
+        const bool isA = a < C::kGA;
+        int64_t g = isA ? gA0 + a : gB0 + (a - C::kGA);
         const int64_t gmax = (isA ? nGA : nGB) - 1;
         g = g < gmax ? g : gmax;
-        c.ld_row[r] = (int)(g * c.ksteps * 1024);
+        c.lo_row[r] = (int)(g * c.ksteps * 1024);
     }
     const float scale = a_scale_inv[0] * b_scale_inv[0];
 
-    v16f acc[kMB][kMA];
+    v16f acc[C::kMB][C::kMA];
 #pragma unroll
-    for (int i = 0; i < kMB; ++i)
+    for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) acc[i][j] = v16f{};
+        for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
 
     fp8_dma_step<0>(c, 0);
     fp8_dma_step<1>(c, 1);
     fp8_dma_step<2>(c, 2);
     const int lrow = lane & 31, lhi = lane >> 5;
     const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 32 * lhi) * 16;
-    const int a_atom0 = wm * kTA, b_atom0 = kGA + wn * kTB;
+    const int a_atom0 = wm * C::kTA, b_atom0 = C::kGA + wn * C::kTB;
     for (int64_t k = 0; k < c.ksteps; k += 4) {
         fp8_step<0>(c, k, acc, frag_off, a_atom0, b_atom0);
         fp8_step<1>(c, k + 1, acc, frag_off, a_atom0, b_atom0);
@@ -966,21 +1219,114 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(int64_t M, int64_t N
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < kMB; ++i)
+    for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < kMA; ++j) acc[i][j] *= scale;
-    store_tile<OUT_BF16>(acc, tm, tn, M, N, C, ldc, wave, lane);
+        for (int j = 0; j < C::kMA; ++j) acc[i][j] *= scale;
+    store_tile<C, OUT_BF16>(acc, tm, tn, M, N, Cout, ldc, 0, wave, wave, lane);
 }
 
 // K == 0: C[i][j] = 0, or bias[j] (bf16 bits; exact in either output type).
 template <typename T>
-__global__ void fill_kernel(T *C, int64_t M, int64_t N, int64_t ldc, const uint16_t *bias) {
-    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= M * N) return;
-    const int64_t j = idx % N;
-    const uint16_t b = bias ? bias[j] : (uint16_t)0;
-    if constexpr (sizeof(T) == 2) C[(idx / N) * ldc + j] = b;
-    else C[(idx / N) * ldc + j] = __uint_as_float((uint32_t)b << 16);
+__global__ void fill_kernel(T *Cout, int64_t M, int64_t N, int64_t ldc, const uint16_t *bias) {
+    const int64_t n = M * N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = e % N;
+        const uint16_t b = bias ? bias[j] : (uint16_t)0;
+        if constexpr (sizeof(T) == 2) Cout[(e / N) * ldc + j] = b;
+        else Cout[(e / N) * ldc + j] = __uint_as_float((uint32_t)b << 16);
+    }
+}
+
+hipError_t launch_fill(int64_t M, int64_t N, const uint16_t *bias, mx_dtype out_dtype, void *Cout, int64_t ldc,
+                       hipStream_t stream) {
+    const int64_t blocks = cdiv(M * N, 256);
+    const dim3 grid((unsigned)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536));
+    if (out_dtype == MX_BF16)
+        hipLaunchKernelGGL(fill_kernel<uint16_t>, grid, dim3(256), 0, stream, reinterpret_cast<uint16_t *>(Cout), M,
+                           N, ldc, bias);
+    else
+        hipLaunchKernelGGL(fill_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<float *>(Cout), M, N, ldc,
+                           bias);
+    return hipGetLastError();
+}
+
+// Tile rows per band of the tile order.  At any time an XCD's 32 CUs work on
+// about 32 consecutive tiles of the order, which share A row blocks and B
+// column blocks through its L2.  Same-box timings on MI355X: 4-row bands
+// take 3-4% off the fc2 wgrad (12 x 48 tiles) and leave the 72-row shapes
+// unchanged within 1%, where 8-row bands stay.
+int band_rows(int tiles_m) { return tiles_m <= 16 ? 4 : 8; }
+
+// The kernel instance for the output type and bias (HAS_BIAS false: the
+// format's entry point takes no bias, so no bias instances exist).
+template <class C, bool HAS_BIAS>
+auto one_tile_kernel(bool bf, bool bias) {
+    if constexpr (HAS_BIAS)
+        return bf ? (bias ? gemm_kernel<C, true, true> : gemm_kernel<C, true, false>)
+                  : (bias ? gemm_kernel<C, false, true> : gemm_kernel<C, false, false>);
+    else
+        return bf ? gemm_kernel<C, true, false> : gemm_kernel<C, false, false>;
+}
+template <class C, bool HAS_BIAS>
+auto stream_kernel(bool bias) {
+    if constexpr (HAS_BIAS) return bias ? gemm_stream_kernel<C, true> : gemm_stream_kernel<C, false>;
+    else return gemm_stream_kernel<C, false>;
+}
+
+// Launch of one element format: main tiles (persistent form when it
+// applies), then the leftover tiles of a last round that would fill at most
+// 1 / tail_div of the CUs, as 128x128 tiles (the split form when they give
+// at most one per CU and K has at least 8 k-steps).
+template <class F, bool HAS_BIAS>
+hipError_t launch_format(int64_t M, int64_t N, int64_t K_pad, int tail_div, const uint8_t *A, const uint8_t *As,
+                         const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *Cout,
+                         int64_t ldc, hipStream_t stream) {
+    using CM = Cfg<F, MainShape>;
+    using CT = Cfg<F, TailShape>;
+    using CS = Cfg<F, SplitShape>;
+    const int tiles_m = (int)cdiv(M, 256), tiles_n = (int)cdiv(N, 256);
+    const int tiles = tiles_m * tiles_n;
+    const int group_m = band_rows(tiles_m);
+    const int cus = device_cu_count();
+    const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / tail_div) ? tiles % cus : 0;
+    const bool bf = out_dtype == MX_BF16;
+    const int64_t kgroups = cdiv(K_pad, 512);
+    // Several tiles per workgroup: one persistent workgroup per CU.  Same-box
+    // FP4 timings at 18432 rows: the stream form takes 7% off at 12-24
+    // k-steps per tile and 3.5% at 48, ties at 96, and with its wave-private
+    // epilogue takes 0.9% off at 144 (the fc2 wgrad).  Longer K is not
+    // measured, so it keeps one tile per workgroup.
+    bool streamed = false;
+    if constexpr (F::kStream) {
+        if (bf && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 144 * 128 && cus > 0 &&
+            tiles - tail > cus && (4 * kgroups) % F::kPeriod == 0) {
+            auto kernel = stream_kernel<CM, HAS_BIAS>(bias != nullptr);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)cus), dim3(CM::kThreads), 0, stream, (int)M, (int)N,
+                               (int)K_pad, tiles_m, tiles_n, group_m, tiles - tail, A, As, B, Bs, bias, Cout,
+                               (int)ldc);
+            streamed = true;
+        }
+    }
+    if (!streamed) {
+        auto kernel = one_tile_kernel<CM, HAS_BIAS>(bf, bias != nullptr);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles - tail)), dim3(CM::kThreads), 0, stream, M, N, K_pad,
+                           tiles_m, tiles_n, group_m, 0, A, As, B, Bs, bias, Cout, ldc);
+    }
+    if (!tail) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int first = tiles - tail;
+    // at most one 128x128 tile per CU (and K long enough to halve): the split form
+    if (4 * tail <= cus && K_pad >= 8 * 128) {
+        auto kernel = one_tile_kernel<CS, HAS_BIAS>(bf, bias != nullptr);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * tail)), dim3(CS::kThreads), 0, stream, M, N, K_pad, tiles_m,
+                           tiles_n, group_m, first, A, As, B, Bs, bias, Cout, ldc);
+    } else {
+        auto kernel = one_tile_kernel<CT, HAS_BIAS>(bf, bias != nullptr);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * tail)), dim3(CT::kThreads), 0, stream, M, N, K_pad, tiles_m,
+                           tiles_n, group_m, first, A, As, B, Bs, bias, Cout, ldc);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1002,76 +1348,48 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream) {
     const int64_t K_pad = padded(K);
-    if (K_pad == 0) {
-        const int64_t n = M * N;
-        dim3 grid((unsigned)cdiv(n, 256));
-        if (out_dtype == MX_BF16)
-            hipLaunchKernelGGL(fill_kernel<uint16_t>, grid, dim3(256), 0, stream, reinterpret_cast<uint16_t *>(C),
-                               M, N, ldc, bias);
-        else
-            hipLaunchKernelGGL(fill_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<float *>(C), M, N,
-                               ldc, bias);
-        return hipGetLastError();
-    }
+    if (K_pad == 0) return launch_fill(M, N, bias, out_dtype, C, ldc, stream);
     // buffer offsets are 32-bit: each operand blob (16-row groups of K_pad/2
     // bytes per row) must stay below 2 GiB
     if (cdiv(M, 16) * 16 * (K_pad / 2) >= (int64_t(1) << 31) || cdiv(N, 16) * 16 * (K_pad / 2) >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
-    const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
-    const int tiles = tiles_m * tiles_n;
-    // Whole rounds of 256x256 tiles here; a last round that would fill at most
-    // half of the CUs goes to the tail kernel as 128x128 tiles instead.
-    const int cus = device_cu_count();
-    const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
-    // Several tiles per workgroup: one persistent workgroup per CU.  Same-box
-    // timings at 18432 rows: the stream form takes 7% off at 12-24 k-steps per
-    // tile and 3.5% at 48, ties at 96, and with its wave-private epilogue
-    // takes 0.9% off at 144 (the fc2 wgrad; with the earlier epilogue it lost
-    // 1-2% there).  Longer K is not measured, so it keeps one tile per
-    // workgroup.
-    if (out_dtype == MX_BF16 && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad <= 144 * 128 && cus > 0 &&
-        tiles - tail > cus) {
-        auto kernel = bias ? gemm_a4w4_stream_kernel<true> : gemm_a4w4_stream_kernel<false>;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)cus), dim3(kThreads), 0, stream, (int)M, (int)N, (int)K_pad,
-                           tiles_m, tiles_n, tiles - tail, A, As, B, Bs, bias, C, (int)ldc);
-    } else {
-        auto kernel = out_dtype == MX_BF16 ? (bias ? gemm_a4w4_kernel<true, true> : gemm_a4w4_kernel<true, false>)
-                                           : (bias ? gemm_a4w4_kernel<false, true> : gemm_a4w4_kernel<false, false>);
-        hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles - tail)), dim3(kThreads), 0, stream, M, N, K_pad, tiles_m,
-                           tiles_n, A, As, B, Bs, bias, C, ldc);
-    }
-    if (tail) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_gemm_tail(M, N, K_pad, tiles_m, tiles_n, tiles - tail, tail, A, As, B, Bs, bias, out_dtype, C,
-                                ldc, stream);
-    }
-    return hipGetLastError();
+    // a last round that would fill at most half of the CUs goes to the tail
+    // tiles (same-box A/B: larger thresholds lose)
+    return launch_format<Fp4Fmt, true>(M, N, K_pad, 2, A, As, B, Bs, bias, out_dtype, C, ldc, stream);
+}
+
+hipError_t launch_gemm_fp6(int64_t M, int64_t N, int64_t K, int fmt_a, const uint8_t *A, const uint8_t *As,
+                           int fmt_b, const uint8_t *B, const uint8_t *Bs, mx_dtype out_dtype, void *C, int64_t ldc,
+                           hipStream_t stream) {
+    const int64_t K_pad = padded(K);
+    if (K_pad == 0) return launch_fill(M, N, nullptr, out_dtype, C, ldc, stream);
+    // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
+    if (cdiv(M, 16) * (K_pad / 128) * 1536 >= (int64_t(1) << 31) ||
+        cdiv(N, 16) * (K_pad / 128) * 1536 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    // a last round that would fill at most a quarter of the CUs goes to the
+    // tail tiles (same-box A/B on the fc2 shapes: 64 leftover tiles -7.5%; 96
+    // no gain; 128 +1%)
+    if (fmt_a == 2)
+        return fmt_b == 2 ? launch_format<Fp6Fmt<2, 2>, false>(M, N, K_pad, 4, A, As, B, Bs, nullptr, out_dtype, C, ldc, stream)
+                          : launch_format<Fp6Fmt<2, 3>, false>(M, N, K_pad, 4, A, As, B, Bs, nullptr, out_dtype, C, ldc, stream);
+    return fmt_b == 2 ? launch_format<Fp6Fmt<3, 2>, false>(M, N, K_pad, 4, A, As, B, Bs, nullptr, out_dtype, C, ldc, stream)
+                      : launch_format<Fp6Fmt<3, 3>, false>(M, N, K_pad, 4, A, As, B, Bs, nullptr, out_dtype, C, ldc, stream);
 }
 
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const float *a_scale_inv,
                            const uint8_t *B, const float *b_scale_inv, mx_dtype out_dtype, void *C, int64_t ldc,
                            hipStream_t stream) {
     const int64_t K_pad = padded(K);
-    if (K_pad == 0) {
-        const int64_t n = M * N;
-        dim3 grid((unsigned)cdiv(n, 256));
-        if (out_dtype == MX_BF16)
-            hipLaunchKernelGGL(fill_kernel<uint16_t>, grid, dim3(256), 0, stream, reinterpret_cast<uint16_t *>(C),
-                               M, N, ldc, nullptr);
-        else
-            hipLaunchKernelGGL(fill_kernel<float>, grid, dim3(256), 0, stream, reinterpret_cast<float *>(C), M, N,
-                               ldc, nullptr);
-        return hipGetLastError();
-    }
+    if (K_pad == 0) return launch_fill(M, N, nullptr, out_dtype, C, ldc, stream);
     // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
     if (cdiv(M, 16) * 16 * K_pad >= (int64_t(1) << 31) || cdiv(N, 16) * 16 * K_pad >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
-    const int tiles_m = (int)cdiv(M, kBM), tiles_n = (int)cdiv(N, kBN);
+    const int tiles_m = (int)cdiv(M, 256), tiles_n = (int)cdiv(N, 256);
     dim3 grid((unsigned)(tiles_m * tiles_n));
     auto kernel = out_dtype == MX_BF16 ? gemm_fp8_kernel<true> : gemm_fp8_kernel<false>;
-    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n, A, a_scale_inv, B,
-                       b_scale_inv, C, ldc);
+    hipLaunchKernelGGL(kernel, grid, dim3(Fp8Cfg::kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n,
+                       band_rows(tiles_m), A, a_scale_inv, B, b_scale_inv, C, ldc);
     return hipGetLastError();
 }
 

@@ -47,12 +47,6 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t *A, const 
                        const uint8_t *B, const uint8_t *Bs, const uint16_t *bias, mx_dtype out_dtype, void *C,
                        int64_t ldc, hipStream_t stream);
 int device_cu_count();   // compute units of the current device (cached), 0 if unknown
-hipError_t launch_gemm_fp6_tail(int64_t M, int64_t N, int64_t K_pad, int tiles_m, int tiles_n, int first, int count,
-                                int fmt_a, const uint8_t *A, const uint8_t *As, int fmt_b, const uint8_t *B,
-                                const uint8_t *Bs, mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream);
-hipError_t launch_gemm_tail(int64_t M, int64_t N, int64_t K_pad, int tiles_m, int tiles_n, int first, int count,
-                            const uint8_t *A, const uint8_t *As, const uint8_t *B, const uint8_t *Bs,
-                            const uint16_t *bias, mx_dtype out_dtype, void *C, int64_t ldc, hipStream_t stream);
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const float *a_scale_inv,
                            const uint8_t *B, const float *b_scale_inv, mx_dtype out_dtype, void *C, int64_t ldc,
                            hipStream_t stream);
