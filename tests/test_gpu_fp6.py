@@ -275,6 +275,20 @@ def test_fp6_gemm_tail_tiles(oracle_mod):
     run_gemm(oracle_mod, a, E3M2, b, E2M3, nsample=8192, seed=9, what="fp6 tail")
 
 
+@pytest.mark.parametrize("K", [1100, 2048])
+def test_fp6_gemm_split_tail_tiles(oracle_mod, K):
+    """As above with K of at least 8 k-steps: the 50 leftover tiles give at
+    most one 128x128 tile per CU, so each runs as two K groups of 4 waves
+    (K = 1100: 3 k-groups, the second group's last k-group past K) whose
+    partial tiles are added through LDS."""
+    _require_gpu()
+    M, N = 4597, 4349
+    log("fp6 gemm split tail tiles %dx%dx%d" % (M, N, K))
+    a = synth.random_bf16(193 + K, (M, K), std=1.0)
+    b = synth.random_bf16(194 + K, (N, K), std=0.05)
+    run_gemm(oracle_mod, a, E2M3, b, E3M2, nsample=8192, seed=10, what="fp6 split tail")
+
+
 def test_fp6_e3m2_group_truncation(oracle_mod):
     """The group structure of the accumulation model, through mx_gemm_fp6 on
     E3M2 x E3M2 operands: C[m][n] = 28*28 (k = k0) + 0.0625*0.0625 (k = k1)
