@@ -300,7 +300,9 @@ __device__ __forceinline__ typename C::Op read_op(const uint8_t *lo, const uint8
     }
 }
 
-template <class C, int SG>
+// ZERO: the tile's first MFMA on these accumulators, which start from 0 (an
+// inline constant, so the accumulators need no clearing between tiles).
+template <class C, int SG, bool ZERO = false>
 __device__ __forceinline__ void mfma_tile(v16f &acc, const typename C::Op &xb, const typename C::Op &xa, uint32_t sbv,
                                           uint32_t sav) {
     v8i bop, aop;
@@ -313,8 +315,8 @@ __device__ __forceinline__ void mfma_tile(v16f &acc, const typename C::Op &xb, c
     }
     // MFMA "A" operand = B rows (columns of C), "B" operand = A rows (rows of C);
     // OPSEL SG picks the k-step's byte of each scale dword
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc, C::Fmt::kFb, C::Fmt::kFa, SG, (int)sbv, SG,
-                                                          (int)sav);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, ZERO ? v16f{} : acc, C::Fmt::kFb, C::Fmt::kFa, SG,
+                                                          (int)sbv, SG, (int)sav);
 }
 
 // DMA instruction V of k-step k into stage S of K group G: V < kLoLoads
@@ -419,7 +421,8 @@ template <class C, int S, int SG, int H, int T, bool FRESH, bool INNER, int G, c
 __device__ __forceinline__ void slot(const X &c, typename X::kint k, v16f (&acc)[C::kMB][C::kMA], Regs<C> &r,
                                      const Lds &l) {
     constexpr int i = T / C::kMA, j = T % C::kMA;
-    if constexpr (H == 0) mfma_tile<C, SG>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
+    // a tile's first half-step in the stream kernel holds the first MFMA on every accumulator tile
+    if constexpr (H == 0) mfma_tile<C, SG, FRESH && SG == 0>(acc[i][j], r.b0[i], r.a0[j], r.sb[i][0], r.sa[j][0]);
     else mfma_tile<C, SG>(acc[i][j], r.b1[i], r.a1[j], r.sb[i][1], r.sa[j][1]);
 
     if constexpr (T < C::kMA + C::kMB) {
@@ -1010,11 +1013,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_stream_kernel(int M, int N, 
         c.knext = c.ksteps;
     }
 
+    // every tile's first k-step starts its accumulators from 0 (FRESH, mfma_tile)
     v16f acc[C::kMB][C::kMA];
-#pragma unroll
-    for (int i = 0; i < C::kMB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
     v2u_t bias_bits[BIAS ? C::kMB * 4 : 1];
     if constexpr (BIAS) load_bias<C>(rBias, tn, wn, lane, bias_bits);
 
@@ -1083,10 +1083,6 @@ __global__ __launch_bounds__(C::kThreads) void gemm_stream_kernel(int M, int N, 
                          c.sc_next);
             c.knext = c.ksteps;
         }
-#pragma unroll
-        for (int i = 0; i < C::kMB; ++i)
-#pragma unroll
-            for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
     }
     // drain the stores and the trailing (out-of-range) DMAs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
