@@ -742,82 +742,63 @@ __device__ __forceinline__ void store_tile(v16f (&acc)[C::kMB][C::kMA], int tm, 
     }
 }
 
-// Epilogue of the stream kernel (bf16 output).  Every wave issues exactly
-// epi_stores<C>() buffer stores per tile whatever the edges: a chunk past row
-// M or column N gets an out-of-range offset, which the buffer range check
-// drops (N % 8 == 0, so a chunk is all in or all out).  The fixed count is
-// what lets the next tile's first waits count past the stores instead of
-// draining them.  Before the stores, the epilogue issues the second part of
-// the next tile's step 2 (its first k-step would otherwise issue it after
-// them), into stage 2, free since the tile's last k-step.
-//  - Four stages (FP4): stages 0-2 already hold the next tile's first
-//    k-steps, so only stage 3 is free.  Each wave takes a 4 KB slot of it:
-//    in pass p (kMA passes) the wave stages its own 32 x 64 block (MFMA row
-//    tile p: tile rows 128 wm + 32p + [0, 32), columns 64 wn + [0, 64)), 128
-//    bytes per row with 16-byte chunk c of row r at c ^ (r % 8), and reads
-//    it back as whole 128-byte row segments, 8 rows per store instruction.
-//    After the first barrier (every wave done with stage 3's last k-step) no
-//    wave waits for another: a wave's LDS operations complete in order, so
-//    its next pass may overwrite the slot it has just read.
-//  - Three stages (FP6): the next tile's first steps occupy every stage, so
-//    each lane writes its 4 consecutive bf16 of each (i, j, q) straight from
-//    registers (8-byte stores; lanes L and L+32 cover 16 bytes of a row).
+// Epilogue of the stream kernel (bf16 output, four stages).  Stages 0-2
+// already hold the next tile's first k-steps, so only stage 3 is free.  Each
+// wave takes a 4 KB slot of it: in pass p (kMA passes) the wave stages its own
+// 32 x 64 block (MFMA row tile p: tile rows 128 wm + 32p + [0, 32), columns
+// 64 wn + [0, 64)), 128 bytes per row with 16-byte chunk c of row r at c ^
+// (r % 8), and reads it back as whole 128-byte row segments, 8 rows per store
+// instruction.  After the first barrier (every wave done with stage 3's last
+// k-step) no wave waits for another: a wave's LDS operations complete in
+// order, so its next pass may overwrite the slot it has just read.  Every
+// wave issues exactly epi_stores<C>() buffer stores per tile whatever the
+// edges: a chunk past row M or column N gets an out-of-range offset, which
+// the buffer range check drops (N % 8 == 0, so a chunk is all in or all out).
+// The fixed count is what lets the next tile's first waits count past the
+// stores instead of draining them.  Before the stores, the epilogue issues
+// the second part of the next tile's step 2 (its first k-step would
+// otherwise issue it after them), into stage 2, free since the tile's last
+// k-step.  (Three stages would leave no stage free at a tile boundary, which
+// is why the FP6 format has no persistent form.)
 template <class C>
 __host__ __device__ constexpr int epi_stores() {
-    return C::kStages == 4 ? C::kMA * 4 : C::kMA * C::kMB * 4;
+    return C::kMA * 4;
 }
 
 template <class C>
 __device__ __forceinline__ void store_tile_stream(const Ctx<C, true> &c, v16f (&acc)[C::kMB][C::kMA], int tm, int tn,
                                                   int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
                                                   int lane) {
+    static_assert(C::kStages == 4, "the stream epilogue stages C through stage 3");
+    constexpr int kSlotBytes = 32 * C::kWN * 2;   // 4 KB per wave
+    static_assert(kSlotBytes * C::kWaves == C::kStageBytes, "one slot per wave fills stage 3");
+    static_assert(C::kWN == 64, "8 lanes per 128-byte row");
     dma_part<C, 2, 2, 1, 0>(c, c.kstream + 2);
     const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
-    const int row_w = tm * C::kBM + C::kWM * wm;   // first C row of this wave's block
-    if constexpr (C::kStages == 4) {
-        constexpr int kSlotBytes = 32 * C::kWN * 2;   // 4 KB per wave
-        static_assert(kSlotBytes * C::kWaves == C::kStageBytes, "one slot per wave fills stage 3");
-        static_assert(C::kWN == 64, "8 lanes per 128-byte row");
-        uint8_t *slot_base = stage_buf<C, 3, 0>() + wave * kSlotBytes;
-        auto c_slot = [&](int r, int chunk) { return slot_base + r * (C::kWN * 2) + ((chunk ^ (r & 7)) * 16); };
-        const int col = tn * C::kBN + C::kWN * wn + 8 * (lane & 7);   // this lane's 8 columns on the way out
-        // every wave is done reading stage 3 (the tile's last k-step); a bare
-        // barrier: a __syncthreads() fence would also wait for the next tile's DMAs
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int row_w = tm * C::kBM + C::kWM * wm;                  // first C row of this wave's block
+    const int col = tn * C::kBN + C::kWN * wn + 8 * (lane & 7);   // this lane's 8 columns on the way out
+    uint8_t *slot_base = stage_buf<C, 3, 0>() + wave * kSlotBytes;
+    auto c_slot = [&](int r, int chunk) { return slot_base + r * (C::kWN * 2) + ((chunk ^ (r & 7)) * 16); };
+    // every wave is done reading stage 3 (the tile's last k-step); a bare
+    // barrier: a __syncthreads() fence would also wait for the next tile's DMAs
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int p = 0; p < C::kMA; ++p) {
+    for (int p = 0; p < C::kMA; ++p) {
 #pragma unroll
-            for (int i = 0; i < C::kMB; ++i)
+        for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<uint2 *>(c_slot(lrow, 4 * i + q) + 8 * lhi) =
-                        uint2{pack_bf16x2(acc[i][p][4 * q], acc[i][p][4 * q + 1]),
-                              pack_bf16x2(acc[i][p][4 * q + 2], acc[i][p][4 * q + 3])};
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2 *>(c_slot(lrow, 4 * i + q) + 8 * lhi) =
+                    uint2{pack_bf16x2(acc[i][p][4 * q], acc[i][p][4 * q + 1]),
+                          pack_bf16x2(acc[i][p][4 * q + 2], acc[i][p][4 * q + 3])};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int r = 8 * s + (lane >> 3);
-                const v4u_t v = *reinterpret_cast<const v4u_t *>(c_slot(r, lane & 7));
-                const int row = row_w + 32 * p + r;
-                const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
-            }
-        }
-    } else {
-        const int col0 = tn * C::kBN + C::kWN * wn + 4 * lhi;
-#pragma unroll
-        for (int j = 0; j < C::kMA; ++j) {
-            const int row = row_w + 32 * j + lrow;
-#pragma unroll
-            for (int i = 0; i < C::kMB; ++i)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = col0 + 32 * i + 8 * q;
-                    const v2u_t v = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                                     pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-                    const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b64(v, rC, off, 0, kCachePolicyNT);
-                }
+        for (int s = 0; s < 4; ++s) {
+            const int r = 8 * s + (lane >> 3);
+            const v4u_t v = *reinterpret_cast<const v4u_t *>(c_slot(r, lane & 7));
+            const int row = row_w + 32 * p + r;
+            const uint32_t off = row < M && col < N ? (uint32_t)(row * ldc + col) * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
         }
     }
 }
