@@ -61,8 +61,7 @@ constexpr int kTileRows = kWaveRows * kWaves;
 
 __device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
     if (amax16 >= 0x7F80u) return 0xFFu;            // Inf or NaN in the block
-    uint32_t e = amax16 >> 7;
-    return e > 2u ? e - 2u : 0u;
+    return __builtin_elementwise_sub_sat(amax16 >> 7, 2u);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -91,37 +90,56 @@ __device__ __forceinline__ uint32_t pair_of(uint32_t lo_word, uint32_t hi_word, 
     return __builtin_amdgcn_perm(hi_word, lo_word, half ? 0x07060302u : 0x05040100u);
 }
 
-// Stochastic E2M1 nibbles of eight bf16 that share the scale byte c: element
-// e is half e%2 of pair word p[e/2] (nibble e of the result); nb(e) holds
-// 255 minus its random byte in bits 16..23 and zeros elsewhere.  With u
-// clamped at code 7, (u << 2) + nb(e) carries into bit 24 iff the byte is
-// below u's bits 14..21, and bits 24..26 are then the code.  Branch-free:
-// the magnitude comes from the ldexp's |.| source modifier, the sign bits
-// (bit 7 of bytes 1 and 3 of each pair) are gathered by four byte permutes,
-// and a block holding Inf/NaN (c = 0xFF) is zeroed once for all eight.
-template <typename NB>
-__device__ __forceinline__ uint32_t pack8_sr(const uint32_t (&p)[4], uint32_t c, NB nb) {
+// Element h (0 = low half) of a bf16 pair word as an fp32 pattern: the bf16
+// in the high 16 bits, zeros below.
+__device__ __forceinline__ uint32_t elem_hi(uint32_t w, int h) {
+    return h ? (w & 0xFFFF0000u) : (w << 16);
+}
+
+// Sign masks of eight elements held as bf16 pairs: element 2i is the low half
+// of p_i, 2i+1 the high half.  Byte i of `even` is 0xFF iff element 2i is
+// negative (0x00 otherwise), byte i of `odd` likewise for element 2i+1.
+// V_PERM_B32 selectors 8..11 replicate bit 15 or 31 of either source across
+// a byte.
+__device__ __forceinline__ void sign_masks(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
+                                           uint32_t &even, uint32_t &odd) {
+    const uint32_t a = __builtin_amdgcn_perm(p1, p0, 0x0B090A08u);   // signs of elements 0 2 1 3
+    const uint32_t b = __builtin_amdgcn_perm(p3, p2, 0x0B090A08u);   // signs of elements 4 6 5 7
+    even = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    odd = __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Stochastic E2M1 nibbles of eight elements that share the scale byte c.
+// xw(e) is element e as an fp32 pattern (elem_hi); nb(e) holds 255 minus its
+// random byte in bits 16..23 and zeros elsewhere; even/odd are the sign
+// masks of sign_masks.  With u = |x| 2^(1-c) clamped at code 7, (u << 2) +
+// nb(e) carries into bit 24 iff the byte is below u's bits 14..21, so byte 3
+// of the sum is the code (0..7).  Four byte permutes gather the eight codes
+// (even elements to the low nibbles, odd ones to the high nibbles), the sign
+// masks supply bit 3 of each nibble, and a block holding Inf/NaN (c = 0xFF)
+// is zeroed once for all eight.
+template <typename XW, typename NB>
+__device__ __forceinline__ uint32_t pack8_sr(XW xw, uint32_t c, NB nb, uint32_t even, uint32_t odd) {
     const int sh = 1 - (int)c;
     constexpr uint32_t top = 7u << 22;
-    uint32_t codes = 0;
+    uint32_t s[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t xhi = (e & 1) ? (p[e >> 1] & 0xFFFF0000u) : (p[e >> 1] << 16);
-        uint32_t u = __float_as_uint(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(xhi)), sh));
+        uint32_t u = __float_as_uint(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(xw(e))), sh));
         u = u < top ? u : top;
-        codes |= (((u << 2) + nb(e)) >> 24) << (4 * e);
+        s[e] = (u << 2) + nb(e);
     }
-    const uint32_t a = __builtin_amdgcn_perm(p[1], p[0], 0x07030501u);   // p0.b1 p1.b1 p0.b3 p1.b3
-    const uint32_t b = __builtin_amdgcn_perm(p[3], p[2], 0x07030501u);   // p2.b1 p3.b1 p2.b3 p3.b3
-    const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);      // sign of element 2i at bit 8i+7
-    const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);       // sign of element 2i+1 at bit 8i+7
-    const uint32_t signs = ((even >> 4) & 0x08080808u) | (odd & 0x80808080u);
-    return c == 0xFFu ? 0u : (codes | signs);
+    // byte 3 of two sums into bytes 0, 1 (selector 0x0C0C0703) or 2, 3 (0x07030C0C)
+    const uint32_t lo = __builtin_amdgcn_perm(s[2], s[0], 0x0C0C0703u) | __builtin_amdgcn_perm(s[6], s[4], 0x07030C0Cu) |
+                        (even & 0x08080808u);
+    const uint32_t hi = __builtin_amdgcn_perm(s[3], s[1], 0x0C0C0703u) | __builtin_amdgcn_perm(s[7], s[5], 0x07030C0Cu) |
+                        (odd & 0x08080808u);
+    return c == 0xFFu ? 0u : (lo | (hi << 4));
 }
 
 // Byte k of w moved to bits 16..23, zeros elsewhere (selector 0x0C gives 0x00).
 __device__ __forceinline__ uint32_t byte_to_b2(uint32_t w, int k) {
-    return __builtin_amdgcn_perm(0u, w, 0x0C000C0Cu | ((uint32_t)k << 16));
+    return __builtin_amdgcn_perm(w, w, 0x0C000C0Cu | ((uint32_t)k << 16));
 }
 
 // ------------------------------------------------------------------ Philox
@@ -569,6 +587,35 @@ __global__ __launch_bounds__(256) __attribute__((
         tile_amax = m;
     }
 
+    // ---- block amax, column direction: per column u of the lane, 8 rows
+    // in-lane, then lanes q^1, q^2.  For MXFP4 without the Hadamard transform
+    // it is taken here, next to the row amax that shares its per-element
+    // magnitudes, so those die before the encode (taken after the row encode,
+    // they stayed live through it: 164 -> 202 VGPRs in the stochastic dual
+    // kernel).  MXFP6 draws its random bytes after this point and takes the
+    // column amax later.
+    uint32_t camax[8];
+    auto col_amax = [&]() {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                lo = umax(lo, d[t][w] & 0x7FFFu);
+                hi = umax(hi, (d[t][w] >> 16) & 0x7FFFu);
+            }
+            uint32_t pk = lo | (hi << 16);
+            uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 16, 64);
+            lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu); hi = umax(pk >> 16, o1 >> 16);
+            pk = lo | (hi << 16);
+            uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 32, 64);
+            camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
+            camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
+        }
+    };
+    constexpr bool kEarlyColAmax = DUAL && ELEM == 4 && !RHT;
+    if constexpr (kEarlyColAmax) col_amax();
+
     if constexpr (ELEM == 6) draw_sr();
 
     // ---- encode both directions into LDS, then write whole 16-byte slices.
@@ -668,12 +715,17 @@ __global__ __launch_bounds__(256) __attribute__((
         uint32_t packed = 0;
         if (ROW_SR) {
             const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
-            packed = pack8_sr(d[t], sc, [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); });
+            uint32_t even, odd;
+            sign_masks(d[t][0], d[t][1], d[t][2], d[t][3], even, odd);
+            packed = pack8_sr([&](int e) { return elem_hi(d[t][e >> 1], e & 1); }, sc,
+                              [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); }, even, odd);
         } else {
             packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
         }
         *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
         if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+        // one row at a time: interleaving rows only raises register pressure
+        if (ROW_SR) __builtin_amdgcn_sched_barrier(0);
     }
 
     if (DUAL && RHT && a.col.rht) {
@@ -707,24 +759,7 @@ __global__ __launch_bounds__(256) __attribute__((
             if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
         }
     } else if (DUAL) {
-        // column-wise: per column u of the lane, 8 rows in-lane, then lanes q^1, q^2
-        uint32_t camax[8];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                lo = umax(lo, d[t][w] & 0x7FFFu);
-                hi = umax(hi, (d[t][w] >> 16) & 0x7FFFu);
-            }
-            uint32_t pk = lo | (hi << 16);
-            uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 16, 64);
-            lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu); hi = umax(pk >> 16, o1 >> 16);
-            pk = lo | (hi << 16);
-            uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 32, 64);
-            camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
-            camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
-        }
+        if constexpr (!kEarlyColAmax) col_amax();
         if (ELEM == 6 && !COL_SR && !a.col.use_2d) {
             // the lane's 8 columns x 8 rows into the buffer as columns (after
             // every reader of the row pass is done), then thread th encodes
@@ -781,11 +816,18 @@ __global__ __launch_bounds__(256) __attribute__((
             const uint32_t sc = j < N ? scale_code(a.col.use_2d ? tile_amax : camax[u]) : 0u;
             uint32_t packed = 0;
             if (COL_SR) {
-                // element t of the column = row t: pairs (rows 2i, 2i+1) of this column's half
+                // element t of the column = row t, half h of word w; the sign
+                // masks of the column pair (2w, 2w+1) come from the same four
+                // permutes of rows (0,2), (4,6), (1,3), (5,7)
                 const int w = u >> 1, h = u & 1;
-                const uint32_t pr[4] = {pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
-                                        pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h)};
-                packed = pack8_sr(pr, sc, [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); });
+                const uint32_t s02 = __builtin_amdgcn_perm(d[2][w], d[0][w], 0x0B090A08u);
+                const uint32_t s46 = __builtin_amdgcn_perm(d[6][w], d[4][w], 0x0B090A08u);
+                const uint32_t s13 = __builtin_amdgcn_perm(d[3][w], d[1][w], 0x0B090A08u);
+                const uint32_t s57 = __builtin_amdgcn_perm(d[7][w], d[5][w], 0x0B090A08u);
+                const uint32_t half = h ? 0x07060302u : 0x05040100u;
+                packed = pack8_sr([&](int t) { return elem_hi(d[t][w], h); }, sc,
+                                  [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); },
+                                  __builtin_amdgcn_perm(s46, s02, half), __builtin_amdgcn_perm(s57, s13, half));
             } else {
                 const int w = u >> 1, h = u & 1;
                 packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
@@ -794,6 +836,7 @@ __global__ __launch_bounds__(256) __attribute__((
             // blob row = tile column 8c+u; this wave's 32 rows are bytes [16*wave, 16*wave+16)
             *reinterpret_cast<uint32_t *>(&s_data[1][(8 * c + u) * kLinePitch + 16 * wave + 4 * q]) = packed;
             if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+            if (COL_SR) __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
