@@ -331,3 +331,36 @@ def test_several_tiles_per_workgroup(oracle_mod, K):
     Cp = host(gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16, ldc=ldc)).view(np.uint16)
     assert np.array_equal(Cp[:M, :N], cb)
     assert (Cp[:, N:] == 0xFFFF).all()
+
+
+def test_output_over_2gib_sampled(oracle_mod):
+    """A bf16 output of 33000 x 32776 with ldc 32784 (2.16 GB, past the 2^31
+    bytes that 32-bit buffer offsets reach) and K 130 (padded to 256): the
+    launcher keeps such an output off the persistent kernel, and the one-tile
+    kernel's 64-bit addressed stores reach every row.  Sampled entries (the
+    last 256 rows weighted in, the four corners included) against the oracle;
+    the padding columns of the last rows stay untouched."""
+    _require_gpu()
+    M, N, K = 33000, 32776, 130
+    ldc = N + 8
+    assert M * ldc * 2 >= 2 ** 31
+    a = synth.random_bf16(301, (M, K), std=1.0)
+    b = synth.random_bf16(302, (N, K), std=0.5)
+    ad, lda = to_dev_bf16(a)
+    bd, ldb = to_dev_bf16(b)
+    qa, sa = quantize_rowwise(ad, M, K, lda, TILED)
+    qb, sb = quantize_rowwise(bd, N, K, ldb, TILED)
+    log("output over 2 GiB %dx%dx%d ldc %d" % (M, N, K, ldc))
+    C = gemm(qa, sa, qb, sb, M, N, K, mx.MX_BF16, ldc=ldc)
+    rng = np.random.default_rng(7)
+    ii = np.concatenate([rng.integers(0, M, 4096), rng.integers(M - 256, M, 1024), [0, M - 1, M - 1, 0]])
+    jj = np.concatenate([rng.integers(0, N, 4096), rng.integers(0, N, 1024), [0, N - 1, 0, N - 1]])
+    got = C[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()].cpu().numpy().view(np.uint16)
+    assert (C[M - 64:, N:].cpu().numpy() == -1).all()
+    del C
+    oqa, osa = oracle_mod.quantize(a, 0)
+    oqb, osb = oracle_mod.quantize(b, 0)
+    ref = oracle_mod.gemm_entries(oqa, osa, oqb, osb, M, N, K, ii, jj)
+    tau = tau_bound(oracle_mod, oqa, osa, oqb, osb, M, N, K, ii, jj)
+    exact, _ = check_gemm_bf16(got, ref, tau, oracle_mod, "over-2GiB")
+    log("over-2GiB: %d/%d bf16 exact" % (exact, ii.size))
