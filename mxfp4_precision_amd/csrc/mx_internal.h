@@ -34,7 +34,13 @@ struct QuantArgs {
     DirOpts row, col;
     uint32_t sr_pairs;          // 1: N and both index bases are multiples of 16
     uint8_t *q_row, *s_row, *q_col, *s_col;
+    int64_t row_tile0;          // first 128-row tile of this launch (set by the launchers)
 };
+
+// Grid dimension y of one launch holds at most 65536 workgroups on gfx950
+// (hipDeviceAttributeMaxGridDimY); the quantize launchers cover taller inputs
+// with several launches of kMaxRowTiles row tiles each.
+constexpr int64_t kMaxRowTiles = 65535;
 
 // Kernel launchers (quantize.hip, gemm.hip, convert.hip, dequantize.hip).  They assume validated arguments.
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream);

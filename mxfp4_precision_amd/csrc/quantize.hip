@@ -408,12 +408,13 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 
 // Dual stochastic rounding holds both directions' random bytes while the
 // staging loads are in flight.  Asking for at least two waves per SIMD (up to
-// 256 VGPRs) lets the compiler schedule it in 164 VGPRs without spills, so
-// three waves still fit a SIMD; asking for three (168 VGPRs) made it spill.
-// Same-box timings of the 18432x3072 dY quantize: 0.0637 ms, against 0.0688
-// ms with the spilling three-wave request and 0.0711 ms for the earlier form
-// that drew the bytes after the loads had landed.  (With the Hadamard
-// transform as well it would spill, so that form keeps its registers.)
+// 256 VGPRs) lets the compiler schedule the MXFP4 kernel in 158 VGPRs without
+// spills, so three waves still fit a SIMD; asking for three (168 VGPRs) made
+// it spill.  Same-box timings of the 18432x3072 dY quantize (before the
+// permute gather of pack8_sr): 0.0637 ms, against 0.0688 ms with the spilling
+// three-wave request and 0.0711 ms for the earlier form that drew the bytes
+// after the loads had landed.  (With the Hadamard transform as well it would
+// spill, so that form keeps its registers.)
 // MXFP6 draws its bytes after the loads have landed; with both directions
 // stochastic it fits three waves (168 VGPRs) without spills, with one
 // direction stochastic (the mixed-options forms) two.
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((
     const int wave = threadIdx.x >> 6;
     const int c = lane & 15;
     const int q = lane >> 4;
-    const int64_t row0 = (int64_t)blockIdx.y * kTileRows + wave * kWaveRows;
+    const int64_t row0 = ((int64_t)blockIdx.y + a.row_tile0) * kTileRows + wave * kWaveRows;
     const int64_t col0 = (int64_t)blockIdx.x * kTileCols;
     const int64_t M = a.M, N = a.N;
 
@@ -941,6 +942,21 @@ __global__ __launch_bounds__(256) __attribute__((
 
 }  // namespace
 
+// One launch per kMaxRowTiles row tiles (grid y is limited; each launch
+// passes its first row tile in the arguments), the same kernel for all.
+template <typename L>
+hipError_t launch_row_chunks(const QuantArgs &a, L launch) {
+    const int64_t row_tiles = cdiv(a.M, kTileRows);
+    for (int64_t t0 = 0; t0 < row_tiles; t0 += kMaxRowTiles) {
+        QuantArgs b = a;
+        b.row_tile0 = t0;
+        const int64_t n = row_tiles - t0 < kMaxRowTiles ? row_tiles - t0 : kMaxRowTiles;
+        const hipError_t e = launch(b, dim3((unsigned)cdiv(a.N, kTileCols), (unsigned)n));
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int ELEM, int LAYOUT, bool DUAL, bool RHT>
 hipError_t launch_sr(const QuantArgs &a, dim3 grid, hipStream_t stream) {
     const bool rs = a.row.use_sr != 0, cs = DUAL && a.col.use_sr != 0;
@@ -958,12 +974,13 @@ hipError_t launch_rht(const QuantArgs &a, dim3 grid, hipStream_t stream) {
 }
 
 hipError_t launch_quantize(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
-    dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
-    if (layout == MX_LAYOUT_CANONICAL)
-        return dual ? launch_rht<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
-                    : launch_rht<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
-    return dual ? launch_rht<MX_LAYOUT_TILED, true>(a, grid, stream)
-                : launch_rht<MX_LAYOUT_TILED, false>(a, grid, stream);
+    return launch_row_chunks(a, [&](const QuantArgs &b, dim3 grid) {
+        if (layout == MX_LAYOUT_CANONICAL)
+            return dual ? launch_rht<MX_LAYOUT_CANONICAL, true>(b, grid, stream)
+                        : launch_rht<MX_LAYOUT_CANONICAL, false>(b, grid, stream);
+        return dual ? launch_rht<MX_LAYOUT_TILED, true>(b, grid, stream)
+                    : launch_rht<MX_LAYOUT_TILED, false>(b, grid, stream);
+    });
 }
 
 template <int LAYOUT, bool DUAL>
@@ -977,20 +994,23 @@ hipError_t launch_mul(const QuantArgs &a, dim3 grid, hipStream_t stream) {
 }
 
 hipError_t launch_quantize_mul(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
-    dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
-    if (layout == MX_LAYOUT_CANONICAL)
-        return dual ? launch_mul<MX_LAYOUT_CANONICAL, true>(a, grid, stream)
-                    : launch_mul<MX_LAYOUT_CANONICAL, false>(a, grid, stream);
-    return dual ? launch_mul<MX_LAYOUT_TILED, true>(a, grid, stream) : launch_mul<MX_LAYOUT_TILED, false>(a, grid, stream);
+    return launch_row_chunks(a, [&](const QuantArgs &b, dim3 grid) {
+        if (layout == MX_LAYOUT_CANONICAL)
+            return dual ? launch_mul<MX_LAYOUT_CANONICAL, true>(b, grid, stream)
+                        : launch_mul<MX_LAYOUT_CANONICAL, false>(b, grid, stream);
+        return dual ? launch_mul<MX_LAYOUT_TILED, true>(b, grid, stream)
+                    : launch_mul<MX_LAYOUT_TILED, false>(b, grid, stream);
+    });
 }
 
 hipError_t launch_quantize_fp6(const QuantArgs &a, bool dual, mx_layout layout, hipStream_t stream) {
-    dim3 grid((unsigned)cdiv(a.N, kTileCols), (unsigned)cdiv(a.M, kTileRows));
-    if (layout == MX_LAYOUT_CANONICAL)
-        return dual ? launch_sr<6, MX_LAYOUT_CANONICAL, true, false>(a, grid, stream)
-                    : launch_sr<6, MX_LAYOUT_CANONICAL, false, false>(a, grid, stream);
-    return dual ? launch_sr<6, MX_LAYOUT_TILED, true, false>(a, grid, stream)
-                : launch_sr<6, MX_LAYOUT_TILED, false, false>(a, grid, stream);
+    return launch_row_chunks(a, [&](const QuantArgs &b, dim3 grid) {
+        if (layout == MX_LAYOUT_CANONICAL)
+            return dual ? launch_sr<6, MX_LAYOUT_CANONICAL, true, false>(b, grid, stream)
+                        : launch_sr<6, MX_LAYOUT_CANONICAL, false, false>(b, grid, stream);
+        return dual ? launch_sr<6, MX_LAYOUT_TILED, true, false>(b, grid, stream)
+                    : launch_sr<6, MX_LAYOUT_TILED, false, false>(b, grid, stream);
+    });
 }
 
 }  // namespace mx

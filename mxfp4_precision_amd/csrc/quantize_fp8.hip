@@ -115,15 +115,15 @@ template <int LAYOUT>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t N,
                                                            int64_t ldx, const float *__restrict__ info_in,
                                                            float *info_out, uint8_t *__restrict__ q_row,
-                                                           uint8_t *__restrict__ q_col) {
+                                                           uint8_t *__restrict__ q_col, int64_t tile0) {
     __shared__ __attribute__((aligned(16))) uint8_t s_t[kTile][kTile + 16];   // transposed codes
     const float amax = __uint_as_float(reinterpret_cast<const uint32_t *>(info_in)[0]);
     const bool finite = __float_as_uint(amax) < 0x7F800000u;
     const float scale = (finite && amax > 0.0f) ? __fdiv_rn(57344.0f, amax) : 1.0f;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) info_out[1] = __frcp_rn(scale);
+    if (tile0 == 0 && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) info_out[1] = __frcp_rn(scale);
 
     const int64_t N_pad = padded(N), M_pad = padded(M);
-    const int64_t r0 = (int64_t)blockIdx.y * kTile, c0 = (int64_t)blockIdx.x * kTile;
+    const int64_t r0 = ((int64_t)blockIdx.y + tile0) * kTile, c0 = (int64_t)blockIdx.x * kTile;
     const int tr = threadIdx.x >> 2, tc = (threadIdx.x & 3) * 16;   // 64 rows x 4 chunks of 16
     const int64_t i = r0 + tr, j0 = c0 + tc;
     uint32_t codes[4] = {0u, 0u, 0u, 0u};                             // 16 bytes, element e in byte e
@@ -179,15 +179,22 @@ hipError_t launch_quantize_fp8(const uint16_t *x, int64_t M, int64_t N, int64_t 
     const int64_t chunks = M * cdiv(N, 8);
     const unsigned ablocks = (unsigned)(cdiv(chunks, 256) < 1024 ? cdiv(chunks, 256) : 1024);
     hipLaunchKernelGGL(fp8_amax_kernel, dim3(ablocks), dim3(256), 0, stream, x, M, N, ldx, info);
-    // the grid covers both padded axes: pad columns of the row blob, pad rows of the column blob
-    dim3 grid((unsigned)(padded(N) / kTile), (unsigned)(padded(M) / kTile));
-    if (layout == MX_LAYOUT_TILED)
-        hipLaunchKernelGGL(fp8_quantize_kernel<MX_LAYOUT_TILED>, grid, dim3(256), 0, stream, x, M, N, ldx, info,
-                           info, q_row, q_col);
-    else
-        hipLaunchKernelGGL(fp8_quantize_kernel<MX_LAYOUT_CANONICAL>, grid, dim3(256), 0, stream, x, M, N, ldx,
-                           info, info, q_row, q_col);
-    return hipGetLastError();
+    // the grids cover both padded axes: pad columns of the row blob, pad rows
+    // of the column blob; one launch per kMaxRowTiles row tiles (grid y is limited)
+    const int64_t row_tiles = padded(M) / kTile;
+    for (int64_t t0 = 0; t0 < row_tiles; t0 += kMaxRowTiles) {
+        const int64_t n = row_tiles - t0 < kMaxRowTiles ? row_tiles - t0 : kMaxRowTiles;
+        dim3 grid((unsigned)(padded(N) / kTile), (unsigned)n);
+        if (layout == MX_LAYOUT_TILED)
+            hipLaunchKernelGGL(fp8_quantize_kernel<MX_LAYOUT_TILED>, grid, dim3(256), 0, stream, x, M, N, ldx, info,
+                               info, q_row, q_col, t0);
+        else
+            hipLaunchKernelGGL(fp8_quantize_kernel<MX_LAYOUT_CANONICAL>, grid, dim3(256), 0, stream, x, M, N, ldx,
+                               info, info, q_row, q_col, t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace mx

@@ -169,3 +169,47 @@ def test_fp8_hybrid_backward_fc2_sampled(oracle_mod):
     log("fp8 hybrid wgrad")
     run_gemm(oracle_mod, np.ascontiguousarray(dY.T), np.ascontiguousarray(X.T), nsample=4096, seed=2,
              what="fp8 wgrad")
+
+
+def test_fp8_quantize_tall_input_spans_launches(oracle_mod):
+    """4,194,504 rows x 48 columns, canonical layout: 65,540 row tiles of 64
+    rows, past the 65,536 workgroups grid dimension y holds, so the launcher
+    covers them with two launches (the second from tile 65,535).  The input
+    is zero except three windows of seeded values (the first 128 rows, the
+    128 rows around the second launch's first row 4,194,240, and the last 72
+    rows); the tensorwise scale is then the windows' own, so the rows of the
+    windows stacked into one tensor are the oracle's reference for both
+    blobs, amax and scale_inv included; the column blob's pad columns past M
+    are zero."""
+    _require_gpu()
+    M, N, ldx = 65536 * 64 + 200, 48, 48
+    wins = [(0, 128), (65535 * 64 - 64, 65535 * 64 + 64), (M - 72, M)]
+    xd = torch.zeros((M, ldx), dtype=torch.int16, device="cuda")
+    parts = []
+    for k, (r0, r1) in enumerate(wins):
+        w = synth.random_bf16(930 + k, (r1 - r0, N), std=3.0)
+        xd[r0:r1] = torch.from_numpy(w.view(np.int16)).cuda()
+        parts.append(w)
+    stacked = np.concatenate(parts)
+    M_pad = -(-M // 128) * 128
+    qr = torch.full((mx.mx_fp8_blob_bytes(M, N, CANON),), 0x5A, dtype=torch.uint8, device="cuda")
+    qc = torch.full((mx.mx_fp8_blob_bytes(N, M, CANON),), 0x5A, dtype=torch.uint8, device="cuda")
+    info = torch.full((4,), -1.0, dtype=torch.float32, device="cuda")
+    log("fp8 tall input %dx%d: %d row tiles of 64" % (M, N, M_pad // 64))
+    mx.mx_quantize_fp8_tw(xd, M, N, ldx, CANON, qr, qc, info)
+    torch.cuda.synchronize()
+    del xd
+    want_r, sinv, amax = oracle_mod.quantize_fp8_tw(stacked, 0)
+    want_c, _, _ = oracle_mod.quantize_fp8_tw(stacked, 1)
+    inf = host(info)
+    assert inf[0] == np.float32(amax) and inf[1] == np.float32(sinv), (inf[:2], amax, sinv)
+    qr, qc = qr.view(M, -1), qc.view(N, M_pad)
+    o = 0
+    for r0, r1 in wins:
+        h = r1 - r0
+        assert np.array_equal(host(qr[r0:r1]), want_r[o:o + h]), ("row", r0)
+        assert np.array_equal(host(qc[:, r0:r1]), want_c[:, o:o + h]), ("col", r0)
+        o += h
+    for r in (128, 2_000_000, 65535 * 64 + 64, M - 73):
+        assert not host(qr[r]).any(), r
+    assert not host(qc[:, M:]).any() and not host(qc[:, 128:500_000]).any()

@@ -474,3 +474,47 @@ def test_multiply_prologue_sr_2d_specials(oracle_mod, layout):
               dict(use_sr=True, seed=12, tensor_id=5))
     w2 = mx.quant_opts(use_2d_block=True)
     check_mul(oracle_mod, x, g, layout, w2, w2, dict(use_2d=True), dict(use_2d=True))
+
+
+def test_tall_input_spans_launches(oracle_mod):
+    """8,388,928 rows (65,539 tiles of 128 rows; grid dimension y holds at
+    most 65,536 workgroups, so the launcher covers them with two launches,
+    the second starting at tile 65,535) x 48 columns, dual, both directions
+    with stochastic rounding (the paired Philox path), canonical layout.  The
+    input is zero except three windows of seeded values: the first 256 rows,
+    the 256 rows around the second launch's first row (8,388,480), and the
+    last 192 rows (ragged, padded to 128).  Every window's row-blob rows and
+    column-blob bytes and scales equal the oracle's dual quantize of the
+    window alone with index_base moved to the window's first element; zero
+    rows elsewhere encode to zero bytes."""
+    _require_gpu()
+    M, N, ldx = 65538 * 128 + 64, 48, 48
+    base = 1 << 20
+    wins = [(0, 256), (65535 * 128 - 128, 65535 * 128 + 128), (65538 * 128 - 128, M)]
+    xd = torch.zeros((M, ldx), dtype=torch.int16, device="cuda")
+    wx = []
+    for k, (r0, r1) in enumerate(wins):
+        w = synth.random_bf16(900 + k, (r1 - r0, N), std=1.0)
+        xd[r0:r1] = torch.from_numpy(w.view(np.int16)).cuda()
+        wx.append(w)
+    o = mx.quant_opts(use_sr=True, seed=(3 << 33) + 17, tensor_id=6, index_base=base)
+    log("tall input %dx%d: %d row tiles" % (M, N, -(-M // 128)))
+    qr, sr, qc, sc = quantize_dual(xd, M, N, ldx, CANON, o, o)
+    torch.cuda.synchronize()
+    del xd
+    M_pad = -(-M // 128) * 128
+    qr, sr = qr.view(M, -1), sr.view(M, -1)
+    qc, sc = qc.view(N, M_pad // 2), sc.view(N, M_pad // 32)
+    for (r0, r1), w in zip(wins, wx):
+        kw = dict(use_sr=True, seed=(3 << 33) + 17, tensor_id=6, index_base=base + r0 * N)
+        qrw, srw = oracle_mod.quantize(w, 0, **kw)
+        qcw, scw = oracle_mod.quantize(w, 1, **kw)
+        what = "rows [%d, %d)" % (r0, r1)
+        assert_equal_bytes(host(qr[r0:r1]), qrw, "tall row data " + what)
+        assert_equal_bytes(host(sr[r0:r1]), srw, "tall row scale " + what)
+        assert_equal_bytes(host(qc[:, r0 // 2: r0 // 2 + qcw.shape[1]]), qcw, "tall col data " + what)
+        assert_equal_bytes(host(sc[:, r0 // 32: r0 // 32 + scw.shape[1]]), scw, "tall col scale " + what)
+    # zero rows between the windows: zero codes and scale bytes everywhere
+    for r in (256, 4_000_000, 65535 * 128 + 128, 65538 * 128 - 129):
+        assert not host(qr[r]).any() and not host(sr[r]).any(), r
+    assert not host(qc[:, 128:1_000_000]).any() and not host(sc[:, 8:60_000]).any()
