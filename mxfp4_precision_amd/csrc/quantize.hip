@@ -64,6 +64,15 @@ __device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
     return __builtin_elementwise_sub_sat(amax16 >> 7, 2u);
 }
 
+// Scale byte of a block row that may lie past the tensor: amax16 counts only
+// if `real` (rows or columns past the tensor are the tiled layout's zero
+// padding and get scale 0); nonfinite is set for an Inf/NaN block.
+__device__ __forceinline__ uint32_t scale_code_if(bool real, uint32_t amax16, bool &nonfinite) {
+    const uint32_t am = real ? amax16 : 0u;
+    nonfinite = am >= 0x7F80u;
+    return nonfinite ? 0xFFu : __builtin_elementwise_sub_sat(am >> 7, 2u);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
@@ -112,14 +121,15 @@ __device__ __forceinline__ void sign_masks(uint32_t p0, uint32_t p1, uint32_t p2
 // Stochastic E2M1 nibbles of eight elements that share the scale byte c.
 // xw(e) is element e as an fp32 pattern (elem_hi); nb(e) holds 255 minus its
 // random byte in bits 16..23 and zeros elsewhere; even/odd are the sign
-// masks of sign_masks.  With u = |x| 2^(1-c) clamped at code 7, (u << 2) +
+// masks of sign_masks; nonfinite: the block holds Inf/NaN (c = 0xFF).  With
+// u = |x| 2^(1-c) clamped at code 7, (u << 2) +
 // nb(e) carries into bit 24 iff the byte is below u's bits 14..21, so byte 3
 // of the sum is the code (0..7).  Four byte permutes gather the eight codes
 // (even elements to the low nibbles, odd ones to the high nibbles), the sign
 // masks supply bit 3 of each nibble, and a block holding Inf/NaN (c = 0xFF)
 // is zeroed once for all eight.
 template <typename XW, typename NB>
-__device__ __forceinline__ uint32_t pack8_sr(XW xw, uint32_t c, NB nb, uint32_t even, uint32_t odd) {
+__device__ __forceinline__ uint32_t pack8_sr(XW xw, uint32_t c, NB nb, uint32_t even, uint32_t odd, bool nonfinite) {
     const int sh = 1 - (int)c;
     constexpr uint32_t top = 7u << 22;
     uint32_t s[8];
@@ -134,7 +144,7 @@ __device__ __forceinline__ uint32_t pack8_sr(XW xw, uint32_t c, NB nb, uint32_t 
                         (even & 0x08080808u);
     const uint32_t hi = __builtin_amdgcn_perm(s[3], s[1], 0x0C0C0703u) | __builtin_amdgcn_perm(s[7], s[5], 0x07030C0Cu) |
                         (odd & 0x08080808u);
-    return c == 0xFFu ? 0u : (lo | (hi << 4));
+    return nonfinite ? 0u : (lo | (hi << 4));
 }
 
 // Byte k of w moved to bits 16..23, zeros elsewhere (selector 0x0C gives 0x00).
@@ -439,6 +449,10 @@ __global__ __launch_bounds__(256) __attribute__((
     const int64_t row0 = ((int64_t)blockIdx.y + a.row_tile0) * kTileRows + wave * kWaveRows;
     const int64_t col0 = (int64_t)blockIdx.x * kTileCols;
     const int64_t M = a.M, N = a.N;
+    // real rows among the lane's 8 (8q..8q+7) and real columns among its 8 (8c..8c+7)
+    const int64_t rl = M - (row0 + 8 * q), cl = N - (col0 + 8 * c);
+    const int rows_here = rl < 0 ? 0 : (rl > 8 ? 8 : (int)rl);
+    const int cols_here = cl < 0 ? 0 : (cl > 8 ? 8 : (int)cl);
 
     // ---- staging read: d[t][w] = bf16 pair (cols 2w, 2w+1 of the lane's 8) of row 8q+t.
     // Non-temporal loads: the input is read once, so it should not displace
@@ -710,16 +724,16 @@ __global__ __launch_bounds__(256) __attribute__((
     } else
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int64_t i = row0 + 8 * q + t;
         // rows past M exist only as zero padding of the tiled layout: scale 0 there
-        const uint32_t sc = i < M ? scale_code(a.row.use_2d ? tile_amax : ramax[t]) : 0u;
+        bool nonfinite;
+        const uint32_t sc = scale_code_if(t < rows_here, a.row.use_2d ? tile_amax : ramax[t], nonfinite);
         uint32_t packed = 0;
         if (ROW_SR) {
             const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
             uint32_t even, odd;
             sign_masks(d[t][0], d[t][1], d[t][2], d[t][3], even, odd);
             packed = pack8_sr([&](int e) { return elem_hi(d[t][e >> 1], e & 1); }, sc,
-                              [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); }, even, odd);
+                              [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); }, even, odd, nonfinite);
         } else {
             packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
         }
@@ -813,8 +827,8 @@ __global__ __launch_bounds__(256) __attribute__((
         } else
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t j = j0 + u;
-            const uint32_t sc = j < N ? scale_code(a.col.use_2d ? tile_amax : camax[u]) : 0u;
+            bool nonfinite;
+            const uint32_t sc = scale_code_if(u < cols_here, a.col.use_2d ? tile_amax : camax[u], nonfinite);
             uint32_t packed = 0;
             if (COL_SR) {
                 // element t of the column = row t, half h of word w; the sign
@@ -828,7 +842,8 @@ __global__ __launch_bounds__(256) __attribute__((
                 const uint32_t half = h ? 0x07060302u : 0x05040100u;
                 packed = pack8_sr([&](int t) { return elem_hi(d[t][w], h); }, sc,
                                   [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); },
-                                  __builtin_amdgcn_perm(s46, s02, half), __builtin_amdgcn_perm(s57, s13, half));
+                                  __builtin_amdgcn_perm(s46, s02, half), __builtin_amdgcn_perm(s57, s13, half),
+                                  nonfinite);
             } else {
                 const int w = u >> 1, h = u & 1;
                 packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
