@@ -337,10 +337,19 @@ __device__ __forceinline__ void dma_op(const X &c, typename X::kint k) {
         constexpr bool isA = C::kWaves * (V + 1) <= C::kGA;
         static_assert(isA || C::kWaves * V >= C::kGA, "A/B split falls on a DMA instruction");
         const int a = C::kWaves * V + c.wave;
-        uint32_t base;
+        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rA : c.rB;
         if constexpr (INNER) {
-            base = (uint32_t)c.lo_row[V] + (uint32_t)k * kStep;
-        } else if constexpr (X::kStream) {
+            // in range by construction: the wave-uniform part as the scalar
+            // offset, the lane's constant part as the vector offset, so the
+            // DMA needs no vector instruction of its own
+            const uint32_t sbase = (uint32_t)c.lo_row[V] + (uint32_t)k * kStep;
+            const uint32_t voff = (uint32_t)c.lane16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((stage_buf<C, S, G>() + a * 1024)), 16, voff, sbase,
+                                                     0, 0);
+            return;
+        }
+        uint32_t base;
+        if constexpr (X::kStream) {
             // steps of the tile, then the next tile's first steps
             const bool cur = k < c.kstream;
             const kint kk = cur ? k : k - c.kstream;
@@ -351,7 +360,6 @@ __device__ __forceinline__ void dma_op(const X &c, typename X::kint k) {
         }
         // (plain-typed locals: a builtin call on template-dependent operands
         // does not resolve in the host compilation pass)
-        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rA : c.rB;
         const uint32_t off = base + (uint32_t)c.lane16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((stage_buf<C, S, G>() + a * 1024)), 16, off, 0, 0, 0);
     } else if constexpr (V < C::kLoads) {
@@ -379,16 +387,20 @@ __device__ __forceinline__ void dma_op(const X &c, typename X::kint k) {
         static_assert(isA || C::kWaves * R >= C::kGA, "A/B split falls on a DMA instruction");
         const int a = C::kWaves * R + c.wave;
         const kint h = k / 4;
-        uint32_t base;
+        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rAs : c.rBs;
         if constexpr (INNER) {
-            base = (uint32_t)c.sc_row[R] + (uint32_t)(h * 256);
-        } else {
+            const uint32_t sbase = (uint32_t)c.sc_row[R] + (uint32_t)(h * 256);
+            const uint32_t voff = (uint32_t)c.lane4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((scale_buf<C, G>() + a * 256)), 4, voff, sbase, 0, 0);
+            return;
+        }
+        uint32_t base;
+        {
             base = h < c.kgroups ? (uint32_t)c.sc_row[R] + (uint32_t)(h * 256) : kOutOfRange;
             // only step kstream (the next tile's first) opens a k-group past the tile
             if constexpr (X::kStream)
                 if (k >= c.kstream) base = c.knext > 0 ? (uint32_t)c.sc_next[R] : kOutOfRange;
         }
-        const __amdgpu_buffer_rsrc_t rsrc = isA ? c.rAs : c.rBs;
         const uint32_t off = base + (uint32_t)c.lane4;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((scale_buf<C, G>() + a * 256)), 4, off, 0, 0, 0);
     }
