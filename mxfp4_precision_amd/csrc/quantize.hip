@@ -645,6 +645,12 @@ __global__ __launch_bounds__(256) __attribute__((
     constexpr int kXPitch = 272;
     __shared__ __attribute__((aligned(16))) uint8_t s_x[ELEM == 6 ? kTileRows * kXPitch : 16];
     const int r_loc0 = wave * kWaveRows + 8 * q;      // this lane's first tile row
+    // the lane's staging addresses for row t / column u of its 8 (MXFP4):
+    // kept in registers (opaque to the compiler), so that every write adds
+    // only a constant offset instead of recomputing the address per row
+    uint32_t row_line = r_loc0 * kLinePitch + 4 * c, row_scale = r_loc0 * 4 + c / 4;
+    uint32_t col_line = 8 * c * kLinePitch + 16 * wave + 4 * q, col_scale = 8 * c * 4 + wave;
+    asm volatile("" : "+v"(row_line), "+v"(row_scale), "+v"(col_line), "+v"(col_scale));
 
     // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
     if (RHT && a.row.rht) {
@@ -737,8 +743,8 @@ __global__ __launch_bounds__(256) __attribute__((
         } else {
             packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
         }
-        *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
-        if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+        *reinterpret_cast<uint32_t *>(&s_data[0][row_line + t * kLinePitch]) = packed;
+        if ((c & 3) == 0) s_scale[0][row_scale + 4 * t] = (uint8_t)sc;
         // one row at a time: interleaving rows only raises register pressure
         if (ROW_SR) __builtin_amdgcn_sched_barrier(0);
     }
@@ -850,8 +856,8 @@ __global__ __launch_bounds__(256) __attribute__((
                                    pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h), sc);
             }
             // blob row = tile column 8c+u; this wave's 32 rows are bytes [16*wave, 16*wave+16)
-            *reinterpret_cast<uint32_t *>(&s_data[1][(8 * c + u) * kLinePitch + 16 * wave + 4 * q]) = packed;
-            if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+            *reinterpret_cast<uint32_t *>(&s_data[1][col_line + u * kLinePitch]) = packed;
+            if (q == 0) s_scale[1][col_scale + 4 * u] = (uint8_t)sc;
             if (COL_SR) __builtin_amdgcn_sched_barrier(0);
         }
     }
