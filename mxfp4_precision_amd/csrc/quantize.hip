@@ -59,39 +59,33 @@ constexpr int kTileCols = 128;
 constexpr int kWaves = 4;
 constexpr int kTileRows = kWaveRows * kWaves;
 
-__device__ __forceinline__ uint32_t scale_code(uint32_t amax16) {
-    if (amax16 >= 0x7F80u) return 0xFFu;            // Inf or NaN in the block
-    return __builtin_elementwise_sub_sat(amax16 >> 7, 2u);
-}
-
-// Scale byte of a block row that may lie past the tensor: amax16 counts only
-// if `real` (rows or columns past the tensor are the tiled layout's zero
-// padding and get scale 0); nonfinite is set for an Inf/NaN block.
-__device__ __forceinline__ uint32_t scale_code_if(bool real, uint32_t amax16, bool &nonfinite) {
-    const uint32_t am = real ? amax16 : 0u;
-    nonfinite = am >= 0x7F80u;
-    return nonfinite ? 0xFFu : __builtin_elementwise_sub_sat(am >> 7, 2u);
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 
-// 2^(c-127) as fp32 (c = 0 is the subnormal 2^-127).
+// 2^(c-127) as fp32 (c = 0 is the subnormal 2^-127, c = 255 gives +Inf):
+// one exact ldexp of 2^-127 (fp32 denormals are kept in this build).
 __device__ __forceinline__ float scale_f32(uint32_t c) {
-    return __uint_as_float(c ? (c << 23) : 0x00400000u);
+    return __builtin_ldexpf(__uint_as_float(0x00400000u), (int)c);
 }
 
-// Four bf16 pairs (element 2i in the low half of p_i) -> 8 nibbles, RNE, saturating.
+// Scale byte of a block amax and whether the block holds Inf/NaN.
+__device__ __forceinline__ uint32_t scale_code_nf(uint32_t amax16, bool &nonfinite) {
+    nonfinite = amax16 >= 0x7F80u;
+    return nonfinite ? 0xFFu : __builtin_elementwise_sub_sat(amax16 >> 7, 2u);
+}
+
+// Four bf16 pairs (element 2i in the low half of p_i) -> 8 nibbles, RNE,
+// saturating; a block holding Inf/NaN (scale byte 0xFF) gives all nibbles 0.
 __device__ __forceinline__ uint32_t pack8_rne(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
-                                              uint32_t c) {
+                                              uint32_t c, bool nonfinite) {
     const float sf = scale_f32(c);
     uint32_t r = 0;
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p0), sf, 0);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p1), sf, 1);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p2), sf, 2);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2_t, p3), sf, 3);
-    return c == 0xFFu ? 0u : r;      // Inf/NaN block: all nibbles 0
+    return nonfinite ? 0u : r;
 }
 
 // bf16 pair (lo, hi) from the same half of two words: half 0 = low halves.
@@ -727,12 +721,18 @@ __global__ __launch_bounds__(256) __attribute__((
             lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
             if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
         }
-    } else
+    } else {
+    // each row's block amax: in 2D mode the 32x32 tile's, rows past M taking 0
+    // (the tiled layout's zero padding; in 1D mode their amax is 0 already,
+    // their data being 0), so that the encode reads one value per row
+    if (a.row.use_2d) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ramax[t] = t < rows_here ? tile_amax : 0u;
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        // rows past M exist only as zero padding of the tiled layout: scale 0 there
         bool nonfinite;
-        const uint32_t sc = scale_code_if(t < rows_here, a.row.use_2d ? tile_amax : ramax[t], nonfinite);
+        const uint32_t sc = scale_code_nf(ramax[t], nonfinite);
         uint32_t packed = 0;
         if (ROW_SR) {
             const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
@@ -741,12 +741,13 @@ __global__ __launch_bounds__(256) __attribute__((
             packed = pack8_sr([&](int e) { return elem_hi(d[t][e >> 1], e & 1); }, sc,
                               [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); }, even, odd, nonfinite);
         } else {
-            packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc);
+            packed = pack8_rne(d[t][0], d[t][1], d[t][2], d[t][3], sc, nonfinite);
         }
         *reinterpret_cast<uint32_t *>(&s_data[0][row_line + t * kLinePitch]) = packed;
         if ((c & 3) == 0) s_scale[0][row_scale + 4 * t] = (uint8_t)sc;
         // one row at a time: interleaving rows only raises register pressure
         if (ROW_SR) __builtin_amdgcn_sched_barrier(0);
+    }
     }
 
     if (DUAL && RHT && a.col.rht) {
@@ -830,11 +831,16 @@ __global__ __launch_bounds__(256) __attribute__((
                 lds_put6(s_data[1], (8 * c + u) * kLinePitch + 24 * wave + 6 * q, lo, hi);
                 if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
             }
-        } else
+        } else {
+        // each column's block amax, as for the rows (columns past N take 0)
+        if (a.col.use_2d) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) camax[u] = u < cols_here ? tile_amax : 0u;
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             bool nonfinite;
-            const uint32_t sc = scale_code_if(u < cols_here, a.col.use_2d ? tile_amax : camax[u], nonfinite);
+            const uint32_t sc = scale_code_nf(camax[u], nonfinite);
             uint32_t packed = 0;
             if (COL_SR) {
                 // element t of the column = row t, half h of word w; the sign
@@ -853,12 +859,13 @@ __global__ __launch_bounds__(256) __attribute__((
             } else {
                 const int w = u >> 1, h = u & 1;
                 packed = pack8_rne(pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h),
-                                   pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h), sc);
+                                   pair_of(d[4][w], d[5][w], h), pair_of(d[6][w], d[7][w], h), sc, nonfinite);
             }
             // blob row = tile column 8c+u; this wave's 32 rows are bytes [16*wave, 16*wave+16)
             *reinterpret_cast<uint32_t *>(&s_data[1][col_line + u * kLinePitch]) = packed;
             if (q == 0) s_scale[1][col_scale + 4 * u] = (uint8_t)sc;
             if (COL_SR) __builtin_amdgcn_sched_barrier(0);
+        }
         }
     }
     __syncthreads();
