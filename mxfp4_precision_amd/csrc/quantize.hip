@@ -62,6 +62,7 @@ constexpr int kTileRows = kWaveRows * kWaves;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // 2^(c-127) as fp32 (c = 0 is the subnormal 2^-127, c = 255 gives +Inf):
 // one exact ldexp of 2^-127 (fp32 denormals are kept in this build).
@@ -188,12 +189,13 @@ __device__ __forceinline__ void rand8(uint64_t n0, const DirOpts &o, uint32_t di
     hi = s ? (x1 >> s) | (x2 << (32u - s)) : x1;
 }
 
-__device__ __forceinline__ uint32_t max_abs_pair(uint32_t d) {
-    uint32_t lo = d & 0x7FFFu, hi = (d >> 16) & 0x7FFFu;
-    return lo > hi ? lo : hi;
-}
-
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// max of each 16-bit half (one packed instruction for two magnitudes)
+__device__ __forceinline__ uint32_t pk_umax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
+}
 
 __device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
     return umax(v, (uint32_t)__shfl_xor((int)v, mask, 64));
@@ -365,7 +367,6 @@ __device__ __forceinline__ uint32_t code6(uint32_t x16, uint32_t c, const Fp6Dir
 typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
 typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t fp6_block_hw(const u32x16_t &w, uint32_t fmt, uint32_t emax, u32x6_t &out) {
     u16x2_t m = {0, 0};
 #pragma unroll
@@ -567,23 +568,36 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int w = 0; w < 4; ++w) d[t][w] = mul_bf16_pair(d[t][w], gl[t][w]);
     }
 
-    // ---- block amax, row direction: per row t over the lane's 8 columns, then lanes c^1, c^2
-    uint32_t ramax[8];
+    // ---- block amax.  A magnitude is the bf16 pattern with its sign cleared,
+    // compared as an integer (the order of |x|, Inf and NaN above every finite
+    // value), two per packed 16-bit max.  Row direction: per row t over the
+    // lane's 8 columns, then lanes c^1, c^2.  For MXFP4 without the Hadamard
+    // transform the column maxima are accumulated in the same pass over the
+    // magnitudes, so those die before the encode (taken after the row encode,
+    // they stayed live through it: 164 -> 202 VGPRs in the stochastic dual
+    // kernel).
+    constexpr bool kEarlyColAmax = DUAL && ELEM == 4 && !RHT;
+    uint32_t ramax[8], rpk[8], cpk[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        uint32_t m = umax(umax(max_abs_pair(d[t][0]), max_abs_pair(d[t][1])),
-                          umax(max_abs_pair(d[t][2]), max_abs_pair(d[t][3])));
-        ramax[t] = m;
+        uint32_t m[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) m[w] = d[t][w] & 0x7FFF7FFFu;
+        rpk[t] = pk_umax(pk_umax(m[0], m[1]), pk_umax(m[2], m[3]));   // (even columns, odd columns)
+        if constexpr (kEarlyColAmax) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) cpk[w] = t == 0 ? m[w] : pk_umax(cpk[w], m[w]);
+        }
     }
 #pragma unroll
     for (int t = 0; t < 8; t += 2) {
-        uint32_t pk = ramax[t] | (ramax[t + 1] << 16);
-        uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 1, 64);
-        uint32_t lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu), hi = umax(pk >> 16, o1 >> 16);
-        pk = lo | (hi << 16);
-        uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 2, 64);
-        ramax[t] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
-        ramax[t + 1] = umax(pk >> 16, o2 >> 16);
+        // rows t and t+1 in the low and high halves
+        uint32_t pk = pk_umax(__builtin_amdgcn_perm(rpk[t + 1], rpk[t], 0x05040100u),
+                              __builtin_amdgcn_perm(rpk[t + 1], rpk[t], 0x07060302u));
+        pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 1, 64));
+        pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 2, 64));
+        ramax[t] = pk & 0xFFFFu;
+        ramax[t + 1] = pk >> 16;
     }
     // 32x32 tile amax (2D mode): rows of the lane, then the 4 q-lanes
     uint32_t tile_amax = 0;
@@ -597,32 +611,24 @@ __global__ __launch_bounds__(256) __attribute__((
     }
 
     // ---- block amax, column direction: per column u of the lane, 8 rows
-    // in-lane, then lanes q^1, q^2.  For MXFP4 without the Hadamard transform
-    // it is taken here, next to the row amax that shares its per-element
-    // magnitudes, so those die before the encode (taken after the row encode,
-    // they stayed live through it: 164 -> 202 VGPRs in the stochastic dual
-    // kernel).  MXFP6 draws its random bytes after this point and takes the
+    // in-lane (accumulated above for MXFP4 without the transform), then lanes
+    // q^1, q^2.  MXFP6 draws its random bytes after this point and takes the
     // column amax later.
     uint32_t camax[8];
     auto col_amax = [&]() {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            uint32_t lo = 0, hi = 0;
+            uint32_t pk = cpk[w];   // columns 2w and 2w+1 in the low and high halves
+            if constexpr (!kEarlyColAmax) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                lo = umax(lo, d[t][w] & 0x7FFFu);
-                hi = umax(hi, (d[t][w] >> 16) & 0x7FFFu);
+                for (int t = 0; t < 8; ++t) pk = pk_umax(pk, d[t][w] & 0x7FFF7FFFu);
             }
-            uint32_t pk = lo | (hi << 16);
-            uint32_t o1 = (uint32_t)__shfl_xor((int)pk, 16, 64);
-            lo = umax(pk & 0xFFFFu, o1 & 0xFFFFu); hi = umax(pk >> 16, o1 >> 16);
-            pk = lo | (hi << 16);
-            uint32_t o2 = (uint32_t)__shfl_xor((int)pk, 32, 64);
-            camax[2 * w] = umax(pk & 0xFFFFu, o2 & 0xFFFFu);
-            camax[2 * w + 1] = umax(pk >> 16, o2 >> 16);
+            pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 16, 64));
+            pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 32, 64));
+            camax[2 * w] = pk & 0xFFFFu;
+            camax[2 * w + 1] = pk >> 16;
         }
     };
-    constexpr bool kEarlyColAmax = DUAL && ELEM == 4 && !RHT;
     if constexpr (kEarlyColAmax) col_amax();
 
     if constexpr (ELEM == 6) draw_sr();
