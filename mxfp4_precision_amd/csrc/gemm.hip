@@ -1088,57 +1088,61 @@ __global__ __launch_bounds__(C::kThreads) void gemm_stream_kernel(int M, int N, 
 // V_MFMA_SCALE_F32_32X32X64_F8F6F4 with both formats E5M2 and unit block
 // scales (127): lane L of a 32-row operand tile supplies 32 bytes, row L%32,
 // elements [32*(L/32), 32*(L/32) + 32) of the 64-wide step = two 16-byte
-// slices of the atom, 256 bytes apart.  Same workgroup, wave tiles, XCD
-// order, LDS stages and epilogue as the FP4 main tiles; a k-step is 64
-// elements, its 32 atoms fill one 32 KB stage, step k+3 is in flight while
-// step k computes.
-using Fp8Cfg = Cfg<Fp4Fmt, MainShape>;
+// slices of the atom, 256 bytes apart.  A 64-element step of a 16-row group
+// is one 1 KB atom, as a 128-element MXFP4 step is, so the MXFP4
+// configurations give the atom and DMA counts: the same workgroup shapes
+// (256x256 main tiles; a last round that would fill at most half of the CUs
+// as 128x128 tiles, as two K groups summed through LDS when those give at
+// most one tile per CU), wave tiles, XCD order, LDS stages and epilogue; a
+// stage holds one step, step k+3 is in flight while step k computes.
+template <class S>
+using Fp8Cfg = Cfg<Fp4Fmt, S>;
 constexpr int kFmtBf8 = 1;          // MFMA f8f6f4 format code for E5M2
 constexpr int kUnitScale = 127;     // E8M0 2^0
 
-template <int S>
-__device__ __forceinline__ void fp8_dma_step(const Ctx<Fp8Cfg, false> &c, int64_t k) {
-    using C = Fp8Cfg;
+template <int S, int G, class C>
+__device__ __forceinline__ void fp8_dma_step(const Ctx<C, false> &c, int64_t k) {
 #pragma unroll
     for (int r = 0; r < C::kLoLoads; ++r) {
         const int a = C::kWaves * r + c.wave;
-        const uint32_t base = k < c.ksteps ? (uint32_t)c.lo_row[r] + (uint32_t)(k * 1024) : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a < C::kGA ? c.rA : c.rB, MX_LDS((stage_buf<C, S, 0>() + a * 1024)),
-                                                 16, base + c.lane16, 0, 0, 0);
+        // plain-typed locals: a builtin call on template-dependent operands
+        // does not resolve in the host compilation pass
+        const __amdgpu_buffer_rsrc_t rsrc = a < C::kGA ? c.rA : c.rB;
+        const uint32_t off =
+            (k < c.ksteps ? (uint32_t)c.lo_row[r] + (uint32_t)(k * 1024) : kOutOfRange) + (uint32_t)c.lane16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, MX_LDS((stage_buf<C, S, G>() + a * 1024)), 16, off, 0, 0, 0);
     }
 }
 
-template <int S>
-__device__ __forceinline__ void fp8_step(const Ctx<Fp8Cfg, false> &c, int64_t k,
-                                         v16f (&acc)[Fp8Cfg::kMB][Fp8Cfg::kMA], int frag_off, int a_atom0,
-                                         int b_atom0) {
-    using C = Fp8Cfg;
+template <class C, int S, int G>
+__device__ __forceinline__ void fp8_step(const Ctx<C, false> &c, int64_t k, v16f (&acc)[C::kMB][C::kMA],
+                                         int frag_off, int a_atom0, int b_atom0) {
     // step k landed for every wave (only steps k+1, k+2 may still be in flight),
     // and every wave is done reading step k-1's stage
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * C::kLoLoads) : "memory");
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *st = stage_buf<C, S, 0>() + frag_off;
-    uint4 b[C::kMB][2], a[C::kMA][2];
+    const uint8_t *st = stage_buf<C, S, G>() + frag_off;
+    uint4 bv[C::kMB][2], av[C::kMA][2];
 #pragma unroll
     for (int i = 0; i < C::kMB; ++i) {
-        b[i][0] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024);
-        b[i][1] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024 + 256);
+        bv[i][0] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024);
+        bv[i][1] = *reinterpret_cast<const uint4 *>(st + (b_atom0 + 2 * i) * 1024 + 256);
     }
 #pragma unroll
     for (int j = 0; j < C::kMA; ++j) {
-        a[j][0] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024);
-        a[j][1] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024 + 256);
+        av[j][0] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024);
+        av[j][1] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024 + 256);
     }
-    fp8_dma_step<(S + 3) & 3>(c, k + 3);
+    fp8_dma_step<(S + 3) & 3, G>(c, k + 3);
 #pragma unroll
     for (int i = 0; i < C::kMB; ++i) {
-        const v8i bop = {(int)b[i][0].x, (int)b[i][0].y, (int)b[i][0].z, (int)b[i][0].w,
-                         (int)b[i][1].x, (int)b[i][1].y, (int)b[i][1].z, (int)b[i][1].w};
+        const v8i bop = {(int)bv[i][0].x, (int)bv[i][0].y, (int)bv[i][0].z, (int)bv[i][0].w,
+                         (int)bv[i][1].x, (int)bv[i][1].y, (int)bv[i][1].z, (int)bv[i][1].w};
 #pragma unroll
         for (int j = 0; j < C::kMA; ++j) {
-            const v8i aop = {(int)a[j][0].x, (int)a[j][0].y, (int)a[j][0].z, (int)a[j][0].w,
-                             (int)a[j][1].x, (int)a[j][1].y, (int)a[j][1].z, (int)a[j][1].w};
+            const v8i aop = {(int)av[j][0].x, (int)av[j][0].y, (int)av[j][0].z, (int)av[j][0].w,
+                             (int)av[j][1].x, (int)av[j][1].y, (int)av[j][1].z, (int)av[j][1].w};
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bop, aop, acc[i][j], kFmtBf8, kFmtBf8, 0,
                                                                         kUnitScale, 0, kUnitScale);
         }
@@ -1149,33 +1153,69 @@ __device__ __forceinline__ void fp8_step(const Ctx<Fp8Cfg, false> &c, int64_t k,
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, C::kMA * C::kMB - C::kLoLoads, 0);
+    if constexpr (C::kMA * C::kMB > C::kLoLoads)
+        __builtin_amdgcn_sched_group_barrier(0x008, C::kMA * C::kMB - C::kLoLoads, 0);
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(Fp8Cfg::kThreads) void gemm_fp8_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
-                                                                    int tiles_n, int group_m,
-                                                                    const uint8_t *__restrict__ A,
-                                                                    const float *__restrict__ a_scale_inv,
-                                                                    const uint8_t *__restrict__ B,
-                                                                    const float *__restrict__ b_scale_inv,
-                                                                    void *__restrict__ Cout, int64_t ldc) {
-    using C = Fp8Cfg;
+// `steps` steps (a multiple of 4) of K group G's stages; steps past the
+// group's own c.ksteps land as zeros.
+template <class C, int G>
+__device__ __forceinline__ void fp8_run(const Ctx<C, false> &c, v16f (&acc)[C::kMB][C::kMA], int64_t steps,
+                                        int frag_off, int a_atom0, int b_atom0) {
+    fp8_dma_step<0, G>(c, 0);
+    fp8_dma_step<1, G>(c, 1);
+    fp8_dma_step<2, G>(c, 2);
+    for (int64_t k = 0; k < steps; k += 4) {
+        fp8_step<C, 0, G>(c, k, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 1, G>(c, k + 1, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 2, G>(c, k + 2, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 3, G>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// One output tile per workgroup, 256x256 (workgroup b takes tile b of the
+// XCD-remapped order) or 128x128 (workgroup b computes quarter b % 4 of
+// 256x256 tile first + b / 4).  Split form: group g = wave / 4 takes steps
+// [g * s0, ...) of K (s0 = half of them rounded up to a multiple of 4);
+// both groups run s0 steps, so the per-step barriers line up, and group 1's
+// partial tile is added into group 0's through LDS before the epilogue.
+template <class C, bool OUT_BF16>
+__global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(int64_t M, int64_t N, int64_t K_pad, int tiles_m,
+                                                               int tiles_n, int group_m, int first,
+                                                               const uint8_t *__restrict__ A,
+                                                               const float *__restrict__ a_scale_inv,
+                                                               const uint8_t *__restrict__ B,
+                                                               const float *__restrict__ b_scale_inv,
+                                                               void *__restrict__ Cout, int64_t ldc) {
+    constexpr bool kSplit = C::kKG == 2;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int group = kSplit ? wave_all / C::kWaves : 0;
+    const int wave = wave_all % C::kWaves;
     const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    if constexpr (C::kBM == 256) {
+        tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    } else {
+        const int quarter = (int)(blockIdx.x & 3);
+        tile_at(first + (int)(blockIdx.x >> 2), tiles_m, tiles_n, group_m, tm, tn);
+        tm = 2 * tm + (quarter >> 1);
+        tn = 2 * tn + (quarter & 1);
+    }
 
+    const int64_t ksteps = K_pad / 64;
+    const int64_t s0 = kSplit ? 4 * cdiv(cdiv(ksteps, 2), 4) : ksteps;
+    const int64_t kfirst = group ? s0 : 0;
     Ctx<C, false> c;
-    c.ksteps = K_pad / 64;
+    c.ksteps = group ? ksteps - s0 : (s0 < ksteps ? s0 : ksteps);
     c.kgroups = 0;
     c.wave = wave;
     c.lane16 = lane * 16;
     c.lane4 = 0;
     const int64_t nGA = cdiv(M, 16), nGB = cdiv(N, 16);
-    c.rA = make_rsrc(A, nGA * c.ksteps * 1024);
-    c.rB = make_rsrc(B, nGB * c.ksteps * 1024);
+    c.rA = make_rsrc(A, nGA * ksteps * 1024);
+    c.rB = make_rsrc(B, nGB * ksteps * 1024);
     const int64_t gA0 = (int64_t)tm * C::kGA, gB0 = (int64_t)tn * C::kGB;
 #pragma unroll
     for (int r = 0; r < C::kLoLoads; ++r) {
@@ -1184,7 +1224,7 @@ __global__ __launch_bounds__(Fp8Cfg::kThreads) void gemm_fp8_kernel(int64_t M, i
         int64_t g = isA ? gA0 + a : gB0 + (a - C::kGA);
         const int64_t gmax = (isA ? nGA : nGB) - 1;
         g = g < gmax ? g : gmax;
-        c.lo_row[r] = (int)(g * c.ksteps * 1024);
+        c.lo_row[r] = (int)((g * ksteps + kfirst) * 1024);
     }
     const float scale = a_scale_inv[0] * b_scale_inv[0];
 
@@ -1194,24 +1234,42 @@ __global__ __launch_bounds__(Fp8Cfg::kThreads) void gemm_fp8_kernel(int64_t M, i
 #pragma unroll
         for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
 
-    fp8_dma_step<0>(c, 0);
-    fp8_dma_step<1>(c, 1);
-    fp8_dma_step<2>(c, 2);
     const int lrow = lane & 31, lhi = lane >> 5;
     const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 32 * lhi) * 16;
     const int a_atom0 = wm * C::kTA, b_atom0 = C::kGA + wn * C::kTB;
-    for (int64_t k = 0; k < c.ksteps; k += 4) {
-        fp8_step<0>(c, k, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<1>(c, k + 1, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<2>(c, k + 2, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<3>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+    if (kSplit && group == 1) fp8_run<C, 1>(c, acc, s0, frag_off, a_atom0, b_atom0);
+    else fp8_run<C, 0>(c, acc, s0, frag_off, a_atom0, b_atom0);
+
+    if constexpr (kSplit) {
+        // every wave is past its last stage read; group 1's stages take its partial tile
+        __syncthreads();
+        if (group == 1) {
+#pragma unroll
+            for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kMA; ++j) {
+                    float *p = partial_slot<C>(wave, i * C::kMA + j) + lane;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) p[e * 64] = acc[i][j][e];
+                }
+        }
+        __syncthreads();
+        if (group == 0) {
+#pragma unroll
+            for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+                for (int j = 0; j < C::kMA; ++j) {
+                    const float *p = partial_slot<C>(wave, i * C::kMA + j) + lane;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += p[e * 64];
+                }
+        }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
         for (int j = 0; j < C::kMA; ++j) acc[i][j] *= scale;
-    store_tile<C, OUT_BF16>(acc, tm, tn, M, N, Cout, ldc, 0, wave, wave, lane);
+    store_tile<C, OUT_BF16>(acc, tm, tn, M, N, Cout, ldc, group, wave, wave_all, lane);
 }
 
 // K == 0: C[i][j] = 0, or bias[j] (bf16 bits; exact in either output type).
@@ -1374,11 +1432,33 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, co
     // buffer offsets are 32-bit: each operand blob must stay below 2 GiB
     if (cdiv(M, 16) * 16 * K_pad >= (int64_t(1) << 31) || cdiv(N, 16) * 16 * K_pad >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
+    using CM = Fp8Cfg<MainShape>;
+    using CT = Fp8Cfg<TailShape>;
+    using CS = Fp8Cfg<SplitShape>;
     const int tiles_m = (int)cdiv(M, 256), tiles_n = (int)cdiv(N, 256);
-    dim3 grid((unsigned)(tiles_m * tiles_n));
-    auto kernel = out_dtype == MX_BF16 ? gemm_fp8_kernel<true> : gemm_fp8_kernel<false>;
-    hipLaunchKernelGGL(kernel, grid, dim3(Fp8Cfg::kThreads), 0, stream, M, N, K_pad, tiles_m, tiles_n,
-                       band_rows(tiles_m), A, a_scale_inv, B, b_scale_inv, C, ldc);
+    const int tiles = tiles_m * tiles_n;
+    const int group_m = band_rows(tiles_m);
+    const int cus = device_cu_count();
+    // a last round that would fill at most half of the CUs goes to the tail tiles
+    const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
+    const bool bf = out_dtype == MX_BF16;
+    auto main_kernel = bf ? gemm_fp8_kernel<CM, true> : gemm_fp8_kernel<CM, false>;
+    hipLaunchKernelGGL(main_kernel, dim3((unsigned)(tiles - tail)), dim3(CM::kThreads), 0, stream, M, N, K_pad,
+                       tiles_m, tiles_n, group_m, 0, A, a_scale_inv, B, b_scale_inv, C, ldc);
+    if (!tail) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int first = tiles - tail;
+    // at most one 128x128 tile per CU and at least 16 steps: the split form
+    if (4 * tail <= cus && K_pad >= 16 * 64) {
+        auto kernel = bf ? gemm_fp8_kernel<CS, true> : gemm_fp8_kernel<CS, false>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * tail)), dim3(CS::kThreads), 0, stream, M, N, K_pad, tiles_m,
+                           tiles_n, group_m, first, A, a_scale_inv, B, b_scale_inv, C, ldc);
+    } else {
+        auto kernel = bf ? gemm_fp8_kernel<CT, true> : gemm_fp8_kernel<CT, false>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(4 * tail)), dim3(CT::kThreads), 0, stream, M, N, K_pad, tiles_m,
+                           tiles_n, group_m, first, A, a_scale_inv, B, b_scale_inv, C, ldc);
+    }
     return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ def check_bf16_within(got_bits, ref, tau, oracle_mod, what):
     return int((got_bits == refb).sum())
 
 
-def run_gemm(oracle_mod, a, b, nsample=None, seed=0, what=""):
+def run_gemm(oracle_mod, a, b, nsample=None, seed=0, what="", entries=None):
     M, K = a.shape
     N = b.shape[0]
     qa, _, ia = quant(a, TILED, True, False)
@@ -128,7 +128,9 @@ def run_gemm(oracle_mod, a, b, nsample=None, seed=0, what=""):
         outs[dt] = host(C)[:M, :N]
     oqa, sa, _ = oracle_mod.quantize_fp8_tw(a, 0)
     oqb, sb, _ = oracle_mod.quantize_fp8_tw(b, 0)
-    if nsample is None:
+    if entries is not None:
+        ii, jj = entries
+    elif nsample is None:
         ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
         ii, jj = ii.ravel(), jj.ravel()
     else:
@@ -148,6 +150,7 @@ def run_gemm(oracle_mod, a, b, nsample=None, seed=0, what=""):
     assert rel <= implied, (what, rel, implied)
     log("%s: %d/%d bf16 exact, fp32 max err/tau %.3g, rel Frobenius %.3g (the bar implies <= %.3g)" % (
         what, exact, ii.size, float((err / tau).max()), rel, implied))
+    return outs
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (100, 70, 300), (300, 257, 1000), (512, 513, 640)])
@@ -156,6 +159,36 @@ def test_fp8_gemm(oracle_mod, M, N, K):
     a = synth.random_bf16(M * 7 + K, (M, K), std=1.0)
     b = synth.random_bf16(N * 11 + K, (N, K), std=0.02)
     run_gemm(oracle_mod, a, b, what="fp8 %dx%dx%d" % (M, N, K))
+
+
+def _rne_bf16_bits(f32):
+    """bf16 bits of finite fp32 values, round to nearest even."""
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("K", [384, 1100, 2048])
+def test_fp8_gemm_tail_tiles_every_entry_of_tail_rows(oracle_mod, K):
+    """Tile count past one round on 256 CUs with a small last round: the last
+    round runs as 128x128 tiles (4597x4349 -> 18x17 = 306 tiles of 256x256; the
+    last 50 of the tile order, which hold the ragged last row and column of
+    tiles, become 200 tiles of 128x128).  K 384 (6 steps of 64): one
+    workgroup of 4 waves per small tile; K 1100 (18 steps: 12 + 6, the second
+    group's last steps past K) and 2048 (32 steps: 16 + 16): at most one small
+    tile per CU and at least 16 steps, so each runs as two K groups of 4 waves
+    summed through LDS.  Every entry of rows in the main and the tail region,
+    bf16 and fp32, against the oracle, and the bf16 output equal to the
+    rounding of the fp32 one."""
+    _require_gpu()
+    M, N = 4597, 4349
+    a = synth.random_bf16(191 + K, (M, K), std=1.0)
+    b = synth.random_bf16(192 + K, (N, K), std=0.05)
+    rows = np.array([0, 127, 128, 2047, 2048 + 77, 4095, 4096, 4096 + 128, M - 2, M - 1])
+    ii = np.repeat(rows, N)
+    jj = np.tile(np.arange(N), rows.size)
+    log("fp8 tail tiles %dx%dx%d" % (M, N, K))
+    outs = run_gemm(oracle_mod, a, b, what="fp8 tail %dx%dx%d" % (M, N, K), entries=(ii, jj))
+    assert np.array_equal(outs[mx.MX_BF16].view(np.uint16), _rne_bf16_bits(outs[mx.MX_F32]))
 
 
 def test_fp8_hybrid_backward_fc2_sampled(oracle_mod):
