@@ -70,11 +70,19 @@ __device__ __forceinline__ float scale_f32(uint32_t c) {
     return __builtin_ldexpf(__uint_as_float(0x00400000u), (int)c);
 }
 
-// Scale byte of a block amax and whether the block holds Inf/NaN.
+// Scale byte of a block amax and whether the block holds Inf/NaN.  FINITE:
+// the caller knows no element of the wave's tile is Inf/NaN.
+template <bool FINITE = false>
 __device__ __forceinline__ uint32_t scale_code_nf(uint32_t amax16, bool &nonfinite) {
-    nonfinite = amax16 >= 0x7F80u;
+    nonfinite = FINITE ? false : amax16 >= 0x7F80u;
     return nonfinite ? 0xFFu : __builtin_elementwise_sub_sat(amax16 >> 7, 2u);
 }
+
+// compile-time flag for the two instances of an encode
+template <bool B>
+struct FiniteTag {
+    static constexpr bool value = B;
+};
 
 // Four bf16 pairs (element 2i in the low half of p_i) -> 8 nibbles, RNE,
 // saturating; a block holding Inf/NaN (scale byte 0xFF) gives all nibbles 0.
@@ -589,6 +597,17 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int w = 0; w < 4; ++w) cpk[w] = t == 0 ? m[w] : pk_umax(cpk[w], m[w]);
         }
     }
+    // no Inf/NaN anywhere in the wave's tile (the usual case): the MXFP4
+    // encodes then skip the per-block test and selects.  A magnitude of at
+    // least 0x7F80 carries into bit 15 of its half when 0x80 is added.
+    bool wave_finite = false;
+    if constexpr (ELEM == 4) {
+        const uint32_t m = pk_umax(pk_umax(pk_umax(rpk[0], rpk[1]), pk_umax(rpk[2], rpk[3])),
+                                   pk_umax(pk_umax(rpk[4], rpk[5]), pk_umax(rpk[6], rpk[7])));
+        const uint32_t big =
+            __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, m) + u16x2_t{0x80, 0x80}) & 0x80008000u;
+        wave_finite = __builtin_amdgcn_ballot_w64(big != 0u) == 0u;
+    }
 #pragma unroll
     for (int t = 0; t < 8; t += 2) {
         // rows t and t+1 in the low and high halves
@@ -735,10 +754,11 @@ __global__ __launch_bounds__(256) __attribute__((
 #pragma unroll
         for (int t = 0; t < 8; ++t) ramax[t] = t < rows_here ? tile_amax : 0u;
     }
+    auto encode_rows = [&](auto fin) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         bool nonfinite;
-        const uint32_t sc = scale_code_nf(ramax[t], nonfinite);
+        const uint32_t sc = scale_code_nf<decltype(fin)::value>(ramax[t], nonfinite);
         uint32_t packed = 0;
         if (ROW_SR) {
             const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
@@ -754,6 +774,9 @@ __global__ __launch_bounds__(256) __attribute__((
         // one row at a time: interleaving rows only raises register pressure
         if (ROW_SR) __builtin_amdgcn_sched_barrier(0);
     }
+    };
+    if (wave_finite) encode_rows(FiniteTag<true>{});
+    else encode_rows(FiniteTag<false>{});
     }
 
     if (DUAL && RHT && a.col.rht) {
@@ -843,10 +866,11 @@ __global__ __launch_bounds__(256) __attribute__((
 #pragma unroll
             for (int u = 0; u < 8; ++u) camax[u] = u < cols_here ? tile_amax : 0u;
         }
+        auto encode_cols = [&](auto fin) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             bool nonfinite;
-            const uint32_t sc = scale_code_nf(camax[u], nonfinite);
+            const uint32_t sc = scale_code_nf<decltype(fin)::value>(camax[u], nonfinite);
             uint32_t packed = 0;
             if (COL_SR) {
                 // element t of the column = row t, half h of word w; the sign
@@ -872,6 +896,9 @@ __global__ __launch_bounds__(256) __attribute__((
             if (q == 0) s_scale[1][col_scale + 4 * u] = (uint8_t)sc;
             if (COL_SR) __builtin_amdgcn_sched_barrier(0);
         }
+        };
+        if (wave_finite) encode_cols(FiniteTag<true>{});
+        else encode_cols(FiniteTag<false>{});
         }
     }
     __syncthreads();
