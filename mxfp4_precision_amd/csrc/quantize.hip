@@ -656,13 +656,19 @@ __global__ __launch_bounds__(256) __attribute__((
     // Staging: one 64-byte line per blob row of this workgroup's tile (128 blob
     // rows per direction, 128 quantized elements each), padded to 80 bytes to
     // spread LDS banks; scales as 4 bytes per blob row.
-    __shared__ __attribute__((aligned(16))) uint8_t s_data[2][kTileRows * kLinePitch];
-    __shared__ __attribute__((aligned(16))) uint8_t s_scale[2][kTileRows * 4];
     // MXFP6, round to nearest, 1D blocks: each 32-element block is gathered
-    // into one lane through this 128 x 128 bf16 buffer (rows, then columns)
-    // and encoded by the hardware converter.
+    // into one lane through a 128 x 128 bf16 buffer (rows, then columns) and
+    // encoded by the hardware converter.  The codes wait in registers until
+    // every gather is done, so the staging lines take the same memory
+    // (35 KB of LDS per workgroup instead of 63: four workgroups per CU).
     constexpr int kXPitch = 272;
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[ELEM == 6 ? kTileRows * kXPitch : 16];
+    constexpr int kDataBytes = 2 * kTileRows * kLinePitch;
+    // (only kernels with a round-to-nearest direction can take that path)
+    constexpr int kXBytes = (ELEM == 6 && (!ROW_SR || (DUAL && !COL_SR))) ? kTileRows * kXPitch : 0;
+    __shared__ __attribute__((aligned(16))) uint8_t s_buf[kXBytes > kDataBytes ? kXBytes : kDataBytes];
+    uint8_t(*const s_data)[kTileRows * kLinePitch] = reinterpret_cast<uint8_t(*)[kTileRows * kLinePitch]>(s_buf);
+    uint8_t *const s_x = s_buf;
+    __shared__ __attribute__((aligned(16))) uint8_t s_scale[2][kTileRows * 4];
     const int r_loc0 = wave * kWaveRows + 8 * q;      // this lane's first tile row
     // the lane's staging addresses for row t / column u of its 8 (MXFP4):
     // kept in registers (opaque to the compiler), so that every write adds
@@ -671,6 +677,7 @@ __global__ __launch_bounds__(256) __attribute__((
     uint32_t col_line = 8 * c * kLinePitch + 16 * wave + 4 * q, col_scale = 8 * c * 4 + wave;
     asm volatile("" : "+v"(row_line), "+v"(row_scale), "+v"(col_line), "+v"(col_scale));
 
+    if constexpr (ELEM == 4) {
     // row-wise: row r_loc0+t, 8 elements at columns 8c.. -> dword c of the line
     if (RHT && a.row.rht) {
         // per row t: the lane's 8 columns are slice c%4 of their 32-column block
@@ -702,48 +709,6 @@ __global__ __launch_bounds__(256) __attribute__((
             // all-zero row can hold -0, whose sign bit must not leak into it)
             if (i >= M) packed = 0;
             *reinterpret_cast<uint32_t *>(&s_data[0][(r_loc0 + t) * kLinePitch + 4 * c]) = packed;
-            if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
-        }
-    } else if (ELEM == 6 && !ROW_SR && !a.row.use_2d) {
-        // the lane's 8 rows x 8 columns into the row-major buffer, then thread
-        // th encodes blocks 2(th%2), 2(th%2)+1 of tile row th/2
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            *reinterpret_cast<uint4 *>(&s_x[(r_loc0 + t) * kXPitch + 16 * c]) = uint4{d[t][0], d[t][1], d[t][2], d[t][3]};
-        __syncthreads();
-        const int th = (int)threadIdx.x, rl = th >> 1;
-        const uint32_t emax = a.row.fmt == 2u ? 2u : 4u;
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            const int b = 2 * (th & 1) + bb;
-            const uint8_t *src = &s_x[rl * kXPitch + 64 * b];
-            u32x16_t w;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
-                w[4 * v] = x4.x; w[4 * v + 1] = x4.y; w[4 * v + 2] = x4.z; w[4 * v + 3] = x4.w;
-            }
-            u32x6_t codes;
-            const uint32_t sc = fp6_block_hw(w, a.row.fmt, emax, codes);
-            lds_put24(&s_data[0][rl * kLinePitch + 24 * b], codes);
-            s_scale[0][rl * 4 + b] = (uint8_t)sc;
-        }
-    } else if constexpr (ELEM == 6) {
-        const Fp6Dir f = fp6_dir(a.row.fmt);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int64_t i = row0 + 8 * q + t;
-            const uint32_t sc = i < M ? scale_code_emax(a.row.use_2d ? tile_amax : ramax[t], f.emax) : 0u;
-            uint32_t k6[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                const uint32_t rb = ROW_SR ? ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu : 0u;
-                k6[e] = code6<ROW_SR>(x16, sc, f, rb);
-            }
-            uint32_t lo, hi;
-            pack6(k6, lo, hi);
-            lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
             if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
         }
     } else {
@@ -811,56 +776,6 @@ __global__ __launch_bounds__(256) __attribute__((
         }
     } else if (DUAL) {
         if constexpr (!kEarlyColAmax) col_amax();
-        if (ELEM == 6 && !COL_SR && !a.col.use_2d) {
-            // the lane's 8 columns x 8 rows into the buffer as columns (after
-            // every reader of the row pass is done), then thread th encodes
-            // blocks 2(th%2), 2(th%2)+1 of tile column th/2
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int w = u >> 1, h = u & 1;
-                *reinterpret_cast<uint4 *>(&s_x[(8 * c + u) * kXPitch + 2 * r_loc0]) =
-                    uint4{pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h), pair_of(d[4][w], d[5][w], h),
-                          pair_of(d[6][w], d[7][w], h)};
-            }
-            __syncthreads();
-            const int th = (int)threadIdx.x, cl = th >> 1;
-            const uint32_t emax = a.col.fmt == 2u ? 2u : 4u;
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                const int b = 2 * (th & 1) + bb;
-                const uint8_t *src = &s_x[cl * kXPitch + 64 * b];
-                u32x16_t wv;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
-                    wv[4 * v] = x4.x; wv[4 * v + 1] = x4.y; wv[4 * v + 2] = x4.z; wv[4 * v + 3] = x4.w;
-                }
-                u32x6_t codes;
-                const uint32_t sc = fp6_block_hw(wv, a.col.fmt, emax, codes);
-                lds_put24(&s_data[1][cl * kLinePitch + 24 * b], codes);
-                s_scale[1][cl * 4 + b] = (uint8_t)sc;
-            }
-        } else if constexpr (ELEM == 6) {
-            const Fp6Dir f = fp6_dir(a.col.fmt);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t j = j0 + u;
-                const uint32_t sc = j < N ? scale_code_emax(a.col.use_2d ? tile_amax : camax[u], f.emax) : 0u;
-                uint32_t k6[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-                    const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
-                    k6[t] = code6<COL_SR>(x16, sc, f, rb);
-                }
-                uint32_t lo, hi;
-                pack6(k6, lo, hi);
-                // blob row = tile column 8c+u; this wave's 32 rows are bytes [24*wave, 24*wave+24)
-                lds_put6(s_data[1], (8 * c + u) * kLinePitch + 24 * wave + 6 * q, lo, hi);
-                if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
-            }
-        } else {
         // each column's block amax, as for the rows (columns past N take 0)
         if (a.col.use_2d) {
 #pragma unroll
@@ -899,6 +814,117 @@ __global__ __launch_bounds__(256) __attribute__((
         };
         if (wave_finite) encode_cols(FiniteTag<true>{});
         else encode_cols(FiniteTag<false>{});
+    }
+    } else {
+        // MXFP6: the hardware-converter passes gather through s_x (rows, then
+        // columns) into registers; every staging write comes after the last
+        // gather, since the staging lines share s_x's memory
+        const bool row_hw = !ROW_SR && !a.row.use_2d;
+        const bool col_hw = DUAL && !COL_SR && !a.col.use_2d;
+        const int th = (int)threadIdx.x, tl = th >> 1;   // tile row / column th/2, blocks 2(th%2), 2(th%2)+1
+        u32x6_t hw_codes[2][2];
+        uint32_t hw_sc[2][2];
+        if (row_hw) {
+            // the lane's 8 rows x 8 columns into the row-major buffer
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                *reinterpret_cast<uint4 *>(&s_x[(r_loc0 + t) * kXPitch + 16 * c]) =
+                    uint4{d[t][0], d[t][1], d[t][2], d[t][3]};
+            __syncthreads();
+            const uint32_t emax = a.row.fmt == 2u ? 2u : 4u;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const uint8_t *src = &s_x[tl * kXPitch + 64 * (2 * (th & 1) + bb)];
+                u32x16_t w;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
+                    w[4 * v] = x4.x; w[4 * v + 1] = x4.y; w[4 * v + 2] = x4.z; w[4 * v + 3] = x4.w;
+                }
+                hw_sc[0][bb] = fp6_block_hw(w, a.row.fmt, emax, hw_codes[0][bb]);
+            }
+        }
+        if (col_hw) {
+            // the lane's 8 columns x 8 rows into the buffer as columns (after
+            // every gather of the row pass)
+            if (row_hw) __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int w = u >> 1, h = u & 1;
+                *reinterpret_cast<uint4 *>(&s_x[(8 * c + u) * kXPitch + 2 * r_loc0]) =
+                    uint4{pair_of(d[0][w], d[1][w], h), pair_of(d[2][w], d[3][w], h), pair_of(d[4][w], d[5][w], h),
+                          pair_of(d[6][w], d[7][w], h)};
+            }
+            __syncthreads();
+            const uint32_t emax = a.col.fmt == 2u ? 2u : 4u;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const uint8_t *src = &s_x[tl * kXPitch + 64 * (2 * (th & 1) + bb)];
+                u32x16_t wv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const uint4 x4 = *reinterpret_cast<const uint4 *>(src + 16 * v);
+                    wv[4 * v] = x4.x; wv[4 * v + 1] = x4.y; wv[4 * v + 2] = x4.z; wv[4 * v + 3] = x4.w;
+                }
+                hw_sc[1][bb] = fp6_block_hw(wv, a.col.fmt, emax, hw_codes[1][bb]);
+            }
+        }
+        if (row_hw || col_hw) __syncthreads();
+        if (row_hw) {
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int b = 2 * (th & 1) + bb;
+                lds_put24(&s_data[0][tl * kLinePitch + 24 * b], hw_codes[0][bb]);
+                s_scale[0][tl * 4 + b] = (uint8_t)hw_sc[0][bb];
+            }
+        } else {
+            const Fp6Dir f = fp6_dir(a.row.fmt);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int64_t i = row0 + 8 * q + t;
+                const uint32_t sc = i < M ? scale_code_emax(a.row.use_2d ? tile_amax : ramax[t], f.emax) : 0u;
+                uint32_t k6[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t rb = ROW_SR ? ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu : 0u;
+                    k6[e] = code6<ROW_SR>(x16, sc, f, rb);
+                }
+                uint32_t lo, hi;
+                pack6(k6, lo, hi);
+                lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
+                if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
+            }
+        }
+        if (DUAL) {
+            col_amax();
+            if (col_hw) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const int b = 2 * (th & 1) + bb;
+                    lds_put24(&s_data[1][tl * kLinePitch + 24 * b], hw_codes[1][bb]);
+                    s_scale[1][tl * 4 + b] = (uint8_t)hw_sc[1][bb];
+                }
+            } else {
+                const Fp6Dir f = fp6_dir(a.col.fmt);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int64_t j = j0 + u;
+                    const uint32_t sc = j < N ? scale_code_emax(a.col.use_2d ? tile_amax : camax[u], f.emax) : 0u;
+                    uint32_t k6[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+                        const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
+                        k6[t] = code6<COL_SR>(x16, sc, f, rb);
+                    }
+                    uint32_t lo, hi;
+                    pack6(k6, lo, hi);
+                    // blob row = tile column 8c+u; this wave's 32 rows are bytes [24*wave, 24*wave+24)
+                    lds_put6(s_data[1], (8 * c + u) * kLinePitch + 24 * wave + 6 * q, lo, hi);
+                    if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;
+                }
+            }
         }
     }
     __syncthreads();
