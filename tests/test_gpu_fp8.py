@@ -87,6 +87,25 @@ def test_fp8_quantize_special_tensors(oracle_mod):
     check_quant(oracle_mod, z, CANON)
 
 
+@pytest.mark.parametrize("amax_bits", [0x3A80, 0x3F80, 0x4780, 0x7F7F])
+def test_fp8_quantize_every_finite_bf16_up_to_amax(oracle_mod, amax_bits):
+    """Every bf16 pattern of magnitude at most A (both signs, zeros and bf16
+    subnormals included) in one tensor whose amax is A = 2^-10, 1, 2^16 and
+    the largest finite bf16: the products x * 57344/A then cover the whole
+    E5M2 range, its subnormals and values below them included, at four
+    scales.  Every byte of both blobs and the inverse scale against the
+    oracle (the finite-tensor encode)."""
+    _require_gpu()
+    mags = np.arange(0, amax_bits + 1, dtype=np.uint32)
+    vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+    cols = 256
+    rows = -(-vals.size // cols)
+    x = np.zeros(rows * cols, np.uint16)
+    x[:vals.size] = vals
+    log("fp8 quantize every finite bf16 up to 0x%04x: %d values" % (amax_bits, vals.size))
+    check_quant(oracle_mod, x.reshape(rows, cols), TILED)
+
+
 E5M2_EMIN = -14      # exponent of the smallest normal E5M2 (subnormals sit there)
 
 
