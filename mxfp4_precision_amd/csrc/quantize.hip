@@ -421,9 +421,10 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 
 // Dual stochastic rounding holds both directions' random bytes while the
 // staging loads are in flight.  Asking for at least two waves per SIMD (up to
-// 256 VGPRs) lets the compiler schedule the MXFP4 kernel in 158 VGPRs without
-// spills, so three waves still fit a SIMD; asking for three (168 VGPRs) made
-// it spill.  Same-box timings of the 18432x3072 dY quantize (before the
+// 256 VGPRs) let the compiler schedule the MXFP4 kernel in 158 VGPRs without
+// spills, so three waves fitted a SIMD, where asking for three (168 VGPRs)
+// made it spill; with the packed amax and the all-finite encode it now takes
+// 121 VGPRs (four waves) under the same request.  Same-box timings of the 18432x3072 dY quantize (before the
 // permute gather of pack8_sr): 0.0637 ms, against 0.0688 ms with the spilling
 // three-wave request and 0.0711 ms for the earlier form that drew the bytes
 // after the loads had landed.  (With the Hadamard transform as well it would
