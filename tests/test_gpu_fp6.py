@@ -61,10 +61,10 @@ def assert_equal_bytes(got, want, what):
         what, bad.size, bad[:5].tolist(), got[bad[:5]].tolist(), want[bad[:5]].tolist())
 
 
-def check_fp6(oracle_mod, x, layout, row_fmt, col_fmt=None, rkw=None, ckw=None):
-    """col_fmt None: row-wise only."""
+def check_fp6(oracle_mod, x, layout, row_fmt, col_fmt=None, rkw=None, ckw=None, ldx=None):
+    """col_fmt None: row-wise only.  ldx: row stride of the device copy."""
     M, N = x.shape
-    xd, ldx = to_dev_bf16(x)
+    xd, ldx = to_dev_bf16(x, ldx)
     qr, sr = fp6_blob(M, N, layout)
     qc = sc = None
     if col_fmt is not None:
@@ -122,6 +122,25 @@ def test_fp6_stochastic_rounding(oracle_mod, layout):
     check_fp6(oracle_mod, y, layout, E2M3, E3M2, dict(rk, index_base=5), ck)
     log("fp6 sr 2d layout %d" % layout)
     check_fp6(oracle_mod, x, layout, E2M3, E2M3, dict(rk, use_2d_block=True), dict(ck, use_2d_block=True))
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+@pytest.mark.parametrize("shape", [(97, 200), (160, 256)])
+def test_fp6_dual_mixed_paths(oracle_mod, layout, shape):
+    """One direction through the hardware converter (round to nearest, 1D
+    blocks) and the other through the software encode (stochastic rounding or
+    2D blocks), each way round, from a strided input: the converter's codes
+    wait in registers while the software encode and the staging share its
+    gather buffer."""
+    _require_gpu()
+    x = synth.random_bf16(900 + shape[0], shape, std=0.4)
+    ldx = (shape[1] + 7) // 8 * 8 + 24
+    sr = dict(use_sr=True, seed=21, tensor_id=6, index_base=64)
+    two_d = dict(use_2d_block=True)
+    for rk, ck, what in ((None, sr, "row RNE, column SR"), (sr, None, "row SR, column RNE"),
+                         (two_d, None, "row 2D, column RNE"), (None, two_d, "row RNE, column 2D")):
+        log("fp6 mixed %s %s layout %d" % (what, shape, layout))
+        check_fp6(oracle_mod, x, layout, E2M3, E3M2, rk, ck, ldx=ldx)
 
 
 @pytest.mark.parametrize("fmt", [E2M3, E3M2])
