@@ -398,6 +398,41 @@ __device__ __forceinline__ void pack6(const uint32_t (&k)[8], uint32_t &lo, uint
     lo = k[0] | (k[1] << 6) | (k[2] << 12) | (k[3] << 18) | (k[4] << 24) | (k[5] << 30);
     hi = (k[5] >> 2) | (k[6] << 4) | (k[7] << 10);
 }
+
+// Four six-bit values in bytes 0..3 -> 24 bits (byte i at bits [6i, 6i+6)).
+__device__ __forceinline__ uint32_t pack24(uint32_t x) {
+    const uint32_t y = (x & 0x003F003Fu) | ((x >> 2) & 0x0FC00FC0u);
+    return (y & 0xFFFu) | ((y >> 4) & 0xFFF000u);
+}
+
+// Stochastic MXFP6 codes of eight elements that share the scale byte c, laid
+// out as pack6 does.  The carry form of pack8_sr with the format's shift:
+// with u = |x| 2^(adj-c) clamped at code 31, (u << (24-sh)) + nb(e) carries
+// into bit 24 iff the random byte is below u's 8 bits under the code, so byte
+// 3 of the sum is code6's stochastic code.  xw(e): element e as an fp32
+// pattern; nb(e): 255 minus its random byte in bits 16..23; s0123, s4567:
+// 0xFF in byte i iff element i (i + 4) is negative.  A block holding Inf/NaN
+// (c = 0xFF) gives all codes 0.
+template <typename XW, typename NB>
+__device__ __forceinline__ void pack8_sr6(XW xw, uint32_t c, const Fp6Dir &f, NB nb, uint32_t s0123, uint32_t s4567,
+                                          uint32_t &lo, uint32_t &hi) {
+    const int sh = f.sh, ex = f.adj - (int)c;
+    const uint32_t top = 31u << sh;
+    uint32_t s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t u = __float_as_uint(__builtin_ldexpf(__builtin_fabsf(__uint_as_float(xw(e))), ex));
+        u = u < top ? u : top;
+        s[e] = (u << (24 - sh)) + nb(e);
+    }
+    const uint32_t w0 = __builtin_amdgcn_perm(s[1], s[0], 0x0C0C0703u) | __builtin_amdgcn_perm(s[3], s[2], 0x07030C0Cu) |
+                        (s0123 & 0x20202020u);
+    const uint32_t w1 = __builtin_amdgcn_perm(s[5], s[4], 0x0C0C0703u) | __builtin_amdgcn_perm(s[7], s[6], 0x07030C0Cu) |
+                        (s4567 & 0x20202020u);
+    const uint32_t z0 = pack24(w0), z1 = pack24(w1);
+    lo = c == 0xFFu ? 0u : z0 | (z1 << 24);
+    hi = c == 0xFFu ? 0u : z1 >> 8;
+}
 // 6 bytes at an even LDS byte offset o.
 __device__ __forceinline__ void lds_put6(uint8_t *base, int o, uint32_t lo, uint32_t hi) {
     if ((o & 3) == 0) {
@@ -889,15 +924,19 @@ __global__ __launch_bounds__(256) __attribute__((
             for (int t = 0; t < 8; ++t) {
                 const int64_t i = row0 + 8 * q + t;
                 const uint32_t sc = i < M ? scale_code_emax(a.row.use_2d ? tile_amax : ramax[t], f.emax) : 0u;
-                uint32_t k6[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t x16 = (d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    const uint32_t rb = ROW_SR ? ((e < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (e & 3))) & 0xFFu : 0u;
-                    k6[e] = code6<ROW_SR>(x16, sc, f, rb);
-                }
                 uint32_t lo, hi;
-                pack6(k6, lo, hi);
+                if constexpr (ROW_SR) {
+                    const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
+                    pack8_sr6([&](int e) { return elem_hi(d[t][e >> 1], e & 1); }, sc, f,
+                              [&](int e) { return byte_to_b2(e < 4 ? nlo : nhi, e & 3); },
+                              __builtin_amdgcn_perm(d[t][1], d[t][0], 0x0B0A0908u),
+                              __builtin_amdgcn_perm(d[t][3], d[t][2], 0x0B0A0908u), lo, hi);
+                } else {
+                    uint32_t k6[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) k6[e] = code6<false>((d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, sc, f, 0u);
+                    pack6(k6, lo, hi);
+                }
                 lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
                 if ((c & 3) == 0) s_scale[0][(r_loc0 + t) * 4 + c / 4] = (uint8_t)sc;
             }
@@ -917,15 +956,24 @@ __global__ __launch_bounds__(256) __attribute__((
                 for (int u = 0; u < 8; ++u) {
                     const int64_t j = j0 + u;
                     const uint32_t sc = j < N ? scale_code_emax(a.col.use_2d ? tile_amax : camax[u], f.emax) : 0u;
-                    uint32_t k6[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const uint32_t x16 = (d[t][u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-                        const uint32_t rb = COL_SR ? ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu : 0u;
-                        k6[t] = code6<COL_SR>(x16, sc, f, rb);
-                    }
                     uint32_t lo, hi;
-                    pack6(k6, lo, hi);
+                    const int w = u >> 1, h = u & 1;
+                    if constexpr (COL_SR) {
+                        // signs of rows 0..3 and 4..7 (bit 15 or 31 of each word, by selector)
+                        const uint32_t sa = h ? 0x0C0C0B09u : 0x0C0C0A08u, sb = h ? 0x0B090C0Cu : 0x0A080C0Cu;
+                        const uint32_t s0123 = __builtin_amdgcn_perm(d[1][w], d[0][w], sa) |
+                                               __builtin_amdgcn_perm(d[3][w], d[2][w], sb);
+                        const uint32_t s4567 = __builtin_amdgcn_perm(d[5][w], d[4][w], sa) |
+                                               __builtin_amdgcn_perm(d[7][w], d[6][w], sb);
+                        pack8_sr6([&](int t) { return elem_hi(d[t][w], h); }, sc, f,
+                                  [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); }, s0123,
+                                  s4567, lo, hi);
+                    } else {
+                        uint32_t k6[8];
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) k6[t] = code6<false>((d[t][w] >> (16 * h)) & 0xFFFFu, sc, f, 0u);
+                        pack6(k6, lo, hi);
+                    }
                     // blob row = tile column 8c+u; this wave's 32 rows are bytes [24*wave, 24*wave+24)
                     lds_put6(s_data[1], (8 * c + u) * kLinePitch + 24 * wave + 6 * q, lo, hi);
                     if (q == 0) s_scale[1][(8 * c + u) * 4 + wave] = (uint8_t)sc;

@@ -145,8 +145,9 @@ def test_fp6_dual_mixed_paths(oracle_mod, layout, shape):
 
 @pytest.mark.parametrize("fmt", [E2M3, E3M2])
 def test_fp6_specials_and_every_bf16(oracle_mod, fmt):
-    """Every finite bf16 pattern once (blocks of mixed magnitudes), then Inf/NaN
-    blocks, zeros, signed zeros and subnormal-range values."""
+    """Every finite bf16 pattern once (blocks of mixed magnitudes), rounded to
+    nearest and stochastically in both directions, then Inf/NaN blocks, zeros,
+    signed zeros and subnormal-range values."""
     _require_gpu()
     allbits = np.arange(0, 0x10000, dtype=np.uint16)
     allbits = allbits[((allbits >> 7) & 0xFF) != 0xFF]
@@ -154,6 +155,9 @@ def test_fp6_specials_and_every_bf16(oracle_mod, fmt):
     x = rng.permutation(allbits)[: (allbits.size // 512) * 512].reshape(-1, 512)
     log("fp6 all bf16 fmt %d" % fmt)
     check_fp6(oracle_mod, x, TILED, fmt, fmt)
+    log("fp6 all bf16 fmt %d, stochastic rounding" % fmt)
+    check_fp6(oracle_mod, x, TILED, fmt, fmt, dict(use_sr=True, seed=5, tensor_id=3),
+              dict(use_sr=True, seed=(7 << 33) + 6, tensor_id=4))
     sp = synth.random_bf16(13, (64, 256), std=1.0)
     sp[0, 5] = 0x7F80; sp[1, 40] = 0xFF80; sp[2, 77] = 0x7FC1; sp[3, :] = 0x8000; sp[4, :32] = 0
     sp[5, :] = 0x0001; sp[6, 3] = 0x0080
