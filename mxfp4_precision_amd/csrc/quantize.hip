@@ -290,29 +290,39 @@ __device__ __forceinline__ uint32_t scale_code_f32(uint32_t amax_bits) {
     return e > 2u ? e - 2u : 0u;
 }
 
-// Stochastic code of v: the lower grid index and floor(256 (v-lo)/(hi-lo)),
-// both read off v's bits (exact), round up iff the random byte is below it.
-__device__ __forceinline__ uint32_t code_sr_f32(float v, uint32_t rbyte) {
-    const uint32_t b = __float_as_uint(v);
-    uint32_t lo, t;
-    if (v >= 1.0f) {
-        lo = 2u + 2u * ((b >> 23) - 127u) + ((b >> 22) & 1u);
-        t = (b >> 14) & 0xFFu;
-    } else if (v >= 0.5f) {
-        lo = 1u;
-        t = (b >> 15) & 0xFFu;
-    } else {
-        lo = 0u;
-        t = (uint32_t)__builtin_ldexpf(v, 9);
+// Stochastic E2M1 nibbles of eight fp32 values y (element e in nibble e)
+// that share the scale byte c: pack8_sr's carry form with u taken exactly
+// for fp32 inputs.  With v = |y| 2^(127-c) (below 8 in a finite block), u
+// should be the fp32 bits of v 2^-126 with the bits under 2^-149 cut off: that
+// pattern itself is exact for v >= 1, while below 1 ldexp rounds into the
+// subnormal range (to floor(v 2^23) or one more), so u is the smaller of the
+// pattern and the truncating conversion of v 2^23 (equal for v in [1, 2),
+// larger above), clamped at code 7 by the same three-way minimum.  Signs as
+// in sign_masks, from bit 31 of each value.  A block holding Inf/NaN (c = 0xFF)
+// gives all nibbles 0.
+template <typename NB>
+__device__ __forceinline__ uint32_t pack8_sr_f32(const float (&y)[8], uint32_t c, NB nb) {
+    const auto sgn = [&](int e) { return __float_as_uint(y[e]); };
+    // byte i of even / odd: 0xFF iff element 2i / 2i+1 is negative (selectors
+    // 9, 11: bit 31 of src1, src0), taken first so that each y dies with its sum
+    const uint32_t even = __builtin_amdgcn_perm(sgn(2), sgn(0), 0x0C0C0B09u) | __builtin_amdgcn_perm(sgn(6), sgn(4), 0x0B090C0Cu);
+    const uint32_t odd = __builtin_amdgcn_perm(sgn(3), sgn(1), 0x0C0C0B09u) | __builtin_amdgcn_perm(sgn(7), sgn(5), 0x0B090C0Cu);
+    const int ex = 1 - (int)c;
+    constexpr uint32_t top = 7u << 22;
+    uint32_t s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = __builtin_fabsf(y[e]);
+        const uint32_t pat = __float_as_uint(__builtin_ldexpf(a, ex));
+        const uint32_t fl = (uint32_t)__builtin_ldexpf(a, ex + 149);
+        const uint32_t u = __builtin_elementwise_min(__builtin_elementwise_min(pat, fl), top);
+        s[e] = (u << 2) + nb(e);
     }
-    const uint32_t r = lo + (rbyte < t ? 1u : 0u);
-    return r < 7u ? r : 7u;
-}
-
-__device__ __forceinline__ uint32_t nibble_f32_sr(float y, uint32_t c, uint32_t rbyte) {
-    if (c == 0xFFu) return 0u;
-    const float v = __builtin_ldexpf(__builtin_fabsf(y), 127 - (int)c);
-    return code_sr_f32(v, rbyte) | ((__float_as_uint(y) >> 28) & 8u);
+    const uint32_t lo = __builtin_amdgcn_perm(s[2], s[0], 0x0C0C0703u) | __builtin_amdgcn_perm(s[6], s[4], 0x07030C0Cu) |
+                        (even & 0x08080808u);
+    const uint32_t hi = __builtin_amdgcn_perm(s[3], s[1], 0x0C0C0703u) | __builtin_amdgcn_perm(s[7], s[5], 0x07030C0Cu) |
+                        (odd & 0x08080808u);
+    return c == 0xFFu ? 0u : (lo | (hi << 4));
 }
 
 // Eight fp32 values (element e in nibble e) -> E2M1 codes of y / 2^(c-127), RNE, saturating, sign kept.
@@ -470,10 +480,13 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 // forms without stochastic rounding would take 133 VGPRs (three waves); asked
 // for four they fit 128 with 5 spilled, and the dual quantize of an
 // 18432x12288 activation with its column blob transformed ran 0.164 -> 0.157 ms
-// (same box, three alternations).
+// (same box, three alternations).  Those with stochastic rounding would take
+// 171 (two waves); asked for three they fit 168 with 4 spilled: the dual SR
+// quantize of an 18432x3072 gradient with its column blob transformed 0.079
+// (two waves) -> 0.071 ms.
 template <int ELEM, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
 constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? (ELEM == 6 ? (ROW_SR && COL_SR ? 3 : 2) : 2)
-                          : (RHT && !ROW_SR && !COL_SR ? 4 : 1);
+                          : (RHT ? (!ROW_SR && !COL_SR ? 4 : 3) : 1);
 
 // ELEM 4: MXFP4 (E2M1); ELEM 6: MXFP6 with each direction's format in its
 // options (no Hadamard transform).  Staged blob-row lines hold 128 elements:
@@ -738,11 +751,8 @@ __global__ __launch_bounds__(256) __attribute__((
             const uint32_t sc = i < M ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
             if (ROW_SR) {
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t rb = ((u < 4 ? rrow_lo[t] : rrow_hi[t]) >> (8 * (u & 3))) & 0xFFu;
-                    packed |= nibble_f32_sr(v[u], sc, rb) << (4 * u);
-                }
+                const uint32_t nlo = ~rrow_lo[t], nhi = ~rrow_hi[t];
+                packed = pack8_sr_f32(v, sc, [&](int u) { return byte_to_b2(u < 4 ? nlo : nhi, u & 3); });
             } else {
                 packed = pack8_rne_f32(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
             }
@@ -803,11 +813,7 @@ __global__ __launch_bounds__(256) __attribute__((
             const uint32_t sc = j < N ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
             if (COL_SR) {
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t rb = ((u < 4 ? rcol_lo[t] : rcol_hi[t]) >> (8 * (u & 3))) & 0xFFu;
-                    packed |= nibble_f32_sr(v[t], sc, rb) << (4 * t);
-                }
+                packed = pack8_sr_f32(v, sc, [&](int t) { return byte_to_b2(~(u < 4 ? rcol_lo[t] : rcol_hi[t]), u & 3); });
             } else {
                 packed = pack8_rne_f32(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7], sc);
             }
