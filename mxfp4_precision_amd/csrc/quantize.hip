@@ -205,8 +205,24 @@ __device__ __forceinline__ uint32_t pk_umax(uint32_t a, uint32_t b) {
                               __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a), __builtin_bit_cast(u16x2_t, b)));
 }
 
-__device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
-    return umax(v, (uint32_t)__shfl_xor((int)v, mask, 64));
+// Maximum with lane l^M, without an LDS round trip: l^1 and l^2 through DPP
+// quad permutes ([1,0,3,2], [2,3,0,1]), l^16 and l^32 through the lane-swap
+// instructions, whose two results hold this lane's value and the other
+// lane's in an order that depends on the lane (so both go into the max).
+// Every lane of the wave must be active.  PK: two 16-bit halves (pk_umax).
+template <int M, bool PK>
+__device__ __forceinline__ uint32_t lane_max(uint32_t v) {
+    const auto mx = [](uint32_t a, uint32_t b) { return PK ? pk_umax(a, b) : umax(a, b); };
+    static_assert(M == 1 || M == 2 || M == 16 || M == 32, "lane distance");
+    if constexpr (M == 1) return mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    else if constexpr (M == 2) return mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return mx(r[0], r[1]);
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return mx(r[0], r[1]);
+    }
 }
 
 // ------------------------------------------------------------------ RHT
@@ -478,12 +494,13 @@ __device__ __forceinline__ uint32_t mul_bf16_pair(uint32_t x, uint32_t y) {
 // stochastic it fits three waves (168 VGPRs) without spills, with one
 // direction stochastic (the mixed-options forms) two.  The Hadamard-transform
 // forms without stochastic rounding would take 133 VGPRs (three waves); asked
-// for four they fit 128 with 5 spilled, and the dual quantize of an
-// 18432x12288 activation with its column blob transformed ran 0.164 -> 0.157 ms
-// (same box, three alternations).  Those with stochastic rounding would take
-// 171 (two waves); asked for three they fit 168 with 4 spilled: the dual SR
-// quantize of an 18432x3072 gradient with its column blob transformed 0.079
-// (two waves) -> 0.071 ms.
+// for four they fit 128 (5 spilled before the lane-swap exchanges, none
+// since), and the dual quantize of an 18432x12288 activation with its column
+// blob transformed ran 0.164 -> 0.157 ms (same box, three alternations).
+// Those with stochastic rounding would take 171 (two waves); asked for three
+// they fit 168 (4 spilled before the lane-swap exchanges, none since): the
+// dual SR quantize of an 18432x3072 gradient with its column blob transformed
+// 0.079 (two waves) -> 0.071 ms.
 template <int ELEM, bool DUAL, bool ROW_SR, bool COL_SR, bool RHT>
 constexpr int kMinWaves = (DUAL && (ROW_SR || COL_SR) && !RHT) ? (ELEM == 6 ? (ROW_SR && COL_SR ? 3 : 2) : 2)
                           : (RHT ? (!ROW_SR && !COL_SR ? 4 : 3) : 1);
@@ -667,8 +684,7 @@ __global__ __launch_bounds__(256) __attribute__((
         // rows t and t+1 in the low and high halves
         uint32_t pk = pk_umax(__builtin_amdgcn_perm(rpk[t + 1], rpk[t], 0x05040100u),
                               __builtin_amdgcn_perm(rpk[t + 1], rpk[t], 0x07060302u));
-        pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 1, 64));
-        pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 2, 64));
+        pk = lane_max<2, true>(lane_max<1, true>(pk));
         ramax[t] = pk & 0xFFFFu;
         ramax[t + 1] = pk >> 16;
     }
@@ -678,9 +694,7 @@ __global__ __launch_bounds__(256) __attribute__((
         uint32_t m = 0;
 #pragma unroll
         for (int t = 0; t < 8; ++t) m = umax(m, ramax[t]);
-        m = xor_max(m, 16);
-        m = xor_max(m, 32);
-        tile_amax = m;
+        tile_amax = lane_max<32, false>(lane_max<16, false>(m));
     }
 
     // ---- block amax, column direction: per column u of the lane, 8 rows
@@ -696,8 +710,7 @@ __global__ __launch_bounds__(256) __attribute__((
 #pragma unroll
                 for (int t = 0; t < 8; ++t) pk = pk_umax(pk, d[t][w] & 0x7FFF7FFFu);
             }
-            pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 16, 64));
-            pk = pk_umax(pk, (uint32_t)__shfl_xor((int)pk, 32, 64));
+            pk = lane_max<32, true>(lane_max<16, true>(pk));
             camax[2 * w] = pk & 0xFFFFu;
             camax[2 * w + 1] = pk >> 16;
         }
@@ -745,8 +758,7 @@ __global__ __launch_bounds__(256) __attribute__((
             uint32_t m = 0;
 #pragma unroll
             for (int u = 0; u < 8; ++u) m = umax(m, __float_as_uint(v[u]) & 0x7FFFFFFFu);
-            m = xor_max(m, 1);
-            m = xor_max(m, 2);
+            m = lane_max<2, false>(lane_max<1, false>(m));
             const int64_t i = row0 + 8 * q + t;
             const uint32_t sc = i < M ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
@@ -807,8 +819,7 @@ __global__ __launch_bounds__(256) __attribute__((
             uint32_t m = 0;
 #pragma unroll
             for (int t = 0; t < 8; ++t) m = umax(m, __float_as_uint(v[t]) & 0x7FFFFFFFu);
-            m = xor_max(m, 16);
-            m = xor_max(m, 32);
+            m = lane_max<32, false>(lane_max<16, false>(m));
             const int64_t j = j0 + u;
             const uint32_t sc = j < N ? scale_code_f32(m) : 0u;
             uint32_t packed = 0;
