@@ -376,20 +376,13 @@ __device__ __forceinline__ uint32_t scale_code_emax(uint32_t amax16, uint32_t em
     const uint32_t e = amax16 >> 7;
     return e > emax ? e - emax : 0u;
 }
-// 6-bit code (sign in bit 5) of bf16 x16 under scale byte c.
-template <bool SR>
-__device__ __forceinline__ uint32_t code6(uint32_t x16, uint32_t c, const Fp6Dir &f, uint32_t rbyte) {
+// 6-bit code (sign in bit 5) of bf16 x16 under scale byte c, round to
+// nearest even with saturation (the stochastic code is pack8_sr6's).
+__device__ __forceinline__ uint32_t code6(uint32_t x16, uint32_t c, const Fp6Dir &f) {
     const float xf = __uint_as_float((x16 & 0x7FFFu) << 16);
-    uint32_t u = __float_as_uint(__builtin_ldexpf(xf, f.adj - (int)c));
-    uint32_t code;
-    if constexpr (SR) {
-        const uint32_t top = 31u << f.sh;
-        u = u < top ? u : top;
-        code = (u + ((255u - rbyte) << (f.sh - 8))) >> f.sh;
-    } else {
-        code = (u + (1u << (f.sh - 1)) - 1u + ((u >> f.sh) & 1u)) >> f.sh;
-        code = code < 31u ? code : 31u;
-    }
+    const uint32_t u = __float_as_uint(__builtin_ldexpf(xf, f.adj - (int)c));
+    uint32_t code = (u + (1u << (f.sh - 1)) - 1u + ((u >> f.sh) & 1u)) >> f.sh;
+    code = code < 31u ? code : 31u;
     return c == 0xFFu ? 0u : (code | ((x16 >> 10) & 0x20u));
 }
 // One 32-element block (16 bf16 pairs, element e in half e%2 of w[e/2]) ->
@@ -432,10 +425,12 @@ __device__ __forceinline__ uint32_t pack24(uint32_t x) {
 }
 
 // Stochastic MXFP6 codes of eight elements that share the scale byte c, laid
-// out as pack6 does.  The carry form of pack8_sr with the format's shift:
-// with u = |x| 2^(adj-c) clamped at code 31, (u << (24-sh)) + nb(e) carries
-// into bit 24 iff the random byte is below u's 8 bits under the code, so byte
-// 3 of the sum is code6's stochastic code.  xw(e): element e as an fp32
+// out as pack6 does.  With u = |x| 2^(adj-c) as fp32 bits clamped at code 31
+// (bits [sh, sh+5) hold the lower grid point's code, the 8 bits under them
+// floor(256 (v-lo)/(hi-lo))), the code rounds up iff the random byte is
+// below those 8 bits: the carry form of pack8_sr with the format's shift,
+// (u << (24-sh)) + nb(e) carrying into bit 24, so byte 3 of the sum is the
+// code.  xw(e): element e as an fp32
 // pattern; nb(e): 255 minus its random byte in bits 16..23; s0123, s4567:
 // 0xFF in byte i iff element i (i + 4) is negative.  A block holding Inf/NaN
 // (c = 0xFF) gives all codes 0.
@@ -951,7 +946,7 @@ __global__ __launch_bounds__(256) __attribute__((
                 } else {
                     uint32_t k6[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) k6[e] = code6<false>((d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, sc, f, 0u);
+                    for (int e = 0; e < 8; ++e) k6[e] = code6((d[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, sc, f);
                     pack6(k6, lo, hi);
                 }
                 lds_put6(s_data[0], (r_loc0 + t) * kLinePitch + 6 * c, lo, hi);
@@ -988,7 +983,7 @@ __global__ __launch_bounds__(256) __attribute__((
                     } else {
                         uint32_t k6[8];
 #pragma unroll
-                        for (int t = 0; t < 8; ++t) k6[t] = code6<false>((d[t][w] >> (16 * h)) & 0xFFFFu, sc, f, 0u);
+                        for (int t = 0; t < 8; ++t) k6[t] = code6((d[t][w] >> (16 * h)) & 0xFFFFu, sc, f);
                         pack6(k6, lo, hi);
                     }
                     // blob row = tile column 8c+u; this wave's 32 rows are bytes [24*wave, 24*wave+24)
