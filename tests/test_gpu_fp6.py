@@ -344,3 +344,38 @@ def test_fp6_e3m2_group_truncation(oracle_mod):
     assert (d[~same] == 784.0 + 2.0 ** -8).all(), d[~same][d[~same] != 784.0 + 2.0 ** -8][:5]
     log("e3m2 group truncation: %d same-group pairs lost the small product, %d others kept it"
         % (int(same.sum()), int((~same).sum())))
+
+
+_FP6_MODES = {"rne": {}, "rne2d": {"use_2d_block": True}, "sr": {"use_sr": True}, "sr2d": {"use_sr": True, "use_2d_block": True}}
+
+
+def _fp6_kw(mode, rng):
+    kw = dict(_FP6_MODES[mode])
+    if kw.get("use_sr"):
+        kw.update(seed=int(rng.integers(0, 2 ** 63)), tensor_id=int(rng.integers(0, 2 ** 32)),
+                  index_base=int(rng.integers(0, 2 ** 40)))
+    return kw or None
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_fp6_option_matrix(oracle_mod, layout):
+    """Every pair of per-direction modes (round to nearest or stochastic, 1D or
+    32x32 blocks; 16 pairs, every dual kernel instance, the converter path
+    beside each software path) and each mode row-wise only, with the two
+    directions' formats drawn per case, seeded ragged shapes, strided input and
+    non-finite values in half the cases; every byte against the oracle."""
+    _require_gpu()
+    rng = np.random.Generator(np.random.PCG64(97 + layout))
+    pairs = [(r, c) for r in _FP6_MODES for c in _FP6_MODES] + [(r, None) for r in _FP6_MODES]
+    for case, (rmode, cmode) in enumerate(pairs):
+        M, N = int(rng.integers(1, 300)), int(rng.integers(1, 420))
+        x = synth.random_bf16(2000 + case, (M, N), std=float(rng.choice([1e-3, 1.0, 50.0])))
+        if case % 2:
+            for bits in (0x7F80, 0xFFC0, 0xFF80):
+                x[int(rng.integers(0, M)), int(rng.integers(0, N))] = bits
+        ldx = (N + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+        rf = int(rng.choice([E2M3, E3M2]))
+        cf = None if cmode is None else int(rng.choice([E2M3, E3M2]))
+        rkw, ckw = _fp6_kw(rmode, rng), (None if cmode is None else _fp6_kw(cmode, rng))
+        log("fp6 matrix %s/%s fmts %s/%s layout %d shape %s ldx %d" % (rmode, cmode, rf, cf, layout, x.shape, ldx))
+        check_fp6(oracle_mod, x, layout, rf, cf, rkw, ckw, ldx=ldx)

@@ -518,3 +518,80 @@ def test_tall_input_spans_launches(oracle_mod):
     for r in (256, 4_000_000, 65535 * 128 + 128, 65538 * 128 - 129):
         assert not host(qr[r]).any() and not host(sr[r]).any(), r
     assert not host(qc[:, 128:1_000_000]).any() and not host(sc[:, 8:60_000]).any()
+
+
+# Per-direction option sets: every kernel instance of the MXFP4 quantizer
+# (round-to-nearest or stochastic rounding per direction, with or without the
+# Hadamard transform) and the 32x32 block option, which is a run-time choice.
+_MODES = {
+    "rne": dict(),
+    "rne2d": dict(use_2d=True),
+    "sr": dict(use_sr=True),
+    "sr2d": dict(use_sr=True, use_2d=True),
+    "rht": dict(rht=True),
+    "rhtsr": dict(rht=True, use_sr=True),
+}
+
+
+def _mode_kwargs(mode, rng):
+    """(device options, oracle keywords) for one direction's mode, with seeded
+    random seeds, tensor ids, index bases and transform seeds."""
+    m = _MODES[mode]
+    kw = {}
+    if m.get("use_2d"):
+        kw["use_2d"] = True
+    if m.get("use_sr"):
+        kw.update(use_sr=True, seed=int(rng.integers(0, 2 ** 63)), tensor_id=int(rng.integers(0, 2 ** 32)),
+                  index_base=int(rng.integers(0, 2 ** 40)))
+    if m.get("rht"):
+        kw["rht"] = int(rng.integers(1, 2 ** 32))
+    dev = mx.quant_opts(use_2d_block=kw.get("use_2d", False), use_sr=kw.get("use_sr", False),
+                        seed=kw.get("seed", 0), tensor_id=kw.get("tensor_id", 0),
+                        index_base=kw.get("index_base", 0), rht=kw.get("rht", 0))
+    return dev, kw
+
+
+def _matrix_input(rng, case):
+    M, N = int(rng.integers(1, 300)), int(rng.integers(1, 420))
+    x = synth.random_bf16(1000 + case, (M, N), std=float(rng.choice([1e-3, 1.0, 50.0])))
+    if case % 2:
+        # non-finite values in some blocks: the waves holding them take the
+        # general encode, the others the all-finite one
+        for bits in (0x7F80, 0xFFC0, 0xFF80):
+            x[int(rng.integers(0, M)), int(rng.integers(0, N))] = bits
+    if case % 3 == 0 and M >= 32 and N >= 32:
+        x[:32, :32] = 0                 # an all-zero block in both directions
+    ldx = (N + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+    return x, ldx
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_option_matrix_rowwise(oracle_mod, layout):
+    """Row-wise quantize under every per-direction mode, on seeded ragged shapes
+    with strided input and non-finite values in half the cases, bit-exact."""
+    _require_gpu()
+    rng = np.random.Generator(np.random.PCG64(71 + layout))
+    for case, mode in enumerate(_MODES):
+        x, ldx = _matrix_input(rng, case)
+        dev, kw = _mode_kwargs(mode, rng)
+        log("row matrix %s layout %d shape %s ldx %d" % (mode, layout, x.shape, ldx))
+        check_rowwise(oracle_mod, x, layout, dev, kw, ldx=ldx)
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_option_matrix_dual(oracle_mod, layout):
+    """Dual quantize under every pair of per-direction modes (36 pairs: every
+    dual kernel instance, each 32x32-block and transform combination across
+    the two directions), seeded ragged shapes, strided input, non-finite values
+    in half the cases; both blobs bit-exact."""
+    _require_gpu()
+    rng = np.random.Generator(np.random.PCG64(83 + layout))
+    case = 0
+    for rmode in _MODES:
+        for cmode in _MODES:
+            x, ldx = _matrix_input(rng, case)
+            rdev, rkw = _mode_kwargs(rmode, rng)
+            cdev, ckw = _mode_kwargs(cmode, rng)
+            log("dual matrix %s/%s layout %d shape %s ldx %d" % (rmode, cmode, layout, x.shape, ldx))
+            check_dual(oracle_mod, x, layout, rdev, cdev, rkw, ckw, ldx=ldx)
+            case += 1
