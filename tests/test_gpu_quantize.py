@@ -595,3 +595,23 @@ def test_option_matrix_dual(oracle_mod, layout):
             log("dual matrix %s/%s layout %d shape %s ldx %d" % (rmode, cmode, layout, x.shape, ldx))
             check_dual(oracle_mod, x, layout, rdev, cdev, rkw, ckw, ldx=ldx)
             case += 1
+
+
+@pytest.mark.parametrize("layout", [CANON, TILED])
+def test_option_matrix_multiply_prologue(oracle_mod, layout):
+    """Quantizer prologue under every pair of per-direction modes without the
+    transform (16 pairs, every dual prologue instance, stochastic rounding in
+    one direction only included) and each mode row-wise only, seeded ragged
+    shapes, strided inputs, non-finite factors in half the cases; bit-exact."""
+    _require_gpu()
+    rng = np.random.Generator(np.random.PCG64(89 + layout))
+    modes = [m for m in _MODES if not _MODES[m].get("rht")]
+    pairs = [(r, c) for r in modes for c in modes] + [(r, None) for r in modes]
+    for case, (rmode, cmode) in enumerate(pairs):
+        x, ldx = _matrix_input(rng, case)
+        g = synth.random_bf16(3000 + case, x.shape, std=float(rng.choice([0.5, 4.0])))
+        rdev, rkw = _mode_kwargs(rmode, rng)
+        cdev, ckw = _mode_kwargs(cmode or "rne", rng)
+        log("mul matrix %s/%s layout %d shape %s ldx %d" % (rmode, cmode, layout, x.shape, ldx))
+        check_mul(oracle_mod, x, g, layout, rdev, cdev if cmode else None, rkw, ckw if cmode else None,
+                  dual=cmode is not None, ldx=ldx)
