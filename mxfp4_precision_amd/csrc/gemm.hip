@@ -778,14 +778,12 @@ __host__ __device__ constexpr int epi_stores() {
 }
 
 template <class C>
-__device__ __forceinline__ void store_tile_stream(const Ctx<C, true> &c, v16f (&acc)[C::kMB][C::kMA], int tm, int tn,
-                                                  int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
-                                                  int lane) {
+__device__ __forceinline__ void store_tile_private(v16f (&acc)[C::kMB][C::kMA], int tm, int tn, int M, int N,
+                                                   __amdgpu_buffer_rsrc_t rC, int ldc, int wave, int lane) {
     static_assert(C::kStages == 4, "the stream epilogue stages C through stage 3");
     constexpr int kSlotBytes = 32 * C::kWN * 2;   // 4 KB per wave
     static_assert(kSlotBytes * C::kWaves == C::kStageBytes, "one slot per wave fills stage 3");
     static_assert(C::kWN == 64, "8 lanes per 128-byte row");
-    dma_part<C, 2, 2, 1, 0>(c, c.kstream + 2);
     const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
     const int lrow = lane & 31, lhi = lane >> 5;
     const int row_w = tm * C::kBM + C::kWM * wm;                  // first C row of this wave's block
@@ -813,6 +811,14 @@ __device__ __forceinline__ void store_tile_stream(const Ctx<C, true> &c, v16f (&
             __builtin_amdgcn_raw_buffer_store_b128(v, rC, off, 0, kCachePolicyNT);
         }
     }
+}
+
+template <class C>
+__device__ __forceinline__ void store_tile_stream(const Ctx<C, true> &c, v16f (&acc)[C::kMB][C::kMA], int tm, int tn,
+                                                  int M, int N, __amdgpu_buffer_rsrc_t rC, int ldc, int wave,
+                                                  int lane) {
+    dma_part<C, 2, 2, 1, 0>(c, c.kstream + 2);
+    store_tile_private<C>(acc, tm, tn, M, N, rC, ldc, wave, lane);
 }
 
 // ------------------------------------------------------------ kernels
@@ -1093,12 +1099,18 @@ __global__ __launch_bounds__(C::kThreads) void gemm_stream_kernel(int M, int N, 
 // configurations give the atom and DMA counts: the same workgroup shapes
 // (256x256 main tiles; a last round that would fill at most half of the CUs
 // as 128x128 tiles, as two K groups summed through LDS when those give at
-// most one tile per CU), wave tiles, XCD order, LDS stages and epilogue; a
-// stage holds one step, step k+3 is in flight while step k computes.
+// most one tile per CU), wave tiles, XCD order, LDS stages and epilogues
+// (for bf16 output and short K, a persistent form with the wave-private
+// epilogue of the block-scaled stream kernel); a stage holds one step, step
+// k+3 is in flight while step k computes.
 template <class S>
 using Fp8Cfg = Cfg<Fp4Fmt, S>;
 constexpr int kFmtBf8 = 1;          // MFMA f8f6f4 format code for E5M2
 constexpr int kUnitScale = 127;     // E8M0 2^0
+// Longest K of the persistent FP8 form: same box, bit-identical, the fc2
+// dgrad (48 steps per tile) 0.548 -> 0.520 ms, the wgrad (288 steps, this K)
+// a tie; longer K is not measured, so it keeps one tile per workgroup.
+constexpr int64_t kFp8StreamKMax = 288 * 64;
 
 template <int S, int G, class C>
 __device__ __forceinline__ void fp8_dma_step(const Ctx<C, false> &c, int64_t k) {
@@ -1114,13 +1126,18 @@ __device__ __forceinline__ void fp8_dma_step(const Ctx<C, false> &c, int64_t k) 
     }
 }
 
-template <class C, int S, int G>
-__device__ __forceinline__ void fp8_step(const Ctx<C, false> &c, int64_t k, v16f (&acc)[C::kMB][C::kMA],
+// One k-step from stage S: wait until at most W of this wave's vector-memory
+// instructions are outstanding (the step's own DMAs then have landed: by
+// default the next two steps' DMAs may still be in flight), read the
+// operands, issue the DMA of step kd of context cd into stage (S + 3) % 4,
+// then the MFMAs.
+template <class C, int S, int G, int W = 2 * C::kLoLoads>
+__device__ __forceinline__ void fp8_step(const Ctx<C, false> &cd, int64_t kd, v16f (&acc)[C::kMB][C::kMA],
                                          int frag_off, int a_atom0, int b_atom0) {
-    // step k landed for every wave (only steps k+1, k+2 may still be in flight),
-    // and every wave is done reading step k-1's stage
+    // this step's data landed for every wave, and every wave is done reading
+    // the previous step's stage
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * C::kLoLoads) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(W) : "memory");
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *st = stage_buf<C, S, G>() + frag_off;
     uint4 bv[C::kMB][2], av[C::kMA][2];
@@ -1134,7 +1151,7 @@ __device__ __forceinline__ void fp8_step(const Ctx<C, false> &c, int64_t k, v16f
         av[j][0] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024);
         av[j][1] = *reinterpret_cast<const uint4 *>(st + (a_atom0 + 2 * j) * 1024 + 256);
     }
-    fp8_dma_step<(S + 3) & 3, G>(c, k + 3);
+    fp8_dma_step<(S + 3) & 3, G>(cd, kd);
 #pragma unroll
     for (int i = 0; i < C::kMB; ++i) {
         const v8i bop = {(int)bv[i][0].x, (int)bv[i][0].y, (int)bv[i][0].z, (int)bv[i][0].w,
@@ -1166,10 +1183,10 @@ __device__ __forceinline__ void fp8_run(const Ctx<C, false> &c, v16f (&acc)[C::k
     fp8_dma_step<1, G>(c, 1);
     fp8_dma_step<2, G>(c, 2);
     for (int64_t k = 0; k < steps; k += 4) {
-        fp8_step<C, 0, G>(c, k, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<C, 1, G>(c, k + 1, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<C, 2, G>(c, k + 2, acc, frag_off, a_atom0, b_atom0);
-        fp8_step<C, 3, G>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 0, G>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 1, G>(c, k + 4, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 2, G>(c, k + 5, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 3, G>(c, k + 6, acc, frag_off, a_atom0, b_atom0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -1270,6 +1287,124 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(int64_t M, int64_
 #pragma unroll
         for (int j = 0; j < C::kMA; ++j) acc[i][j] *= scale;
     store_tile<C, OUT_BF16>(acc, tm, tn, M, N, Cout, ldc, group, wave, wave_all, lane);
+}
+
+// Persistent form of the 256x256 FP8 kernel (bf16 output), as the
+// block-scaled stream kernel: one workgroup per CU runs tiles b, b +
+// gridDim.x, ... of the first `tiles` of the tile order as one stream of
+// k-steps.  A tile is `steps` = ksteps rounded up to a multiple of 4 steps
+// (at least 8), so every tile starts at stage 0; its last three steps issue
+// the DMAs of the next tile's first three, and its epilogue stages C through
+// stage 3 (the wave-private epilogue) while those land.  The stores are then
+// in flight under the next tile's first steps: the first three waits count
+// past the epi_stores() stores, the fourth needs them done.  Needs N % 8 == 0
+// and M * ldc * 2 < 2^31 (32-bit store offsets).
+template <class C>
+__global__ __launch_bounds__(C::kThreads) void gemm_fp8_stream_kernel(int M, int N, int K_pad, int tiles_m,
+                                                                      int tiles_n, int group_m, int tiles,
+                                                                      const uint8_t *__restrict__ A,
+                                                                      const float *__restrict__ a_scale_inv,
+                                                                      const uint8_t *__restrict__ B,
+                                                                      const float *__restrict__ b_scale_inv,
+                                                                      void *__restrict__ Cout, int ldc) {
+    static_assert(C::kKG == 1 && C::kBM == 256, "stream form: main tiles");
+    constexpr int kWaitStores = 2 * C::kLoLoads + epi_stores<C>();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % C::kWavesM, wn = wave / C::kWavesM;
+    const int P = gridDim.x;
+    const int ksteps = K_pad / 64;
+    const int steps = 4 * ((ksteps + 3) / 4);
+    const int nGA = (M + 15) / 16, nGB = (N + 15) / 16;
+    Ctx<C, false> c;
+    c.ksteps = ksteps;
+    c.kgroups = 0;
+    c.wave = wave;
+    c.lane16 = lane * 16;
+    c.lane4 = 0;
+    c.rA = make_rsrc(A, (int64_t)nGA * ksteps * 1024);
+    c.rB = make_rsrc(B, (int64_t)nGB * ksteps * 1024);
+    Ctx<C, false> cn = c;   // the next tile's DMAs (ksteps 0: none left, out-of-range loads of zeros)
+    const __amdgpu_buffer_rsrc_t rC = make_rsrc(Cout, (int64_t)M * ldc * 2);
+    // byte offsets of this wave's unit rows (16-row groups, clamped to the last) at step 0
+    const auto unit_rows = [&](int tm, int tn, int(&lo)[C::kLoLoads]) {
+#pragma unroll
+        for (int r = 0; r < C::kLoLoads; ++r) {
+            const int a = C::kWaves * r + wave;
+            const bool isA = a < C::kGA;
+            const int g = isA ? tm * C::kGA + a : tn * C::kGB + (a - C::kGA);
+            const int gmax = (isA ? nGA : nGB) - 1;
+            lo[r] = (g < gmax ? g : gmax) * ksteps * 1024;
+        }
+    };
+    int vb = blockIdx.x;
+    int tm, tn, tm_next = 0, tn_next = 0;
+    tile_of(vb, tiles, tiles_m, tiles_n, group_m, tm, tn);
+    unit_rows(tm, tn, c.lo_row);
+    cn.ksteps = 0;
+    if (vb + P < tiles) {
+        tile_of(vb + P, tiles, tiles_m, tiles_n, group_m, tm_next, tn_next);
+        unit_rows(tm_next, tn_next, cn.lo_row);
+        cn.ksteps = ksteps;
+    }
+    const float scale = a_scale_inv[0] * b_scale_inv[0];
+    const int lrow = lane & 31, lhi = lane >> 5;
+    const int frag_off = ((lrow >> 4) * 1024) + ((lrow & 15) + 32 * lhi) * 16;
+    const int a_atom0 = wm * C::kTA, b_atom0 = C::kGA + wn * C::kTB;
+
+    fp8_dma_step<0, 0>(c, 0);
+    fp8_dma_step<1, 0>(c, 1);
+    fp8_dma_step<2, 0>(c, 2);
+    v16f acc[C::kMB][C::kMA];
+    bool first = true;
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
+        // first period: steps 0-2 count past the previous tile's stores
+        if (first) {
+            fp8_step<C, 0, 0>(c, 3, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 1, 0>(c, 4, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 2, 0>(c, 5, acc, frag_off, a_atom0, b_atom0);
+        } else {
+            fp8_step<C, 0, 0, kWaitStores>(c, 3, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 1, 0, kWaitStores>(c, 4, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 2, 0, kWaitStores>(c, 5, acc, frag_off, a_atom0, b_atom0);
+        }
+        fp8_step<C, 3, 0>(c, 6, acc, frag_off, a_atom0, b_atom0);
+        for (int k = 4; k < steps - 4; k += 4) {
+            fp8_step<C, 0, 0>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 1, 0>(c, k + 4, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 2, 0>(c, k + 5, acc, frag_off, a_atom0, b_atom0);
+            fp8_step<C, 3, 0>(c, k + 6, acc, frag_off, a_atom0, b_atom0);
+        }
+        // last period: its last three steps fetch the next tile's first three
+        fp8_step<C, 0, 0>(c, steps - 1, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 1, 0>(cn, 0, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 2, 0>(cn, 1, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 3, 0>(cn, 2, acc, frag_off, a_atom0, b_atom0);
+#pragma unroll
+        for (int i = 0; i < C::kMB; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kMA; ++j) acc[i][j] *= scale;
+        store_tile_private<C>(acc, tm, tn, M, N, rC, ldc, wave, lane);
+        vb += P;
+        if (vb >= tiles) break;
+        first = false;
+        tm = tm_next;
+        tn = tn_next;
+#pragma unroll
+        for (int r = 0; r < C::kLoLoads; ++r) c.lo_row[r] = cn.lo_row[r];
+        cn.ksteps = 0;
+        if (vb + P < tiles) {
+            tile_of(vb + P, tiles, tiles_m, tiles_n, group_m, tm_next, tn_next);
+            unit_rows(tm_next, tn_next, cn.lo_row);
+            cn.ksteps = ksteps;
+        }
+    }
+    // drain the stores and the trailing (out-of-range) DMAs
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // K == 0: C[i][j] = 0, or bias[j] (bf16 bits; exact in either output type).
@@ -1442,9 +1577,18 @@ hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, co
     // a last round that would fill at most half of the CUs goes to the tail tiles
     const int tail = (cus > 0 && tiles > cus && tiles % cus <= cus / 2) ? tiles % cus : 0;
     const bool bf = out_dtype == MX_BF16;
-    auto main_kernel = bf ? gemm_fp8_kernel<CM, true> : gemm_fp8_kernel<CM, false>;
-    hipLaunchKernelGGL(main_kernel, dim3((unsigned)(tiles - tail)), dim3(CM::kThreads), 0, stream, M, N, K_pad,
-                       tiles_m, tiles_n, group_m, 0, A, a_scale_inv, B, b_scale_inv, C, ldc);
+    // several tiles per workgroup (persistent form): bf16 output, 8 to 288
+    // steps per tile, more main tiles than CUs
+    if (bf && N % 8 == 0 && M * ldc * 2 < (int64_t(1) << 31) && K_pad >= 8 * 64 && K_pad <= kFp8StreamKMax &&
+        cus > 0 && tiles - tail > cus) {
+        hipLaunchKernelGGL(gemm_fp8_stream_kernel<CM>, dim3((unsigned)cus), dim3(CM::kThreads), 0, stream, (int)M,
+                           (int)N, (int)K_pad, tiles_m, tiles_n, group_m, tiles - tail, A, a_scale_inv, B, b_scale_inv,
+                           C, (int)ldc);
+    } else {
+        auto main_kernel = bf ? gemm_fp8_kernel<CM, true> : gemm_fp8_kernel<CM, false>;
+        hipLaunchKernelGGL(main_kernel, dim3((unsigned)(tiles - tail)), dim3(CM::kThreads), 0, stream, M, N, K_pad,
+                           tiles_m, tiles_n, group_m, 0, A, a_scale_inv, B, b_scale_inv, C, ldc);
+    }
     if (!tail) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

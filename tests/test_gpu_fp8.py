@@ -210,6 +210,38 @@ def test_fp8_gemm_tail_tiles_every_entry_of_tail_rows(oracle_mod, K):
     assert np.array_equal(outs[mx.MX_BF16].view(np.uint16), _rne_bf16_bits(outs[mx.MX_F32]))
 
 
+@pytest.mark.parametrize("K", [200, 700, 1100, 18432, 18560])
+def test_fp8_gemm_several_tiles_per_workgroup(oracle_mod, K):
+    """5020x7640 output = 20x30 = 600 tiles of 256x256: two whole rounds on
+    256 CUs, where each persistent workgroup runs two tiles as one stream of
+    steps (the first tile's last three steps fetch the second's first three,
+    its stores drain under the second's first steps), plus an 88-tile tail;
+    ragged last row and column of tiles.  K 200 (4 steps: below the 8 the
+    persistent form needs, so one tile per workgroup), 700 (12 steps), 1100
+    (18 steps run as 20, the last two past K), 18432 (288 steps, the longest
+    K the persistent form takes) and 18560 (one tile per workgroup again).
+    Sampled entries against the oracle; the bf16 output (persistent kernel
+    where it applies) equal to the round-to-nearest-even of the fp32 output
+    (one tile per workgroup), which accumulates in the same order; an
+    ldc-strided call leaves everything past column N untouched."""
+    _require_gpu()
+    M, N = 5020, 7640
+    a = synth.random_bf16(301 + K, (M, K), std=1.0)
+    b = synth.random_bf16(302 + K, (N, K), std=0.05)
+    log("fp8 several tiles per workgroup %dx%dx%d" % (M, N, K))
+    outs = run_gemm(oracle_mod, a, b, nsample=8192, seed=K, what="fp8 stream %d" % K)
+    cb = outs[mx.MX_BF16].view(np.uint16)
+    assert np.array_equal(cb, _rne_bf16_bits(outs[mx.MX_F32]))
+    qa, _, ia = quant(a, TILED, True, False)
+    qb, _, ib = quant(b, TILED, True, False)
+    ldc = N + 24
+    C = torch.full((M, ldc), -1, dtype=torch.int16, device="cuda")
+    mx.mx_gemm_f8_tw(0, 1, M, N, K, qa, ia[1:], qb, ib[1:], TILED, mx.MX_BF16, C, ldc)
+    Cp = host(C).view(np.uint16)
+    assert np.array_equal(Cp[:, :N], cb)
+    assert (Cp[:, N:] == 0xFFFF).all()
+
+
 def test_fp8_hybrid_backward_fc2_sampled(oracle_mod):
     """The hybrid backward at the fc2 shape (18432 tokens, 12288 -> 3072): dgrad
     dY . W and wgrad dY^T . X from tensorwise E5M2 operands, sampled entries."""
