@@ -1356,22 +1356,17 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_stream_kernel(int M, int
     fp8_dma_step<1, 0>(c, 1);
     fp8_dma_step<2, 0>(c, 2);
     v16f acc[C::kMB][C::kMA];
-    bool first = true;
-    for (;;) {
+    // one tile of the stream; FIRST: no stores of a previous tile are in flight
+    const auto run = [&](auto first) {
 #pragma unroll
         for (int i = 0; i < C::kMB; ++i)
 #pragma unroll
             for (int j = 0; j < C::kMA; ++j) acc[i][j] = v16f{};
         // first period: steps 0-2 count past the previous tile's stores
-        if (first) {
-            fp8_step<C, 0, 0>(c, 3, acc, frag_off, a_atom0, b_atom0);
-            fp8_step<C, 1, 0>(c, 4, acc, frag_off, a_atom0, b_atom0);
-            fp8_step<C, 2, 0>(c, 5, acc, frag_off, a_atom0, b_atom0);
-        } else {
-            fp8_step<C, 0, 0, kWaitStores>(c, 3, acc, frag_off, a_atom0, b_atom0);
-            fp8_step<C, 1, 0, kWaitStores>(c, 4, acc, frag_off, a_atom0, b_atom0);
-            fp8_step<C, 2, 0, kWaitStores>(c, 5, acc, frag_off, a_atom0, b_atom0);
-        }
+        constexpr int kW0 = decltype(first)::value ? 2 * C::kLoLoads : kWaitStores;
+        fp8_step<C, 0, 0, kW0>(c, 3, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 1, 0, kW0>(c, 4, acc, frag_off, a_atom0, b_atom0);
+        fp8_step<C, 2, 0, kW0>(c, 5, acc, frag_off, a_atom0, b_atom0);
         fp8_step<C, 3, 0>(c, 6, acc, frag_off, a_atom0, b_atom0);
         for (int k = 4; k < steps - 4; k += 4) {
             fp8_step<C, 0, 0>(c, k + 3, acc, frag_off, a_atom0, b_atom0);
@@ -1389,9 +1384,13 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_stream_kernel(int M, int
 #pragma unroll
             for (int j = 0; j < C::kMA; ++j) acc[i][j] *= scale;
         store_tile_private<C>(acc, tm, tn, M, N, rC, ldc, wave, lane);
+    };
+    // the first tile is peeled off the loop, so that every entry of the loop
+    // has the previous tile's stores in flight
+    run(std::true_type{});
+    for (;;) {
         vb += P;
         if (vb >= tiles) break;
-        first = false;
         tm = tm_next;
         tn = tn_next;
 #pragma unroll
@@ -1402,6 +1401,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_stream_kernel(int M, int
             unit_rows(tm_next, tn_next, cn.lo_row);
             cn.ksteps = ksteps;
         }
+        run(std::false_type{});
     }
     // drain the stores and the trailing (out-of-range) DMAs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
